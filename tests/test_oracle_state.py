@@ -1,0 +1,276 @@
+"""Pins for the oracle's allocator, segment, eviction, ladder and classify
+rules (CPU only).
+
+Method passages: ThinKV technical summary, "Methodologie" > TBE bullet
+(segment-granular progressive eviction) and Continuous Thinking bullet
+(evicted slots reused in place through a block table with thought type,
+start index and eviction mask); lay summary "Astuce B" (a small safety net of
+Transition thoughts is always kept).  The dict-based spec in spec_allocator.py
+restates the rules independently; brute force over short op sequences on a
+tiny pool must agree with the oracle after every call.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import spec_allocator as S
+
+BS = 16
+
+
+def logical(oc):
+    """Oracle arrays -> the spec's representation."""
+    L = oc.L
+    seqs = {}
+    for s in range(L.max_seqs):
+        q = oc.seq_record(s)
+        if not q.any():
+            continue
+        rec = {"blocks": [], "stack": [], "segs": [], "length": int(q[7]), "nret": int(q[8]), "napp": int(q[9])}
+        for c in range(3):
+            bt = oc.bufs["btab"][(s * 3 + c) * L.max_blocks_per_seq:][:int(q[c])]
+            st = oc.bufs["sstk"][(s * 3 + c) * L.max_blocks_per_seq * BS:][:int(q[3 + c])]
+            rec["blocks"].append([int(b) for b in bt]); rec["stack"].append([int(x) for x in st])
+        for g in oc.segments(s):
+            rec["segs"].append({"type": int(g[0]), "bits": int(g[1]), "first": int(g[2]), "last": int(g[3]),
+                                "ntot": int(g[4]), "nret": int(g[5])})
+        seqs[s] = rec
+    blocks, slots, free = {}, {}, []
+    for c in range(3):
+        P = L.pool_blocks[c]
+        cnt = int(oc.bufs["hdr"][c])
+        free.append([int(b) for b in oc.bufs[f"free{c}"][:cnt][::-1]])
+        blk = oc.bufs[f"blk{c}"].reshape(P, 4)
+        for b in range(P):
+            mask, mp, owner = int(blk[b, 0]), int(blk[b, 1]), int(blk[b, 2])
+            if owner < 0:
+                assert mask == 0 and mp == -1
+                continue
+            valid = {t for t in range(BS) if (mask >> t) & 1}
+            blocks[(c, b)] = {"valid": valid, "maxpos": mp, "owner": owner}
+            for t in valid:
+                sl = b * BS + t
+                slots[(c, sl)] = tuple(int(x) for x in oc.bufs[f"slot{c}"][sl * 2:sl * 2 + 2])
+    return seqs, blocks, slots, free
+
+
+def spec_view(sp):
+    seqs = {s: {"blocks": q["blocks"], "stack": q["stack"], "segs": q["segs"], "length": q["length"],
+                "nret": q["nret"], "napp": q["napp"]} for s, q in sp.seqs.items()
+            if any(q["blocks"]) or q["segs"] or q["length"] or q["nret"] or q["napp"]}
+    slots = {}
+    for (c, b), rec in sp.block.items():
+        for t in rec["valid"]:
+            slots[(c, b * BS + t)] = sp.slot[(c, b * BS + t)]
+    return seqs, sp.block, slots, sp.free
+
+
+def check_invariants(oc):
+    seqs, blocks, slots, free = logical(oc)
+    for s, q in seqs.items():
+        n_valid = 0
+        for c in range(3):
+            owned = set()
+            for b in q["blocks"][c]:
+                assert blocks[(c, b)]["owner"] == s
+                owned |= {b * BS + t for t in range(BS)}
+            valid = {b * BS + t for b in q["blocks"][c] for t in blocks[(c, b)]["valid"]}
+            stack = q["stack"][c]
+            assert len(set(stack)) == len(stack)          # no slot twice on the stack
+            assert set(stack) | valid == owned and not (set(stack) & valid)
+            n_valid += len(valid)
+            for sl in valid:
+                seg = q["segs"][slots[(c, sl)][1]]
+                assert {8: 0, 4: 1, 2: 2}[seg["bits"]] == c  # segment bits match slot class
+        assert n_valid == q["nret"] == sum(g["nret"] for g in q["segs"])
+    all_blocks = [(c, b) for q in seqs.values() for c in range(3) for b in q["blocks"][c]]
+    assert len(all_blocks) == len(set(all_blocks))
+    for c in range(3):
+        in_tables = {b for (cc, b) in all_blocks if cc == c}
+        assert not (in_tables & set(free[c])) and len(in_tables) + len(free[c]) == oc.L.pool_blocks[c]
+
+
+def compare(oc, sp):
+    a = logical(oc); b = spec_view(sp)
+    assert a[0] == b[0], "sequence records"
+    assert {k: (v["valid"], v["maxpos"], v["owner"]) for k, v in a[1].items()} == \
+           {k: (v["valid"], v["maxpos"], v["owner"]) for k, v in b[1].items()}, "block records"
+    assert a[2] == b[2], "slot records"
+    assert a[3] == b[3], "free stacks"
+    f, m, n = oc.error()
+    assert (f, m, n) == (sp.flags, sp.minseq, sp.count), "error word"
+
+
+def random_program(rng, max_seqs, n_ops):
+    prog = []
+    length = [0] * max_seqs
+    nseg = [0] * max_seqs
+    last_t = [0] * max_seqs
+    for _ in range(n_ops):
+        r = rng.random()
+        if r < 0.55:
+            toks = []
+            for _ in range(int(rng.integers(1, 24))):
+                s = int(rng.integers(0, max_seqs + (1 if rng.random() < 0.03 else 0)))
+                if s >= max_seqs:
+                    toks.append((s, 0, 0)); continue
+                y = last_t[s] if rng.random() < 0.7 else int(rng.integers(0, 3))
+                if rng.random() < 0.02:
+                    y = 3
+                pos = length[s] + int(rng.integers(0, 3))
+                if rng.random() < 0.03:
+                    pos = max(0, length[s] - 1)
+                if y <= 2 and pos >= length[s]:
+                    if not nseg[s] or y != last_t[s]:
+                        nseg[s] += 1
+                    length[s] = pos + 1; last_t[s] = y
+                toks.append((s, pos, y))
+            prog.append(("A", toks))
+        elif r < 0.85:
+            ops = []
+            for _ in range(int(rng.integers(1, 4))):
+                s = int(rng.integers(0, max_seqs))
+                k = int(rng.integers(-1, nseg[s] + 2))
+                keep = int(rng.choice([0, 0, 1, 3, 7, 40, -1]))
+                nb = int(rng.choice([0, 0, 2, 2, 4, 8, 3]))
+                ops.append((s, k, keep, nb))
+            prog.append(("X", ops))
+        elif r < 0.93:
+            prog.append(("P", [int(s) for s in rng.permutation(max_seqs)], int(rng.integers(1, 4)), 4))
+        else:
+            s = int(rng.integers(0, max_seqs))
+            prog.append(("Z", [s]))
+            length[s] = 0; nseg[s] = 0
+    return prog
+
+
+def run_program(prog, pools, max_seqs, max_blocks, max_segs, order, seed):
+    L = oracle.OracleLayout(1, 1, 64, 32, pools, max_seqs, max_blocks, max_segs)
+    oc = oracle.OracleCache(L, order)
+    sp = S.Spec(pools, max_seqs, max_blocks, max_segs, order=order)
+    rng = np.random.default_rng(seed)
+    for step in prog:
+        kind = step[0]
+        if kind == "A":
+            toks = step[1]
+            n = len(toks)
+            kv = rng.standard_normal((2, n, 1, 64)).astype(np.float32)
+            got = oc.append([t[0] for t in toks], [t[1] for t in toks], [t[2] for t in toks], kv[0], kv[1])
+            want = sp.append(toks)
+            assert [(-1 if w is None else (w[0] << 28) | w[1]) for w in want] == got.tolist()
+        elif kind == "X":
+            ops = step[1]
+            oc.evict([o[0] for o in ops], [o[1] for o in ops], [o[2] for o in ops], [o[3] for o in ops])
+            sp.evict(ops)
+        elif kind == "P":
+            seqs, num, den = step[1], step[2], step[3]
+            got = oc.plan_budget(seqs, num, den, 16)
+            want = sp.plan(seqs, num, den, 16)
+            assert list(zip(*[a.tolist() for a in got])) == want
+            if want:
+                oc.evict(*[list(x) for x in zip(*want)])
+                sp.evict(want)
+        else:
+            oc.seq_reset(step[1]); sp.reset(step[1])
+        compare(oc, sp)
+        check_invariants(oc)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_brute_force_against_spec(seed):
+    rng = np.random.default_rng(seed)
+    pools = (2, 3, 2) if seed % 2 else (3, 2, 3)
+    order = None
+    if seed % 3 == 0:
+        order = [rng.permutation(p).astype(np.int32) for p in pools]
+    for rep in range(12):
+        prog = random_program(rng, 2, 8)
+        run_program(prog, pools, 2, 2, 5, order, seed * 100 + rep)
+
+
+def test_pool_exhaustion_leaves_failed_sequence_untouched():
+    L = oracle.OracleLayout(1, 1, 64, 32, (1, 1, 1), 2, 4, 8)
+    oc = oracle.OracleCache(L)
+    kv = np.zeros((20, 1, 64), np.float32)
+    # seq 0 takes the only 8-bit block; seq 1's first 8-bit token finds the pool dry
+    got = oc.append([0] * 16 + [1, 0, 1, 1], list(range(16)) + [0, 16, 1, 2], [0] * 20, kv, kv)
+    assert (got[:16] >= 0).all() and got[16] == -1 and got[17] == -1 and got[18] == -1 and got[19] == -1
+    flags, minseq, count = oc.error()
+    assert flags == 1 << 2 and minseq == 0 and count == 2
+    assert not oc.seq_record(1).any()          # seq 1 untouched
+    assert oc.seq_record(0)[8] == 16
+
+
+def test_bad_segment_and_duplicate_ops():
+    L = oracle.OracleLayout(1, 1, 64, 32, (2, 2, 2), 2, 2, 8)
+    oc = oracle.OracleCache(L)
+    kv = np.zeros((6, 1, 64), np.float32)
+    oc.append([0] * 6, range(6), [0, 0, 2, 2, 1, 1], kv, kv)
+    oc.evict([0], [7], [0], [0])
+    assert oc.error()[0] == 1 << 3
+    oc.clear_error()
+    oc.evict([0, 0], [1, 1], [0, 0], [0, 0])   # second op on the same segment
+    assert oc.error()[0] == 1 << 1
+    assert oc.segments(0)[1, 5] == 0
+    oc.clear_error()
+    oc.evict([0], [1], [0], [0])               # already fully evicted
+    assert oc.error()[0] == 1 << 3
+
+
+def test_ladder_hand_example():
+    """Segments R10 T5 E8 T4 E6 T3 (open), budget 1/2 of 36 = 18 tokens:
+    evict T1 (-> 31), T3 (-> 27); T5 is open and newest; then downgrade the
+    oldest E (segment 2, 8 tokens) to 2 bits."""
+    L = oracle.OracleLayout(1, 1, 64, 32, (4, 4, 4), 1, 4, 8)
+    oc = oracle.OracleCache(L)
+    types = [0] * 10 + [2] * 5 + [1] * 8 + [2] * 4 + [1] * 6 + [2] * 3
+    kv = np.zeros((36, 1, 64), np.float32)
+    oc.append([0] * 36, range(36), types, kv, kv)
+    ops = oc.plan_budget([0], 1, 2, 8)
+    assert list(zip(*[a.tolist() for a in ops])) == [(0, 1, 0, 0), (0, 3, 0, 0), (0, 2, 8, 2)]
+    oc.evict(*ops)
+    segs = oc.segments(0)
+    assert segs[1, 5] == 0 and segs[3, 5] == 0 and segs[2, 1] == 2 and segs[2, 5] == 8
+    assert oc.seq_record(0)[8] == 27
+
+
+def test_downgrade_requantizes_dequantized_values():
+    """A 4->2 bit downgrade quantizes the 4-bit reconstruction, not the
+    original row (the originals are gone)."""
+    L = oracle.OracleLayout(1, 1, 64, 32, (1, 2, 2), 1, 2, 4)
+    oc = oracle.OracleCache(L)
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((3, 1, 64)).astype(np.float32)
+    oc.append([0] * 3, [0, 1, 2], [1, 1, 1], x, x)
+    oc.evict([0], [0], [3], [2])
+    seg = oc.segments(0)[0]
+    assert seg[1] == 2 and seg[5] == 3
+    # reference: quantize at 4 bits, dequantize in fp32, quantize at 2 bits
+    for gi in range(2):
+        c4, s4, z4 = oracle.quantize_group(x[0, 0, gi * 32:(gi + 1) * 32], 4)
+        s = np.float32(np.uint16(s4).view(np.float16)); z = np.float32(np.uint16(z4).view(np.float16))
+        xr = (s * c4.astype(np.float32) + z).astype(np.float32)
+        c2, s2, z2 = oracle.quantize_group(xr, 2)
+        blk = oc.bufs["btab"][2 * 2]   # seq 0, class 2, first block
+        slot = int(blk) * 16 + 0
+        # first kept token (position 0) went to the first popped 2-bit slot (slot 0)
+        bh = oc.bufs["pool2"][int(blk) * L.block_head_bytes(2):]
+        meta = bh[2 * 16 * 64 * 2 // 8 + gi * 4: 2 * 16 * 64 * 2 // 8 + gi * 4 + 4].view(np.uint16)
+        assert (int(meta[0]), int(meta[1])) == (s2, z2)
+        codes = [(int.from_bytes(bh[b // 8:b // 8 + 2].tobytes(), "little") >> (b % 8)) & 3
+                 for b in (L.code_bit(2, 0, 0, gi * 32 + j) for j in range(32))]
+        assert codes == c2.tolist()
+        assert slot == int(blk) * 16
+
+
+def test_classify_hand_examples():
+    # tau_T = 0.375, tau_E = 0.875 (exact in fp32); two heads
+    st = np.zeros((4, 2, 3), np.float32)
+    st[0, :, 1] = [0.25, 0.5]      # mean 0.375 -> T (<=)
+    st[1, :, 1] = [0.875, 0.875]   # mean 0.875 -> E (>=)
+    st[2, :, 1] = [0.5, 0.75]      # mean 0.625 -> R
+    st[3, :, 1] = [1.0, 0.8]       # mean 0.9 -> E
+    assert oracle.classify(st, 0.375, 0.875).tolist() == [2, 1, 0, 1]
+    st[:, :, 2] = np.array([[0.9, 0.8], [0.1, 0.2], [0.5, 0.5], [0.0, 0.0]], np.float32)
+    # kind 1: score = mean(1 - M_k) = 0.15, 0.85, 0.5, 1.0
+    assert oracle.classify(st, 0.375, 0.875, kind=1).tolist() == [2, 0, 0, 1]
