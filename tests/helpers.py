@@ -25,3 +25,108 @@ def build_oracle(w: synth.Workload):
         else:
             oc.evict(call.seq_ids, call.seg_ids, call.keep_n, call.new_bits)
     return oc
+
+
+# ---------------------------------------------------------------------------
+# HIP path (GPU tests only)
+# ---------------------------------------------------------------------------
+def gpu_layout(L: synth.Layout):
+    from thought_adaptive_mixed_amd import binding
+    return binding.make_layout(L.num_kv_heads, L.num_q_heads, L.head_dim, L.group_size, L.pool_blocks,
+                               L.max_seqs, L.max_blocks_per_seq, L.max_segments_per_seq, L.max_tokens_per_call,
+                               L.bits)
+
+
+def dev(a, dtype=None):
+    import torch
+    a = np.ascontiguousarray(a if dtype is None else np.asarray(a, dtype))
+    return torch.from_numpy(a).cuda()
+
+
+def build_gpu(w: synth.Workload, cache=None):
+    from thought_adaptive_mixed_amd import binding
+    gc = cache or binding.Cache(gpu_layout(w.layout), w.block_order)
+    for call in w.calls:
+        if isinstance(call, synth.AppendCall):
+            k, v = w.kv(call)
+            gc.append(dev(call.seq_ids), dev(call.positions), dev(call.thought), dev(k), dev(v))
+        else:
+            gc.evict(dev(call.seq_ids), dev(call.seg_ids), dev(call.keep_n), dev(call.new_bits))
+    return gc
+
+
+_TEMPLATES = {}
+
+
+def _templates(L, c):
+    """Per slot-in-block t: byte masks of the bits token t owns in one
+    (block, KV head) record (K codes, V codes, K and V meta)."""
+    import oracle
+    key = (L.head_dim, L.group_size, c)
+    if key in _TEMPLATES:
+        return _TEMPLATES[key]
+    ol = oracle.OracleLayout(1, 1, L.head_dim, L.group_size, (1, 1, 1), 1, 1, 1)
+    R = ol.block_head_bytes(c)
+    bits = (8, 4, 2)[c]
+    NG = L.head_dim // L.group_size
+    codes_bytes = 2 * 16 * L.head_dim * bits // 8
+    tm = np.zeros((16, R), np.uint8)
+    for t in range(16):
+        for kv in range(2):
+            for d in range(L.head_dim):
+                b0 = ol.code_bit(c, kv, t, d)
+                for b in range(b0, b0 + bits):
+                    tm[t, b // 8] |= 1 << (b % 8)
+            for gi in range(NG):
+                off = codes_bytes + kv * 16 * NG * 4 + (t * NG + gi) * 4
+                tm[t, off:off + 4] = 0xFF
+    _TEMPLATES[key] = tm
+    return tm
+
+
+def compare_states(L: synth.Layout, g: dict, o: dict, label=""):
+    """Bit-exact comparison on every defined region of the state format."""
+    BS_ = 16
+    assert np.array_equal(g["hdr"], o["hdr"]), f"{label} hdr {g['hdr'][:8]} vs {o['hdr'][:8]}"
+    assert np.array_equal(g["seq"], o["seq"]), f"{label} seq records differ"
+    seq = o["seq"].reshape(L.max_seqs, 16)
+    for c in range(3):
+        P = L.pool_blocks[c]
+        gb, ob = g[f"blk{c}"].reshape(P, 4), o[f"blk{c}"].reshape(P, 4)
+        assert np.array_equal(gb, ob), f"{label} block records class {c}: rows {np.nonzero((gb != ob).any(1))[0][:10]}"
+        n = int(o["hdr"][c])
+        assert np.array_equal(g[f"free{c}"][:n], o[f"free{c}"][:n]), f"{label} free stack {c}"
+        valid = ((ob[:, 0:1] >> np.arange(16)[None, :]) & 1).astype(bool)          # [P, 16]
+        gs, os_ = g[f"slot{c}"].reshape(P, 16, 2), o[f"slot{c}"].reshape(P, 16, 2)
+        assert np.array_equal(gs[valid], os_[valid]), f"{label} slot records class {c}"
+        # pools: differing bits must all lie outside valid tokens' bits
+        R = g[f"pool{c}"].size // (P * L.num_kv_heads)
+        gp = g[f"pool{c}"].reshape(P, L.num_kv_heads, R)
+        op = o[f"pool{c}"].reshape(P, L.num_kv_heads, R)
+        diff = gp ^ op
+        rows = np.nonzero(diff.reshape(P, -1).any(1))[0]
+        if rows.size:
+            tm = _templates(L, c)
+            for blk in rows:
+                own = np.bitwise_or.reduce(tm[valid[blk]], axis=0) if valid[blk].any() else np.zeros(R, np.uint8)
+                bad = diff[blk] & own[None, :]
+                assert not bad.any(), (f"{label} pool class {c} block {blk}: token bytes differ at "
+                                       f"{np.argwhere(bad)[:8].tolist()}")
+    bt_g = g["btab"].reshape(L.max_seqs, 3, L.max_blocks_per_seq)
+    bt_o = o["btab"].reshape(L.max_seqs, 3, L.max_blocks_per_seq)
+    st_g = g["sstk"].reshape(L.max_seqs, 3, -1)
+    st_o = o["sstk"].reshape(L.max_seqs, 3, -1)
+    sg_g = g["segt"].reshape(L.max_seqs, L.max_segments_per_seq, 8)
+    sg_o = o["segt"].reshape(L.max_seqs, L.max_segments_per_seq, 8)
+    for s in range(L.max_seqs):
+        for c in range(3):
+            nb, ns = seq[s, c], seq[s, 3 + c]
+            assert np.array_equal(bt_g[s, c, :nb], bt_o[s, c, :nb]), f"{label} block table seq {s} class {c}"
+            assert np.array_equal(st_g[s, c, :ns], st_o[s, c, :ns]), f"{label} slot stack seq {s} class {c}"
+        k = seq[s, 6]
+        assert np.array_equal(sg_g[s, :k], sg_o[s, :k]), f"{label} segment table seq {s}"
+
+
+def attn_metrics(out_gpu, out_ref):
+    d = out_gpu.astype(np.float64) - out_ref
+    return float(np.abs(d).max()), float(np.linalg.norm(d) / max(np.linalg.norm(out_ref), 1e-300))

@@ -1,0 +1,153 @@
+// Internal declarations of libthinkv: the handle, the device view of the
+// cache state, and device helpers shared by the state and attention kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "tkv.h"
+
+#define TKV_BS 16                 // tokens per block
+#define TKV_SEQ_W 16              // words per sequence record
+#define TKV_SEG_W 8               // words per segment record
+#define TKV_BLK_W 4               // words per block record
+#define TKV_SLOT_W 2              // words per slot record
+#define TKV_MAX_TOK 8192          // items per append / evict / plan call
+#define TKV_MAX_SEQS 1024
+#define TKV_MAX_BLOCKS 256        // per sequence and class
+#define TKV_INF 0x7fffffff
+
+// SEQ record words
+enum { Q_NBLK = 0, Q_NSLOT = 3, Q_NSEG = 6, Q_LEN = 7, Q_NRET = 8, Q_NAPP = 9 };
+// SEGT record words
+enum { G_TYPE = 0, G_BITS = 1, G_FIRST = 2, G_LAST = 3, G_NTOT = 4, G_NRET = 5 };
+// HDR words
+enum { H_FREE = 0, H_EKIND = 3, H_EMINSEQ = 4, H_ECOUNT = 5 };
+
+// Device view of the state: raw pointers plus geometry, passed by value.
+struct DevState {
+  uint8_t* pool[3];
+  int32_t* blk[3];
+  int32_t* slot[3];
+  int32_t* freestk[3];
+  int32_t* hdr;
+  int32_t* seq;
+  int32_t* btab;
+  int32_t* sstk;
+  int32_t* segt;
+  int32_t* scratch;
+  int Hkv, Hq, D, g, NG;
+  int type_class[3];              // class index for thought type R, E, T
+  int pool_blocks[3];
+  int max_seqs, max_blocks, max_segs, max_tokens;
+  int64_t bh_bytes[3];            // bytes per (block, KV head) record
+  int chunk_bytes[3];             // bytes per lane chunk = D*bits/32
+};
+
+struct tkv_cache {
+  tkv_layout L;
+  void* buf[TKV_NUM_BUFFERS];
+  size_t size[TKV_NUM_BUFFERS];
+  DevState S;
+  hipStream_t last_stream;
+};
+
+__host__ __device__ inline int class_bits(int c) { return c == 0 ? 8 : (c == 1 ? 4 : 2); }
+__host__ __device__ inline int class_of_bits(int b) { return b == 8 ? 0 : (b == 4 ? 1 : (b == 2 ? 2 : -1)); }
+
+// Scratch carve-up (int32 words), sized 6*TKV_MAX_TOK + 64 by tkv_buffer_sizes.
+__host__ __device__ inline int32_t* scr_idx(int32_t* s) { return s; }                       // [MAX_TOK]
+__host__ __device__ inline int32_t* scr_info(int32_t* s) { return s + TKV_MAX_TOK; }        // [MAX_TOK]
+__host__ __device__ inline int32_t* scr_status(int32_t* s) { return s + 2 * TKV_MAX_TOK; }  // [MAX_TOK]
+__host__ __device__ inline int32_t* scr_need(int32_t* s) { return s + 3 * TKV_MAX_TOK; }    // [MAX_TOK]
+__host__ __device__ inline int32_t* scr_misc(int32_t* s) { return s + 6 * TKV_MAX_TOK; }    // [64]
+
+// ---------------------------------------------------------------------------
+// Code placement inside a (block, KV head) record.  Codes of one lane chunk
+// sit in 32-bit words of W = 32/bits codes: even elements in the low
+// half-word, odd elements in the high half-word, so one AND-OR with
+// 0x64006400 turns a pair of codes into two fp16 values 1024 + code.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int elem_bit(int e, int bits) {
+  int W = 32 / bits, w = e / W, f = e % W;
+  return w * 32 + ((f >> 1) + (f & 1) * (W >> 1)) * bits;
+}
+// K: token t, dim d -> chunk 16*lg + t, element gi*(g/4) + e'
+__host__ __device__ inline int k_code_bit(int D, int g, int bits, int t, int d) {
+  int q4 = g >> 2, gi = d / g, w = d % g, lg = w / q4, ep = w % q4;
+  int chunk = 16 * lg + t;
+  return chunk * (D * bits / 32) * 8 + elem_bit(gi * q4 + ep, bits);
+}
+// V: token t = 4q + r, dim d = 16n + i -> chunk 16*q + i, element 4n + r
+__host__ __device__ inline int v_code_bit(int D, int bits, int t, int d) {
+  int q = t >> 2, r = t & 3, n = d >> 4, i = d & 15;
+  int chunk = 16 * q + i;
+  return 64 * (D * bits / 32) * 8 + chunk * (D * bits / 32) * 8 + elem_bit(4 * n + r, bits);
+}
+__host__ __device__ inline int meta_byte(int D, int g, int bits, int kv, int t, int gi) {
+  int NG = D / g;
+  return 2 * 64 * (D * bits / 32) + kv * (16 * NG * 4) + (t * NG + gi) * 4;
+}
+
+// Sticky error word.
+__device__ inline void record_error(int32_t* hdr, int code, int seq) {
+  atomicOr(&hdr[H_EKIND], 1 << (-code));
+  atomicMin(&hdr[H_EMINSEQ], seq);
+  atomicAdd(&hdr[H_ECOUNT], 1);
+}
+
+// ---------------------------------------------------------------------------
+// Group quantizer, bit-exact IEEE fp32 (no contraction): scale =
+// fp16((max-min)/(2^bits-1)), zero = fp16(min), -0 -> +0, codes =
+// clamp(rint-half-even((x - zero)/scale)); zero scale -> all codes 0.
+// `get(i)` yields the group's i-th fp32 value.
+// ---------------------------------------------------------------------------
+__device__ inline uint16_t f16_bits_rne(float x) {
+  _Float16 h = (_Float16)x;   // v_cvt_f16_f32, round to nearest even
+  uint16_t b = __builtin_bit_cast(uint16_t, h);
+  return b == 0x8000u ? (uint16_t)0 : b;
+}
+__device__ inline float f16_bits_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+template <class Get>
+__device__ inline void quant_scale_zero(Get get, int n, int bits, float& sf, float& zf, uint16_t& sh, uint16_t& zh) {
+#pragma clang fp contract(off)
+  float mn = get(0), mx = mn;
+  for (int i = 1; i < n; i++) {
+    float x = get(i);
+    mn = x < mn ? x : mn;
+    mx = x > mx ? x : mx;
+  }
+  float levels = (float)((1 << bits) - 1);
+  float range = mx - mn;
+  float s32 = range / levels;
+  sh = f16_bits_rne(s32);
+  zh = f16_bits_rne(mn);
+  sf = f16_bits_to_f32(sh);
+  zf = f16_bits_to_f32(zh);
+}
+__device__ inline unsigned quant_code(float x, float sf, float zf, int bits) {
+#pragma clang fp contract(off)
+  if (sf == 0.0f) return 0u;
+  float diff = x - zf;
+  float q = diff / sf;
+  float r = __builtin_rintf(q);
+  float top = (float)((1 << bits) - 1);
+  r = r < 0.0f ? 0.0f : r;
+  r = r > top ? top : r;
+  return (unsigned)r;
+}
+
+// Launchers (state kernels)
+int launch_init(tkv_cache* c, hipStream_t st);
+int launch_append(tkv_cache* c, int n, const int32_t* seq_ids, const int32_t* pos, const uint8_t* thought,
+                  const float* k, const float* v, int32_t* slot_out, hipStream_t st);
+int launch_evict(tkv_cache* c, int n_ops, const int32_t* n_ops_dev, const int32_t* seq_ids, const int32_t* seg_ids,
+                 const int32_t* keep_n, const uint8_t* new_bits, hipStream_t st);
+int launch_plan(tkv_cache* c, int n, const int32_t* seq_ids, int num, int den, int max_ops, int32_t* n_ops_dev,
+                int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st);
+int launch_seq_reset(tkv_cache* c, int n, const int32_t* seq_ids, hipStream_t st);
+int launch_classify(int batch, int Hq, const float* stats, float tau_T, float tau_E, int kind, uint8_t* labels,
+                    hipStream_t st);
+// Attention
+int attn_choose_splits(const tkv_cache* c, int batch);
+size_t attn_workspace_bytes(const tkv_cache* c, int batch, int splits);
+int launch_attention(tkv_cache* c, const tkv_attn_args* a, int splits, hipStream_t st);

@@ -426,6 +426,7 @@ def bench_cycle(seed=1002, B=32, L=16384, steps=64) -> Churn:
 
 
 def small_churn(seed=88, B=8, steps=96, lo=600, hi=1600, frac=(1, 10)) -> Churn:
+    """Parity-sized decode loop (lockstep with the oracle every step)."""
     rng = np.random.default_rng(seed + 60000)
     L0 = rng.integers(lo, hi + 1, B)
     n = (L0 * frac[0]) // frac[1]
