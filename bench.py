@@ -1,0 +1,240 @@
+"""Benchmark of the ThinKV decode hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: paged decode attention
+over the mixed-precision, hole-bearing cache (with the staged self token) ->
+thought_classify -> kv_append_quant of the new token at its label's precision
+-> kv_plan_budget (token budget ladder) -> kv_evict_segment.  Workload: the
+Llama-8B-like reasoning-decode layer (B32, Hq32/Hkv8, D128, g64, 16k generated
+tokens per sequence, 10% budget -> 1638 retained, R/E/T 8/4/2-bit) with
+planted-temperature queries, synthetic data.
+
+The state is replicated into enough copies to exceed the 256 MB Infinity Cache
+and consecutive steps rotate through them, so each step reads its cache from
+HBM.  All inputs are resident in HBM before the timed region.
+
+Prints ONE JSON line (see the fields below).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn KV tokens/s and achieved HBM GB/s (% of MI355X peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0
+CLASS_BITS = (8, 4, 2)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def state_class_tokens(exported, L):
+    """Retained tokens per (sequence, class) from an exported state."""
+    out = np.zeros((L.max_seqs, 3), np.int64)
+    seq = exported["seq"].reshape(L.max_seqs, 16)
+    bt = exported["btab"].reshape(L.max_seqs, 3, L.max_blocks_per_seq)
+    blocks_used = np.zeros((L.max_seqs, 3), np.int64)
+    for c in range(3):
+        masks = exported[f"blk{c}"].reshape(-1, 4)[:, 0].astype(np.uint32)
+        pop = np.array([bin(int(m)).count("1") for m in range(1 << 16)], np.int64)
+        for s in range(L.max_seqs):
+            nb = int(seq[s, c])
+            ids = bt[s, c, :nb]
+            out[s, c] = int(pop[masks[ids]].sum())
+            blocks_used[s, c] = nb
+    return out, blocks_used
+
+
+def algorithmic_bytes(tokens_c, blocks_c, L, batch, self_token=True):
+    """Bytes one attention call must move: codes + fp16 (scale, zero) of every
+    attended cached token and KV head, the block id and mask word of every
+    visited block (per KV head), the queries, outputs, statistics and the
+    staged self token."""
+    D, g, Hkv, Hq = L.head_dim, L.group_size, L.num_kv_heads, L.num_q_heads
+    NG = D // g
+    per_tok = [Hkv * 2 * (D * b // 8 + NG * 4) for b in CLASS_BITS]
+    kv = sum(int(tokens_c[:, c].sum()) * per_tok[c] for c in range(3))
+    blk = int(blocks_c.sum()) * Hkv * (4 + 4)
+    io = batch * Hq * D * 2 + batch * Hq * D * 4 + batch * Hq * 12
+    if self_token:
+        io += batch * Hkv * D * 4 * 2
+    return kv + blk + io, kv
+
+
+def cpu_baseline(w, state, ch, n_seq, reps_budget_s=20.0):
+    """The oracle as it stands, on a sample of n_seq sequences of the same
+    workload: one full step (attention with the self token, classify, append,
+    ladder, evict) per repetition, on all host cores the process may use."""
+    import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import helpers
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    oc = oracle.OracleCache(helpers.oracle_layout(w.layout), w.block_order)
+    oc.import_(state)
+    sel = np.arange(n_seq, dtype=np.int32)
+    q, k, v, pos = ch.step_inputs(0)
+    tokens = 0
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        p = (pos[:n_seq] + reps).astype(np.int32)
+        out, st, na = oc.attention(sel, p, q[:n_seq], k_self=k[:n_seq], v_self=v[:n_seq])
+        lab = oracle.classify(st.astype(np.float32), *ch.tau)
+        oc.append(sel, p, lab, k[:n_seq], v[:n_seq])
+        ops = oc.plan_budget(sel, ch.budget[0], ch.budget[1], 256)
+        if ops[0].size:
+            oc.evict(*ops)
+        tokens += int(na.sum())
+        reps += 1
+        if time.perf_counter() - t0 > reps_budget_s or reps >= 50:
+            break
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {"value": tokens / dt, "unit": "KV tokens/s", "cores": min(threads, cores), "kind": "oracle",
+            "sample": f"{reps} full steps (attention+classify+append+ladder+evict) on {n_seq} of "
+                      f"{w.seq_ids.size} sequences of the same cache, fp64 attention, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=6)
+    ap.add_argument("--copies", type=int, default=0, help="state copies (0 = enough for > 1 GiB)")
+    ap.add_argument("--cpu-seqs", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attn-only", action="store_true", help="time only the attention call (diagnostic)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path shards by "
+              f"sequence with no exchange, so N GPUs would run N independent copies of this step.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from thought_adaptive_mixed_amd import binding, synth
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import helpers
+
+    total_steps = args.warmup + args.steps
+    log("[bench] building workload")
+    t0 = time.time()
+    ch = synth.bench_cycle(steps=total_steps)
+    w = ch.base
+    L = w.layout
+    B = w.seq_ids.size
+    sizes = binding.buffer_sizes(helpers.gpu_layout(L))
+    state_bytes = sum(sizes[:-1])
+    R = args.copies or max(2, math.ceil((1 << 30) / state_bytes))
+    log(f"[bench] state {state_bytes / 1e6:.1f} MB, {R} copies")
+    c0 = helpers.build_gpu(w)
+    torch.cuda.synchronize()
+    state = c0.export()
+    caches = [c0] + [binding.Cache(helpers.gpu_layout(L), w.block_order) for _ in range(R - 1)]
+    for c in caches[1:]:
+        c.import_(state)
+    tok_c, blk_c = state_class_tokens(state, L)
+    abytes, kvbytes = algorithmic_bytes(tok_c, blk_c, L, B)
+    log(f"[bench] built in {time.time() - t0:.1f} s; algorithmic bytes per attention call {abytes / 1e6:.2f} MB")
+
+    # inputs for every step, resident on the device
+    dv = helpers.dev
+    seq_d = dv(w.seq_ids, np.int32)
+    steps_in = []
+    for s in range(total_steps):
+        q, k, v, pos = ch.step_inputs(s)
+        pos = (w.q_pos + s // R).astype(np.int32)       # each copy advances one position per step it serves
+        steps_in.append((dv(q, np.uint16), dv(k, np.float32), dv(v, np.float32), dv(pos, np.int32)))
+    Hq, D = L.num_q_heads, L.head_dim
+    out = torch.empty(B, Hq, D, dtype=torch.float32, device="cuda")
+    stats = torch.empty(B, Hq, 3, dtype=torch.float32, device="cuda")
+    n_att = torch.zeros(B, dtype=torch.int32, device="cuda")
+    n_att_sum = torch.zeros(B, dtype=torch.int64, device="cuda")
+    ws = torch.empty(c0.workspace_bytes(B), dtype=torch.uint8, device="cuda")
+    labels = torch.empty(B, dtype=torch.uint8, device="cuda")
+    max_ops = 256
+    n_ops = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o_seq = torch.zeros(max_ops, dtype=torch.int32, device="cuda")
+    o_seg, o_keep = torch.zeros_like(o_seq), torch.zeros_like(o_seq)
+    o_bits = torch.zeros(max_ops, dtype=torch.uint8, device="cuda")
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(total_steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(total_steps)]
+
+    def step(s, timed):
+        c = caches[s % R]
+        q, k, v, pos = steps_in[s]
+        ev_a[s].record()
+        c.attention(seq_d, pos, q, out, ws, stats=stats, n_attended=n_att, k_self=k, v_self=v)
+        ev_b[s].record()
+        if timed:
+            n_att_sum.add_(n_att)
+        if args.attn_only:
+            return
+        binding.classify(stats, ch.tau[0], ch.tau[1], labels)
+        c.append(seq_d, pos, labels, k, v)
+        c.plan_budget(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, o_seq, o_seg, o_keep, o_bits)
+        c.evict(o_seq, o_seg, o_keep, o_bits, n_ops_dev=n_ops, n_ops=max_ops)
+
+    log("[bench] warmup")
+    for s in range(args.warmup):
+        step(s, False)
+    torch.cuda.synchronize()
+    log("[bench] timed")
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for s in range(args.warmup, total_steps):
+        step(s, True)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    attn_ms = [ev_a[s].elapsed_time(ev_b[s]) for s in range(args.warmup, total_steps)]
+    errs = [c.get_error() for c in caches]
+    if any(e[0] for e in errs):
+        log(f"[bench] WARNING device errors: {errs}")
+    tokens = int(n_att_sum.sum().item())
+    ms_step = ms_total / args.steps
+    attn_avg = float(np.mean(attn_ms))
+    achieved = abytes / (attn_avg * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms_total * 1e-3),
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8/4/2 codes as exact f16, f16 MFMA, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": "llama8b-like reasoning decode, one layer: B32, Hq32/Hkv8, D128, g64, "
+                               "16k generated tokens/seq, 10% budget (1638 retained), R/E/T 8/4/2-bit, "
+                               "planted-temperature queries; step = attention+classify+append+ladder+evict",
+                   "batch": B, "copies": R, "attended_per_step": tokens / args.steps},
+        "attn_ms": attn_avg,
+        "attn_kv_tokens_per_s": (tokens / args.steps) / (attn_avg * 1e-3),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "paged_decode_attn (split-K kernel + combine kernel)",
+                     "bytes_per_launch": abytes},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(w, state, ch, args.cpu_seqs)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

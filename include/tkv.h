@@ -198,7 +198,7 @@ typedef struct {
   float* out;                 /* fp32 [batch][Hq][D]                               */
   float* stats;               /* nullable fp32 [batch][Hq][3] = {H, H/ln n, M_k}   */
   int32_t* n_attended;        /* nullable i32[batch]                               */
-  void* workspace;            /* >= tkv_attn_workspace(c, batch, num_splits) bytes */
+  void* workspace;            /* >= tkv_attn_workspace(c, batch, num_splits) bytes; nullable when that is 0 */
   size_t workspace_bytes;
 } tkv_attn_args;
 

@@ -152,7 +152,8 @@ extern "C" int kv_plan_budget(tkv_cache* c, int32_t n, const int32_t* seq_ids, i
 
 extern "C" size_t tkv_attn_workspace(const tkv_cache* c, int32_t batch, int32_t num_splits) {
   if (!c || batch < 0) return 0;
-  int s = num_splits > 0 ? num_splits : attn_choose_splits(c, batch);
+  int nw, s;
+  attn_plan(c, batch, num_splits, &nw, &s);
   return attn_workspace_bytes(c, batch, s);
 }
 
@@ -160,12 +161,14 @@ extern "C" int paged_decode_attn(tkv_cache* c, const tkv_attn_args* a, hipStream
   if (!c || !a) return TKV_EINVAL;
   if (a->batch < 0 || a->batch > c->S.max_seqs) return TKV_EINVAL;
   if (a->topk < 1 || a->topk > 8 || a->window < 0 || a->num_splits < 0 || a->num_splits > 64) return TKV_EINVAL;
-  if (a->batch > 0 && (!a->seq_ids || !a->q_pos || !a->q || !a->out || !a->workspace)) return TKV_EINVAL;
+  if (a->batch > 0 && (!a->seq_ids || !a->q_pos || !a->q || !a->out)) return TKV_EINVAL;
   if ((a->k_self == nullptr) != (a->v_self == nullptr)) return TKV_EINVAL;
-  const int s = a->num_splits > 0 ? a->num_splits : attn_choose_splits(c, a->batch);
-  if (a->workspace_bytes < attn_workspace_bytes(c, a->batch, s)) return TKV_EINVAL;
+  int nw, s;
+  attn_plan(c, a->batch, a->num_splits, &nw, &s);
+  const size_t need = attn_workspace_bytes(c, a->batch, s);
+  if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return TKV_EINVAL;
   c->last_stream = stream;
-  return launch_attention(c, a, s, stream);
+  return launch_attention(c, a, nw, s, stream);
 }
 
 extern "C" int thought_classify(int32_t batch, int32_t num_q_heads, const float* stats, float tau_T, float tau_E,
