@@ -114,6 +114,7 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-only", action="store_true", help="time only the attention call (diagnostic)")
+    ap.add_argument("--no-graph", action="store_true", help="launch each call from Python instead of HIP graphs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path shards by "
@@ -158,8 +159,7 @@ def main():
     Hq, D = L.num_q_heads, L.head_dim
     out = torch.empty(B, Hq, D, dtype=torch.float32, device="cuda")
     stats = torch.empty(B, Hq, 3, dtype=torch.float32, device="cuda")
-    n_att = torch.zeros(B, dtype=torch.int32, device="cuda")
-    n_att_sum = torch.zeros(B, dtype=torch.int64, device="cuda")
+    n_att = torch.zeros(total_steps, B, dtype=torch.int32, device="cuda")   # one row per step
     ws = torch.empty(c0.workspace_bytes(B), dtype=torch.uint8, device="cuda")
     labels = torch.empty(B, dtype=torch.uint8, device="cuda")
     max_ops = 256
@@ -170,31 +170,62 @@ def main():
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(total_steps)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(total_steps)]
 
-    def step(s, timed):
+    def attn(s):
         c = caches[s % R]
         q, k, v, pos = steps_in[s]
-        ev_a[s].record()
-        c.attention(seq_d, pos, q, out, ws, stats=stats, n_attended=n_att, k_self=k, v_self=v)
-        ev_b[s].record()
-        if timed:
-            n_att_sum.add_(n_att)
-        if args.attn_only:
-            return
+        c.attention(seq_d, pos, q, out, ws, stats=stats, n_attended=n_att[s], k_self=k, v_self=v)
+
+    def rest(s):
+        c = caches[s % R]
+        q, k, v, pos = steps_in[s]
         binding.classify(stats, ch.tau[0], ch.tau[1], labels)
         c.append(seq_d, pos, labels, k, v)
         c.plan_budget(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, o_seq, o_seg, o_keep, o_bits)
         c.evict(o_seq, o_seg, o_keep, o_bits, n_ops_dev=n_ops, n_ops=max_ops)
 
+    # Each step as two HIP graphs (attention; classify..evict), captured before
+    # anything runs and replayed in order, so the host launches two graphs
+    # per step; the attention is timed with events between the launches.
+    graphs = None
+    if not args.no_graph:
+        log("[bench] capturing graphs")
+        graphs = []
+        torch.cuda.synchronize()
+        for s in range(total_steps):
+            ga, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(ga):
+                attn(s)
+            gb_ok = not args.attn_only
+            if gb_ok:
+                with torch.cuda.graph(gb):
+                    rest(s)
+            graphs.append((ga, gb if gb_ok else None))
+        torch.cuda.synchronize()
+
+    def step(s):
+        ev_a[s].record()
+        if graphs:
+            graphs[s][0].replay()
+        else:
+            attn(s)
+        ev_b[s].record()
+        if args.attn_only:
+            return
+        if graphs:
+            graphs[s][1].replay()
+        else:
+            rest(s)
+
     log("[bench] warmup")
     for s in range(args.warmup):
-        step(s, False)
+        step(s)
     torch.cuda.synchronize()
     log("[bench] timed")
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
     for s in range(args.warmup, total_steps):
-        step(s, True)
+        step(s)
     t_end.record()
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
@@ -202,7 +233,7 @@ def main():
     errs = [c.get_error() for c in caches]
     if any(e[0] for e in errs):
         log(f"[bench] WARNING device errors: {errs}")
-    tokens = int(n_att_sum.sum().item())
+    tokens = int(n_att[args.warmup:].sum().item())
     ms_step = ms_total / args.steps
     attn_avg = float(np.mean(attn_ms))
     achieved = abytes / (attn_avg * 1e-3) / 1e9
@@ -222,7 +253,8 @@ def main():
         "config": {"workload": "llama8b-like reasoning decode, one layer: B32, Hq32/Hkv8, D128, g64, "
                                "16k generated tokens/seq, 10% budget (1638 retained), R/E/T 8/4/2-bit, "
                                "planted-temperature queries; step = attention+classify+append+ladder+evict",
-                   "batch": B, "copies": R, "attended_per_step": tokens / args.steps},
+                   "batch": B, "copies": R, "attended_per_step": tokens / args.steps,
+                   "launch": "python" if args.no_graph else "hip graphs (2 per step)"},
         "attn_ms": attn_avg,
         "attn_kv_tokens_per_s": (tokens / args.steps) / (attn_avg * 1e-3),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

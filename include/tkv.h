@@ -102,7 +102,7 @@ typedef struct {
   int32_t max_seqs;               /* 1..1024                                   */
   int32_t max_blocks_per_seq;     /* per class, 1..256                         */
   int32_t max_segments_per_seq;   /* >= 1                                      */
-  int32_t max_tokens_per_call;    /* bound on items per append/evict/plan call, 1..8192 */
+  int32_t max_tokens_per_call;    /* bound on items per append/evict/plan call, 1..4096 */
 } tkv_layout;
 
 /* Byte sizes of the TKV_NUM_BUFFERS buffers for layout L_h.  EINVAL for a

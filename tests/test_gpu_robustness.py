@@ -1,0 +1,101 @@
+"""GPU robustness: random append / evict / downgrade / ladder / reset programs
+on a tiny pool (exhaustion, full tables, bad ids, repeated segments), applied
+to the HIP path and the oracle call by call with the whole state compared
+after every call; determinism of builds and attention."""
+import numpy as np
+import pytest
+
+import helpers
+from thought_adaptive_mixed_amd import synth
+from test_gpu_parity import gpu_attention, say
+from test_oracle_state import random_program
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_gpu_program(prog, pools, max_seqs, max_blocks, max_segs, order, seed):
+    import torch
+    import oracle
+    from thought_adaptive_mixed_amd import binding
+    dv = helpers.dev
+    lay = synth.Layout(1, 1, 64, 32, pools, max_seqs, max_blocks, max_segs, 64)
+    oc = oracle.OracleCache(helpers.oracle_layout(lay), order)
+    gc = binding.Cache(helpers.gpu_layout(lay), order)
+    rng = np.random.default_rng(seed)
+    n_ops = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bufs = [torch.zeros(16, dtype=torch.int32, device="cuda") for _ in range(3)]
+    bits = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    for si, step in enumerate(prog):
+        kind = step[0]
+        if kind == "A":
+            toks = step[1]
+            n = len(toks)
+            kv = rng.standard_normal((2, n, 1, 64)).astype(np.float32)
+            sl = torch.zeros(n, dtype=torch.int32, device="cuda")
+            gc.append(dv([t[0] for t in toks], np.int32), dv([t[1] for t in toks], np.int32),
+                      dv([t[2] for t in toks], np.uint8), dv(kv[0]), dv(kv[1]), slot_out=sl)
+            want = oc.append([t[0] for t in toks], [t[1] for t in toks], [t[2] for t in toks], kv[0], kv[1])
+            assert np.array_equal(sl.cpu().numpy(), want), f"slots at call {si}"
+        elif kind == "X":
+            ops = step[1]
+            cols = list(zip(*ops))
+            gc.evict(dv(cols[0], np.int32), dv(cols[1], np.int32), dv(cols[2], np.int32), dv(cols[3], np.uint8))
+            oc.evict(*[list(c) for c in cols])
+        elif kind == "P":
+            seqs, num, den = step[1], step[2], step[3]
+            gc.plan_budget(dv(seqs, np.int32), num, den, 16, n_ops, *bufs, bits)
+            want = oc.plan_budget(seqs, num, den, 16)
+            m = int(n_ops.item())
+            got = [b.cpu().numpy()[:m] for b in (*bufs, bits)]
+            assert m == want[0].size and all(np.array_equal(a, b) for a, b in zip(got, want)), f"plan at call {si}"
+            gc.evict(bufs[0], bufs[1], bufs[2], bits, n_ops_dev=n_ops, n_ops=16)
+            if m:
+                oc.evict(*want)
+        else:
+            gc.seq_reset(dv(step[1], np.int32))
+            oc.seq_reset(step[1])
+        helpers.compare_states(lay, gc.export(), oc.export(), f"call {si} ({kind})")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_programs_match_oracle(seed):
+    rng = np.random.default_rng(1000 + seed)
+    pools = (2, 3, 2) if seed % 2 else (3, 2, 3)
+    order = [rng.permutation(p).astype(np.int32) for p in pools] if seed % 3 == 0 else None
+    for rep in range(4):
+        prog = random_program(rng, 2, 10)
+        _run_gpu_program(prog, pools, 2, 2, 5, order, seed * 100 + rep)
+
+
+def test_error_word_and_tkv_get_error():
+    """Errors are sticky until tkv_get_error, which reports and clears them."""
+    import oracle
+    from thought_adaptive_mixed_amd import binding
+    dv = helpers.dev
+    lay = synth.Layout(1, 1, 64, 32, (1, 1, 1), 2, 4, 8, 64)
+    gc = binding.Cache(helpers.gpu_layout(lay))
+    oc = oracle.OracleCache(helpers.oracle_layout(lay))
+    kv = np.zeros((20, 1, 64), np.float32)
+    seqs, pos = [0] * 16 + [1, 0, 1, 1], list(range(16)) + [0, 16, 1, 2]
+    gc.append(dv(seqs, np.int32), dv(pos, np.int32), dv([0] * 20, np.uint8), dv(kv), dv(kv))
+    oc.append(seqs, pos, [0] * 20, kv, kv)
+    assert gc.get_error() == oc.error() == (1 << 2, 0, 2)
+    assert gc.get_error() == (0, 0x7FFFFFFF, 0)            # cleared
+    gc.evict(dv([0], np.int32), dv([9], np.int32), dv([0], np.int32), dv([0], np.uint8))
+    assert gc.get_error() == (1 << 3, 0, 1)                 # unknown segment
+    with pytest.raises(binding.TkvError):                   # host-detectable: nothing enqueued
+        gc.append(dv(np.zeros(65, np.int32)), dv(np.arange(65, dtype=np.int32)), dv(np.zeros(65, np.uint8)),
+                  dv(np.zeros((65, 1, 64), np.float32)), dv(np.zeros((65, 1, 64), np.float32)))
+
+
+def test_build_and_attention_are_deterministic():
+    w = synth.small_static(seed=90, B=4, Hq=16, Hkv=4, D=128, g=64)
+    a = helpers.build_gpu(w)
+    b = helpers.build_gpu(w)
+    ea, eb = a.export(), b.export()
+    for k in ea:
+        assert np.array_equal(ea[k], eb[k]), k
+    ra = gpu_attention(a, w.seq_ids, w.q_pos, w.q_bf16)
+    rb = gpu_attention(a, w.seq_ids, w.q_pos, w.q_bf16)
+    for x, y in zip(ra, rb):
+        assert np.array_equal(x, y)

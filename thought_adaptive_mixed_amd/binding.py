@@ -92,11 +92,17 @@ def _check(rc, what):
         raise TkvError(rc, what)
 
 
+_torch_mod = None
+
+
 def _torch():
-    import torch
-    if not torch.cuda.is_available():
-        raise RuntimeError("thought_adaptive_mixed_amd needs a ROCm GPU (torch.cuda.is_available() is False)")
-    return torch
+    global _torch_mod
+    if _torch_mod is None:
+        import torch
+        if not torch.cuda.is_available():
+            raise RuntimeError("thought_adaptive_mixed_amd needs a ROCm GPU (torch.cuda.is_available() is False)")
+        _torch_mod = torch
+    return _torch_mod
 
 
 def _ptr(t) -> Optional[int]:
@@ -108,7 +114,7 @@ def _stream():
 
 
 def make_layout(num_kv_heads, num_q_heads, head_dim, group_size, pool_blocks, max_seqs, max_blocks_per_seq,
-                max_segments_per_seq, max_tokens_per_call=8192, bits=(8, 4, 2)) -> Layout:
+                max_segments_per_seq, max_tokens_per_call=4096, bits=(8, 4, 2)) -> Layout:
     return Layout(num_kv_heads, num_q_heads, head_dim, group_size, (C.c_int32 * 3)(*bits),
                   (C.c_int32 * 3)(*pool_blocks), max_seqs, max_blocks_per_seq, max_segments_per_seq,
                   max_tokens_per_call)

@@ -43,7 +43,8 @@ extern "C" int tkv_buffer_sizes(const tkv_layout* L, size_t sizes[TKV_NUM_BUFFER
   sizes[TKV_BUF_BTAB] = (size_t)L->max_seqs * 3 * L->max_blocks_per_seq * 4;
   sizes[TKV_BUF_SSTK] = (size_t)L->max_seqs * 3 * L->max_blocks_per_seq * TKV_BS * 4;
   sizes[TKV_BUF_SEGT] = (size_t)L->max_seqs * L->max_segments_per_seq * TKV_SEG_W * 4;
-  sizes[TKV_BUF_SCRATCH] = (size_t)(6 * TKV_MAX_TOK + 64) * 4;
+  sizes[TKV_BUF_SCRATCH] = ((size_t)(6 * TKV_MAX_TOK + 64) + (size_t)L->max_seqs +
+                            (size_t)L->max_seqs * L->max_blocks_per_seq * TKV_BS * 2) * 4;
   return TKV_OK;
 }
 

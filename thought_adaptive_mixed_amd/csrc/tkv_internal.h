@@ -10,7 +10,7 @@
 #define TKV_SEG_W 8               // words per segment record
 #define TKV_BLK_W 4               // words per block record
 #define TKV_SLOT_W 2              // words per slot record
-#define TKV_MAX_TOK 8192          // items per append / evict / plan call
+#define TKV_MAX_TOK 4096          // items per append / evict / plan call
 #define TKV_MAX_SEQS 1024
 #define TKV_MAX_BLOCKS 256        // per sequence and class
 #define TKV_INF 0x7fffffff
@@ -53,12 +53,17 @@ struct tkv_cache {
 __host__ __device__ inline int class_bits(int c) { return c == 0 ? 8 : (c == 1 ? 4 : 2); }
 __host__ __device__ inline int class_of_bits(int b) { return b == 8 ? 0 : (b == 4 ? 1 : (b == 2 ? 2 : -1)); }
 
-// Scratch carve-up (int32 words), sized 6*TKV_MAX_TOK + 64 by tkv_buffer_sizes.
+// Scratch carve-up (int32 words), sized by tkv_buffer_sizes as 6*TKV_MAX_TOK +
+// 64 + max_seqs (per-sequence move counts) + max_seqs*max_blocks*16*2 (moves).
 __host__ __device__ inline int32_t* scr_idx(int32_t* s) { return s; }                       // [MAX_TOK]
 __host__ __device__ inline int32_t* scr_info(int32_t* s) { return s + TKV_MAX_TOK; }        // [MAX_TOK]
 __host__ __device__ inline int32_t* scr_status(int32_t* s) { return s + 2 * TKV_MAX_TOK; }  // [MAX_TOK]
 __host__ __device__ inline int32_t* scr_need(int32_t* s) { return s + 3 * TKV_MAX_TOK; }    // [MAX_TOK]
 __host__ __device__ inline int32_t* scr_misc(int32_t* s) { return s + 6 * TKV_MAX_TOK; }    // [64]
+__host__ __device__ inline int32_t* scr_mcnt(int32_t* s) { return s + 6 * TKV_MAX_TOK + 64; }  // [max_seqs]
+__host__ __device__ inline int32_t* scr_moves(int32_t* s, int max_seqs) {                       // [max_seqs][max_blocks*16][2]
+  return s + 6 * TKV_MAX_TOK + 64 + max_seqs;
+}
 
 // ---------------------------------------------------------------------------
 // Code placement inside a (block, KV head) record.  Codes of one lane chunk

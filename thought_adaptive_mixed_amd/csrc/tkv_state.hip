@@ -101,100 +101,138 @@ int launch_init(tkv_cache* c, hipStream_t st) {
 // whose index exceeds what the pool holds marks the class dry from there on
 // and the walk is redone (at most once per class).  A final walk commits.
 // ---------------------------------------------------------------------------
-struct AppendWalk {
-  // per-sequence running state
-  int failed, fail_code, nblk[3], nslot[3], nseg, len, open_type, open_bits, nret, napp;
+// Per-class counters as scalars (selected by class) so that walks never index
+// private arrays dynamically (which would place them in scratch memory).
+struct C3 {
+  int a, b, c;
+  __device__ int get(int k) const { return k == 0 ? a : (k == 1 ? b : c); }
+  __device__ void add(int k, int d) { a += k == 0 ? d : 0; b += k == 1 ? d : 0; c += k == 2 ? d : 0; }
+};
+struct SeqRec {
+  C3 nblk, nslot;
+  int nseg, len, nret, napp, open_type, open_bits;
 };
 
-__device__ void append_walk(const DevState& S, int s, int n, const uint16_t* s_seq, const uint8_t* s_type,
-                            uint8_t* s_need, const int32_t* pos, const int* dry_from, const int* avail,
-                            const int32_t* idx, int32_t* info, int32_t* slot_out, bool commit) {
-  int32_t* q = S.seq + (int64_t)s * TKV_SEQ_W;
-  AppendWalk w;
-  w.failed = 0; w.fail_code = 0;
-  for (int c = 0; c < 3; c++) { w.nblk[c] = q[Q_NBLK + c]; w.nslot[c] = q[Q_NSLOT + c]; }
-  w.nseg = q[Q_NSEG]; w.len = q[Q_LEN]; w.nret = q[Q_NRET]; w.napp = q[Q_NAPP];
-  w.open_type = -1; w.open_bits = -1;
-  if (w.nseg > 0) {
-    const int32_t* g = S.segt + ((int64_t)s * S.max_segs + w.nseg - 1) * TKV_SEG_W;
-    w.open_type = g[G_TYPE]; w.open_bits = g[G_BITS];
+__device__ inline SeqRec load_seq(const DevState& S, int s) {
+  const int4* q4 = (const int4*)(S.seq + (int64_t)s * TKV_SEQ_W);
+  const int4 a = q4[0], b = q4[1], c = q4[2];
+  SeqRec r;
+  r.nblk = C3{a.x, a.y, a.z};
+  r.nslot = C3{a.w, b.x, b.y};
+  r.nseg = b.z; r.len = b.w;
+  r.nret = c.x; r.napp = c.y;
+  r.open_type = -1; r.open_bits = -1;
+  if (r.nseg > 0) {
+    const int2 g = *(const int2*)(S.segt + ((int64_t)s * S.max_segs + r.nseg - 1) * TKV_SEG_W);
+    r.open_type = g.x; r.open_bits = g.y;
   }
+  return r;
+}
+
+// s_flags: bits 0-1 thought type (3 = invalid), bit 2 = token needs a fresh block
+#define F_TYPE 3u
+#define F_NEED 4u
+
+__device__ void append_walk(const DevState& S, int s, SeqRec w, int n, const uint16_t* s_seq, uint8_t* s_flags,
+                            const int* s_pos, const int* dry_from, const int* avail, const uint16_t* s_idx,
+                            int32_t* info, int32_t* slot_out, bool commit) {
+  int failed = 0, fail_code = 0;
   int32_t* bt = S.btab + (int64_t)s * 3 * S.max_blocks;
   int32_t* st = S.sstk + (int64_t)s * 3 * S.max_blocks * TKV_BS;
-  for (int i = 0; i < n; i++) {
-    if (s_seq[i] != s) continue;
-    if (!commit) s_need[i] = 0;
-    if (w.failed) continue;
-    int y = s_type[i];
-    int p = pos[i];
-    if (y > 2 || p < w.len) { w.failed = 1; w.fail_code = TKV_EINVAL; continue; }
-    int c = S.type_class[y];
-    int cb = class_bits(c);
-    int new_seg = (w.nseg == 0) || (w.open_type != y) || (w.open_bits != cb);
-    if (new_seg && w.nseg == S.max_segs) { w.failed = 1; w.fail_code = TKV_ENOMEM; continue; }
-    int need = w.nslot[c] == 0;
-    if (need) {
-      if (w.nblk[c] == S.max_blocks || i >= dry_from[c]) { w.failed = 1; w.fail_code = TKV_ENOMEM; continue; }
-    }
+  // Each walker advances a cursor to its next token with cheap LDS compares;
+  // the body below then runs for all walkers of the wave together (not once
+  // per lane, as a plain scan of the list would make it).
+  int i = -1;
+  while (true) {
+    i++;
+    while (i < n && s_seq[i] != s) i++;
+    if (__builtin_amdgcn_ballot_w64(i < n) == 0) break;
+    if (i >= n) continue;
+    const uint32_t fl = s_flags[i];
+    if (!commit) s_flags[i] = (uint8_t)(fl & F_TYPE);
+    if (failed) continue;
+    const int y = (int)(fl & F_TYPE);
+    const int p = s_pos[i];
+    if (y > 2 || p < w.len) { failed = 1; fail_code = TKV_EINVAL; continue; }
+    const int c = S.type_class[y];
+    const int cb = class_bits(c);
+    const int new_seg = (w.nseg == 0) || (w.open_type != y) || (w.open_bits != cb);
+    if (new_seg && w.nseg == S.max_segs) { failed = 1; fail_code = TKV_ENOMEM; continue; }
+    const int need = w.nslot.get(c) == 0;
+    if (need && (w.nblk.get(c) == S.max_blocks || i >= dry_from[c])) { failed = 1; fail_code = TKV_ENOMEM; continue; }
     if (!commit) {
-      s_need[i] = (uint8_t)need;
-      if (need) { w.nblk[c]++; w.nslot[c] += TKV_BS; }
-      w.nslot[c]--;
+      if (need) { s_flags[i] = (uint8_t)((fl & F_TYPE) | F_NEED); w.nblk.add(c, 1); w.nslot.add(c, TKV_BS); }
+      w.nslot.add(c, -1);
       if (new_seg) { w.nseg++; w.open_type = y; w.open_bits = cb; }
       w.len = p + 1;
       continue;
     }
     // commit
+    const int ix = s_idx[i];
+    if (need && ix >= avail[c]) {   // cannot happen after the dry passes; keeps indexing in bounds
+      failed = 1; fail_code = TKV_ENOMEM; continue;
+    }
     int32_t* btc = bt + c * S.max_blocks;
     int32_t* stc = st + (int64_t)c * S.max_blocks * TKV_BS;
-    if (need && (idx[i] < 0 || idx[i] >= avail[c])) {   // cannot happen after the dry passes; keeps indexing in bounds
-      w.failed = 1; w.fail_code = TKV_ENOMEM; continue;
-    }
+    int slot;
     if (need) {
-      int blk = S.freestk[c][avail[c] - 1 - idx[i]];
-      btc[w.nblk[c]++] = blk;
+      // a fresh block: push its 16 slots (slot 0 on top) and pop slot 0
+      const int blk = S.freestk[c][avail[c] - 1 - ix];
+      const int nb = w.nblk.get(c), ns = w.nslot.get(c);
+      btc[nb] = blk;
       S.blk[c][(int64_t)blk * TKV_BLK_W + 2] = s;
-      for (int t = TKV_BS - 1; t >= 0; t--) stc[w.nslot[c]++] = blk * TKV_BS + t;
+      for (int t = TKV_BS - 1; t >= 1; t--) stc[ns + TKV_BS - 1 - t] = blk * TKV_BS + t;
+      w.nblk.add(c, 1);
+      w.nslot.add(c, TKV_BS - 1);
+      slot = blk * TKV_BS;
+    } else {
+      w.nslot.add(c, -1);
+      slot = stc[w.nslot.get(c)];
     }
-    int slot = stc[--w.nslot[c]];
     if (new_seg) {
       int32_t* g = S.segt + ((int64_t)s * S.max_segs + w.nseg) * TKV_SEG_W;
-      g[G_TYPE] = y; g[G_BITS] = cb; g[G_FIRST] = p; g[G_LAST] = p; g[G_NTOT] = 0; g[G_NRET] = 0;
-      g[6] = 0; g[7] = 0;
+      *(int4*)g = make_int4(y, cb, p, p);
+      *(int4*)(g + 4) = make_int4(1, 1, 0, 0);
       w.nseg++; w.open_type = y; w.open_bits = cb;
+    } else {
+      int32_t* g = S.segt + ((int64_t)s * S.max_segs + w.nseg - 1) * TKV_SEG_W;
+      g[G_LAST] = p; g[G_NTOT] += 1; g[G_NRET] += 1;
     }
-    int32_t* g = S.segt + ((int64_t)s * S.max_segs + w.nseg - 1) * TKV_SEG_W;
-    g[G_LAST] = p; g[G_NTOT] += 1; g[G_NRET] += 1;
-    int blk = slot / TKV_BS, t = slot % TKV_BS;
+    const int blk = slot / TKV_BS, t = slot % TKV_BS;
     int32_t* br = S.blk[c] + (int64_t)blk * TKV_BLK_W;
-    br[0] |= 1 << t;
-    if (p > br[1]) br[1] = p;
-    S.slot[c][(int64_t)slot * 2] = p;
-    S.slot[c][(int64_t)slot * 2 + 1] = w.nseg - 1;
+    atomicOr(&br[0], 1 << t);
+    atomicMax(&br[1], p);
+    *(int2*)(S.slot[c] + (int64_t)slot * 2) = make_int2(p, w.nseg - 1);
     w.len = p + 1; w.nret++; w.napp++;
-    int code = (c << 28) | slot;
+    const int code = (c << 28) | slot;
     info[i] = code;
     if (slot_out) slot_out[i] = code;
   }
   if (commit) {
-    for (int c = 0; c < 3; c++) { q[Q_NBLK + c] = w.nblk[c]; q[Q_NSLOT + c] = w.nslot[c]; }
-    q[Q_NSEG] = w.nseg; q[Q_LEN] = w.len; q[Q_NRET] = w.nret; q[Q_NAPP] = w.napp;
-    if (w.failed) record_error(S.hdr, w.fail_code, s);
+    int4* q4 = (int4*)(S.seq + (int64_t)s * TKV_SEQ_W);
+    q4[0] = make_int4(w.nblk.a, w.nblk.b, w.nblk.c, w.nslot.a);
+    q4[1] = make_int4(w.nslot.b, w.nslot.c, w.nseg, w.len);
+    S.seq[(int64_t)s * TKV_SEQ_W + Q_NRET] = w.nret;
+    S.seq[(int64_t)s * TKV_SEQ_W + Q_NAPP] = w.napp;
+    if (failed) record_error(S.hdr, fail_code, s);
   }
 }
 
 __global__ __launch_bounds__(WG) void k_append_alloc(DevState S, int n, const int32_t* seq_ids, const int32_t* pos,
                                                      const uint8_t* thought, int32_t* slot_out) {
   __shared__ uint16_t s_seq[TKV_MAX_TOK];
-  __shared__ uint8_t s_type[TKV_MAX_TOK];
-  __shared__ uint8_t s_need[TKV_MAX_TOK];
+  __shared__ uint8_t s_flags[TKV_MAX_TOK];
+  __shared__ int s_pos[TKV_MAX_TOK];
+  __shared__ uint16_t s_idx[TKV_MAX_TOK];
   __shared__ int s_tmp[48];
   __shared__ int dry_from[3], avail[3], viol[3], total[3];
   const int tid = threadIdx.x;
-  int32_t* idx = scr_idx(S.scratch);
   int32_t* info = scr_info(S.scratch);
+  const bool walker = tid < S.max_seqs;
+  SeqRec rec;
+  if (walker) rec = load_seq(S, tid);
   for (int i = tid; i < n; i += WG) {
-    int s = seq_ids[i];
+    const int s = seq_ids[i];
     info[i] = -1;
     if (slot_out) slot_out[i] = -1;
     if (s < 0 || s >= S.max_seqs) {
@@ -203,28 +241,29 @@ __global__ __launch_bounds__(WG) void k_append_alloc(DevState S, int n, const in
     } else {
       s_seq[i] = (uint16_t)s;
     }
-    s_type[i] = thought[i];
-    s_need[i] = 0;
+    const uint32_t y = thought[i];
+    s_flags[i] = (uint8_t)(y > 2 ? 3u : y);
+    s_pos[i] = pos[i];
   }
   if (tid < 3) { dry_from[tid] = TKV_INF; avail[tid] = S.hdr[H_FREE + tid]; }
   __syncthreads();
   const int per = (n + WG - 1) / WG;
   const int lo = tid * per, hi = min(n, lo + per);
   for (int iter = 0; iter < 4; iter++) {
-    if (tid < S.max_seqs)
-      append_walk(S, tid, n, s_seq, s_type, s_need, pos, dry_from, avail, idx, info, slot_out, false);
+    if (walker) append_walk(S, tid, rec, n, s_seq, s_flags, s_pos, dry_from, avail, s_idx, info, slot_out, false);
     __syncthreads();
     int v[3] = {0, 0, 0}, ex[3], tot[3];
     for (int i = lo; i < hi; i++)
-      if (s_need[i]) v[S.type_class[s_type[i]]]++;
+      if (s_flags[i] & F_NEED) v[S.type_class[s_flags[i] & F_TYPE]]++;
     wg_scan3(v, ex, tot, s_tmp);
     if (tid < 3) viol[tid] = TKV_INF;
     __syncthreads();
     for (int i = lo; i < hi; i++) {
-      if (!s_need[i]) continue;
-      int c = S.type_class[s_type[i]];
-      idx[i] = ex[c]++;
-      if (idx[i] >= avail[c]) atomicMin(&viol[c], i);
+      if (!(s_flags[i] & F_NEED)) continue;
+      const int c = S.type_class[s_flags[i] & F_TYPE];
+      const int ix = ex[c]++;
+      s_idx[i] = (uint16_t)ix;
+      if (ix >= avail[c]) atomicMin(&viol[c], i);
     }
     if (tid < 3) total[tid] = tot[tid];
     __syncthreads();
@@ -237,101 +276,125 @@ __global__ __launch_bounds__(WG) void k_append_alloc(DevState S, int n, const in
   }
   __threadfence_block();
   __syncthreads();
-  if (tid < S.max_seqs)
-    append_walk(S, tid, n, s_seq, s_type, s_need, pos, dry_from, avail, idx, info, slot_out, true);
+  if (walker) append_walk(S, tid, rec, n, s_seq, s_flags, s_pos, dry_from, avail, s_idx, info, slot_out, true);
   __syncthreads();
   if (tid < 3) S.hdr[H_FREE + tid] = avail[tid] - total[tid];
 }
 
 // ---------------------------------------------------------------------------
-// Append, part 2: quantize and pack.  One thread per (token, KV head, tensor)
-// row; K codes of a token fill whole words of its own chunks (plain stores);
-// V codes of 4 tokens share bytes, so 4- and 2-bit V codes are merged with
-// atomic AND/OR on their words.
+// Append, part 2: quantize and pack.  One wave per (token, KV head, tensor)
+// row: lane l holds elements E*l .. E*l+E-1 (E = D/64); a group's min and max
+// are butterfly reductions over its g/E lanes; every lane of the group then
+// derives the same fp16 scale and zero-point and quantizes its own elements.
+// The codes go through a per-wave LDS row so that each lane can assemble
+// whole 32-bit words: a token's K codes fill whole words of its own chunks
+// (plain stores); its V codes share words with 3 other tokens, so 4- and
+// 2-bit V fields are merged with atomic AND/OR (8-bit ones are byte stores).
 // ---------------------------------------------------------------------------
-template <class Get>
-__device__ void store_row(const DevState& S, int c, int blk, int t, int h, int kv, Get get) {
-  const int D = S.D, g = S.g, NG = S.NG, bits = class_bits(c);
-  uint8_t* base = S.pool[c] + ((int64_t)blk * S.Hkv + h) * S.bh_bytes[c];
-  uint8_t codes[128];
-  for (int gi = 0; gi < NG; gi++) {
-    float sf, zf; uint16_t sh, zh;
-    auto gg = [&](int i) { return get(gi * g + i); };
-    quant_scale_zero(gg, g, bits, sf, zf, sh, zh);
-    for (int i = 0; i < g; i++) codes[gi * g + i] = (uint8_t)quant_code(get(gi * g + i), sf, zf, bits);
-    *(uint32_t*)(base + meta_byte(D, g, bits, kv, t, gi)) = (uint32_t)sh | ((uint32_t)zh << 16);
-  }
-  const int W = 32 / bits;
-  const int cw = D * bits / 32 / 4;            // words per chunk
-  if (kv == 0) {
-    // chunk 16*lg + t holds dims gi*g + lg*(g/4) + e' at element gi*(g/4) + e'
-    const int q4 = g / 4;
-    for (int lg = 0; lg < 4; lg++) {
-      uint32_t* ch = (uint32_t*)(base + (16 * lg + t) * (D * bits / 32));
-      for (int w = 0; w < cw; w++) {
-        uint32_t word = 0;
-        for (int f = 0; f < W; f++) {
-          int e = w * W + f;
-          int d = (e / q4) * g + lg * q4 + (e % q4);
-          int p = (f >> 1) + (f & 1) * (W >> 1);
-          word |= (uint32_t)codes[d] << (p * bits);
-        }
-        ch[w] = word;
-      }
-    }
-  } else {
-    // chunk 16*q + i, element 4n + r, for token t = 4q + r and dim d = 16n + i
-    const int q = t >> 2, r = t & 3;
-    uint8_t* vbase = base + 64 * (D * bits / 32);
-    for (int i = 0; i < 16; i++) {
-      uint8_t* ch = vbase + (16 * q + i) * (D * bits / 32);
-      if (bits == 8) {
-        for (int n = 0; n < D / 16; n++) {
-          int e = 4 * n + r;
-          int bit = elem_bit(e, 8);
-          ch[bit >> 3] = codes[16 * n + i];
-        }
-      } else {
-        for (int w = 0; w < cw; w++) {
-          uint32_t mask = 0, val = 0;
-          for (int f = 0; f < W; f++) {
-            int e = w * W + f;
-            if ((e & 3) != r) continue;
-            int n = e >> 2;
-            int p = (f >> 1) + (f & 1) * (W >> 1);
-            mask |= ((1u << bits) - 1u) << (p * bits);
-            val |= (uint32_t)codes[16 * n + i] << (p * bits);
-          }
-          uint32_t* wp = (uint32_t*)ch + w;
-          atomicAnd(wp, ~mask);
-          atomicOr(wp, val);
-        }
-      }
-    }
-  }
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__global__ void k_append_store(DevState S, int n, const float* k, const float* v) {
-  int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int64_t total = (int64_t)n * S.Hkv * 2;
-  if (gid >= total) return;
-  int kv = (int)(gid & 1);
-  int64_t th = gid >> 1;
-  int h = (int)(th % S.Hkv);
-  int i = (int)(th / S.Hkv);
-  int info = scr_info(S.scratch)[i];
+template <int E>
+__device__ void quant_row_wave(const DevState& S, int c, int blk, int t, int h, int kv, int lane, const float (&x)[E],
+                               uint8_t* codes /* per-wave LDS, D bytes */) {
+#pragma clang fp contract(off)
+  const int D = S.D, g = S.g, bits = class_bits(c);
+  const int lpg = g / E;                       // lanes per group
+  const int gi = (lane * E) / g;
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int e = 1; e < E; e++) { mn = x[e] < mn ? x[e] : mn; mx = x[e] > mx ? x[e] : mx; }
+  for (int o = 1; o < lpg; o <<= 1) {
+    const float a = __shfl_xor(mn, o, 64), b = __shfl_xor(mx, o, 64);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  // (the sign of a zero extremum cannot change the scale, the zero-point or any code)
+  const float levels = (float)((1 << bits) - 1);
+  const float range = mx - mn;
+  const float s32 = range / levels;
+  const uint16_t sh = f16_bits_rne(s32), zh = f16_bits_rne(mn);
+  const float sf = f16_bits_to_f32(sh), zf = f16_bits_to_f32(zh);
+#pragma unroll
+  for (int e = 0; e < E; e++) codes[lane * E + e] = (uint8_t)quant_code(x[e], sf, zf, bits);
+  uint8_t* base = S.pool[c] + ((int64_t)blk * S.Hkv + h) * S.bh_bytes[c];
+  if ((lane * E) % g == 0) *(uint32_t*)(base + meta_byte(D, g, bits, kv, t, gi)) = (uint32_t)sh | ((uint32_t)zh << 16);
+  wave_lds_sync();
+  const int W = 32 / bits;
+  const int CB = D * bits / 32;                // bytes per chunk
+  const int wpc = CB / 4;                      // words per chunk
+  if (kv == 0) {
+    // word l: chunk 16*lg + t, word w; element e = w*W + f holds dim (e/(g/4))*g + lg*(g/4) + e%(g/4)
+    const int q4 = g / 4;
+    for (int l = lane; l < 4 * wpc; l += 64) {
+      const int lg = l / wpc, w = l % wpc;
+      uint32_t word = 0;
+      for (int f = 0; f < W; f++) {
+        const int e = w * W + f;
+        const int d = (e / q4) * g + lg * q4 + (e % q4);
+        word |= (uint32_t)codes[d] << (((f >> 1) + (f & 1) * (W >> 1)) * bits);
+      }
+      *(uint32_t*)(base + (16 * lg + t) * CB + w * 4) = word;
+    }
+  } else {
+    // chunk 16*q + i, element 4n + r: token t = 4q + r, dim d = 16n + i
+    const int q = t >> 2, r = t & 3;
+    uint8_t* vbase = base + 64 * CB;
+    for (int l = lane; l < 16 * wpc; l += 64) {
+      const int i = l / wpc, w = l % wpc;
+      uint8_t* ch = vbase + (16 * q + i) * CB;
+      if (bits == 8) {
+        // word w holds dim n = w for tokens r = 0..3: our byte is field r
+        const int f = r, p = (f >> 1) + (f & 1) * 2;
+        ch[w * 4 + p] = codes[16 * w + i];
+      } else {
+        uint32_t mask = 0, val = 0;
+        for (int f = 0; f < W; f++) {
+          const int e = w * W + f;
+          if ((e & 3) != r) continue;
+          const int p = (f >> 1) + (f & 1) * (W >> 1);
+          mask |= ((1u << bits) - 1u) << (p * bits);
+          val |= (uint32_t)codes[16 * (e >> 2) + i] << (p * bits);
+        }
+        uint32_t* wp = (uint32_t*)ch + w;
+        atomicAnd(wp, ~mask);
+        atomicOr(wp, val);
+      }
+    }
+  }
+  wave_lds_sync();     // the LDS row may be reused by this wave's next row
+}
+
+template <int E>
+__global__ __launch_bounds__(256) void k_append_store(DevState S, int n, const float* k, const float* v) {
+  __shared__ uint8_t s_codes[4][128];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wv;
+  if (row >= (int64_t)n * S.Hkv * 2) return;
+  const int kv = (int)(row & 1);
+  const int h = (int)((row >> 1) % S.Hkv);
+  const int i = (int)((row >> 1) / S.Hkv);
+  const int info = scr_info(S.scratch)[i];
   if (info < 0) return;
-  int c = info >> 28, slot = info & 0x0FFFFFFF;
-  const float* row = (kv ? v : k) + ((int64_t)i * S.Hkv + h) * S.D;
-  store_row(S, c, slot / TKV_BS, slot % TKV_BS, h, kv, [&](int d) { return row[d]; });
+  const int c = info >> 28, slot = info & 0x0FFFFFFF;
+  const float* src = (kv ? v : k) + ((int64_t)i * S.Hkv + h) * S.D + lane * E;
+  float x[E];
+#pragma unroll
+  for (int e = 0; e < E; e++) x[e] = src[e];
+  quant_row_wave<E>(S, c, slot / TKV_BS, slot % TKV_BS, h, kv, lane, x, s_codes[wv]);
 }
 
 int launch_append(tkv_cache* c, int n, const int32_t* seq_ids, const int32_t* pos, const uint8_t* thought,
                   const float* k, const float* v, int32_t* slot_out, hipStream_t st) {
   if (n == 0) return TKV_OK;
   k_append_alloc<<<1, WG, 0, st>>>(c->S, n, seq_ids, pos, thought, slot_out);
-  int64_t total = (int64_t)n * c->S.Hkv * 2;
-  k_append_store<<<(int)((total + 255) / 256), 256, 0, st>>>(c->S, n, k, v);
+  const int64_t rows = (int64_t)n * c->S.Hkv * 2;
+  const int blocks = (int)((rows + 3) / 4);
+  if (c->S.D == 128) k_append_store<2><<<blocks, 256, 0, st>>>(c->S, n, k, v);
+  else k_append_store<1><<<blocks, 256, 0, st>>>(c->S, n, k, v);
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
 
@@ -341,57 +404,63 @@ int launch_append(tkv_cache* c, int n, const int32_t* seq_ids, const int32_t* po
 // status[j]: 1 = apply, 0 = skipped or failed.  need[j] = fresh blocks,
 // idx[j] = index of its first global pop.
 // ---------------------------------------------------------------------------
-__device__ void evict_walk(const DevState& S, int s, int n, const uint16_t* s_seq, const int32_t* seg_ids,
-                           const int32_t* keep_n, const uint8_t* new_bits, uint8_t* s_cls, int32_t* need,
-                           int32_t* status, const int* dry_from, bool final_pass) {
-  const int32_t* q = S.seq + (int64_t)s * TKV_SEQ_W;
-  int nslot[3], nblk[3];
-  for (int c = 0; c < 3; c++) { nslot[c] = q[Q_NSLOT + c]; nblk[c] = q[Q_NBLK + c]; }
-  int nseg = q[Q_NSEG];
+__device__ void evict_walk(const DevState& S, int s, const SeqRec& rec, int n, const uint16_t* s_seq,
+                           const int32_t* seg_ids, const int32_t* keep_n, const uint8_t* new_bits,
+                           const int2* s_seg, uint8_t* s_cls, int32_t* need, int32_t* status, const int* dry_from,
+                           bool final_pass) {
+  C3 nslot = rec.nslot, nblk = rec.nblk;
+  const int nseg = rec.nseg;
   int failed = 0, code = 0;
-  for (int j = 0; j < n; j++) {
-    if (s_seq[j] != s) continue;
+  int j = -1;
+  while (true) {
+    j++;
+    while (j < n && s_seq[j] != s) j++;
+    if (__builtin_amdgcn_ballot_w64(j < n) == 0) break;
+    if (j >= n) continue;
     need[j] = 0; status[j] = 0; s_cls[j] = 0;
     if (failed) continue;
-    int k = seg_ids[j];
+    const int k = seg_ids[j];
     if (k < 0 || k >= nseg) { failed = 1; code = TKV_ENOSEG; continue; }
     int dup = 0;
     for (int j2 = 0; j2 < j; j2++) if (s_seq[j2] == s && seg_ids[j2] == k) { dup = 1; break; }
-    const int32_t* g = S.segt + ((int64_t)s * S.max_segs + k) * TKV_SEG_W;
-    int nb = new_bits[j], gb = g[G_BITS];
+    const int nb = new_bits[j], gb = s_seg[j].x;
     if (dup || keep_n[j] < 0 || !(nb == 0 || nb == 2 || nb == 4 || nb == 8) || (nb != 0 && nb > gb)) {
       failed = 1; code = TKV_EINVAL; continue;
     }
-    int r = g[G_NRET];
+    const int r = s_seg[j].y;
     if (r == 0) { failed = 1; code = TKV_ENOSEG; continue; }
-    int c = class_of_bits(gb);
-    int keep = keep_n[j] < r ? keep_n[j] : r;
-    int down = (nb != 0 && nb < gb && keep > 0);
-    int c2 = down ? class_of_bits(nb) : c;
+    const int c = class_of_bits(gb);
+    const int keep = keep_n[j] < r ? keep_n[j] : r;
+    const int down = (nb != 0 && nb < gb && keep > 0);
+    const int c2 = down ? class_of_bits(nb) : c;
     int nd = 0;
     if (down) {
-      int have = nslot[c2];
+      const int have = nslot.get(c2);
       nd = keep > have ? (keep - have + TKV_BS - 1) / TKV_BS : 0;
-      if (nblk[c2] + nd > S.max_blocks) { failed = 1; code = TKV_ENOMEM; continue; }
+      if (nblk.get(c2) + nd > S.max_blocks) { failed = 1; code = TKV_ENOMEM; continue; }
       if (nd > 0 && j >= dry_from[c2]) { failed = 1; code = TKV_ENOMEM; continue; }
     }
-    int ev = r - keep;
-    nslot[c] += ev;
+    const int ev = r - keep;
+    nslot.add(c, ev);
     if (down) {
-      nblk[c2] += nd;
-      nslot[c2] = nslot[c2] + TKV_BS * nd - keep;
-      nslot[c] += keep;
+      nblk.add(c2, nd);
+      nslot.add(c2, TKV_BS * nd - keep);
+      nslot.add(c, keep);
     }
     need[j] = nd; status[j] = 1; s_cls[j] = (uint8_t)c2;
   }
   if (final_pass && failed) record_error(S.hdr, code, s);
 }
 
+#define EV_STAGE 2048     // ops whose fields are staged in LDS
 __global__ __launch_bounds__(WG) void k_evict_plan(DevState S, int n_cap, const int32_t* n_dev, const int32_t* seq_ids,
-                                                   const int32_t* seg_ids, const int32_t* keep_n,
-                                                   const uint8_t* new_bits) {
+                                                   const int32_t* g_seg, const int32_t* g_keep,
+                                                   const uint8_t* g_bits) {
   __shared__ uint16_t s_seq[TKV_MAX_TOK];
   __shared__ uint8_t s_cls[TKV_MAX_TOK];
+  __shared__ int32_t s_seg[EV_STAGE], s_keep[EV_STAGE];
+  __shared__ uint8_t s_bits[EV_STAGE];
+  __shared__ int2 s_segrec[TKV_MAX_TOK];   // (bits, retained) of each op's segment, read up front
   __shared__ int s_tmp[48];
   __shared__ int dry_from[3], avail[3], viol[3], total[3];
   const int tid = threadIdx.x;
@@ -401,11 +470,29 @@ __global__ __launch_bounds__(WG) void k_evict_plan(DevState S, int n_cap, const 
   int32_t* status = scr_status(S.scratch);
   int32_t* need = scr_need(S.scratch);
   int32_t* misc = scr_misc(S.scratch);
+  // op fields: staged in LDS when they fit, read in place otherwise
+  const bool staged = n <= EV_STAGE;
+  const int32_t* seg_ids = staged ? s_seg : g_seg;
+  const int32_t* keep_n = staged ? s_keep : g_keep;
+  const uint8_t* new_bits = staged ? s_bits : g_bits;
+  const bool walker = tid < S.max_seqs;
+  SeqRec rec;
+  if (walker) rec = load_seq(S, tid);
   for (int j = tid; j < n; j += WG) {
     int s = seq_ids[j];
+    const int k = g_seg[j];
+    if (staged) { s_seg[j] = k; s_keep[j] = g_keep[j]; s_bits[j] = g_bits[j]; }
     status[j] = 0; need[j] = 0; idx[j] = 0;
+    s_segrec[j] = make_int2(0, 0);
     if (s < 0 || s >= S.max_seqs) { s_seq[j] = 0xFFFF; record_error(S.hdr, TKV_EINVAL, s < 0 ? TKV_INF : s); }
-    else s_seq[j] = (uint16_t)s;
+    else {
+      s_seq[j] = (uint16_t)s;
+      if (k >= 0 && k < S.max_segs) {
+        const int2 gr = *(const int2*)(S.segt + ((int64_t)s * S.max_segs + k) * TKV_SEG_W + G_BITS);
+        const int nr = S.segt[((int64_t)s * S.max_segs + k) * TKV_SEG_W + G_NRET];
+        s_segrec[j] = make_int2(gr.x, nr);
+      }
+    }
   }
   if (tid < 3) { dry_from[tid] = TKV_INF; avail[tid] = S.hdr[H_FREE + tid]; }
   if (tid == 0) misc[3] = n;
@@ -413,8 +500,8 @@ __global__ __launch_bounds__(WG) void k_evict_plan(DevState S, int n_cap, const 
   const int per = (n + WG - 1) / WG;
   const int lo = tid * per, hi = min(n, lo + per);
   for (int iter = 0; iter < 4; iter++) {
-    if (tid < S.max_seqs)
-      evict_walk(S, tid, n, s_seq, seg_ids, keep_n, new_bits, s_cls, need, status, dry_from, false);
+    if (walker)
+      evict_walk(S, tid, rec, n, s_seq, seg_ids, keep_n, new_bits, s_segrec, s_cls, need, status, dry_from, false);
     __threadfence_block();
     __syncthreads();
     int v[3] = {0, 0, 0}, ex[3], tot[3];
@@ -440,7 +527,7 @@ __global__ __launch_bounds__(WG) void k_evict_plan(DevState S, int n_cap, const 
   }
   // final walk records the errors (state of the last iteration is the truth)
   if (tid < S.max_seqs)
-    evict_walk(S, tid, n, s_seq, seg_ids, keep_n, new_bits, s_cls, need, status, dry_from, true);
+    evict_walk(S, tid, rec, n, s_seq, seg_ids, keep_n, new_bits, s_segrec, s_cls, need, status, dry_from, true);
   __syncthreads();
   if (tid < 3) { misc[tid] = avail[tid]; S.hdr[H_FREE + tid] = avail[tid] - total[tid]; }
 }
@@ -462,11 +549,87 @@ __device__ float deq_code(const DevState& S, int c, int blk, int t, int h, int k
   return prod + zf;
 }
 
+// Sort m (position, slot) pairs by position (unique) in LDS: bitonic network
+// over the next power of two, padded with +inf positions.
+__device__ void lds_sort_pairs(int32_t* pos, int32_t* slot, int m, int tid, int nthreads) {
+  int n2 = 1;
+  while (n2 < m) n2 <<= 1;
+  for (int i = m + tid; i < n2; i += nthreads) { pos[i] = TKV_INF; slot[i] = -1; }
+  __syncthreads();
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < n2; i += nthreads) {
+        const int l = i ^ j;
+        if (l > i) {
+          const bool up = (i & k) == 0;
+          const int pi = pos[i], pl = pos[l];
+          if ((pi > pl) == up) {
+            pos[i] = pl; pos[l] = pi;
+            const int t = slot[i]; slot[i] = slot[l]; slot[l] = t;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Re-quantize one moved row (K or V of one KV head of one token) from the
+// fp32 values its old codes decode to, into its new slot.  One wave.
+__device__ void requant_row(const DevState& S, int src, int dst, int h, int kv, int lane, uint8_t* codes) {
+  const int c = src >> 28, old = src & 0x0FFFFFFF, c2 = dst >> 28, ns = dst & 0x0FFFFFFF;
+  const int ob = old / TKV_BS, ot = old % TKV_BS;
+  if (S.D == 128) {
+    float x[2];
+    for (int e = 0; e < 2; e++) x[e] = deq_code(S, c, ob, ot, h, kv, lane * 2 + e);
+    quant_row_wave<2>(S, c2, ns / TKV_BS, ns % TKV_BS, h, kv, lane, x, codes);
+  } else {
+    float x[1];
+    x[0] = deq_code(S, c, ob, ot, h, kv, lane);
+    quant_row_wave<1>(S, c2, ns / TKV_BS, ns % TKV_BS, h, kv, lane, x, codes);
+  }
+}
+
+// Deferred downgrade moves of all sequences, one wave per row: a flat grid
+// strides over sum(moves) * Hkv * 2 rows.
+#define RQ_THREADS 256
+__global__ __launch_bounds__(RQ_THREADS) void k_requant(DevState S) {
+  __shared__ int s_off[TKV_MAX_SEQS + 1];
+  __shared__ int s_tmp[48];
+  __shared__ uint8_t s_codes[RQ_THREADS / 64][128];
+  const int tid = threadIdx.x;
+  const int32_t* mcnt = scr_mcnt(S.scratch);
+  const int32_t* moves = scr_moves(S.scratch, S.max_seqs);
+  const int per_seq = S.max_blocks * TKV_BS * 2;
+  // exclusive prefix of the per-sequence move counts (rows = moves * Hkv * 2)
+  const int per = (S.max_seqs + RQ_THREADS - 1) / RQ_THREADS;
+  const int lo = tid * per, hi = min(S.max_seqs, lo + per);
+  int v[3] = {0, 0, 0}, ex[3], tot[3];
+  for (int i = lo; i < hi; i++) v[0] += mcnt[i];
+  wg_scan3(v, ex, tot, s_tmp);
+  int run = ex[0];
+  for (int i = lo; i < hi; i++) { s_off[i] = run; run += mcnt[i]; }
+  if (tid == 0) s_off[S.max_seqs] = tot[0];
+  __syncthreads();
+  const int total_rows = tot[0] * S.Hkv * 2;
+  const int wv = tid >> 6, lane = tid & 63;
+  const int nwaves = gridDim.x * (RQ_THREADS / 64);
+  for (int row = blockIdx.x * (RQ_THREADS / 64) + wv; row < total_rows; row += nwaves) {
+    const int kv = row & 1, h = (row >> 1) % S.Hkv, mv = (row >> 1) / S.Hkv;
+    // sequence owning move mv: last s with s_off[s] <= mv
+    int a = 0, b = S.max_seqs;
+    while (b - a > 1) { const int mid = (a + b) >> 1; if (s_off[mid] <= mv) a = mid; else b = mid; }
+    const int j = mv - s_off[a];
+    const int32_t* m2 = moves + (int64_t)a * per_seq + 2 * j;
+    requant_row(S, m2[0], m2[1], h, kv, lane, s_codes[wv]);
+  }
+}
+
 __global__ __launch_bounds__(EV_THREADS) void k_evict_apply(DevState S, const int32_t* seq_ids, const int32_t* seg_ids,
                                                             const int32_t* keep_n, const uint8_t* new_bits) {
   __shared__ int32_t s_pos[EV_MAXSLOT];
   __shared__ int32_t s_slot[EV_MAXSLOT];
-  __shared__ int32_t s_sorted[EV_MAXSLOT];
+  __shared__ uint8_t s_codes[EV_THREADS / 64][128];
   __shared__ int s_cnt;
   const int s = blockIdx.x, tid = threadIdx.x;
   const int32_t* status = scr_status(S.scratch);
@@ -477,6 +640,20 @@ __global__ __launch_bounds__(EV_THREADS) void k_evict_apply(DevState S, const in
   int32_t* q = S.seq + (int64_t)s * TKV_SEQ_W;
   int32_t* bt = S.btab + (int64_t)s * 3 * S.max_blocks;
   int32_t* st = S.sstk + (int64_t)s * 3 * S.max_blocks * TKV_BS;
+  int32_t* moves = scr_moves(S.scratch, S.max_seqs) + (int64_t)s * S.max_blocks * TKV_BS * 2;
+  // With one downgrade for this sequence in the call, its re-quantization is
+  // deferred to a wide kernel (the old slots cannot be overwritten within the
+  // call); with several, a later one could reuse slots an earlier one still
+  // reads from, so they are re-quantized here, in op order.
+  int ndown = 0;
+  for (int j = 0; j < n; j++)
+    if (seq_ids[j] == s && status[j] == 1 && need[j] >= 0) {
+      const int32_t* g = S.segt + ((int64_t)s * S.max_segs + seg_ids[j]) * TKV_SEG_W;
+      const int gb = g[G_BITS], nb = new_bits[j];
+      if (nb != 0 && nb < gb && keep_n[j] > 0) ndown++;
+    }
+  const bool defer = ndown <= 1;
+  int nmoves = 0;
   for (int j = 0; j < n; j++) {
     if (seq_ids[j] != s || status[j] != 1) continue;
     const int k = seg_ids[j];
@@ -502,12 +679,8 @@ __global__ __launch_bounds__(EV_THREADS) void k_evict_apply(DevState S, const in
     }
     __syncthreads();
     const int m = s_cnt < EV_MAXSLOT ? s_cnt : EV_MAXSLOT;
-    for (int a = tid; a < m; a += EV_THREADS) {
-      int pa = s_pos[a], rank = 0;
-      for (int b = 0; b < m; b++) rank += s_pos[b] < pa;
-      s_sorted[rank] = s_slot[a];
-    }
-    __syncthreads();
+    lds_sort_pairs(s_pos, s_slot, m, tid, EV_THREADS);
+    const int32_t* s_sorted = s_slot;
     if (keep > m) keep = m;                 // m == r on a consistent state
     const int ev = m - keep;
     const int ns_c = q[Q_NSLOT + c];
@@ -529,15 +702,24 @@ __global__ __launch_bounds__(EV_THREADS) void k_evict_apply(DevState S, const in
       __threadfence_block();
       __syncthreads();
       // re-quantize each kept token (K and V rows of every head) into its new slot
-      for (int wi = tid; wi < keep * S.Hkv * 2; wi += EV_THREADS) {
-        int kv = wi & 1, h = (wi >> 1) % S.Hkv, p = (wi >> 1) / S.Hkv;
-        int old = s_sorted[ev + p];
-        int ns;
-        if (p < S0) ns = st2[S0 - 1 - p];
-        else { int pp = p - S0; ns = bt[c2 * S.max_blocks + nbk2 + pp / TKV_BS] * TKV_BS + pp % TKV_BS; }
-        int ob = old / TKV_BS, ot = old % TKV_BS;
-        store_row(S, c2, ns / TKV_BS, ns % TKV_BS, h, kv,
-                  [&](int d) { return deq_code(S, c, ob, ot, h, kv, d); });
+      if (defer) {
+        for (int p = tid; p < keep; p += EV_THREADS) {
+          int ns;
+          if (p < S0) ns = st2[S0 - 1 - p];
+          else { int pp = p - S0; ns = bt[c2 * S.max_blocks + nbk2 + pp / TKV_BS] * TKV_BS + pp % TKV_BS; }
+          moves[2 * (nmoves + p)] = (c << 28) | s_sorted[ev + p];
+          moves[2 * (nmoves + p) + 1] = (c2 << 28) | ns;
+        }
+        nmoves += keep;
+      } else {
+        const int wv = tid >> 6, lane = tid & 63;
+        for (int row = wv; row < keep * S.Hkv * 2; row += EV_THREADS / 64) {
+          const int kv = row & 1, h = (row >> 1) % S.Hkv, p = (row >> 1) / S.Hkv;
+          int ns;
+          if (p < S0) ns = st2[S0 - 1 - p];
+          else { int pp = p - S0; ns = bt[c2 * S.max_blocks + nbk2 + pp / TKV_BS] * TKV_BS + pp % TKV_BS; }
+          requant_row(S, (c << 28) | s_sorted[ev + p], (c2 << 28) | ns, h, kv, lane, s_codes[wv]);
+        }
       }
       __threadfence_block();
       __syncthreads();
@@ -580,6 +762,7 @@ __global__ __launch_bounds__(EV_THREADS) void k_evict_apply(DevState S, const in
     __threadfence_block();
     __syncthreads();
   }
+  if (tid == 0) scr_mcnt(S.scratch)[s] = nmoves;
 }
 
 int launch_evict(tkv_cache* c, int n_ops, const int32_t* n_ops_dev, const int32_t* seq_ids, const int32_t* seg_ids,
@@ -587,6 +770,7 @@ int launch_evict(tkv_cache* c, int n_ops, const int32_t* n_ops_dev, const int32_
   if (n_ops == 0) return TKV_OK;
   k_evict_plan<<<1, WG, 0, st>>>(c->S, n_ops, n_ops_dev, seq_ids, seg_ids, keep_n, new_bits);
   k_evict_apply<<<c->S.max_seqs, EV_THREADS, 0, st>>>(c->S, seq_ids, seg_ids, keep_n, new_bits);
+  k_requant<<<512, RQ_THREADS, 0, st>>>(c->S);
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
 

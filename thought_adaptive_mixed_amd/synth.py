@@ -60,7 +60,7 @@ class Layout:
     max_seqs: int
     max_blocks_per_seq: int
     max_segments_per_seq: int
-    max_tokens_per_call: int = 8192
+    max_tokens_per_call: int = 4096
     bits: Tuple[int, int, int] = (8, 4, 2)
 
 
@@ -310,7 +310,7 @@ def tiny(seed=1001) -> Workload:
 
 
 def _static(name, seed, B, Hq, Hkv, D, g, lengths, n_keep, occupancy=None, permute=False, sinks=False,
-            windows=(0,), max_call=8192, slack_blocks=8, segs=None) -> Workload:
+            windows=(0,), max_call=4096, slack_blocks=8, segs=None) -> Workload:
     rng = np.random.default_rng(seed)
     plans = [plan_sequence(rng, int(lengths[b]), int(n_keep[b])) for b in range(B)]
     need = blocks_needed(plans)
