@@ -12,7 +12,7 @@ import pytest
 
 import helpers
 from thought_adaptive_mixed_amd import synth
-from test_gpu_parity import check_attention, gpu_attention, say
+from test_gpu_parity import _check_labels, check_attention, gpu_attention, say
 
 pytestmark = pytest.mark.gpu
 
@@ -73,18 +73,18 @@ def test_fullshape_churn():
     labels_d = torch.zeros(B, dtype=torch.uint8, device="cuda")
     tT, tE = ch.tau
     rng = np.random.default_rng(3)
+    amb = 0
     for s in range(steps):
         q, k, v, pos = ch.step_inputs(s)
         go, gs, gn = gpu_attention(gc, w.seq_ids, pos, q, k_self=k, v_self=v)
         ro, rs, rn = oc.attention(w.seq_ids, pos, q, k_self=k, v_self=v)
         sample = rng.choice(B, 8, replace=False)
         check_attention(f"step {s} rows", (go[sample], gs[sample], gn[sample]), (ro[sample], rs[sample], rn[sample]))
-        score = rs[..., 1].astype(np.float32).mean(axis=1)
-        assert np.all(np.abs(score - tT) > 1e-4) and np.all(np.abs(score - tE) > 1e-4), "score in ambiguity band"
         lab_o = oracle.classify(rs.astype(np.float32), tT, tE)
         binding.classify(dv(gs, np.float32), tT, tE, labels_d)
-        assert np.array_equal(labels_d.cpu().numpy(), lab_o), f"labels step {s}"
-        gc.append(seq_d, dv(pos, np.int32), labels_d, dv(k, np.float32), dv(v, np.float32))
+        amb += _check_labels(labels_d.cpu().numpy(), lab_o, rs, tT, tE, s)
+        # both sides append at the oracle's labels (they agree outside the band)
+        gc.append(seq_d, dv(pos, np.int32), dv(lab_o, np.uint8), dv(k, np.float32), dv(v, np.float32))
         oc.append(w.seq_ids, pos, lab_o, k, v)
         gc.plan_budget(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, *o, o_bits)
         ops = oc.plan_budget(w.seq_ids, ch.budget[0], ch.budget[1], max_ops)
@@ -98,3 +98,4 @@ def test_fullshape_churn():
         if s % 8 == 7:
             say(f"[churn-full] step {s}: state")
             helpers.compare_states(L, gc.export(), oc.export(), f"churn-full step {s}")
+    say(f"[churn-full] {steps} steps x {B} sequences: {amb} labels in the ambiguity band")

@@ -41,6 +41,18 @@ def gpu_attention(gc, seq_ids, q_pos, q, window=0, sinks=None, k_self=None, v_se
     return out.cpu().numpy(), stats.cpu().numpy(), n_att.cpu().numpy()
 
 
+AMBIGUITY = 1e-4     # half-width of the band around a threshold where either label is accepted
+
+
+def _check_labels(lab_g, lab_o, rs, tT, tE, step):
+    """GPU labels equal the oracle's wherever the oracle's score is farther
+    than AMBIGUITY from both thresholds; returns the number of in-band cases."""
+    score = rs[..., 1].astype(np.float32).mean(axis=1)
+    band = (np.abs(score - tT) <= AMBIGUITY) | (np.abs(score - tE) <= AMBIGUITY)
+    assert np.array_equal(lab_g[~band], lab_o[~band]), f"labels step {step}"
+    return int(band.sum())
+
+
 def check_attention(tag, got, ref):
     (go, gs, gn), (ro, rs, rn) = got, ref
     mabs, rl2 = helpers.attn_metrics(go, ro)
@@ -139,16 +151,18 @@ def test_churn_lockstep():
         check_attention(f"step {s}", (go, gs, gn), (ro, rs, rn)) if s % 16 == 0 else None
         mabs, rl2 = helpers.attn_metrics(go, ro)
         assert mabs <= TOL_ABS and rl2 <= TOL_L2 and np.abs(gs[..., 1:] - rs[..., 1:]).max() <= TOL_STAT, s
-        # labels: the oracle classifies its own statistics
-        score = rs[..., 1].astype(np.float32).mean(axis=1)
-        assert np.all(np.abs(score - tT) > 1e-4) and np.all(np.abs(score - tE) > 1e-4), "score in ambiguity band"
+        # labels: the oracle classifies its own statistics; the GPU's labels
+        # must agree wherever the oracle's score is outside the ambiguity band
         lab_o = oracle.classify(rs.astype(np.float32), tT, tE)
         from thought_adaptive_mixed_amd import binding
         binding.classify(dv(gs, np.float32), tT, tE, labels_d)
         lab_g = labels_d.cpu().numpy()
-        assert np.array_equal(lab_g, lab_o), f"labels step {s}"
+        if _check_labels(lab_g, lab_o, rs, tT, tE, s) == 0:
+            labels_in = labels_d          # the device labels drive the append directly
+        else:
+            labels_in = dv(lab_o, np.uint8)
         # append at the label's precision
-        gc.append(seq_d, dv(pos, np.int32), labels_d, dv(k, np.float32), dv(v, np.float32))
+        gc.append(seq_d, dv(pos, np.int32), labels_in, dv(k, np.float32), dv(v, np.float32))
         oc.append(w.seq_ids, pos, lab_o, k, v)
         # ladder + evict
         gc.plan_budget(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, o_seq, o_seg, o_keep, o_bits)
