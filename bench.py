@@ -37,6 +37,48 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+class HipEvents:
+    """Timing events of the HIP runtime torch has loaded, created with
+    hipEventDisableSystemFence: recording one then costs no system-scope cache
+    writeback / invalidation, which a default event performs and which would
+    both slow the following work and inflate what the event pair measures."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n, torch_events=False):
+        import ctypes as C
+        self.C = C
+        self.torch_events = torch_events
+        if torch_events:
+            import torch
+            self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+            return
+        self.hip = C.CDLL("libamdhip64.so.7")          # the runtime already in the process
+        self.hip.hipEventCreateWithFlags.argtypes = [C.c_void_p, C.c_uint]
+        self.hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = C.c_void_p()
+            if self.hip.hipEventCreateWithFlags(C.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(e)
+
+    def record(self, i, stream):
+        if self.torch_events:
+            self.ev[i].record()
+        elif self.hip.hipEventRecord(self.ev[i], self.C.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, i, j):
+        if self.torch_events:
+            return self.ev[i].elapsed_time(self.ev[j])
+        ms = self.C.c_float()
+        if self.hip.hipEventElapsedTime(self.C.byref(ms), self.ev[i], self.ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+
 def state_class_tokens(exported, L):
     """Retained tokens per (sequence, class) from an exported state."""
     out = np.zeros((L.max_seqs, 3), np.int64)
@@ -114,7 +156,7 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-only", action="store_true", help="time only the attention call (diagnostic)")
-    ap.add_argument("--no-graph", action="store_true", help="launch each call from Python instead of HIP graphs")
+    ap.add_argument("--torch-events", action="store_true", help="time with torch's default events (diagnostic)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path shards by "
@@ -167,76 +209,63 @@ def main():
     o_seq = torch.zeros(max_ops, dtype=torch.int32, device="cuda")
     o_seg, o_keep = torch.zeros_like(o_seq), torch.zeros_like(o_seq)
     o_bits = torch.zeros(max_ops, dtype=torch.uint8, device="cuda")
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(total_steps)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(total_steps)]
+    ev = HipEvents(2 * total_steps + 2, torch_events=args.torch_events)   # (before, after) each attention
 
-    def attn(s):
+    # every call's C arguments are converted once, before anything is timed
+    sh = torch.cuda.current_stream().cuda_stream
+    calls_a, calls_b = [], []
+    for s in range(total_steps):
         c = caches[s % R]
         q, k, v, pos = steps_in[s]
-        c.attention(seq_d, pos, q, out, ws, stats=stats, n_attended=n_att[s], k_self=k, v_self=v)
+        calls_a.append(c.attention(seq_d, pos, q, out, ws, stats=stats, n_attended=n_att[s], k_self=k, v_self=v,
+                                   stream=sh, prepare=True))
+        calls_b.append([
+            binding.classify(stats, ch.tau[0], ch.tau[1], labels, stream=sh, prepare=True),
+            c.append(seq_d, pos, labels, k, v, stream=sh, prepare=True),
+            c.plan_budget(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, o_seq, o_seg, o_keep, o_bits,
+                          stream=sh, prepare=True),
+            c.evict(o_seq, o_seg, o_keep, o_bits, n_ops_dev=n_ops, n_ops=max_ops, stream=sh, prepare=True),
+        ])
 
-    def rest(s):
-        c = caches[s % R]
-        q, k, v, pos = steps_in[s]
-        binding.classify(stats, ch.tau[0], ch.tau[1], labels)
-        c.append(seq_d, pos, labels, k, v)
-        c.plan_budget(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, o_seq, o_seg, o_keep, o_bits)
-        c.evict(o_seq, o_seg, o_keep, o_bits, n_ops_dev=n_ops, n_ops=max_ops)
-
-    # Each step as two HIP graphs (attention; classify..evict), captured before
-    # anything runs and replayed in order, so the host launches two graphs
-    # per step; the attention is timed with events between the launches.
-    graphs = None
-    if not args.no_graph:
-        log("[bench] capturing graphs")
-        graphs = []
-        torch.cuda.synchronize()
-        for s in range(total_steps):
-            ga, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-            with torch.cuda.graph(ga):
-                attn(s)
-            gb_ok = not args.attn_only
-            if gb_ok:
-                with torch.cuda.graph(gb):
-                    rest(s)
-            graphs.append((ga, gb if gb_ok else None))
-        torch.cuda.synchronize()
-
+    # Steps are launched eagerly on torch's current stream: on this stack a
+    # replayed HIP graph per step measured slower than direct launches.  The
+    # attention launch is bracketed by events on the same stream.
     def step(s):
-        ev_a[s].record()
-        if graphs:
-            graphs[s][0].replay()
-        else:
-            attn(s)
-        ev_b[s].record()
-        if args.attn_only:
-            return
-        if graphs:
-            graphs[s][1].replay()
-        else:
-            rest(s)
+        ev.record(2 * s, sh)
+        calls_a[s]()
+        ev.record(2 * s + 1, sh)
+        if not args.attn_only:
+            for f in calls_b[s]:
+                f()
 
     log("[bench] warmup")
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
     log("[bench] timed")
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    T0, T1 = 2 * total_steps, 2 * total_steps + 1
     torch.cuda.synchronize()
-    t_start.record()
+    h0 = time.perf_counter()
+    ev.record(T0, sh)
     for s in range(args.warmup, total_steps):
         step(s)
-    t_end.record()
+    ev.record(T1, sh)
+    h1 = time.perf_counter()
     torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    attn_ms = [ev_a[s].elapsed_time(ev_b[s]) for s in range(args.warmup, total_steps)]
+    ms_total = ev.elapsed_ms(T0, T1)
+    log(f"[bench] host enqueue {(h1 - h0) * 1e6 / args.steps:.1f} us/step, device {ms_total * 1e3 / args.steps:.1f} us/step")
+    attn_ms = [ev.elapsed_ms(2 * s, 2 * s + 1) for s in range(args.warmup, total_steps)]
     errs = [c.get_error() for c in caches]
     if any(e[0] for e in errs):
         log(f"[bench] WARNING device errors: {errs}")
     tokens = int(n_att[args.warmup:].sum().item())
     ms_step = ms_total / args.steps
     attn_avg = float(np.mean(attn_ms))
-    achieved = abytes / (attn_avg * 1e-3) / 1e9
+    # the cache changes a little from step to step (appends, evictions): scale
+    # the KV part of the byte count by the attended tokens actually seen
+    init_tokens = int(tok_c[:B].sum())
+    abytes_step = abytes - kvbytes + kvbytes * (tokens / args.steps) / max(init_tokens, 1)
+    achieved = abytes_step / (attn_avg * 1e-3) / 1e9
     result = {
         "metric": METRIC,
         "value": tokens / (ms_total * 1e-3),
@@ -254,13 +283,13 @@ def main():
                                "16k generated tokens/seq, 10% budget (1638 retained), R/E/T 8/4/2-bit, "
                                "planted-temperature queries; step = attention+classify+append+ladder+evict",
                    "batch": B, "copies": R, "attended_per_step": tokens / args.steps,
-                   "launch": "python" if args.no_graph else "hip graphs (2 per step)"},
+                   "launch": "eager, one stream"},
         "attn_ms": attn_avg,
         "attn_kv_tokens_per_s": (tokens / args.steps) / (attn_avg * 1e-3),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "paged_decode_attn (split-K kernel + combine kernel)",
-                     "bytes_per_launch": abytes},
+                     "kernel": "k_attn (paged_decode_attn; one launch per step)",
+                     "bytes_per_launch": abytes_step},
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")

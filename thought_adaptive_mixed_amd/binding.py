@@ -109,8 +109,33 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
 
-def _stream():
+def _stream(stream=None):
+    if stream is not None:
+        return C.c_void_p(int(stream))
     return C.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+class Prepared:
+    """One library call with its C arguments converted once; calling it
+    re-issues the call (for launch loops where argument marshalling would
+    otherwise dominate).  The referenced buffers must outlive it."""
+
+    __slots__ = ("fn", "args", "what", "keep")
+
+    def __init__(self, fn, args, what, keep=None):
+        self.fn, self.args, self.what, self.keep = fn, tuple(args), what, keep
+
+    def __call__(self):
+        rc = self.fn(*self.args)
+        if rc != TKV_OK:
+            raise TkvError(rc, self.what)
+
+
+def _issue(fn, args, what, prepare, keep=None):
+    if prepare:
+        return Prepared(fn, args, what, keep)
+    _check(fn(*args), what)
+    return None
 
 
 def make_layout(num_kv_heads, num_q_heads, head_dim, group_size, pool_blocks, max_seqs, max_blocks_per_seq,
@@ -161,34 +186,41 @@ class Cache:
         except Exception:
             pass
 
-    # -- calls ------------------------------------------------------------------
-    def append(self, seq_ids, positions, thought, k, v, slot_out=None):
+    # -- calls ----------------------------------------------------------------
+    # Each call enqueues on `stream` (a raw HIP stream handle; default: torch's
+    # current stream).  With prepare=True nothing is enqueued: a Prepared call
+    # is returned instead.
+    def append(self, seq_ids, positions, thought, k, v, slot_out=None, *, stream=None, prepare=False):
         n = int(seq_ids.numel())
-        _check(self.L.kv_append_quant(self.h, n, _ptr(seq_ids), _ptr(positions), _ptr(thought), _ptr(k), _ptr(v),
-                                      _ptr(slot_out), _stream()), "kv_append_quant")
+        args = (self.h, n, _ptr(seq_ids), _ptr(positions), _ptr(thought), _ptr(k), _ptr(v), _ptr(slot_out),
+                _stream(stream))
+        return _issue(self.L.kv_append_quant, args, "kv_append_quant", prepare)
 
-    def evict(self, seq_ids, seg_ids, keep_n, new_bits, n_ops_dev=None, n_ops=None):
+    def evict(self, seq_ids, seg_ids, keep_n, new_bits, n_ops_dev=None, n_ops=None, *, stream=None, prepare=False):
         n = int(seq_ids.numel()) if n_ops is None else int(n_ops)
-        _check(self.L.kv_evict_segment(self.h, n, _ptr(n_ops_dev), _ptr(seq_ids), _ptr(seg_ids), _ptr(keep_n),
-                                       _ptr(new_bits), _stream()), "kv_evict_segment")
+        args = (self.h, n, _ptr(n_ops_dev), _ptr(seq_ids), _ptr(seg_ids), _ptr(keep_n), _ptr(new_bits),
+                _stream(stream))
+        return _issue(self.L.kv_evict_segment, args, "kv_evict_segment", prepare)
 
-    def plan_budget(self, seq_ids, num, den, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits):
-        _check(self.L.kv_plan_budget(self.h, int(seq_ids.numel()), _ptr(seq_ids), int(num), int(den), int(max_ops),
-                                     _ptr(n_ops_dev), _ptr(op_seq), _ptr(op_seg), _ptr(op_keep), _ptr(op_bits),
-                                     _stream()), "kv_plan_budget")
+    def plan_budget(self, seq_ids, num, den, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits, *, stream=None,
+                    prepare=False):
+        args = (self.h, int(seq_ids.numel()), _ptr(seq_ids), int(num), int(den), int(max_ops), _ptr(n_ops_dev),
+                _ptr(op_seq), _ptr(op_seg), _ptr(op_keep), _ptr(op_bits), _stream(stream))
+        return _issue(self.L.kv_plan_budget, args, "kv_plan_budget", prepare)
 
-    def seq_reset(self, seq_ids):
-        _check(self.L.tkv_seq_reset(self.h, int(seq_ids.numel()), _ptr(seq_ids), _stream()), "tkv_seq_reset")
+    def seq_reset(self, seq_ids, *, stream=None):
+        _check(self.L.tkv_seq_reset(self.h, int(seq_ids.numel()), _ptr(seq_ids), _stream(stream)), "tkv_seq_reset")
 
     def workspace_bytes(self, batch, num_splits=0):
         return int(self.L.tkv_attn_workspace(self.h, int(batch), int(num_splits)))
 
     def attention(self, seq_ids, q_pos, q, out, workspace, stats=None, n_attended=None, k_self=None, v_self=None,
-                  sinks=None, window=0, topk=8, num_splits=0):
+                  sinks=None, window=0, topk=8, num_splits=0, *, stream=None, prepare=False):
         a = AttnArgs(int(seq_ids.numel()), _ptr(seq_ids), _ptr(q_pos), _ptr(q), _ptr(k_self), _ptr(v_self),
                      _ptr(sinks), int(window), int(topk), int(num_splits), _ptr(out), _ptr(stats), _ptr(n_attended),
                      _ptr(workspace), int(workspace.numel() * workspace.element_size()))
-        _check(self.L.paged_decode_attn(self.h, C.byref(a), _stream()), "paged_decode_attn")
+        args = (self.h, C.byref(a), _stream(stream))
+        return _issue(self.L.paged_decode_attn, args, "paged_decode_attn", prepare, keep=a)
 
     def get_error(self):
         k, m, n = C.c_int32(), C.c_int32(), C.c_int32()
@@ -211,7 +243,8 @@ class Cache:
         _check(self.L.tkv_import_state(self.h, ptrs), "tkv_import_state")
 
 
-def classify(stats, tau_T, tau_E, labels_out, score_kind=0):
+def classify(stats, tau_T, tau_E, labels_out, score_kind=0, *, stream=None, prepare=False):
     B, Hq = int(stats.shape[0]), int(stats.shape[1])
-    _check(load().thought_classify(B, Hq, _ptr(stats), C.c_float(tau_T), C.c_float(tau_E), int(score_kind),
-                                   _ptr(labels_out), _stream()), "thought_classify")
+    args = (B, Hq, _ptr(stats), C.c_float(tau_T), C.c_float(tau_E), int(score_kind), _ptr(labels_out),
+            _stream(stream))
+    return _issue(load().thought_classify, args, "thought_classify", prepare)

@@ -16,7 +16,7 @@ static int layout_ok(const tkv_layout* L) {
   if (L->group_size > L->head_dim) return 0;
   for (int t = 0; t < 3; t++) {
     if (class_of_bits(L->bits[t]) < 0) return 0;
-    if (L->pool_blocks[t] < 1) return 0;
+    if (L->pool_blocks[t] < 1 || L->pool_blocks[t] > TKV_MAX_POOL_BLOCKS) return 0;
   }
   if (L->max_seqs < 1 || L->max_seqs > TKV_MAX_SEQS) return 0;
   if (L->max_blocks_per_seq < 1 || L->max_blocks_per_seq > TKV_MAX_BLOCKS) return 0;
@@ -43,7 +43,7 @@ extern "C" int tkv_buffer_sizes(const tkv_layout* L, size_t sizes[TKV_NUM_BUFFER
   sizes[TKV_BUF_BTAB] = (size_t)L->max_seqs * 3 * L->max_blocks_per_seq * 4;
   sizes[TKV_BUF_SSTK] = (size_t)L->max_seqs * 3 * L->max_blocks_per_seq * TKV_BS * 4;
   sizes[TKV_BUF_SEGT] = (size_t)L->max_seqs * L->max_segments_per_seq * TKV_SEG_W * 4;
-  sizes[TKV_BUF_SCRATCH] = ((size_t)(6 * TKV_MAX_TOK + 64) + (size_t)L->max_seqs +
+  sizes[TKV_BUF_SCRATCH] = ((size_t)TKV_SCR_FIXED + (size_t)L->max_seqs +
                             (size_t)L->max_seqs * L->max_blocks_per_seq * TKV_BS * 2) * 4;
   return TKV_OK;
 }

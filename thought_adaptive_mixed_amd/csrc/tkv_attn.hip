@@ -303,9 +303,9 @@ __device__ inline void run_class(const AttnParams& P, int c, const int2* lst, in
                                  const float (&sumq)[D / GS], float alpha, AttnState<D, GS>& st) {
   typedef Blk<D, GS, BITS, WINDOW> B;
   const DevState& S = P.S;
-  const int64_t stride = (int64_t)S.Hkv * S.bh_bytes[c];
-  const uint8_t* pool = S.pool[c] + (int64_t)kvh * S.bh_bytes[c];
-  const int32_t* slot = S.slot[c];
+  const int64_t stride = (int64_t)S.Hkv * pick3(S.bh_bytes, c);
+  const uint8_t* pool = pick3(S.pool, c) + (int64_t)kvh * pick3(S.bh_bytes, c);
+  const int32_t* slot = pick3(S.slot, c);
   int e0 = next_live(lst, n, w, nw);
   if (e0 >= n) return;
   int e1 = next_live(lst, n, e0 + nw, nw);
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
       const int c = e < ncls[0] ? 0 : (e < ncls[0] + ncls[1] ? 1 : 2);
       const int i = e - (c == 0 ? 0 : (c == 1 ? ncls[0] : ncls[0] + ncls[1]));
       const int id = bt[c * S.max_blocks + j0s[c] + i];
-      const int2 rec = *(const int2*)(S.blk[c] + (int64_t)id * TKV_BLK_W);
+      const int2 rec = *(const int2*)(pick3(S.blk, c) + (int64_t)id * TKV_BLK_W);
       int m = rec.x;
       if (WINDOW && rec.y < lo_pos) m = 0;
       lst[c * lmax + i] = make_int2(id, m);

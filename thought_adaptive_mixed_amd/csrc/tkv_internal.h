@@ -13,6 +13,7 @@
 #define TKV_MAX_TOK 4096          // items per append / evict / plan call
 #define TKV_MAX_SEQS 1024
 #define TKV_MAX_BLOCKS 256        // per sequence and class
+#define TKV_MAX_POOL_BLOCKS (1 << 22)   // per class (global pop indices are packed in 23 bits)
 #define TKV_INF 0x7fffffff
 
 // SEQ record words
@@ -50,19 +51,32 @@ struct tkv_cache {
   hipStream_t last_stream;
 };
 
+// Per-class fields of DevState indexed by a run-time class: select among the
+// three kernel-argument values (held in scalar registers) instead of indexing
+// the by-value argument, which would turn into a load from the kernel-argument
+// segment on every use.
+template <class T>
+__device__ __forceinline__ T pick3(const T (&a)[3], int c) {
+  return c == 0 ? a[0] : (c == 1 ? a[1] : a[2]);
+}
+
 __host__ __device__ inline int class_bits(int c) { return c == 0 ? 8 : (c == 1 ? 4 : 2); }
 __host__ __device__ inline int class_of_bits(int b) { return b == 8 ? 0 : (b == 4 ? 1 : (b == 2 ? 2 : -1)); }
 
-// Scratch carve-up (int32 words), sized by tkv_buffer_sizes as 6*TKV_MAX_TOK +
-// 64 + max_seqs (per-sequence move counts) + max_seqs*max_blocks*16*2 (moves).
+// Scratch carve-up (int32 words), sized by tkv_buffer_sizes as TKV_SCR_FIXED +
+// max_seqs (per-sequence move counts) + max_seqs*max_blocks*16*2 (moves).
+#define TKV_SCR_FIXED (14 * TKV_MAX_TOK + 64)
 __host__ __device__ inline int32_t* scr_idx(int32_t* s) { return s; }                       // [MAX_TOK]
 __host__ __device__ inline int32_t* scr_info(int32_t* s) { return s + TKV_MAX_TOK; }        // [MAX_TOK]
 __host__ __device__ inline int32_t* scr_status(int32_t* s) { return s + 2 * TKV_MAX_TOK; }  // [MAX_TOK]
 __host__ __device__ inline int32_t* scr_need(int32_t* s) { return s + 3 * TKV_MAX_TOK; }    // [MAX_TOK]
-__host__ __device__ inline int32_t* scr_misc(int32_t* s) { return s + 6 * TKV_MAX_TOK; }    // [64]
-__host__ __device__ inline int32_t* scr_mcnt(int32_t* s) { return s + 6 * TKV_MAX_TOK + 64; }  // [max_seqs]
-__host__ __device__ inline int32_t* scr_moves(int32_t* s, int max_seqs) {                       // [max_seqs][max_blocks*16][2]
-  return s + 6 * TKV_MAX_TOK + 64 + max_seqs;
+__host__ __device__ inline int32_t* scr_list(int32_t* s) { return s + 4 * TKV_MAX_TOK; }    // [MAX_TOK] ops by sequence
+__host__ __device__ inline int32_t* scr_grp(int32_t* s) { return s + 5 * TKV_MAX_TOK; }     // [3][max_seqs] off, count, downgrades
+__host__ __device__ inline int32_t* scr_oprec(int32_t* s) { return s + 6 * TKV_MAX_TOK; }   // [MAX_TOK][8] op records
+__host__ __device__ inline int32_t* scr_misc(int32_t* s) { return s + 14 * TKV_MAX_TOK; }   // [64]
+__host__ __device__ inline int32_t* scr_mcnt(int32_t* s) { return s + TKV_SCR_FIXED; }      // [max_seqs]
+__host__ __device__ inline int32_t* scr_moves(int32_t* s, int max_seqs) {                    // [max_seqs][max_blocks*16][2]
+  return s + TKV_SCR_FIXED + max_seqs;
 }
 
 // ---------------------------------------------------------------------------

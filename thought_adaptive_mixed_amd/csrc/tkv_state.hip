@@ -16,26 +16,36 @@
 #define WG 1024
 
 // ---------------------------------------------------------------------------
-// Work-group exclusive scan of three counters per thread (list order follows
-// thread order).  Returns the totals in tot[3].
+// Scans.  A wave's inclusive prefix sum in six DPP steps: shifts by 1, 2, 4
+// and 8 lanes inside each row of 16, then row 15 / lane 31 broadcasts.
 // ---------------------------------------------------------------------------
-__device__ void wg_scan3(int v[3], int excl[3], int tot[3], int* s_tmp /* [3][WG/64] */) {
+__device__ inline int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return x;
+}
+__device__ inline int wave_total(int incl) { return __builtin_amdgcn_readlane(incl, 63); }
+
+// Work-group exclusive scan of three counters per thread (list order follows
+// thread order; any multiple of 64 threads up to 1024).  Returns the totals.
+__device__ void wg_scan3(int v[3], int excl[3], int tot[3], int* s_tmp /* [3][16] */) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
   int incl[3];
+#pragma unroll
   for (int c = 0; c < 3; c++) {
-    int x = v[c];
-    for (int o = 1; o < 64; o <<= 1) {
-      int y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
-    incl[c] = x;
-    if (lane == 63) s_tmp[c * 16 + wave] = x;
+    incl[c] = wave_incl_scan(v[c]);
+    if (lane == 63) s_tmp[c * 16 + wave] = incl[c];
   }
   __syncthreads();
+#pragma unroll
   for (int c = 0; c < 3; c++) {
     int base = 0, all = 0;
     for (int w = 0; w < nwave; w++) {
-      int t = s_tmp[c * 16 + w];
+      const int t = s_tmp[c * 16 + w];
       if (w < wave) base += t;
       all += t;
     }
@@ -45,17 +55,23 @@ __device__ void wg_scan3(int v[3], int excl[3], int tot[3], int* s_tmp /* [3][WG
   __syncthreads();
 }
 
+// Threads of the single-work-group state kernels: one walker per sequence.
+static inline int walker_threads(int max_seqs) {
+  const int t = (max_seqs + 63) / 64 * 64;
+  return t < 64 ? 64 : (t > WG ? WG : t);
+}
+
 // ---------------------------------------------------------------------------
 // init
 // ---------------------------------------------------------------------------
 __global__ void k_init_blocks(DevState S, int c) {
   int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= S.pool_blocks[c]) return;
-  int32_t* r = S.blk[c] + (int64_t)b * TKV_BLK_W;
+  if (b >= pick3(S.pool_blocks, c)) return;
+  int32_t* r = pick3(S.blk, c) + (int64_t)b * TKV_BLK_W;
   r[0] = 0; r[1] = -1; r[2] = -1; r[3] = 0;
   for (int t = 0; t < TKV_BS; t++) {
-    S.slot[c][((int64_t)b * TKV_BS + t) * 2] = -1;
-    S.slot[c][((int64_t)b * TKV_BS + t) * 2 + 1] = -1;
+    pick3(S.slot, c)[((int64_t)b * TKV_BS + t) * 2] = -1;
+    pick3(S.slot, c)[((int64_t)b * TKV_BS + t) * 2 + 1] = -1;
   }
 }
 __global__ void k_fill(int32_t* p, int64_t n, int32_t v) {
@@ -65,7 +81,7 @@ __global__ void k_fill(int32_t* p, int64_t n, int32_t v) {
 __global__ void k_init_hdr(DevState S) {
   if (threadIdx.x == 0) {
     for (int i = 0; i < 16; i++) S.hdr[i] = 0;
-    for (int c = 0; c < 3; c++) S.hdr[H_FREE + c] = S.pool_blocks[c];
+    for (int c = 0; c < 3; c++) S.hdr[H_FREE + c] = pick3(S.pool_blocks, c);
     S.hdr[H_EMINSEQ] = TKV_INF;
   }
 }
@@ -94,12 +110,53 @@ int launch_init(tkv_cache* c, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Append, part 1: allocation.  One work-group; thread s walks the token list
-// for sequence s.  A first walk simulates the sequence's stacks to flag the
-// tokens that need a fresh block; an exclusive scan over the list gives each
-// flagged token its index among the class's global pops.  The earliest token
-// whose index exceeds what the pool holds marks the class dry from there on
-// and the walk is redone (at most once per class).  A final walk commits.
+// Stable grouping of list items by sequence, in LDS: afterwards
+// s_list[s_off[s] .. s_off[s] + s_cnt[s]) holds, in list order, the items whose
+// key is s (keys >= max_seqs are left out); returns how many items were
+// grouped.  s_cnt must be zero on entry.
+// Whole work-group; max_seqs <= blockDim.x.
+// ---------------------------------------------------------------------------
+__device__ int group_by_seq(int n, int max_seqs, const uint16_t* s_key, int* s_cnt, int* s_off, uint16_t* s_list,
+                            int* s_tmp) {
+  const int tid = threadIdx.x, NT = blockDim.x;
+  for (int i = tid; i < n; i += NT) {
+    const int k = s_key[i];
+    if (k < max_seqs) atomicAdd(&s_cnt[k], 1);
+  }
+  __syncthreads();
+  int v[3] = {tid < max_seqs ? s_cnt[tid] : 0, 0, 0}, ex[3], tot[3];
+  wg_scan3(v, ex, tot, s_tmp);
+  if (tid < max_seqs) s_off[tid] = ex[0];
+  __syncthreads();
+  const uint32_t* kw = (const uint32_t*)s_key;
+  for (int i = tid; i < n; i += NT) {
+    const uint32_t k = s_key[i];
+    if ((int)k >= max_seqs) continue;
+    int rank = 0;
+    if (s_cnt[k] > 1) {                      // rank among the earlier items of the same sequence
+      int j = 0;
+      for (; j + 1 < i; j += 2) {
+        const uint32_t w = kw[j >> 1];
+        rank += ((w & 0xFFFFu) == k) + ((w >> 16) == k);
+      }
+      if (j < i) rank += s_key[j] == k;
+    }
+    s_list[s_off[k] + rank] = (uint16_t)i;
+  }
+  __syncthreads();
+  return tot[0];
+}
+
+// ---------------------------------------------------------------------------
+// Append, part 1: allocation.  One work-group.  Items are grouped by sequence
+// in LDS; thread s then walks sequence s's items in list order.  A first walk
+// simulates the sequence's stacks to flag the tokens that need a fresh block;
+// an exclusive scan over the list gives each flagged token its index among
+// the class's global pops.  The earliest token whose index exceeds what the
+// pool holds marks the class dry from there on and the walk is redone (at
+// most once per class).  A final walk commits.  The sequence record, its open
+// segment and the top of each slot stack are read before the grouping, so
+// their latency overlaps it; a segment's record is written once per call.
 // ---------------------------------------------------------------------------
 // Per-class counters as scalars (selected by class) so that walks never index
 // private arrays dynamically (which would place them in scratch memory).
@@ -107,13 +164,15 @@ struct C3 {
   int a, b, c;
   __device__ int get(int k) const { return k == 0 ? a : (k == 1 ? b : c); }
   __device__ void add(int k, int d) { a += k == 0 ? d : 0; b += k == 1 ? d : 0; c += k == 2 ? d : 0; }
+  __device__ void set(int k, int v) { a = k == 0 ? v : a; b = k == 1 ? v : b; c = k == 2 ? v : c; }
 };
 struct SeqRec {
   C3 nblk, nslot;
-  int nseg, len, nret, napp, open_type, open_bits;
+  int nseg, len, nret, napp;
+  int open_type, open_bits, open_first, open_last, open_ntot, open_nret;   // segment nseg-1
 };
 
-__device__ inline SeqRec load_seq(const DevState& S, int s) {
+__device__ inline SeqRec load_seq_rec(const DevState& S, int s) {
   const int4* q4 = (const int4*)(S.seq + (int64_t)s * TKV_SEQ_W);
   const int4 a = q4[0], b = q4[1], c = q4[2];
   SeqRec r;
@@ -121,40 +180,42 @@ __device__ inline SeqRec load_seq(const DevState& S, int s) {
   r.nslot = C3{a.w, b.x, b.y};
   r.nseg = b.z; r.len = b.w;
   r.nret = c.x; r.napp = c.y;
-  r.open_type = -1; r.open_bits = -1;
-  if (r.nseg > 0) {
-    const int2 g = *(const int2*)(S.segt + ((int64_t)s * S.max_segs + r.nseg - 1) * TKV_SEG_W);
-    r.open_type = g.x; r.open_bits = g.y;
-  }
+  r.open_type = -1; r.open_bits = -1; r.open_first = 0; r.open_last = 0; r.open_ntot = 0; r.open_nret = 0;
   return r;
+}
+__device__ inline void load_open_seg(const DevState& S, int s, SeqRec& r) {
+  if (r.nseg > 0) {
+    const int32_t* g = S.segt + ((int64_t)s * S.max_segs + r.nseg - 1) * TKV_SEG_W;
+    const int4 a = *(const int4*)g;
+    const int2 b = *(const int2*)(g + 4);
+    r.open_type = a.x; r.open_bits = a.y; r.open_first = a.z; r.open_last = a.w;
+    r.open_ntot = b.x; r.open_nret = b.y;
+  }
 }
 
 // s_flags: bits 0-1 thought type (3 = invalid), bit 2 = token needs a fresh block
 #define F_TYPE 3u
 #define F_NEED 4u
 
-__device__ void append_walk(const DevState& S, int s, SeqRec w, int n, const uint16_t* s_seq, uint8_t* s_flags,
-                            const int* s_pos, const int* dry_from, const int* avail, const uint16_t* s_idx,
-                            int32_t* info, int32_t* slot_out, bool commit) {
+__device__ void append_walk(const DevState& S, int s, SeqRec w, const C3& top, int cnt, const uint16_t* lst,
+                            uint8_t* s_flags, const int* s_pos, const int* dry_from, const int* avail,
+                            const uint16_t* s_idx, int32_t* info, int32_t* slot_out, bool commit) {
   int failed = 0, fail_code = 0;
   int32_t* bt = S.btab + (int64_t)s * 3 * S.max_blocks;
-  int32_t* st = S.sstk + (int64_t)s * 3 * S.max_blocks * TKV_BS;
-  // Each walker advances a cursor to its next token with cheap LDS compares;
-  // the body below then runs for all walkers of the wave together (not once
-  // per lane, as a plain scan of the list would make it).
-  int i = -1;
-  while (true) {
-    i++;
-    while (i < n && s_seq[i] != s) i++;
-    if (__builtin_amdgcn_ballot_w64(i < n) == 0) break;
-    if (i >= n) continue;
+  const int32_t* st = S.sstk + (int64_t)s * 3 * S.max_blocks * TKV_BS;
+  int popped = 0;              // bit c: class c's stack top (read up front) has been taken
+  C3 fresh{-1, -1, -1};        // block whose slots refilled class c's empty stack in this call
+  // the segment being extended: its index, whether this call opened it, and its fields
+  int cur = -1, cur_new = 0, cur_type = 0, cur_bits = 0, cur_first = 0, cur_last = 0, cur_ntot = 0, cur_nret = 0;
+  for (int r = 0; r < cnt; r++) {
+    const int i = lst[r];
     const uint32_t fl = s_flags[i];
     if (!commit) s_flags[i] = (uint8_t)(fl & F_TYPE);
     if (failed) continue;
     const int y = (int)(fl & F_TYPE);
     const int p = s_pos[i];
     if (y > 2 || p < w.len) { failed = 1; fail_code = TKV_EINVAL; continue; }
-    const int c = S.type_class[y];
+    const int c = pick3(S.type_class, y);
     const int cb = class_bits(c);
     const int new_seg = (w.nseg == 0) || (w.open_type != y) || (w.open_bits != cb);
     if (new_seg && w.nseg == S.max_segs) { failed = 1; fail_code = TKV_ENOMEM; continue; }
@@ -173,66 +234,87 @@ __device__ void append_walk(const DevState& S, int s, SeqRec w, int n, const uin
       failed = 1; fail_code = TKV_ENOMEM; continue;
     }
     int32_t* btc = bt + c * S.max_blocks;
-    int32_t* stc = st + (int64_t)c * S.max_blocks * TKV_BS;
+    int32_t* stc = S.sstk + (int64_t)s * 3 * S.max_blocks * TKV_BS + (int64_t)c * S.max_blocks * TKV_BS;
     int slot;
     if (need) {
       // a fresh block: push its 16 slots (slot 0 on top) and pop slot 0
-      const int blk = S.freestk[c][avail[c] - 1 - ix];
+      const int blk = pick3(S.freestk, c)[avail[c] - 1 - ix];
       const int nb = w.nblk.get(c), ns = w.nslot.get(c);
       btc[nb] = blk;
-      S.blk[c][(int64_t)blk * TKV_BLK_W + 2] = s;
+      pick3(S.blk, c)[(int64_t)blk * TKV_BLK_W + 2] = s;
       for (int t = TKV_BS - 1; t >= 1; t--) stc[ns + TKV_BS - 1 - t] = blk * TKV_BS + t;
       w.nblk.add(c, 1);
       w.nslot.add(c, TKV_BS - 1);
+      fresh.set(c, blk);
       slot = blk * TKV_BS;
     } else {
       w.nslot.add(c, -1);
-      slot = stc[w.nslot.get(c)];
+      const int at = w.nslot.get(c);
+      const int fb = fresh.get(c);
+      if (fb >= 0) slot = fb * TKV_BS + (TKV_BS - 1 - at);       // stack positions 0..14 hold slots 15..1
+      else if (!((popped >> c) & 1)) slot = top.get(c);
+      else slot = st[(int64_t)c * S.max_blocks * TKV_BS + at];
+      popped |= 1 << c;
     }
     if (new_seg) {
-      int32_t* g = S.segt + ((int64_t)s * S.max_segs + w.nseg) * TKV_SEG_W;
-      *(int4*)g = make_int4(y, cb, p, p);
-      *(int4*)(g + 4) = make_int4(1, 1, 0, 0);
+      if (cur >= 0) {   // close the previous segment of this call
+        int32_t* g = S.segt + ((int64_t)s * S.max_segs + cur) * TKV_SEG_W;
+        *(int4*)g = make_int4(cur_type, cur_bits, cur_first, cur_last);
+        *(int2*)(g + 4) = make_int2(cur_ntot, cur_nret);
+      }
+      cur = w.nseg; cur_new = 1; cur_type = y; cur_bits = cb; cur_first = p; cur_ntot = 0; cur_nret = 0;
       w.nseg++; w.open_type = y; w.open_bits = cb;
-    } else {
-      int32_t* g = S.segt + ((int64_t)s * S.max_segs + w.nseg - 1) * TKV_SEG_W;
-      g[G_LAST] = p; g[G_NTOT] += 1; g[G_NRET] += 1;
+    } else if (cur < 0) {   // extending the segment that was open before the call
+      cur = w.nseg - 1; cur_new = 0; cur_type = w.open_type; cur_bits = w.open_bits; cur_first = w.open_first;
+      cur_ntot = w.open_ntot; cur_nret = w.open_nret;
     }
+    cur_last = p; cur_ntot++; cur_nret++;
     const int blk = slot / TKV_BS, t = slot % TKV_BS;
-    int32_t* br = S.blk[c] + (int64_t)blk * TKV_BLK_W;
+    int32_t* br = pick3(S.blk, c) + (int64_t)blk * TKV_BLK_W;
     atomicOr(&br[0], 1 << t);
     atomicMax(&br[1], p);
-    *(int2*)(S.slot[c] + (int64_t)slot * 2) = make_int2(p, w.nseg - 1);
+    *(int2*)(pick3(S.slot, c) + (int64_t)slot * 2) = make_int2(p, w.nseg - 1);
     w.len = p + 1; w.nret++; w.napp++;
     const int code = (c << 28) | slot;
     info[i] = code;
     if (slot_out) slot_out[i] = code;
   }
   if (commit) {
+    if (cur >= 0) {
+      int32_t* g = S.segt + ((int64_t)s * S.max_segs + cur) * TKV_SEG_W;
+      if (cur_new) *(int4*)g = make_int4(cur_type, cur_bits, cur_first, cur_last);
+      else g[G_LAST] = cur_last;
+      *(int2*)(g + 4) = make_int2(cur_ntot, cur_nret);
+    }
     int4* q4 = (int4*)(S.seq + (int64_t)s * TKV_SEQ_W);
     q4[0] = make_int4(w.nblk.a, w.nblk.b, w.nblk.c, w.nslot.a);
     q4[1] = make_int4(w.nslot.b, w.nslot.c, w.nseg, w.len);
-    S.seq[(int64_t)s * TKV_SEQ_W + Q_NRET] = w.nret;
-    S.seq[(int64_t)s * TKV_SEQ_W + Q_NAPP] = w.napp;
+    *(int2*)(S.seq + (int64_t)s * TKV_SEQ_W + Q_NRET) = make_int2(w.nret, w.napp);
     if (failed) record_error(S.hdr, fail_code, s);
   }
 }
 
 __global__ __launch_bounds__(WG) void k_append_alloc(DevState S, int n, const int32_t* seq_ids, const int32_t* pos,
                                                      const uint8_t* thought, int32_t* slot_out) {
-  __shared__ uint16_t s_seq[TKV_MAX_TOK];
+  __shared__ __align__(16) uint16_t s_seq[TKV_MAX_TOK];
+  __shared__ uint16_t s_list[TKV_MAX_TOK];
+  __shared__ uint16_t s_idx[TKV_MAX_TOK];
   __shared__ uint8_t s_flags[TKV_MAX_TOK];
   __shared__ int s_pos[TKV_MAX_TOK];
-  __shared__ uint16_t s_idx[TKV_MAX_TOK];
+  __shared__ int s_cnt[TKV_MAX_SEQS], s_off[TKV_MAX_SEQS];
   __shared__ int s_tmp[48];
   __shared__ int dry_from[3], avail[3], viol[3], total[3];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, NT = blockDim.x;
   int32_t* info = scr_info(S.scratch);
   const bool walker = tid < S.max_seqs;
   SeqRec rec;
-  if (walker) rec = load_seq(S, tid);
-  for (int i = tid; i < n; i += WG) {
+  if (walker) rec = load_seq_rec(S, tid);
+  if (walker) s_cnt[tid] = 0;
+  if (tid < 3) { dry_from[tid] = TKV_INF; avail[tid] = S.hdr[H_FREE + tid]; }
+  for (int i = tid; i < n; i += NT) {
     const int s = seq_ids[i];
+    const uint32_t y = thought[i];
+    const int p = pos[i];
     info[i] = -1;
     if (slot_out) slot_out[i] = -1;
     if (s < 0 || s >= S.max_seqs) {
@@ -241,26 +323,38 @@ __global__ __launch_bounds__(WG) void k_append_alloc(DevState S, int n, const in
     } else {
       s_seq[i] = (uint16_t)s;
     }
-    const uint32_t y = thought[i];
     s_flags[i] = (uint8_t)(y > 2 ? 3u : y);
-    s_pos[i] = pos[i];
+    s_pos[i] = p;
   }
-  if (tid < 3) { dry_from[tid] = TKV_INF; avail[tid] = S.hdr[H_FREE + tid]; }
   __syncthreads();
-  const int per = (n + WG - 1) / WG;
+  // second round of reads (their latency overlaps the grouping below)
+  C3 top{-1, -1, -1};
+  if (walker) {
+    load_open_seg(S, tid, rec);
+    const int32_t* st = S.sstk + (int64_t)tid * 3 * S.max_blocks * TKV_BS;
+    const int64_t cs = (int64_t)S.max_blocks * TKV_BS;
+    if (rec.nslot.a > 0) top.a = st[rec.nslot.a - 1];
+    if (rec.nslot.b > 0) top.b = st[cs + rec.nslot.b - 1];
+    if (rec.nslot.c > 0) top.c = st[2 * cs + rec.nslot.c - 1];
+  }
+  group_by_seq(n, S.max_seqs, s_seq, s_cnt, s_off, s_list, s_tmp);
+  const int my_cnt = walker ? s_cnt[tid] : 0;
+  const uint16_t* my_list = s_list + (walker ? s_off[tid] : 0);
+  const int per = (n + NT - 1) / NT;
   const int lo = tid * per, hi = min(n, lo + per);
   for (int iter = 0; iter < 4; iter++) {
-    if (walker) append_walk(S, tid, rec, n, s_seq, s_flags, s_pos, dry_from, avail, s_idx, info, slot_out, false);
+    if (walker)
+      append_walk(S, tid, rec, top, my_cnt, my_list, s_flags, s_pos, dry_from, avail, s_idx, info, slot_out, false);
     __syncthreads();
     int v[3] = {0, 0, 0}, ex[3], tot[3];
     for (int i = lo; i < hi; i++)
-      if (s_flags[i] & F_NEED) v[S.type_class[s_flags[i] & F_TYPE]]++;
+      if (s_flags[i] & F_NEED) v[pick3(S.type_class, s_flags[i] & F_TYPE)]++;
     wg_scan3(v, ex, tot, s_tmp);
     if (tid < 3) viol[tid] = TKV_INF;
     __syncthreads();
     for (int i = lo; i < hi; i++) {
       if (!(s_flags[i] & F_NEED)) continue;
-      const int c = S.type_class[s_flags[i] & F_TYPE];
+      const int c = pick3(S.type_class, s_flags[i] & F_TYPE);
       const int ix = ex[c]++;
       s_idx[i] = (uint16_t)ix;
       if (ix >= avail[c]) atomicMin(&viol[c], i);
@@ -274,9 +368,8 @@ __global__ __launch_bounds__(WG) void k_append_alloc(DevState S, int n, const in
     if (tid == 0) dry_from[fc] = first;
     __syncthreads();
   }
-  __threadfence_block();
-  __syncthreads();
-  if (walker) append_walk(S, tid, rec, n, s_seq, s_flags, s_pos, dry_from, avail, s_idx, info, slot_out, true);
+  if (walker)
+    append_walk(S, tid, rec, top, my_cnt, my_list, s_flags, s_pos, dry_from, avail, s_idx, info, slot_out, true);
   __syncthreads();
   if (tid < 3) S.hdr[H_FREE + tid] = avail[tid] - total[tid];
 }
@@ -320,7 +413,7 @@ __device__ void quant_row_wave(const DevState& S, int c, int blk, int t, int h, 
   const float sf = f16_bits_to_f32(sh), zf = f16_bits_to_f32(zh);
 #pragma unroll
   for (int e = 0; e < E; e++) codes[lane * E + e] = (uint8_t)quant_code(x[e], sf, zf, bits);
-  uint8_t* base = S.pool[c] + ((int64_t)blk * S.Hkv + h) * S.bh_bytes[c];
+  uint8_t* base = pick3(S.pool, c) + ((int64_t)blk * S.Hkv + h) * pick3(S.bh_bytes, c);
   if ((lane * E) % g == 0) *(uint32_t*)(base + meta_byte(D, g, bits, kv, t, gi)) = (uint32_t)sh | ((uint32_t)zh << 16);
   wave_lds_sync();
   const int W = 32 / bits;
@@ -377,20 +470,21 @@ __global__ __launch_bounds__(256) void k_append_store(DevState S, int n, const f
   const int kv = (int)(row & 1);
   const int h = (int)((row >> 1) % S.Hkv);
   const int i = (int)((row >> 1) / S.Hkv);
-  const int info = scr_info(S.scratch)[i];
-  if (info < 0) return;
-  const int c = info >> 28, slot = info & 0x0FFFFFFF;
+  // the row's values do not depend on the slot: read them first
   const float* src = (kv ? v : k) + ((int64_t)i * S.Hkv + h) * S.D + lane * E;
   float x[E];
 #pragma unroll
   for (int e = 0; e < E; e++) x[e] = src[e];
+  const int info = scr_info(S.scratch)[i];
+  if (info < 0) return;
+  const int c = info >> 28, slot = info & 0x0FFFFFFF;
   quant_row_wave<E>(S, c, slot / TKV_BS, slot % TKV_BS, h, kv, lane, x, s_codes[wv]);
 }
 
 int launch_append(tkv_cache* c, int n, const int32_t* seq_ids, const int32_t* pos, const uint8_t* thought,
                   const float* k, const float* v, int32_t* slot_out, hipStream_t st) {
   if (n == 0) return TKV_OK;
-  k_append_alloc<<<1, WG, 0, st>>>(c->S, n, seq_ids, pos, thought, slot_out);
+  k_append_alloc<<<1, walker_threads(c->S.max_seqs), 0, st>>>(c->S, n, seq_ids, pos, thought, slot_out);
   const int64_t rows = (int64_t)n * c->S.Hkv * 2;
   const int blocks = (int)((rows + 3) / 4);
   if (c->S.D == 128) k_append_store<2><<<blocks, 256, 0, st>>>(c->S, n, k, v);
@@ -400,37 +494,39 @@ int launch_append(tkv_cache* c, int n, const int32_t* seq_ids, const int32_t* po
 
 // ---------------------------------------------------------------------------
 // Evict, part 1: validation and reservation of fresh lower-class blocks for
-// downgrades, in list order (same walk / scan / dry scheme as append).
-// status[j]: 1 = apply, 0 = skipped or failed.  need[j] = fresh blocks,
-// idx[j] = index of its first global pop.
+// downgrades, in list order (same grouping / walk / scan / dry scheme as
+// append).  Results in scratch: status[j] (1 = apply), need[j] (fresh blocks),
+// idx[j] (index of its first global pop); the ops of each sequence in list
+// order (list, offset, count) and its number of downgrades.
 // ---------------------------------------------------------------------------
-__device__ void evict_walk(const DevState& S, int s, const SeqRec& rec, int n, const uint16_t* s_seq,
+#define ST_APPLY 4u       // s_st: bits 0-1 target class, bit 2 = apply
+
+__device__ void evict_walk(const DevState& S, int s, const SeqRec& rec, int cnt, const uint16_t* lst,
                            const int32_t* seg_ids, const int32_t* keep_n, const uint8_t* new_bits,
-                           const int2* s_seg, uint8_t* s_cls, int32_t* need, int32_t* status, const int* dry_from,
-                           bool final_pass) {
+                           const uint16_t* s_segrec, uint8_t* s_st, int32_t* s_ni, const int* dry_from,
+                           int* ndown_out, bool final_pass) {
   C3 nslot = rec.nslot, nblk = rec.nblk;
   const int nseg = rec.nseg;
-  int failed = 0, code = 0;
-  int j = -1;
-  while (true) {
-    j++;
-    while (j < n && s_seq[j] != s) j++;
-    if (__builtin_amdgcn_ballot_w64(j < n) == 0) break;
-    if (j >= n) continue;
-    need[j] = 0; status[j] = 0; s_cls[j] = 0;
+  int failed = 0, code = 0, ndown = 0;
+  for (int r = 0; r < cnt; r++) {
+    const int j = lst[r];
+    // the final pass repeats the last simulated walk: it only records errors
+    // and leaves the per-op results (and the pop indices packed with them) alone
+    if (!final_pass) { s_ni[j] = 0; s_st[j] = 0; }
     if (failed) continue;
     const int k = seg_ids[j];
     if (k < 0 || k >= nseg) { failed = 1; code = TKV_ENOSEG; continue; }
     int dup = 0;
-    for (int j2 = 0; j2 < j; j2++) if (s_seq[j2] == s && seg_ids[j2] == k) { dup = 1; break; }
-    const int nb = new_bits[j], gb = s_seg[j].x;
+    for (int r2 = 0; r2 < r; r2++) if (seg_ids[lst[r2]] == k) { dup = 1; break; }
+    const int nb = new_bits[j];
+    const int sr = s_segrec[j];
+    const int c = sr >> 14, gb = class_bits(c);
     if (dup || keep_n[j] < 0 || !(nb == 0 || nb == 2 || nb == 4 || nb == 8) || (nb != 0 && nb > gb)) {
       failed = 1; code = TKV_EINVAL; continue;
     }
-    const int r = s_seg[j].y;
-    if (r == 0) { failed = 1; code = TKV_ENOSEG; continue; }
-    const int c = class_of_bits(gb);
-    const int keep = keep_n[j] < r ? keep_n[j] : r;
+    const int rr = sr & 0x3FFF;
+    if (rr == 0) { failed = 1; code = TKV_ENOSEG; continue; }
+    const int keep = keep_n[j] < rr ? keep_n[j] : rr;
     const int down = (nb != 0 && nb < gb && keep > 0);
     const int c2 = down ? class_of_bits(nb) : c;
     int nd = 0;
@@ -440,35 +536,39 @@ __device__ void evict_walk(const DevState& S, int s, const SeqRec& rec, int n, c
       if (nblk.get(c2) + nd > S.max_blocks) { failed = 1; code = TKV_ENOMEM; continue; }
       if (nd > 0 && j >= dry_from[c2]) { failed = 1; code = TKV_ENOMEM; continue; }
     }
-    const int ev = r - keep;
+    const int ev = rr - keep;
     nslot.add(c, ev);
     if (down) {
       nblk.add(c2, nd);
       nslot.add(c2, TKV_BS * nd - keep);
       nslot.add(c, keep);
     }
-    need[j] = nd; status[j] = 1; s_cls[j] = (uint8_t)c2;
+    if (!final_pass) { s_ni[j] = nd; s_st[j] = (uint8_t)(c2 | ST_APPLY); }
+    ndown += down;
   }
-  if (final_pass && failed) record_error(S.hdr, code, s);
+  if (final_pass) {
+    if (failed) record_error(S.hdr, code, s);
+    *ndown_out = ndown;
+  }
 }
 
-#define EV_STAGE 2048     // ops whose fields are staged in LDS
+#define EV_STAGE 1024     // ops whose fields are staged in LDS
 __global__ __launch_bounds__(WG) void k_evict_plan(DevState S, int n_cap, const int32_t* n_dev, const int32_t* seq_ids,
                                                    const int32_t* g_seg, const int32_t* g_keep,
                                                    const uint8_t* g_bits) {
-  __shared__ uint16_t s_seq[TKV_MAX_TOK];
-  __shared__ uint8_t s_cls[TKV_MAX_TOK];
+  __shared__ __align__(16) uint16_t s_seq[TKV_MAX_TOK];
+  __shared__ uint16_t s_list[TKV_MAX_TOK];
+  __shared__ int32_t s_ni[TKV_MAX_TOK];       // fresh blocks an op needs | index of its first pop << 9
+  __shared__ uint16_t s_segrec[TKV_MAX_TOK];   // retained tokens | class << 14 of each op's segment
+  __shared__ uint8_t s_st[TKV_MAX_TOK];
+  __shared__ int s_cnt[TKV_MAX_SEQS], s_off[TKV_MAX_SEQS];
   __shared__ int32_t s_seg[EV_STAGE], s_keep[EV_STAGE];
   __shared__ uint8_t s_bits[EV_STAGE];
-  __shared__ int2 s_segrec[TKV_MAX_TOK];   // (bits, retained) of each op's segment, read up front
   __shared__ int s_tmp[48];
   __shared__ int dry_from[3], avail[3], viol[3], total[3];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, NT = blockDim.x;
   int n = n_cap;
   if (n_dev) { int m = *n_dev; n = m < n_cap ? (m < 0 ? 0 : m) : n_cap; }
-  int32_t* idx = scr_idx(S.scratch);
-  int32_t* status = scr_status(S.scratch);
-  int32_t* need = scr_need(S.scratch);
   int32_t* misc = scr_misc(S.scratch);
   // op fields: staged in LDS when they fit, read in place otherwise
   const bool staged = n <= EV_STAGE;
@@ -476,45 +576,54 @@ __global__ __launch_bounds__(WG) void k_evict_plan(DevState S, int n_cap, const 
   const int32_t* keep_n = staged ? s_keep : g_keep;
   const uint8_t* new_bits = staged ? s_bits : g_bits;
   const bool walker = tid < S.max_seqs;
+  if (n == 0) {                 // nothing listed: every sequence's op count is zero
+    if (walker) scr_grp(S.scratch)[S.max_seqs + tid] = 0;
+    if (tid == 0) misc[3] = 0;
+    return;
+  }
   SeqRec rec;
-  if (walker) rec = load_seq(S, tid);
-  for (int j = tid; j < n; j += WG) {
-    int s = seq_ids[j];
+  if (walker) { rec = load_seq_rec(S, tid); s_cnt[tid] = 0; }
+  for (int j = tid; j < n; j += NT) {
+    const int s = seq_ids[j];
     const int k = g_seg[j];
     if (staged) { s_seg[j] = k; s_keep[j] = g_keep[j]; s_bits[j] = g_bits[j]; }
-    status[j] = 0; need[j] = 0; idx[j] = 0;
-    s_segrec[j] = make_int2(0, 0);
+    s_segrec[j] = 0; s_ni[j] = 0; s_st[j] = 0;
     if (s < 0 || s >= S.max_seqs) { s_seq[j] = 0xFFFF; record_error(S.hdr, TKV_EINVAL, s < 0 ? TKV_INF : s); }
     else {
       s_seq[j] = (uint16_t)s;
       if (k >= 0 && k < S.max_segs) {
-        const int2 gr = *(const int2*)(S.segt + ((int64_t)s * S.max_segs + k) * TKV_SEG_W + G_BITS);
-        const int nr = S.segt[((int64_t)s * S.max_segs + k) * TKV_SEG_W + G_NRET];
-        s_segrec[j] = make_int2(gr.x, nr);
+        const int32_t* g = S.segt + ((int64_t)s * S.max_segs + k) * TKV_SEG_W;
+        const int gb = g[G_BITS], nr = g[G_NRET];
+        s_segrec[j] = (uint16_t)((nr & 0x3FFF) | ((class_of_bits(gb) & 3) << 14));
       }
     }
   }
   if (tid < 3) { dry_from[tid] = TKV_INF; avail[tid] = S.hdr[H_FREE + tid]; }
   if (tid == 0) misc[3] = n;
   __syncthreads();
-  const int per = (n + WG - 1) / WG;
+  const int n_valid = group_by_seq(n, S.max_seqs, s_seq, s_cnt, s_off, s_list, s_tmp);
+  const int my_cnt = walker ? s_cnt[tid] : 0;
+  const uint16_t* my_list = s_list + (walker ? s_off[tid] : 0);
+  int ndown = 0;
+  const int per = (n + NT - 1) / NT;
   const int lo = tid * per, hi = min(n, lo + per);
   for (int iter = 0; iter < 4; iter++) {
     if (walker)
-      evict_walk(S, tid, rec, n, s_seq, seg_ids, keep_n, new_bits, s_segrec, s_cls, need, status, dry_from, false);
-    __threadfence_block();
+      evict_walk(S, tid, rec, my_cnt, my_list, seg_ids, keep_n, new_bits, s_segrec, s_st, s_ni, dry_from, &ndown,
+                 false);
     __syncthreads();
     int v[3] = {0, 0, 0}, ex[3], tot[3];
-    for (int j = lo; j < hi; j++) if (need[j] > 0) v[s_cls[j]] += need[j];
+    for (int j = lo; j < hi; j++) v[s_st[j] & 3] += s_ni[j] & 511;
     wg_scan3(v, ex, tot, s_tmp);
     if (tid < 3) viol[tid] = TKV_INF;
     __syncthreads();
     for (int j = lo; j < hi; j++) {
-      if (need[j] <= 0) continue;
-      int c = s_cls[j];
-      idx[j] = ex[c];
-      ex[c] += need[j];
-      if (idx[j] + need[j] > avail[c]) atomicMin(&viol[c], j);
+      const int nd = s_ni[j] & 511;
+      if (nd == 0) continue;
+      const int c = s_st[j] & 3;
+      s_ni[j] = nd | (ex[c] << 9);
+      if (ex[c] + nd > avail[c]) atomicMin(&viol[c], j);
+      ex[c] += nd;
     }
     if (tid < 3) total[tid] = tot[tid];
     __syncthreads();
@@ -526,20 +635,45 @@ __global__ __launch_bounds__(WG) void k_evict_plan(DevState S, int n_cap, const 
     __syncthreads();
   }
   // final walk records the errors (state of the last iteration is the truth)
-  if (tid < S.max_seqs)
-    evict_walk(S, tid, rec, n, s_seq, seg_ids, keep_n, new_bits, s_segrec, s_cls, need, status, dry_from, true);
+  if (walker)
+    evict_walk(S, tid, rec, my_cnt, my_list, seg_ids, keep_n, new_bits, s_segrec, s_st, s_ni, dry_from, &ndown,
+               true);
   __syncthreads();
+  // one record per listed op, grouped by sequence in list order: what the
+  // apply kernel needs, so that it reads nothing else about the op
+  int32_t* recs = scr_oprec(S.scratch);
+  for (int r = tid; r < n_valid; r += NT) {
+    const int j = s_list[r];
+    const int st = s_st[j], sr = s_segrec[j];
+    const int c = sr >> 14, rr = sr & 0x3FFF, k = seg_ids[j], nb = new_bits[j];
+    const int kn = keep_n[j], keep = kn < rr ? kn : rr;
+    int first = 0, span = 0;
+    if (st & ST_APPLY) {
+      const int2 fl = *(const int2*)(S.segt + ((int64_t)s_seq[j] * S.max_segs + k) * TKV_SEG_W + G_FIRST);
+      first = fl.x; span = fl.y - fl.x + 1;
+    }
+    int4* o = (int4*)(recs + 8 * r);
+    o[0] = make_int4((st & ST_APPLY ? 1 : 0) | (c << 4) | ((st & 3) << 8), k, keep, nb);
+    o[1] = make_int4(s_ni[j] & 511, s_ni[j] >> 9, first, span);
+  }
+  if (walker) {
+    int32_t* grp = scr_grp(S.scratch);
+    grp[tid] = s_off[tid];
+    grp[S.max_seqs + tid] = my_cnt;
+    grp[2 * S.max_seqs + tid] = ndown;
+  }
   if (tid < 3) { misc[tid] = avail[tid]; S.hdr[H_FREE + tid] = avail[tid] - total[tid]; }
 }
 
-// Evict, part 2: one work-group per sequence applies its ops in list order.
+// Evict, part 2: one work-group per sequence applies its own ops in list order.
 #define EV_THREADS 256
 #define EV_MAXSLOT (TKV_MAX_BLOCKS * TKV_BS)   // every slot of one class of one sequence
+#define EV_BMW 1024                            // position bitmap words: segments spanning <= 32768 positions
 
 __device__ float deq_code(const DevState& S, int c, int blk, int t, int h, int kv, int d) {
 #pragma clang fp contract(off)
   const int bits = class_bits(c);
-  const uint8_t* base = S.pool[c] + ((int64_t)blk * S.Hkv + h) * S.bh_bytes[c];
+  const uint8_t* base = pick3(S.pool, c) + ((int64_t)blk * S.Hkv + h) * pick3(S.bh_bytes, c);
   int bit = kv ? v_code_bit(S.D, bits, t, d) : k_code_bit(S.D, S.g, bits, t, d);
   uint32_t word = *(const uint32_t*)(base + ((bit >> 5) << 2));
   unsigned code = (word >> (bit & 31)) & ((1u << bits) - 1u);
@@ -625,18 +759,25 @@ __global__ __launch_bounds__(RQ_THREADS) void k_requant(DevState S) {
   }
 }
 
-__global__ __launch_bounds__(EV_THREADS) void k_evict_apply(DevState S, const int32_t* seq_ids, const int32_t* seg_ids,
-                                                            const int32_t* keep_n, const uint8_t* new_bits) {
+__global__ __launch_bounds__(EV_THREADS) void k_evict_apply(DevState S) {
   __shared__ int32_t s_pos[EV_MAXSLOT];
   __shared__ int32_t s_slot[EV_MAXSLOT];
+  __shared__ int32_t s_rank[EV_MAXSLOT];
+  __shared__ uint32_t s_bm[EV_BMW];
+  __shared__ int32_t s_bpre[EV_BMW];
   __shared__ uint8_t s_codes[EV_THREADS / 64][128];
+  __shared__ int s_tmp[48];
   __shared__ int s_cnt;
   const int s = blockIdx.x, tid = threadIdx.x;
-  const int32_t* status = scr_status(S.scratch);
-  const int32_t* idx = scr_idx(S.scratch);
-  const int32_t* need = scr_need(S.scratch);
+  const int32_t* grp = scr_grp(S.scratch);
+  const int cnt = grp[S.max_seqs + s];
+  if (cnt == 0) {
+    if (tid == 0) scr_mcnt(S.scratch)[s] = 0;
+    return;
+  }
+  const int32_t* recs = scr_oprec(S.scratch) + 8 * grp[s];
+  const int ndown = grp[2 * S.max_seqs + s];
   const int32_t* misc = scr_misc(S.scratch);
-  const int n = misc[3];
   int32_t* q = S.seq + (int64_t)s * TKV_SEQ_W;
   int32_t* bt = S.btab + (int64_t)s * 3 * S.max_blocks;
   int32_t* st = S.sstk + (int64_t)s * 3 * S.max_blocks * TKV_BS;
@@ -645,59 +786,87 @@ __global__ __launch_bounds__(EV_THREADS) void k_evict_apply(DevState S, const in
   // deferred to a wide kernel (the old slots cannot be overwritten within the
   // call); with several, a later one could reuse slots an earlier one still
   // reads from, so they are re-quantized here, in op order.
-  int ndown = 0;
-  for (int j = 0; j < n; j++)
-    if (seq_ids[j] == s && status[j] == 1 && need[j] >= 0) {
-      const int32_t* g = S.segt + ((int64_t)s * S.max_segs + seg_ids[j]) * TKV_SEG_W;
-      const int gb = g[G_BITS], nb = new_bits[j];
-      if (nb != 0 && nb < gb && keep_n[j] > 0) ndown++;
-    }
   const bool defer = ndown <= 1;
   int nmoves = 0;
-  for (int j = 0; j < n; j++) {
-    if (seq_ids[j] != s || status[j] != 1) continue;
-    const int k = seg_ids[j];
-    int32_t* g = S.segt + ((int64_t)s * S.max_segs + k) * TKV_SEG_W;
-    const int gb = g[G_BITS], c = class_of_bits(gb), r = g[G_NRET];
-    int keep = keep_n[j] < r ? keep_n[j] : r;
-    const int nb = new_bits[j];
+  for (int r0 = 0; r0 < cnt; r0++) {
+    const int4 o0 = *(const int4*)(recs + 8 * r0), o1 = *(const int4*)(recs + 8 * r0 + 4);
+    if (!(o0.x & 1)) continue;
+    const int c = (o0.x >> 4) & 3, c2 = (o0.x >> 8) & 3;
+    const int k = o0.y, nb = o0.w, gb = class_bits(c);
+    int keep = o0.z;
     const int down = (nb != 0 && nb < gb && keep > 0);
-    const int c2 = down ? class_of_bits(nb) : c;
-    // gather the segment's valid slots
+    const int nd = o1.x, base = o1.y, first = o1.z, span = o1.w;
+    int32_t* g = S.segt + ((int64_t)s * S.max_segs + k) * TKV_SEG_W;
+    // gather the segment's valid slots; rank them by position with a bitmap of
+    // the segment's position span (a sort when the span is too wide)
+    const bool use_bm = span > 0 && span <= EV_BMW * 32;
+    const int nbw = use_bm ? (span + 31) >> 5 : 0;
+    for (int w = tid; w < nbw; w += EV_THREADS) s_bm[w] = 0;
     if (tid == 0) s_cnt = 0;
     __syncthreads();
     const int nbk = q[Q_NBLK + c];
     for (int x = tid; x < nbk * TKV_BS; x += EV_THREADS) {
-      int blk = bt[c * S.max_blocks + x / TKV_BS], t = x % TKV_BS;
-      int mask = S.blk[c][(int64_t)blk * TKV_BLK_W];
-      if (((mask >> t) & 1) && S.slot[c][((int64_t)blk * TKV_BS + t) * 2 + 1] == k) {
-        int at = atomicAdd(&s_cnt, 1);
-        if (at >= EV_MAXSLOT) continue;
-        s_pos[at] = S.slot[c][((int64_t)blk * TKV_BS + t) * 2];
-        s_slot[at] = blk * TKV_BS + t;
-      }
+      const int blk = bt[c * S.max_blocks + x / TKV_BS], t = x % TKV_BS;
+      // both reads depend only on the block id: issued together
+      const int mask = pick3(S.blk, c)[(int64_t)blk * TKV_BLK_W];
+      const int2 sr = *(const int2*)(pick3(S.slot, c) + ((int64_t)blk * TKV_BS + t) * 2);
+      if (!((mask >> t) & 1) || sr.y != k) continue;
+      const int at = atomicAdd(&s_cnt, 1);
+      if (at >= EV_MAXSLOT) continue;
+      s_pos[at] = sr.x;
+      s_slot[at] = blk * TKV_BS + t;
+      const unsigned off = (unsigned)(sr.x - first);
+      if (use_bm && off < (unsigned)span) atomicOr(&s_bm[off >> 5], 1u << (off & 31));
     }
     __syncthreads();
     const int m = s_cnt < EV_MAXSLOT ? s_cnt : EV_MAXSLOT;
-    lds_sort_pairs(s_pos, s_slot, m, tid, EV_THREADS);
-    const int32_t* s_sorted = s_slot;
+    const int32_t* sorted;
+    if (use_bm) {
+      // exclusive prefix of the bitmap words' popcounts (EV_BMW / EV_THREADS words per thread)
+      int pc[EV_BMW / EV_THREADS], v[3] = {0, 0, 0}, ex[3], tot[3];
+#pragma unroll
+      for (int u = 0; u < EV_BMW / EV_THREADS; u++) {
+        const int w = tid * (EV_BMW / EV_THREADS) + u;
+        pc[u] = w < nbw ? __popc(s_bm[w]) : 0;
+        v[0] += pc[u];
+      }
+      wg_scan3(v, ex, tot, s_tmp);
+      int run = ex[0];
+#pragma unroll
+      for (int u = 0; u < EV_BMW / EV_THREADS; u++) {
+        s_bpre[tid * (EV_BMW / EV_THREADS) + u] = run;
+        run += pc[u];
+      }
+      __syncthreads();
+      for (int a = tid; a < m; a += EV_THREADS) {
+        const unsigned off = (unsigned)(s_pos[a] - first);
+        if (off >= (unsigned)span) continue;          // not on a consistent state
+        const int rk = s_bpre[off >> 5] + __popc(s_bm[off >> 5] & ((1u << (off & 31)) - 1u));
+        if (rk < m) s_rank[rk] = s_slot[a];
+      }
+      __syncthreads();
+      sorted = s_rank;
+    } else {
+      lds_sort_pairs(s_pos, s_slot, m, tid, EV_THREADS);
+      sorted = s_slot;
+    }
     if (keep > m) keep = m;                 // m == r on a consistent state
     const int ev = m - keep;
     const int ns_c = q[Q_NSLOT + c];
     for (int a = tid; a < ev; a += EV_THREADS) {
-      int sl = s_sorted[a];
-      atomicAnd(&S.blk[c][(int64_t)(sl / TKV_BS) * TKV_BLK_W], ~(1 << (sl % TKV_BS)));
+      int sl = sorted[a];
+      atomicAnd(&pick3(S.blk, c)[(int64_t)(sl / TKV_BS) * TKV_BLK_W], ~(1 << (sl % TKV_BS)));
       st[(int64_t)c * S.max_blocks * TKV_BS + ns_c + a] = sl;
     }
     if (down) {
       const int S0 = q[Q_NSLOT + c2];
       const int nbk2 = q[Q_NBLK + c2];
-      const int nd = need[j], base = idx[j], av = misc[c2];
+      const int av = misc[c2];
       int32_t* st2 = st + (int64_t)c2 * S.max_blocks * TKV_BS;
       for (int b = tid; b < nd; b += EV_THREADS) {
-        int blk = S.freestk[c2][av - 1 - (base + b)];
+        int blk = pick3(S.freestk, c2)[av - 1 - (base + b)];
         bt[c2 * S.max_blocks + nbk2 + b] = blk;
-        S.blk[c2][(int64_t)blk * TKV_BLK_W + 2] = s;
+        pick3(S.blk, c2)[(int64_t)blk * TKV_BLK_W + 2] = s;
       }
       __threadfence_block();
       __syncthreads();
@@ -707,7 +876,7 @@ __global__ __launch_bounds__(EV_THREADS) void k_evict_apply(DevState S, const in
           int ns;
           if (p < S0) ns = st2[S0 - 1 - p];
           else { int pp = p - S0; ns = bt[c2 * S.max_blocks + nbk2 + pp / TKV_BS] * TKV_BS + pp % TKV_BS; }
-          moves[2 * (nmoves + p)] = (c << 28) | s_sorted[ev + p];
+          moves[2 * (nmoves + p)] = (c << 28) | sorted[ev + p];
           moves[2 * (nmoves + p) + 1] = (c2 << 28) | ns;
         }
         nmoves += keep;
@@ -718,22 +887,22 @@ __global__ __launch_bounds__(EV_THREADS) void k_evict_apply(DevState S, const in
           int ns;
           if (p < S0) ns = st2[S0 - 1 - p];
           else { int pp = p - S0; ns = bt[c2 * S.max_blocks + nbk2 + pp / TKV_BS] * TKV_BS + pp % TKV_BS; }
-          requant_row(S, (c << 28) | s_sorted[ev + p], (c2 << 28) | ns, h, kv, lane, s_codes[wv]);
+          requant_row(S, (c << 28) | sorted[ev + p], (c2 << 28) | ns, h, kv, lane, s_codes[wv]);
         }
       }
       __threadfence_block();
       __syncthreads();
       for (int p = tid; p < keep; p += EV_THREADS) {
-        int old = s_sorted[ev + p];
+        int old = sorted[ev + p];
         int ns;
         if (p < S0) ns = st2[S0 - 1 - p];
         else { int pp = p - S0; ns = bt[c2 * S.max_blocks + nbk2 + pp / TKV_BS] * TKV_BS + pp % TKV_BS; }
-        int pos = S.slot[c][(int64_t)old * 2];
-        atomicOr(&S.blk[c2][(int64_t)(ns / TKV_BS) * TKV_BLK_W], 1 << (ns % TKV_BS));
-        atomicMax(&S.blk[c2][(int64_t)(ns / TKV_BS) * TKV_BLK_W + 1], pos);
-        S.slot[c2][(int64_t)ns * 2] = pos;
-        S.slot[c2][(int64_t)ns * 2 + 1] = k;
-        atomicAnd(&S.blk[c][(int64_t)(old / TKV_BS) * TKV_BLK_W], ~(1 << (old % TKV_BS)));
+        int pos = pick3(S.slot, c)[(int64_t)old * 2];
+        atomicOr(&pick3(S.blk, c2)[(int64_t)(ns / TKV_BS) * TKV_BLK_W], 1 << (ns % TKV_BS));
+        atomicMax(&pick3(S.blk, c2)[(int64_t)(ns / TKV_BS) * TKV_BLK_W + 1], pos);
+        pick3(S.slot, c2)[(int64_t)ns * 2] = pos;
+        pick3(S.slot, c2)[(int64_t)ns * 2 + 1] = k;
+        atomicAnd(&pick3(S.blk, c)[(int64_t)(old / TKV_BS) * TKV_BLK_W], ~(1 << (old % TKV_BS)));
         st[(int64_t)c * S.max_blocks * TKV_BS + ns_c + ev + p] = old;
       }
       __threadfence_block();
@@ -768,41 +937,98 @@ __global__ __launch_bounds__(EV_THREADS) void k_evict_apply(DevState S, const in
 int launch_evict(tkv_cache* c, int n_ops, const int32_t* n_ops_dev, const int32_t* seq_ids, const int32_t* seg_ids,
                  const int32_t* keep_n, const uint8_t* new_bits, hipStream_t st) {
   if (n_ops == 0) return TKV_OK;
-  k_evict_plan<<<1, WG, 0, st>>>(c->S, n_ops, n_ops_dev, seq_ids, seg_ids, keep_n, new_bits);
-  k_evict_apply<<<c->S.max_seqs, EV_THREADS, 0, st>>>(c->S, seq_ids, seg_ids, keep_n, new_bits);
+  k_evict_plan<<<1, walker_threads(c->S.max_seqs), 0, st>>>(c->S, n_ops, n_ops_dev, seq_ids, seg_ids, keep_n, new_bits);
+  k_evict_apply<<<c->S.max_seqs, EV_THREADS, 0, st>>>(c->S);
   k_requant<<<512, RQ_THREADS, 0, st>>>(c->S);
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
 
 // ---------------------------------------------------------------------------
-// Budget ladder: one thread per listed sequence counts and then writes its
-// ops at its exclusive-scan offset (list order).
+// Budget ladder.  Every listed sequence's record is read in parallel to find
+// those over budget; one wave then walks each of these, reading 64 segment
+// records at a time: the newest retained T segment is the highest set bit of
+// a ballot over the table read from its end; eviction candidates are T
+// segments (oldest first) and a candidate is taken while the retained count
+// before it still exceeds the budget, i.e. for a prefix of the candidates,
+// found with a prefix sum of their retained counts; the downgrade is the
+// lowest set bit of a ballot.  A first walk counts each sequence's ops, a scan
+// over the list places them, a second walk writes them.
 // ---------------------------------------------------------------------------
-__device__ int ladder(const DevState& S, int s, int num, int den, int base, int max_ops, int32_t* os, int32_t* og,
-                      int32_t* ok, uint8_t* ob, bool write) {
+__device__ inline bool over_budget(const DevState& S, int s, int num, int den) {
+  if (s < 0 || s >= S.max_seqs) return false;
+  const int32_t* q = S.seq + (int64_t)s * TKV_SEQ_W;
+  const int len = q[Q_LEN], nr = q[Q_NRET];
+  return (long long)nr > (long long)len * num / den;
+}
+
+// write: place the ops at base.. in the output lists; otherwise only count
+// them, keeping the first PL_STAGE_K (segment, keep, bits) in `stage` if given.
+#define PL_STAGE_K 8
+__device__ int ladder_wave(const DevState& S, int s, int num, int den, int base, int max_ops, int32_t* os,
+                           int32_t* og, int32_t* ok, uint8_t* ob, bool write, int lane, int2* stage) {
   if (s < 0 || s >= S.max_seqs) return 0;
   const int32_t* q = S.seq + (int64_t)s * TKV_SEQ_W;
-  const int nseg = q[Q_NSEG];
-  long long B = (long long)q[Q_LEN] * num / den;
-  long long nr = q[Q_NRET];
+  const int nseg = __builtin_amdgcn_readfirstlane(q[Q_NSEG]);
+  const int len = __builtin_amdgcn_readfirstlane(q[Q_LEN]);
+  const int nr0 = __builtin_amdgcn_readfirstlane(q[Q_NRET]);
+  const long long B = (long long)len * num / den;
+  long long nr = nr0;
   if (nr <= B) return 0;
   const int32_t* segs = S.segt + (int64_t)s * S.max_segs * TKV_SEG_W;
+  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  // newest retained T segment
   int newest_t = -1;
-  for (int k = 0; k < nseg; k++)
-    if (segs[k * TKV_SEG_W + G_TYPE] == TKV_T && segs[k * TKV_SEG_W + G_NRET] > 0) newest_t = k;
-  int m = 0;
-  for (int k = 0; k < nseg - 1 && nr > B; k++) {
-    const int32_t* g = segs + k * TKV_SEG_W;
-    if (g[G_TYPE] != TKV_T || g[G_NRET] == 0 || k == newest_t) continue;
-    if (write && base + m < max_ops) { os[base + m] = s; og[base + m] = k; ok[base + m] = 0; ob[base + m] = 0; }
-    m++;
-    nr -= g[G_NRET];
+  for (int b0 = ((nseg - 1) >> 6) << 6; b0 >= 0; b0 -= 64) {
+    const int k = b0 + lane;
+    bool hit = false;
+    if (k < nseg) {
+      const int32_t* g = segs + (int64_t)k * TKV_SEG_W;
+      hit = g[G_TYPE] == TKV_T && g[G_NRET] > 0;
+    }
+    const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
+    if (m) { newest_t = b0 + 63 - __builtin_clzll(m); break; }
   }
+  // whole T segments, oldest first, never the open one nor the newest retained T
+  int m = 0;
+  for (int b0 = 0; b0 < nseg - 1 && nr > B; b0 += 64) {
+    const int k = b0 + lane;
+    int amt = 0;
+    if (k < nseg - 1 && k != newest_t) {
+      const int32_t* g = segs + (int64_t)k * TKV_SEG_W;
+      if (g[G_TYPE] == TKV_T) amt = g[G_NRET];
+    }
+    const int incl = wave_incl_scan(amt);
+    const bool take = amt > 0 && nr - (incl - amt) > B;
+    const uint64_t tm = __builtin_amdgcn_ballot_w64(take);
+    if (take) {
+      const int rel = m + __popcll(tm & lt);
+      if (write) {
+        if (base + rel < max_ops) { os[base + rel] = s; og[base + rel] = k; ok[base + rel] = 0; ob[base + rel] = 0; }
+      } else if (stage && rel < PL_STAGE_K) {
+        stage[rel] = make_int2(k, 0);
+      }
+    }
+    m += __popcll(tm);
+    nr -= wave_total(wave_incl_scan(take ? amt : 0));
+  }
+  // then one downgrade: the oldest non-open E segment above 2 bits
   if (nr > B) {
-    for (int k = 0; k < nseg - 1; k++) {
-      const int32_t* g = segs + k * TKV_SEG_W;
-      if (g[G_TYPE] == TKV_E && g[G_BITS] > 2 && g[G_NRET] > 0) {
-        if (write && base + m < max_ops) { os[base + m] = s; og[base + m] = k; ok[base + m] = g[G_NRET]; ob[base + m] = 2; }
+    for (int b0 = 0; b0 < nseg - 1; b0 += 64) {
+      const int k = b0 + lane;
+      int r = 0;
+      if (k < nseg - 1) {
+        const int32_t* g = segs + (int64_t)k * TKV_SEG_W;
+        if (g[G_TYPE] == TKV_E && g[G_BITS] > 2) r = g[G_NRET];
+      }
+      const uint64_t hm = __builtin_amdgcn_ballot_w64(r > 0);
+      if (hm) {
+        if (lane == __builtin_ctzll(hm)) {
+          if (write) {
+            if (base + m < max_ops) { os[base + m] = s; og[base + m] = k; ok[base + m] = r; ob[base + m] = 2; }
+          } else if (stage && m < PL_STAGE_K) {
+            stage[m] = make_int2(k, r | (2 << 24));
+          }
+        }
         m++;
         break;
       }
@@ -811,23 +1037,66 @@ __device__ int ladder(const DevState& S, int s, int num, int den, int base, int 
   return m;
 }
 
+#define PL_STAGE_R 256     // over-budget sequences whose first ops are staged in LDS
 __global__ __launch_bounds__(WG) void k_plan(DevState S, int n, const int32_t* seq_ids, int num, int den, int max_ops,
                                              int32_t* n_ops, int32_t* os, int32_t* og, int32_t* ok, uint8_t* ob) {
+  __shared__ uint16_t s_over[TKV_MAX_TOK];   // items over budget, in list order
+  __shared__ int s_cnt[TKV_MAX_TOK];         // their op counts
+  __shared__ int s_base[TKV_MAX_TOK];        // their first op's index
+  __shared__ int2 s_stage[PL_STAGE_R][PL_STAGE_K];
   __shared__ int s_tmp[48];
-  const int tid = threadIdx.x;
-  const int per = (n + WG - 1) / WG;
+  const int tid = threadIdx.x, NT = blockDim.x, wv = tid >> 6, lane = tid & 63, NW = NT >> 6;
+  // 1. the listed sequences over budget
+  for (int i = tid; i < n; i += NT) s_cnt[i] = over_budget(S, seq_ids[i], num, den);
+  __syncthreads();
+  const int per = (n + NT - 1) / NT;
   const int lo = tid * per, hi = min(n, lo + per);
   int v[3] = {0, 0, 0}, ex[3], tot[3];
-  for (int i = lo; i < hi; i++) v[0] += ladder(S, seq_ids[i], num, den, 0, 0, os, og, ok, ob, false);
+  for (int i = lo; i < hi; i++) v[0] += s_cnt[i];
   wg_scan3(v, ex, tot, s_tmp);
-  int base = ex[0];
-  for (int i = lo; i < hi; i++) base += ladder(S, seq_ids[i], num, den, base, max_ops, os, og, ok, ob, true);
-  if (tid == 0) *n_ops = tot[0] < max_ops ? tot[0] : max_ops;
+  for (int i = lo, r = ex[0]; i < hi; i++) if (s_cnt[i]) s_over[r++] = (uint16_t)i;
+  const int nover = tot[0];
+  __syncthreads();
+  if (nover == 0) {
+    if (tid == 0) *n_ops = 0;
+    return;
+  }
+  // 2. count each one's ops (staging the first few), place them in list order, write them
+  for (int r = wv; r < nover; r += NW) {
+    const int s = __builtin_amdgcn_readfirstlane(seq_ids[s_over[r]]);
+    const int m = ladder_wave(S, s, num, den, 0, 0, os, og, ok, ob, false, lane,
+                              r < PL_STAGE_R ? s_stage[r] : nullptr);
+    if (lane == 0) s_cnt[r] = m;
+  }
+  __syncthreads();
+  const int per2 = (nover + NT - 1) / NT;
+  const int lo2 = tid * per2, hi2 = min(nover, lo2 + per2);
+  int v2[3] = {0, 0, 0}, ex2[3], tot2[3];
+  for (int r = lo2; r < hi2; r++) v2[0] += s_cnt[r];
+  wg_scan3(v2, ex2, tot2, s_tmp);
+  for (int r = lo2, run = ex2[0]; r < hi2; r++) { s_base[r] = run; run += s_cnt[r]; }
+  __syncthreads();
+  for (int r = wv; r < nover; r += NW) {
+    const int m = s_cnt[r], b0 = s_base[r];
+    if (m == 0) continue;
+    const int s = __builtin_amdgcn_readfirstlane(seq_ids[s_over[r]]);
+    if (r < PL_STAGE_R && m <= PL_STAGE_K) {
+      if (lane < m && b0 + lane < max_ops) {
+        const int2 e = s_stage[r][lane];
+        os[b0 + lane] = s; og[b0 + lane] = e.x; ok[b0 + lane] = e.y & 0xFFFFFF; ob[b0 + lane] = (uint8_t)(e.y >> 24);
+      }
+    } else {
+      ladder_wave(S, s, num, den, b0, max_ops, os, og, ok, ob, true, lane, nullptr);
+    }
+  }
+  if (tid == 0) *n_ops = tot2[0] < max_ops ? tot2[0] : max_ops;
 }
 
 int launch_plan(tkv_cache* c, int n, const int32_t* seq_ids, int num, int den, int max_ops, int32_t* n_ops_dev,
                 int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st) {
-  k_plan<<<1, WG, 0, st>>>(c->S, n, seq_ids, num, den, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits);
+  // a wave per listed sequence, up to 16 waves
+  const int nt = n < 1 ? 64 : (n >= WG / 64 ? WG : 64 * n);
+  k_plan<<<1, nt, 0, st>>>(c->S, n, seq_ids, num, den, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits);
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
 
@@ -862,9 +1131,9 @@ __global__ __launch_bounds__(WG) void k_seq_reset(DevState S, int n, const int32
     for (int c = 0; c < 3; c++) {
       for (int j = 0; j < q[Q_NBLK + c]; j++) {
         int blk = S.btab[((int64_t)s * 3 + c) * S.max_blocks + j];
-        int32_t* br = S.blk[c] + (int64_t)blk * TKV_BLK_W;
+        int32_t* br = pick3(S.blk, c) + (int64_t)blk * TKV_BLK_W;
         br[0] = 0; br[1] = -1; br[2] = -1;
-        S.freestk[c][base_cnt[c] + ex[c]++] = blk;
+        pick3(S.freestk, c)[base_cnt[c] + ex[c]++] = blk;
       }
     }
     for (int w = 0; w < TKV_SEQ_W; w++) q[w] = 0;
@@ -880,25 +1149,33 @@ int launch_seq_reset(tkv_cache* c, int n, const int32_t* seq_ids, hipStream_t st
 }
 
 // ---------------------------------------------------------------------------
-// thought_classify: fp32 mean over heads in head order, then thresholds.
+// thought_classify: one wave per batch entry; lane h reads head h's statistic
+// and the sum runs over the heads in head order (fp32, sequential), then the
+// thresholds.
 // ---------------------------------------------------------------------------
-__global__ void k_classify(int batch, int Hq, const float* stats, float tT, float tE, int kind, uint8_t* labels) {
+__global__ __launch_bounds__(256) void k_classify(int batch, int Hq, const float* stats, float tT, float tE, int kind,
+                                                  uint8_t* labels) {
 #pragma clang fp contract(off)
-  int b = blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (b >= batch) return;
   float sum = 0.0f;
-  for (int h = 0; h < Hq; h++) {
-    const float* st = stats + ((int64_t)b * Hq + h) * 3;
-    float v = kind == 0 ? st[1] : 1.0f - st[2];
-    sum = sum + v;
+  for (int h0 = 0; h0 < Hq; h0 += 64) {
+    const int h = h0 + lane;
+    float v = 0.0f;
+    if (h < Hq) {
+      const float* st = stats + ((int64_t)b * Hq + h) * 3;
+      v = kind == 0 ? st[1] : 1.0f - st[2];
+    }
+    const int m = Hq - h0 < 64 ? Hq - h0 : 64;
+    for (int j = 0; j < m; j++) sum = sum + __shfl(v, j, 64);
   }
-  float score = sum / (float)Hq;
-  labels[b] = score <= tT ? (uint8_t)TKV_T : (score >= tE ? (uint8_t)TKV_E : (uint8_t)TKV_R);
+  const float score = sum / (float)Hq;
+  if (lane == 0) labels[b] = score <= tT ? (uint8_t)TKV_T : (score >= tE ? (uint8_t)TKV_E : (uint8_t)TKV_R);
 }
 
 int launch_classify(int batch, int Hq, const float* stats, float tau_T, float tau_E, int kind, uint8_t* labels,
                     hipStream_t st) {
   if (batch == 0) return TKV_OK;
-  k_classify<<<(batch + 255) / 256, 256, 0, st>>>(batch, Hq, stats, tau_T, tau_E, kind, labels);
+  k_classify<<<(batch + 3) / 4, 256, 0, st>>>(batch, Hq, stats, tau_T, tau_E, kind, labels);
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
