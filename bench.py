@@ -112,6 +112,24 @@ def algorithmic_bytes(tokens_c, blocks_c, L, batch, self_token=True):
     return kv + blk + io, kv
 
 
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter summary
+    (profiles/), if the kernel's source files are still the ones the counters
+    were taken with; otherwise None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "k_attn_llama8b_B32_hbm_traffic.json")
+    try:
+        with open(path) as f:
+            j = json.load(f)
+        h = hashlib.sha256()
+        for name in j["source_files"]:
+            with open(os.path.join(ROOT, name), "rb") as f:
+                h.update(f.read())
+    except (OSError, KeyError, ValueError):
+        return None
+    return float(j["traffic_bytes_per_launch"]) if h.hexdigest() == j["source_sha256"] else None
+
+
 def cpu_baseline(w, state, ch, n_seq, reps_budget_s=20.0):
     """The oracle as it stands, on a sample of n_seq sequences of the same
     workload: one full step (attention with the self token, classify, append,
@@ -157,6 +175,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-only", action="store_true", help="time only the attention call (diagnostic)")
     ap.add_argument("--torch-events", action="store_true", help="time with torch's default events (diagnostic)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before the timed region, copy MIB MiB device-to-device 3 times (a plain copy kernel of "
+                         "known size, to scale hardware byte counters by)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path shards by "
@@ -238,6 +259,16 @@ def main():
             for f in calls_b[s]:
                 f()
 
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 x {nbytes} bytes read + written")
+        del src, dst
+
     log("[bench] warmup")
     for s in range(args.warmup):
         step(s)
@@ -287,7 +318,7 @@ def main():
         "attn_ms": attn_avg,
         "attn_kv_tokens_per_s": (tokens / args.steps) / (attn_avg * 1e-3),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "k_attn (paged_decode_attn; one launch per step)",
                      "bytes_per_launch": abytes_step},
     }
