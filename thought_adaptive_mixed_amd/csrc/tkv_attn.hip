@@ -8,33 +8,42 @@
 //
 // Work decomposition: one work-group of nw 64-lane waves per (batch entry, KV
 // head, split); a split owns a byte-balanced range of the sequence's block
-// lists [8-bit | 4-bit | 2-bit] and its live blocks are dealt round-robin to
-// the waves.  Block ids and valid masks are read 64 at a time into lanes;
-// fully evicted blocks are skipped; the next block's codes and metadata are
-// loaded while the current one is computed.  Per
-// 16-token block, lane l loads chunk l of the K codes and chunk l of the V
-// codes (D*bits/32 contiguous bytes each), which puts the codes straight into
-// MFMA operand layout:
-//   S^T[t][h] = sum_d K[t][d] Q[h][d]     v_mfma_f32_16x16x16_f16, A = K codes
-//   O^T[d][h] += sum_t V[t][d] P'[t][h]   v_mfma_f32_16x16x16_f16, A = V codes
-// Codes enter the MFMA as exact fp16 integers ((0x6400 | code) - 1024); the
-// fp16 scales and zero-points are applied per (token, group) in fp32:
+// lists [8-bit | 4-bit | 2-bit].  The live blocks (fully evicted ones are
+// dropped) are taken PK at a time, steps dealt round-robin to the waves.  A
+// wave holds two steps of records (codes and metadata of PK blocks) in
+// registers: the loads of the next step are in flight while the current one
+// is computed.  Per 16-token block, lane l takes chunk l of the K codes and
+// chunk l of the V codes (D*bits/32 bytes each), which puts the codes straight
+// into MFMA operand layout (v_mfma_f32_16x16x32_f16; k = 8 (lane / 16) + e):
+//   S^T[t][h] = sum_d K[t][d] Q[h][d]     A = K codes, two 8-dim halves of a
+//                                         lane's 16 dims of a group per k slice
+//   O^T[d][h] += sum_t V[t][d] P'[t][h]   A = V codes, a lane's 4 tokens of two
+//                                         blocks per k slice
+// Codes enter the MFMA as fp16 subnormals (bit pattern = code, value code *
+// 2^-24), so the operand is the masked code word itself; products are exact
+// and the 2^24 is folded back in fp32.  The fp16 scales and zero-points are
+// applied per (token, group) in fp32:
 //   logit = (sum_g sK * (q_g . c_g) + zK * sum(q_g)) / sqrt(D)
 //   out   = sum_t (p sV) c  +  sum_t p zV          (per group of dims)
 // with p sV fed as an fp16 hi + lo pair (two MFMAs), so the product reaches
 // the fp32 accumulator with ~21 significant bits.  The query heads of the GQA
-// group sit in the 16 MFMA columns (heads >= G are padding and masked).
-// Softmax runs online in the log2 domain; the running max is shared by the 4
-// lanes holding a head's tokens and is raised only when a block exceeds it
-// by more than 2^8 (lazy rescale).  Each lane keeps partial Z, S' = sum
-// p (s - m) and a sorted top-8 of its logits, filtered by the head-wide 8th-
-// best bound.  The waves of a work-group merge their records through LDS;
-// with one split the work-group then adds the staged self token and the sink
-// and writes the outputs and statistics, otherwise it writes a partial record
-// that a small combine kernel merges across splits.
+// group sit in the 16 MFMA columns; with G heads only the first G' =
+// roundup(G, 4) columns of each 16-lane row are real, so the PK = 16 / G'
+// blocks of a step are packed side by side (DPP row shifts with bank masks)
+// and the softmax epilogue runs once for all of them on fully used lanes, then
+// P' is unpacked block by block for the P.V products.
+// Softmax runs online in the log2 domain; the running max is shared by the
+// lanes holding a head's tokens and is raised only when a step exceeds it by
+// more than 2^8 (lazy rescale).  Each lane keeps partial Z, S' = sum p (s - m)
+// and a sorted top-8 of its logits, filtered by the head-wide 8th-best bound.
+// The waves of a work-group merge their records through LDS; with one split
+// the work-group then adds the staged self token and the sink and writes the
+// outputs and statistics, otherwise it writes a partial record that a small
+// combine kernel merges across splits.
 #include "tkv_internal.h"
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
@@ -51,23 +60,31 @@ __device__ inline float xorf(float v, int m) { return __shfl_xor(v, m, 64); }
 __device__ inline uint32_t rdlane(uint32_t v, int l) { return (uint32_t)__builtin_amdgcn_readlane((int)v, l); }
 
 // ---------------------------------------------------------------------------
-// code -> exact fp16 operands
+// code -> fp16 operands.  A code c enters the MFMA as the fp16 subnormal with
+// bit pattern c, i.e. the value c * 2^-24: products with the fp16 queries or
+// probabilities are exact in fp32 and every partial sum is the plain code
+// product scaled by 2^-24, so the scale is folded back exactly afterwards
+// (into the logit factor on the K side, into the accumulator on the V side).
 // ---------------------------------------------------------------------------
-__device__ inline half2_t exact_codes(uint32_t u) {
-  half2_t h = __builtin_bit_cast(half2_t, u);
-  const half2_t off = {(_Float16)1024.0f, (_Float16)1024.0f};
-  return h - off;
-}
-// fields p and p + W/2 of word w (elements 2p, 2p+1 of the word) as two fp16 1024 + code
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+constexpr float kCodeUnit = 0x1p-24f;     // value of the fp16 subnormal with bit pattern 1
+constexpr float kCodeScale = 0x1p24f;
+// fields p and p + W/2 of word w (elements 2p, 2p+1 of the word), one per half
 template <int BITS>
 __device__ inline uint32_t code_pair(uint32_t w, int p) {
   if constexpr (BITS == 8) {
-    // bytes [w.p, 0x64, w.p+2, 0x64]: v_perm_b32 with {0x64646464, w}
-    const uint32_t sel = (uint32_t)p | (4u << 8) | ((uint32_t)(p + 2) << 16) | (4u << 24);
-    return __builtin_amdgcn_perm(0x64646464u, w, sel);
+    // bytes [w.p, 0, w.p+2, 0] (selector 0x0c reads a zero byte)
+    const uint32_t sel = (uint32_t)p | (0x0cu << 8) | ((uint32_t)(p + 2) << 16) | (0x0cu << 24);
+    return __builtin_amdgcn_perm(0u, w, sel);
   } else {
+    constexpr int W = 32 / BITS;
     constexpr uint32_t M = ((1u << BITS) - 1u) * 0x00010001u;
-    return ((w >> (p * BITS)) & M) | 0x64006400u;
+    if (p == W / 2 - 1) {
+      // the top field of each half: a packed 16-bit shift leaves nothing above it
+      const ushort2_t h = __builtin_bit_cast(ushort2_t, w) >> (ushort2_t){(unsigned short)(p * BITS), (unsigned short)(p * BITS)};
+      return __builtin_bit_cast(uint32_t, h);
+    }
+    return (w >> (p * BITS)) & M;
   }
 }
 template <int BITS>
@@ -75,10 +92,18 @@ __device__ inline half4_t operand4(const uint32_t* words, int e0) {
   constexpr int W = 32 / BITS;
   const uint32_t w = words[e0 / W];
   const int p = (e0 % W) >> 1;
-  half2_t a = exact_codes(code_pair<BITS>(w, p));
-  half2_t b = exact_codes(code_pair<BITS>(w, p + 1));
+  const half2_t a = __builtin_bit_cast(half2_t, code_pair<BITS>(w, p));
+  const half2_t b = __builtin_bit_cast(half2_t, code_pair<BITS>(w, p + 1));
   half4_t r = {a[0], a[1], b[0], b[1]};
   return r;
+}
+
+__device__ inline half8_t cat8(half4_t a, half4_t b) {
+  return (half8_t){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+// v_mfma_f32_16x16x32_f16: k = 8 * (lane / 16) + e in both operands
+__device__ inline float4_t mfma32(half8_t a, half8_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -134,64 +159,106 @@ struct AttnState {
   int natt;
 };
 
-template <int D, int GS, int BITS, bool WINDOW>
-struct Blk {
+__device__ inline float h_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFF)); }
+__device__ inline float h_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// ---------------------------------------------------------------------------
+// Packing of the PK blocks of a step (GP = 16 / PK lanes per block and row).
+// pack: lanes [GP*J, GP*J + GP) of each row take block J's lanes [0, GP)
+// (row shift right, only the target banks written); unpack: lanes [0, GP) take
+// lanes [GP*J, ...) back, the rest of the row becomes 0.
+// ---------------------------------------------------------------------------
+template <int GP, int J>
+__device__ inline float pack_lane(float dst, float src) {
+  constexpr int BANKS = ((1 << (GP / 4)) - 1) << ((GP / 4) * J);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, dst),
+                                                               __builtin_bit_cast(int, src), 0x110 + GP * J, 0xf,
+                                                               BANKS, false));
+}
+template <int GP, int J>
+__device__ inline uint32_t unpack_lane(uint32_t src) {
+  constexpr int BANKS = (1 << (GP / 4)) - 1;
+  constexpr int CTRL = J == 0 ? 0xE4 : 0x100 + GP * J;      // quad_perm identity / row_shl
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)src, CTRL, 0xf, BANKS, false);
+}
+template <int GP, int J>
+__device__ inline half4_t unpack4(half4_t v) {
+  uint2 u = __builtin_bit_cast(uint2, v);
+  u.x = unpack_lane<GP, J>(u.x);
+  u.y = unpack_lane<GP, J>(u.y);
+  return __builtin_bit_cast(half4_t, u);
+}
+// max / sum over the lanes holding one head's values in the packed layout
+template <int GP>
+__device__ inline float head_max(float v) {
+#pragma unroll
+  for (int o = GP; o < 64; o <<= 1) v = fmaxf(v, xorf(v, o));
+  return v;
+}
+template <int GP>
+__device__ inline float head_sum(float v) {
+#pragma unroll
+  for (int o = GP; o < 64; o <<= 1) v += xorf(v, o);
+  return v;
+}
+
+// One step's data in registers: the K and V code chunks of the PK blocks
+// (lane l: chunk l of each), the metadata of this lane's own block (quad lg)
+// and, with a window, the positions of its four tokens.  Sized for the 8-bit
+// class; a class with fewer bits uses the first D*bits/128 words of a chunk.
+template <int D, int GS, bool WINDOW, int PK>
+struct Buf {
   static constexpr int NG = D / GS;
-  static constexpr int CW = D * BITS / 128;     // 32-bit words per lane chunk
-  uint32_t kw[CW], vw[CW];
+  static constexpr int CWM = D * 8 / 128;       // 32-bit words per lane chunk at 8 bits
+  uint32_t kw[PK][CWM], vw[PK][CWM];
   uint32_t mk[4 * NG], mv[4 * NG];
   int pos[WINDOW ? 4 : 1];
 };
 
-template <int D, int GS, int BITS, bool WINDOW>
-__device__ inline void load_block(Blk<D, GS, BITS, WINDOW>& b, const uint8_t* base, const int32_t* slotrec,
-                                  int lane) {
-  constexpr int NG = D / GS;
-  constexpr int CB = D * BITS / 32;
-  constexpr int CW = CB / 4;
-  const int lg = lane >> 4;
-  const uint32_t* kp = (const uint32_t*)(base + lane * CB);
-  const uint32_t* vp = (const uint32_t*)(base + 64 * CB + lane * CB);
-  if constexpr (CW % 4 == 0) {
-#pragma unroll
-    for (int i = 0; i < CW / 4; i++) {
-      uint4 a = ((const uint4*)kp)[i], c = ((const uint4*)vp)[i];
-      b.kw[4 * i] = a.x; b.kw[4 * i + 1] = a.y; b.kw[4 * i + 2] = a.z; b.kw[4 * i + 3] = a.w;
-      b.vw[4 * i] = c.x; b.vw[4 * i + 1] = c.y; b.vw[4 * i + 2] = c.z; b.vw[4 * i + 3] = c.w;
-    }
-  } else if constexpr (CW == 2) {
-    uint2 a = *(const uint2*)kp, c = *(const uint2*)vp;
-    b.kw[0] = a.x; b.kw[1] = a.y; b.vw[0] = c.x; b.vw[1] = c.y;
-  } else {
-    b.kw[0] = kp[0]; b.vw[0] = vp[0];
-  }
-  const uint4* mkp = (const uint4*)(base + 2 * 64 * CB + lg * 16 * NG);
-  const uint4* mvp = (const uint4*)(base + 2 * 64 * CB + 16 * NG * 4 + lg * 16 * NG);
-#pragma unroll
-  for (int i = 0; i < NG; i++) {
-    uint4 a = mkp[i], c = mvp[i];
-    b.mk[4 * i] = a.x; b.mk[4 * i + 1] = a.y; b.mk[4 * i + 2] = a.z; b.mk[4 * i + 3] = a.w;
-    b.mv[4 * i] = c.x; b.mv[4 * i + 1] = c.y; b.mv[4 * i + 2] = c.z; b.mv[4 * i + 3] = c.w;
-  }
-  if constexpr (WINDOW) {
-    const int4* pr = (const int4*)(slotrec + 4 * lg * 2);
-    int4 a = pr[0], c = pr[1];
-    b.pos[0] = a.x; b.pos[1] = a.z; b.pos[2] = c.x; b.pos[3] = c.z;
-  }
-}
-
-__device__ inline float h_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFF)); }
-__device__ inline float h_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
-
-template <int D, int GS, int BITS, bool WINDOW>
-__device__ inline void compute_block(const Blk<D, GS, BITS, WINDOW>& b, uint32_t mask, int lo_pos, int lane, bool head_ok,
-                                     const half4_t (&qB)[D / 16], const float (&sumq)[D / GS], float alpha,
-                                     AttnState<D, GS>& st) {
+template <int D, int GS, int BITS, bool WINDOW, int PK>
+__device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj, int lo_pos,
+                                    int lane, bool head_ok, const half4_t (&qB)[D / 16], const float (&sumq)[D / GS],
+                                    float alpha, AttnState<D, GS>& st) {
   constexpr int NG = D / GS;
   constexpr int KM = GS / 16;
   constexpr int NT = D / 16;
-  const int lg = lane >> 4;
-  uint32_t valid = (mask >> (4 * lg)) & 0xFu;
+  constexpr int GP = 16 / PK;
+  const int lg = lane >> 4, jl = (lane & 15) / GP;
+  // S^T = K Q^T per block and group (16x16x32: a lane's 16 elements of a
+  // group are two 8-element k slices); the PK blocks packed side by side
+  float4_t spk[NG];
+#pragma unroll
+  for (int j = 0; j < PK; j++) {
+    float4_t sj[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; gi++) {
+      sj[gi] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mm = 0; mm < KM; mm += 2)
+        sj[gi] = mfma32(cat8(operand4<BITS>(b.kw[j], gi * (GS / 4) + 4 * mm),
+                             operand4<BITS>(b.kw[j], gi * (GS / 4) + 4 * mm + 4)),
+                        cat8(qB[gi * KM + mm], qB[gi * KM + mm + 1]), sj[gi]);
+    }
+    if (j == 0) {
+#pragma unroll
+      for (int gi = 0; gi < NG; gi++) spk[gi] = sj[gi];
+    } else {
+#pragma unroll
+      for (int gi = 0; gi < NG; gi++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          if constexpr (PK > 1) {
+            if (j == 1) spk[gi][r] = pack_lane<GP, 1>(spk[gi][r], sj[gi][r]);
+            if constexpr (PK > 2) {
+              if (j == 2) spk[gi][r] = pack_lane<GP, 2>(spk[gi][r], sj[gi][r]);
+              if (j == 3) spk[gi][r] = pack_lane<GP, 3>(spk[gi][r], sj[gi][r]);
+            }
+          }
+        }
+    }
+  }
+  // this lane's block (mask mj) and token quad (lg)
+  uint32_t valid = (mj >> (4 * lg)) & 0xFu;
   if constexpr (WINDOW) {
 #pragma unroll
     for (int r = 0; r < 4; r++)
@@ -199,17 +266,6 @@ __device__ inline void compute_block(const Blk<D, GS, BITS, WINDOW>& b, uint32_t
   }
   st.natt += __builtin_popcount(valid);
   const uint32_t vb = head_ok ? valid : 0u;
-  // S^T = K Q^T, one accumulator per group
-  float4_t sacc[NG];
-#pragma unroll
-  for (int gi = 0; gi < NG; gi++) {
-    sacc[gi] = (float4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int mm = 0; mm < KM; mm++) {
-      half4_t a = operand4<BITS>(b.kw, gi * (GS / 4) + 4 * mm);
-      sacc[gi] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, qB[gi * KM + mm], sacc[gi], 0, 0, 0);
-    }
-  }
   float s2[4];
   float lmax = -INFINITY;
 #pragma unroll
@@ -218,14 +274,13 @@ __device__ inline void compute_block(const Blk<D, GS, BITS, WINDOW>& b, uint32_t
 #pragma unroll
     for (int gi = 0; gi < NG; gi++) {
       const uint32_t m = b.mk[r * NG + gi];
-      x = fmaf(h_lo(m), sacc[gi][r], fmaf(h_hi(m), sumq[gi], x));
+      x = fmaf(h_lo(m), spk[gi][r], fmaf(h_hi(m), sumq[gi], x));
     }
     s2[r] = ((vb >> r) & 1u) ? x * alpha : -INFINITY;
     lmax = fmaxf(lmax, s2[r]);
   }
-  float bm = fmaxf(lmax, xorf(lmax, 16));
-  bm = fmaxf(bm, xorf(bm, 32));
-  // lazy rescale: raise the running max only when a block exceeds it by SLACK
+  const float bm = head_max<GP>(lmax);
+  // lazy rescale: raise the running max only when a step exceeds it by SLACK
   const bool grow = bm > st.m2 + SLACK;
   if (__builtin_amdgcn_ballot_w64(grow)) {
     if (grow) {
@@ -252,14 +307,13 @@ __device__ inline void compute_block(const Blk<D, GS, BITS, WINDOW>& b, uint32_t
     st.S2 = fmaf(p[r], fmaxf(t, -200.f), st.S2);
   }
   // top-8: only values above the head-wide 8th-best bound can enter
-  float thr = fmaxf(st.top[TOPK - 1], xorf(st.top[TOPK - 1], 16));
-  thr = fmaxf(thr, xorf(thr, 32));
+  const float thr = head_max<GP>(st.top[TOPK - 1]);
   if (__builtin_amdgcn_ballot_w64(lmax > thr)) {
 #pragma unroll
     for (int r = 0; r < 4; r++)
       if (s2[r] > thr) topk_insert(st.top, s2[r]);
   }
-  // P' = p sV per group as fp16 hi + lo, and the zero-point term
+  // P' = p sV per group as fp16 hi + lo (packed layout), and the zero-point term
   half4_t pbh[NG], pbl[NG];
 #pragma unroll
   for (int gi = 0; gi < NG; gi++) {
@@ -279,63 +333,157 @@ __device__ inline void compute_block(const Blk<D, GS, BITS, WINDOW>& b, uint32_t
     pbh[gi] = (half4_t){h01[0], h01[1], h23[0], h23[1]};
     pbl[gi] = (half4_t){l01[0], l01[1], l23[0], l23[1]};
   }
-  // O^T += V^T P'
+  // O^T += V^T P', P' unpacked to each block's own columns
+  if constexpr (PK == 1) {
 #pragma unroll
-  for (int n = 0; n < NT; n++) {
-    half4_t a = operand4<BITS>(b.vw, 4 * n);
-    st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pbh[(16 * n) / GS], st.acc[n], 0, 0, 0);
-    st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pbl[(16 * n) / GS], st.acc[n], 0, 0, 0);
+    for (int n = 0; n < NT; n++) {
+      const half4_t a = operand4<BITS>(b.vw[0], 4 * n);
+      st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pbh[(16 * n) / GS], st.acc[n], 0, 0, 0);
+      st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pbl[(16 * n) / GS], st.acc[n], 0, 0, 0);
+    }
+  } else {
+    // blocks 2p and 2p+1 form one 32-token k slice (16x16x32): a lane's 4
+    // tokens of block 2p, then the same 4 of block 2p+1, in both operands
+#pragma unroll
+    for (int jp = 0; jp < PK; jp += 2) {
+      half8_t bh[NG], bl[NG];
+#pragma unroll
+      for (int gi = 0; gi < NG; gi++) {
+        if (jp == 0) {
+          bh[gi] = cat8(unpack4<GP, 0>(pbh[gi]), unpack4<GP, 1>(pbh[gi]));
+          bl[gi] = cat8(unpack4<GP, 0>(pbl[gi]), unpack4<GP, 1>(pbl[gi]));
+        }
+        if constexpr (PK > 2) {
+          if (jp == 2) {
+            bh[gi] = cat8(unpack4<GP, 2>(pbh[gi]), unpack4<GP, 3>(pbh[gi]));
+            bl[gi] = cat8(unpack4<GP, 2>(pbl[gi]), unpack4<GP, 3>(pbl[gi]));
+          }
+        }
+      }
+#pragma unroll
+      for (int n = 0; n < NT; n++) {
+        const half8_t a = cat8(operand4<BITS>(b.vw[jp], 4 * n), operand4<BITS>(b.vw[jp + 1], 4 * n));
+        st.acc[n] = mfma32(a, bh[(16 * n) / GS], st.acc[n]);
+        st.acc[n] = mfma32(a, bl[(16 * n) / GS], st.acc[n]);
+      }
+    }
   }
 }
 
-// The live blocks of one class, as listed in LDS (block id, mask; mask 0 =
-// skip), dealt round-robin to the nw waves.  Three block buffers rotate: while
-// one block is computed, the next two are in flight.  The loads are always
-// issued (past the end they repeat the last block), so no wait drains them.
-__device__ inline int next_live(const int2* lst, int n, int e, int nw) {
-  while (e < n && lst[e].y == 0) e += nw;
-  return e;
+// Load step sigma of class C into a register buffer: lane l takes chunk l
+// of the K and V codes of each of the PK blocks, the metadata of its own
+// block's token quad and, with a window, its tokens' positions.  A last,
+// partial step repeats a live block (its mask is read as 0).
+template <int D, int GS, bool WINDOW, int PK, int C>
+__device__ inline void load_step(Buf<D, GS, WINDOW, PK>& b, const uint8_t* pool_c, const int32_t* slot_c, int Hkv,
+                                 const int2* lv, int n, int sigma, int kvh, int lane) {
+  constexpr int BITS = C == 0 ? 8 : (C == 1 ? 4 : 2);
+  constexpr int NG = D / GS, CB = D * BITS / 32, CW = CB / 4, R = 128 * CB + 128 * NG, GP = 16 / PK;
+  const int lg = lane >> 4, jl = (lane & 15) / GP;
+  int ids[PK];
+#pragma unroll
+  for (int j = 0; j < PK; j++) {
+    const int e = sigma * PK + j;
+    ids[j] = __builtin_amdgcn_readfirstlane(lv[e < n ? e : n - 1].x);
+  }
+  int idj = ids[0];                                 // this lane's block
+#pragma unroll
+  for (int j = 1; j < PK; j++) idj = jl == j ? ids[j] : idj;
+  const uint8_t* base = pool_c + (int64_t)kvh * R;
+  const int64_t stride = (int64_t)Hkv * R;
+#pragma unroll
+  for (int j = 0; j < PK; j++) {
+    const uint8_t* rec = base + (int64_t)ids[j] * stride;
+    const uint8_t* kp = rec + lane * CB;
+    const uint8_t* vp = rec + 64 * CB + lane * CB;
+    if constexpr (CW % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < CW / 4; i++) {
+        const uint4 x = ((const uint4*)kp)[i], y = ((const uint4*)vp)[i];
+        b.kw[j][4 * i] = x.x; b.kw[j][4 * i + 1] = x.y; b.kw[j][4 * i + 2] = x.z; b.kw[j][4 * i + 3] = x.w;
+        b.vw[j][4 * i] = y.x; b.vw[j][4 * i + 1] = y.y; b.vw[j][4 * i + 2] = y.z; b.vw[j][4 * i + 3] = y.w;
+      }
+    } else if constexpr (CW == 2) {
+      const uint2 x = *(const uint2*)kp, y = *(const uint2*)vp;
+      b.kw[j][0] = x.x; b.kw[j][1] = x.y; b.vw[j][0] = y.x; b.vw[j][1] = y.y;
+    } else {
+      b.kw[j][0] = *(const uint32_t*)kp; b.vw[j][0] = *(const uint32_t*)vp;
+    }
+  }
+  const uint8_t* rj = base + (int64_t)idj * stride + 128 * CB;
+  const uint4* mkp = (const uint4*)(rj + lg * 16 * NG);
+  const uint4* mvp = (const uint4*)(rj + 64 * NG + lg * 16 * NG);
+#pragma unroll
+  for (int i = 0; i < NG; i++) {
+    const uint4 x = mkp[i], y = mvp[i];
+    b.mk[4 * i] = x.x; b.mk[4 * i + 1] = x.y; b.mk[4 * i + 2] = x.z; b.mk[4 * i + 3] = x.w;
+    b.mv[4 * i] = y.x; b.mv[4 * i + 1] = y.y; b.mv[4 * i + 2] = y.z; b.mv[4 * i + 3] = y.w;
+  }
+  if constexpr (WINDOW) {
+    const int4* pr = (const int4*)(slot_c + ((int64_t)idj * TKV_BS + 4 * lg) * 2);
+    const int4 x = pr[0], y = pr[1];
+    b.pos[0] = x.x; b.pos[1] = x.z; b.pos[2] = y.x; b.pos[3] = y.z;
+  }
 }
 
-template <int D, int GS, int BITS, bool WINDOW>
-__device__ inline void run_class(const AttnParams& P, int c, const int2* lst, int n, int kvh, int lo_pos, int lane,
-                                 int w, int nw, bool head_ok, const half4_t (&qB)[D / 16],
+// The wave's steps across the three classes, in order: the live blocks of a
+// class (compacted: id, mask), PK per step, steps dealt round-robin to the nw
+// waves.  Two register buffers alternate: the next step's loads are in flight
+// while the current step is computed, also across a class boundary.  Past the
+// last step a wave loads that step again (its lines are still in the L2), so
+// every path issues the same loads and the compiler's waits stay exact.
+template <int D, int GS, bool WINDOW, int PK>
+__device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax, const int* nl, int kvh, int lo_pos,
+                                 int lane, int w, int nw, bool head_ok, const half4_t (&qB)[D / 16],
                                  const float (&sumq)[D / GS], float alpha, AttnState<D, GS>& st) {
-  typedef Blk<D, GS, BITS, WINDOW> B;
-  const DevState& S = P.S;
-  const int64_t stride = (int64_t)S.Hkv * pick3(S.bh_bytes, c);
-  const uint8_t* pool = pick3(S.pool, c) + (int64_t)kvh * pick3(S.bh_bytes, c);
-  const int32_t* slot = pick3(S.slot, c);
-  int e0 = next_live(lst, n, w, nw);
-  if (e0 >= n) return;
-  int e1 = next_live(lst, n, e0 + nw, nw);
-  int e2 = e1 < n ? next_live(lst, n, e1 + nw, nw) : n;
-  int last = e0;
-  auto issue = [&](B& buf, int e) {
-    const int ee = e < n ? e : last;
-    last = ee;
-    const int id = __builtin_amdgcn_readfirstlane(lst[ee].x);
-    load_block(buf, pool + (int64_t)id * stride, slot + (int64_t)id * TKV_BS * 2, lane);
+  typedef Buf<D, GS, WINDOW, PK> B;
+  constexpr int GP = 16 / PK;
+  const int jl = (lane & 15) / GP;
+  const int n0 = nl[0], n1 = nl[1], n2 = nl[2];
+  const int c1 = (n0 + PK - 1) / PK, c2 = c1 + (n1 + PK - 1) / PK, T = c2 + (n2 + PK - 1) / PK;
+  const int2* l0 = live;
+  const int2* l1 = live + lmax;
+  const int2* l2 = live + 2 * lmax;
+  // the per-class pools and slot tables in registers (indexing the argument
+  // struct by a run-time class would copy it to scratch)
+  const uint8_t* pool0 = P.S.pool[0];
+  const uint8_t* pool1 = P.S.pool[1];
+  const uint8_t* pool2 = P.S.pool[2];
+  const int32_t* slt0 = P.S.slot[0];
+  const int32_t* slt1 = P.S.slot[1];
+  const int32_t* slt2 = P.S.slot[2];
+  const int Hkv = P.S.Hkv;
+  auto load = [&](B& b, int g) {
+    g = g < T ? g : T - 1;
+    if (g < c1) load_step<D, GS, WINDOW, PK, 0>(b, pool0, slt0, Hkv, l0, n0, g, kvh, lane);
+    else if (g < c2) load_step<D, GS, WINDOW, PK, 1>(b, pool1, slt1, Hkv, l1, n1, g - c1, kvh, lane);
+    else load_step<D, GS, WINDOW, PK, 2>(b, pool2, slt2, Hkv, l2, n2, g - c2, kvh, lane);
   };
-  auto mask_of = [&](int e) { return (uint32_t)__builtin_amdgcn_readfirstlane(lst[e].y); };
-  B A, Bb, C;
-  issue(A, e0);
-  issue(Bb, e1);
+  auto mask_of = [&](const int2* lv, int n, int sigma) -> uint32_t {
+    const int e = sigma * PK + jl;                  // this lane's block
+    return e < n ? (uint32_t)lv[e].y : 0u;
+  };
+  auto comp = [&](const B& b, int g) {
+    if (g < c1)
+      compute_step<D, GS, 8, WINDOW, PK>(b, mask_of(l0, n0, g), lo_pos, lane, head_ok, qB, sumq, alpha, st);
+    else if (g < c2)
+      compute_step<D, GS, 4, WINDOW, PK>(b, mask_of(l1, n1, g - c1), lo_pos, lane, head_ok, qB, sumq, alpha, st);
+    else
+      compute_step<D, GS, 2, WINDOW, PK>(b, mask_of(l2, n2, g - c2), lo_pos, lane, head_ok, qB, sumq, alpha, st);
+  };
+  int g = w;
+  if (g >= T) return;
+  B A, Bn;
+  load(A, g);
   while (true) {
-    // A holds e0, Bb holds e1 (in flight), C gets e2
-    issue(C, e2);
-    compute_block<D, GS, BITS, WINDOW>(A, mask_of(e0), lo_pos, lane, head_ok, qB, sumq, alpha, st);
-    if (e1 >= n) break;
-    int e3 = e2 < n ? next_live(lst, n, e2 + nw, nw) : n;
-    issue(A, e3);
-    compute_block<D, GS, BITS, WINDOW>(Bb, mask_of(e1), lo_pos, lane, head_ok, qB, sumq, alpha, st);
-    if (e2 >= n) break;
-    int e4 = e3 < n ? next_live(lst, n, e3 + nw, nw) : n;
-    issue(Bb, e4);
-    compute_block<D, GS, BITS, WINDOW>(C, mask_of(e2), lo_pos, lane, head_ok, qB, sumq, alpha, st);
-    if (e3 >= n) break;
-    e0 = e3; e1 = e4;
-    e2 = e4 < n ? next_live(lst, n, e4 + nw, nw) : n;
+    load(Bn, g + nw);
+    comp(A, g);
+    g += nw;
+    if (g >= T) break;
+    load(A, g + nw);
+    comp(Bn, g);
+    g += nw;
+    if (g >= T) break;
   }
 }
 
@@ -433,26 +581,37 @@ __device__ inline void finalize_head(const AttnParams& P, int b, int hq, int lan
   if (P.n_attended && hq == 0 && lane == 0) P.n_attended[b] = n;
 }
 
-template <int D, int GS, bool WINDOW>
+template <int D, int GS, bool WINDOW, int PK>
 __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   constexpr int NG = D / GS;
   constexpr int KM = GS / 16;
   constexpr int NT = D / 16;
+  constexpr int GP = 16 / PK;
   constexpr int RS = D + PART_X;                 // record stride (floats)
-  extern __shared__ float lds[];                 // [nw][G][RS] records, then [3][max_blocks] (id, mask)
+  // Dynamic LDS: first the raw block lists, last the waves' records; the live
+  // lists are a static array.
+  extern __shared__ float lds[];
+  __shared__ int2 s_live[3 * TKV_MAX_BLOCKS];
+  __shared__ int s_nlive[3];
   const DevState& S = P.S;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int lg = lane >> 4, h = lane & 15;
   const int G = S.Hq / S.Hkv;
-  const bool head_ok = h < G;
+  const bool col_ok = h < G;                     // MFMA column h is a real head
+  const int hp = h % GP;                         // head of this lane in the packed layout
+  const bool head_ok = hp < G;
   const int s = P.seq_ids[b];
   const bool seq_ok = s >= 0 && s < S.max_seqs;
+  int2* lst = (int2*)lds;                                 // [3][lmax], before any slot is filled
+  const int lmax = S.max_blocks;
+  int2* live = s_live;                                    // [3][lmax]
+  int* nlive = s_nlive;
   // query B operand: column h, k = 4lg + e <-> dim gi*GS + lg*(GS/4) + 4mm + e
   half4_t qB[NG * KM];
   float sumq[NG];
   {
-    const uint16_t* qr = P.q + ((int64_t)b * S.Hq + (int64_t)kvh * G + (head_ok ? h : 0)) * D;
+    const uint16_t* qr = P.q + ((int64_t)b * S.Hq + (int64_t)kvh * G + (col_ok ? h : 0)) * D;
 #pragma unroll
     for (int gi = 0; gi < NG; gi++) {
       const uint4* src = (const uint4*)(qr + gi * GS + lg * (GS / 4));
@@ -470,7 +629,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
         for (int e = 0; e < 4; e++) {
           const int j = 4 * mm + e;
           const uint32_t bits = (j & 1) ? (wq[j >> 1] & 0xFFFF0000u) : (wq[j >> 1] << 16);
-          const float x = head_ok ? __builtin_bit_cast(float, bits) : 0.f;
+          const float x = col_ok ? __builtin_bit_cast(float, bits) : 0.f;
           v[e] = (_Float16)x;
           sq += (float)v[e];
         }
@@ -478,7 +637,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
       }
       sq += xorf(sq, 16);
       sq += xorf(sq, 32);
-      sumq[gi] = sq;
+      sumq[gi] = __shfl(sq, hp, 64) * kCodeUnit;   // the packed lane's head, in code units
     }
   }
   const float alpha = LOG2E / sqrtf((float)D);
@@ -491,8 +650,6 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
 #pragma unroll
   for (int i = 0; i < TOPK; i++) st.top[i] = -INFINITY;
   // the split's block ids and masks, all three classes, into LDS
-  int2* lst = (int2*)(lds + nw * G * RS);            // [3][lmax]
-  const int lmax = S.max_blocks;
   int ncls[3] = {0, 0, 0};
   const int lo_pos = WINDOW ? P.q_pos[b] - P.window + 1 : 0;
   if (seq_ok) {
@@ -524,31 +681,44 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
     }
   }
   __syncthreads();
-  if (ncls[0]) run_class<D, GS, 8, WINDOW>(P, 0, lst, ncls[0], kvh, lo_pos, lane, w, nw, head_ok, qB, sumq, alpha, st);
-  if (ncls[1])
-    run_class<D, GS, 4, WINDOW>(P, 1, lst + lmax, ncls[1], kvh, lo_pos, lane, w, nw, head_ok, qB, sumq, alpha, st);
-  if (ncls[2])
-    run_class<D, GS, 2, WINDOW>(P, 2, lst + 2 * lmax, ncls[2], kvh, lo_pos, lane, w, nw, head_ok, qB, sumq, alpha,
-                                st);
-  // this wave's record per head, over its 4 lane groups
-  st.Z += xorf(st.Z, 16); st.Z += xorf(st.Z, 32);
-  st.S2 += xorf(st.S2, 16); st.S2 += xorf(st.S2, 32);
+  // keep the live blocks (mask != 0), in order
+  if (w == 0) {
+    const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
 #pragma unroll
-  for (int gi = 0; gi < NG; gi++) { st.zacc[gi] += xorf(st.zacc[gi], 16); st.zacc[gi] += xorf(st.zacc[gi], 32); }
-  {
-    float n = (float)st.natt;
-    n += xorf(n, 16); n += xorf(n, 32);
-    st.natt = (int)n;
+    for (int c = 0; c < 3; c++) {
+      int cnt = 0;
+      for (int b0 = 0; b0 < ncls[c]; b0 += 64) {
+        const int e = b0 + lane;
+        const int2 v = e < ncls[c] ? lst[c * lmax + e] : make_int2(0, 0);
+        const bool lv = v.y != 0;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(lv);
+        if (lv) live[c * lmax + cnt + __popcll(m & lt)] = v;
+        cnt += __popcll(m);
+      }
+      if (lane == 0) nlive[c] = cnt;
+    }
   }
-  topk_merge_xor(st.top, 16);
-  topk_merge_xor(st.top, 32);
-  if (head_ok) {
+  __syncthreads();
+  run_steps<D, GS, WINDOW, PK>(P, live, lmax, nlive, kvh, lo_pos, lane, w, nw, head_ok, qB, sumq, alpha * kCodeScale,
+                               st);
+  // this wave's record per head: sums over the lanes holding the head
+  st.Z = head_sum<GP>(st.Z);
+  st.S2 = head_sum<GP>(st.S2);
+#pragma unroll
+  for (int gi = 0; gi < NG; gi++) st.zacc[gi] = head_sum<GP>(st.zacc[gi]);
+  st.natt = (int)head_sum<GP>((float)st.natt);
+#pragma unroll
+  for (int o = GP; o < 64; o <<= 1) topk_merge_xor(st.top, o);
+  __syncthreads();                                // the raw lists' space takes the records
+  // lanes 16 lg + h (h < G) hold head h both in the accumulator's columns and,
+  // after the sums above, in the packed layout (block 0)
+  if (col_ok) {
     float* rec = lds + ((int64_t)w * G + h) * RS;
 #pragma unroll
     for (int n = 0; n < NT; n++) {
       const float z = st.zacc[(16 * n) / GS];
 #pragma unroll
-      for (int r = 0; r < 4; r++) rec[16 * n + 4 * lg + r] = st.acc[n][r] + z;
+      for (int r = 0; r < 4; r++) rec[16 * n + 4 * lg + r] = st.acc[n][r] * kCodeScale + z;
     }
     if (lg == 0) {
       rec[D] = st.m2; rec[D + 1] = st.Z; rec[D + 2] = st.S2; rec[D + 3] = (float)st.natt;
@@ -597,17 +767,33 @@ __global__ __launch_bounds__(256) void k_combine(AttnParams P) {
 // Launch shape: one work-group of nw waves per (batch entry, KV head, split);
 // about two resident waves per SIMD (1024 SIMDs), the waves of a work-group
 // sharing the sequence's blocks; extra splits only when the batch is small.
+// LDS per work-group: nw step slots of PK records, the block lists.
 // ---------------------------------------------------------------------------
 static const int kTargetWaves = 2048;
+static const int kMaxLds = 160 * 1024;
 
-static int lds_bytes(const tkv_cache* c, int nw) {
-  return nw * (c->S.Hq / c->S.Hkv) * (c->S.D + PART_X) * (int)sizeof(float) + 3 * c->S.max_blocks * 8;
+// blocks packed per step: 16 / roundup(G, 4), and at most 2 at D = 128 so
+// that two steps of codes (the one computed and the one loading) stay within
+// the registers of two waves per SIMD
+static int pack_of(const tkv_cache* c, int G) {
+  if (G <= 4 && c->S.D == 64) return 4;
+  return G <= 8 && (c->S.D == 64 || c->S.D / c->S.g <= 2) ? 2 : 1;
 }
+
+// dynamic LDS: the raw block lists, later the waves' records; the live lists
+// are static
+static int lds_bytes(const tkv_cache* c, int nw) {
+  const int D = c->S.D, G = c->S.Hq / c->S.Hkv;
+  const int recs = nw * G * (D + PART_X) * (int)sizeof(float);
+  const int lists = 3 * c->S.max_blocks * 8;
+  return recs > lists ? recs : lists;
+}
+static const int kStaticLds = 3 * TKV_MAX_BLOCKS * 8 + 16;
 
 void attn_plan(const tkv_cache* c, int batch, int num_splits, int* nw_out, int* splits_out) {
   const int units = batch * c->S.Hkv > 0 ? batch * c->S.Hkv : 1;
   int nw = 1;
-  while (nw < 8 && units * nw * 2 <= kTargetWaves && lds_bytes(c, nw * 2) <= 65536) nw *= 2;
+  while (nw < 8 && units * nw * 2 <= kTargetWaves && lds_bytes(c, nw * 2) + kStaticLds <= kMaxLds) nw *= 2;
   int splits = num_splits;
   if (splits <= 0) {
     splits = (kTargetWaves + units * nw - 1) / (units * nw);
@@ -625,12 +811,32 @@ size_t attn_workspace_bytes(const tkv_cache* c, int batch, int splits) {
   return (size_t)batch * c->S.Hq * splits * (c->S.D + PART_X) * sizeof(float);
 }
 
+template <int D, int GS, bool W, int PK>
+static void launch_one(const AttnParams& P, dim3 grid, int nw, int lds, hipStream_t st) {
+  static bool attr_set = false;            // dynamic LDS above 64 KiB must be allowed once per kernel
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void*)k_attn<D, GS, W, PK>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              kMaxLds - kStaticLds);
+    attr_set = true;
+  }
+  k_attn<D, GS, W, PK><<<grid, 64 * nw, lds, st>>>(P);
+}
+
 template <int D, int GS>
-static void launch_attn_t(const AttnParams& P, int batch, int Hkv, int Hq, int nw, int lds, bool window,
+static void launch_attn_t(const AttnParams& P, int batch, int Hkv, int Hq, int nw, int lds, bool window, int pk,
                           hipStream_t st) {
   dim3 grid(P.splits, Hkv, batch);
-  if (window) k_attn<D, GS, true><<<grid, 64 * nw, lds, st>>>(P);
-  else k_attn<D, GS, false><<<grid, 64 * nw, lds, st>>>(P);
+  constexpr int PK2 = D == 64 || D / GS <= 2 ? 2 : 1;   // (pack_of returns 2 only with at most two groups at D = 128)
+  constexpr int PK4 = D == 64 ? 4 : PK2;                // (and 4 only for D = 64)
+  if (window) {
+    if (pk == 4) launch_one<D, GS, true, PK4>(P, grid, nw, lds, st);
+    else if (pk == 2) launch_one<D, GS, true, PK2>(P, grid, nw, lds, st);
+    else launch_one<D, GS, true, 1>(P, grid, nw, lds, st);
+  } else {
+    if (pk == 4) launch_one<D, GS, false, PK4>(P, grid, nw, lds, st);
+    else if (pk == 2) launch_one<D, GS, false, PK2>(P, grid, nw, lds, st);
+    else launch_one<D, GS, false, 1>(P, grid, nw, lds, st);
+  }
   if (P.splits > 1) k_combine<D><<<dim3((Hq + 3) / 4, batch), 256, 0, st>>>(P);
 }
 
@@ -643,9 +849,10 @@ int launch_attention(tkv_cache* c, const tkv_attn_args* a, int nw, int splits, h
   P.part = (float*)a->workspace; P.out = a->out; P.stats = a->stats; P.n_attended = a->n_attended;
   const int D = c->S.D, g = c->S.g, lds = lds_bytes(c, nw);
   const bool win = a->window > 0;
-  if (D == 128 && g == 64) launch_attn_t<128, 64>(P, a->batch, c->S.Hkv, c->S.Hq, nw, lds, win, st);
-  else if (D == 128 && g == 32) launch_attn_t<128, 32>(P, a->batch, c->S.Hkv, c->S.Hq, nw, lds, win, st);
-  else if (D == 64 && g == 64) launch_attn_t<64, 64>(P, a->batch, c->S.Hkv, c->S.Hq, nw, lds, win, st);
-  else launch_attn_t<64, 32>(P, a->batch, c->S.Hkv, c->S.Hq, nw, lds, win, st);
+  const int pk = pack_of(c, c->S.Hq / c->S.Hkv);
+  if (D == 128 && g == 64) launch_attn_t<128, 64>(P, a->batch, c->S.Hkv, c->S.Hq, nw, lds, win, pk, st);
+  else if (D == 128 && g == 32) launch_attn_t<128, 32>(P, a->batch, c->S.Hkv, c->S.Hq, nw, lds, win, pk, st);
+  else if (D == 64 && g == 64) launch_attn_t<64, 64>(P, a->batch, c->S.Hkv, c->S.Hq, nw, lds, win, pk, st);
+  else launch_attn_t<64, 32>(P, a->batch, c->S.Hkv, c->S.Hq, nw, lds, win, pk, st);
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
