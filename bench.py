@@ -130,7 +130,7 @@ def measured_traffic():
     return float(j["traffic_bytes_per_launch"]) if h.hexdigest() == j["source_sha256"] else None
 
 
-def cpu_baseline(w, state, ch, n_seq, reps_budget_s=20.0):
+def cpu_baseline(w, state, ch, n_seq, budget_s=12.0, max_reps=1000):
     """The oracle as it stands, on a sample of n_seq sequences of the same
     workload: one full step (attention with the self token, classify, append,
     ladder, evict) per repetition, on all host cores the process may use."""
@@ -156,7 +156,7 @@ def cpu_baseline(w, state, ch, n_seq, reps_budget_s=20.0):
             oc.evict(*ops)
         tokens += int(na.sum())
         reps += 1
-        if time.perf_counter() - t0 > reps_budget_s or reps >= 50:
+        if time.perf_counter() - t0 > budget_s or reps >= max_reps:
             break
     dt = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
@@ -171,7 +171,7 @@ def main():
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=6)
     ap.add_argument("--copies", type=int, default=0, help="state copies (0 = enough for > 1 GiB)")
-    ap.add_argument("--cpu-seqs", type=int, default=4)
+    ap.add_argument("--cpu-seqs", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-only", action="store_true", help="time only the attention call (diagnostic)")
     ap.add_argument("--torch-events", action="store_true", help="time with torch's default events (diagnostic)")

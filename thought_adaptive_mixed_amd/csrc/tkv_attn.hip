@@ -163,10 +163,9 @@ __device__ inline float h_lo(uint32_t w) { return (float)__builtin_bit_cast(_Flo
 __device__ inline float h_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
 // ---------------------------------------------------------------------------
-// Packing of the PK blocks of a step (GP = 16 / PK lanes per block and row).
-// pack: lanes [GP*J, GP*J + GP) of each row take block J's lanes [0, GP)
-// (row shift right, only the target banks written); unpack: lanes [0, GP) take
-// lanes [GP*J, ...) back, the rest of the row becomes 0.
+// Packing of the PK blocks of a step (GP = 16 / PK lanes per block and row):
+// lanes [GP*J, GP*J + GP) of each row take block J's lanes [0, GP) (row shift
+// right, only the target banks written).
 // ---------------------------------------------------------------------------
 template <int GP, int J>
 __device__ inline float pack_lane(float dst, float src) {
@@ -175,25 +174,35 @@ __device__ inline float pack_lane(float dst, float src) {
                                                                __builtin_bit_cast(int, src), 0x110 + GP * J, 0xf,
                                                                BANKS, false));
 }
-template <int GP, int J>
-__device__ inline uint32_t unpack_lane(uint32_t src) {
-  constexpr int BANKS = (1 << (GP / 4)) - 1;
-  constexpr int CTRL = J == 0 ? 0xE4 : 0x100 + GP * J;      // quad_perm identity / row_shl
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)src, CTRL, 0xf, BANKS, false);
-}
-template <int GP, int J>
-__device__ inline half4_t unpack4(half4_t v) {
-  uint2 u = __builtin_bit_cast(uint2, v);
-  u.x = unpack_lane<GP, J>(u.x);
-  u.y = unpack_lane<GP, J>(u.y);
-  return __builtin_bit_cast(half4_t, u);
-}
 // max / sum over the lanes holding one head's values in the packed layout
+// (lanes h + GP*i of every row).  The max runs on VALU cross-lane moves only:
+// DPP row rotations by 4 and 8 inside a 16-lane row, then the gfx950 swaps of
+// row pairs (v_permlane16_swap) and wave halves (v_permlane32_swap).  A swap
+// of a value with a copy of itself leaves the even rows (lower half) in one
+// register and the odd rows (upper half) in the other, in every lane, so the
+// max of the two registers is the exact reduction over the pair.  The swap is
+// written as one asm block together with the copy (and the two wait states a
+// permlane needs after a VALU write): given the same value twice, the
+// compiler's builtin folds the two results into one.
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+__device__ inline float max_swap16(float v) {
+  uint32_t a = __builtin_bit_cast(uint32_t, v), b;
+  asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "=&v"(b));
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ inline float max_swap32(float v) {
+  uint32_t a = __builtin_bit_cast(uint32_t, v), b;
+  asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "=&v"(b));
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
 template <int GP>
 __device__ inline float head_max(float v) {
-#pragma unroll
-  for (int o = GP; o < 64; o <<= 1) v = fmaxf(v, xorf(v, o));
-  return v;
+  if constexpr (GP <= 4) v = fmaxf(v, dpp_f<0x124>(v));          // row_ror:4
+  if constexpr (GP <= 8) v = fmaxf(v, dpp_f<0x128>(v));          // row_ror:8
+  return max_swap32(max_swap16(v));
 }
 template <int GP>
 __device__ inline float head_sum(float v) {
@@ -313,7 +322,11 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
     for (int r = 0; r < 4; r++)
       if (s2[r] > thr) topk_insert(st.top, s2[r]);
   }
-  // P' = p sV per group as fp16 hi + lo (packed layout), and the zero-point term
+  // P' = p sV per group as fp16 hi + lo (packed layout), and the zero-point
+  // term.  A masked token has p = 0, but its slot may never have been written
+  // (the tail of an open block, the block repeated to pad a last step): its
+  // fp16 scale and zero-point are cleared so that no stale NaN or inf pattern
+  // reaches the products.
   half4_t pbh[NG], pbl[NG];
 #pragma unroll
   for (int gi = 0; gi < NG; gi++) {
@@ -321,7 +334,7 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
     float z = st.zacc[gi];
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      const uint32_t m = b.mv[r * NG + gi];
+      const uint32_t m = ((vb >> r) & 1u) ? b.mv[r * NG + gi] : 0u;
       pv[r] = p[r] * h_lo(m);
       z = fmaf(p[r], h_hi(m), z);
     }
@@ -343,22 +356,22 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
     }
   } else {
     // blocks 2p and 2p+1 form one 32-token k slice (16x16x32): a lane's 4
-    // tokens of block 2p, then the same 4 of block 2p+1, in both operands
+    // tokens of block 2p, then the same 4 of block 2p+1.  P' stays packed: a
+    // lane keeps its own block's half of the slice and zeroes the other, so
+    // accumulator column h collects head h % GP over the blocks at position
+    // h / GP of every step; the positions are summed once at the end.
+    auto keep = [](half4_t v, bool k) -> half4_t {
+      const uint2 u = __builtin_bit_cast(uint2, v);
+      return __builtin_bit_cast(half4_t, make_uint2(k ? u.x : 0u, k ? u.y : 0u));
+    };
 #pragma unroll
     for (int jp = 0; jp < PK; jp += 2) {
+      const bool k0 = jl == jp, k1 = jl == jp + 1;
       half8_t bh[NG], bl[NG];
 #pragma unroll
       for (int gi = 0; gi < NG; gi++) {
-        if (jp == 0) {
-          bh[gi] = cat8(unpack4<GP, 0>(pbh[gi]), unpack4<GP, 1>(pbh[gi]));
-          bl[gi] = cat8(unpack4<GP, 0>(pbl[gi]), unpack4<GP, 1>(pbl[gi]));
-        }
-        if constexpr (PK > 2) {
-          if (jp == 2) {
-            bh[gi] = cat8(unpack4<GP, 2>(pbh[gi]), unpack4<GP, 3>(pbh[gi]));
-            bl[gi] = cat8(unpack4<GP, 2>(pbl[gi]), unpack4<GP, 3>(pbl[gi]));
-          }
-        }
+        bh[gi] = cat8(keep(pbh[gi], k0), keep(pbh[gi], k1));
+        bl[gi] = cat8(keep(pbl[gi], k0), keep(pbl[gi], k1));
       }
 #pragma unroll
       for (int n = 0; n < NT; n++) {
@@ -701,6 +714,19 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   __syncthreads();
   run_steps<D, GS, WINDOW, PK>(P, live, lmax, nlive, kvh, lo_pos, lane, w, nw, head_ok, qB, sumq, alpha * kCodeScale,
                                st);
+  // accumulator columns h and h + GP*i hold one head (block positions): sum
+  // them into every column of the row (rotations inside the 16-lane row)
+  if constexpr (PK > 1) {
+#pragma unroll
+    for (int n = 0; n < NT; n++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        float v = st.acc[n][r];
+        if constexpr (GP <= 4) v += dpp_f<0x124>(v);              // row_ror:4
+        v += dpp_f<0x128>(v);                                     // row_ror:8
+        st.acc[n][r] = v;
+      }
+  }
   // this wave's record per head: sums over the lanes holding the head
   st.Z = head_sum<GP>(st.Z);
   st.S2 = head_sum<GP>(st.S2);
