@@ -58,6 +58,13 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline float xorf(float v, int m) { return __shfl_xor(v, m, 64); }
 __device__ inline uint32_t rdlane(uint32_t v, int l) { return (uint32_t)__builtin_amdgcn_readlane((int)v, l); }
+// work-group barrier that orders LDS only: global reads in flight (the
+// padding loads past a wave's last step, the self token) are not waited for
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // ---------------------------------------------------------------------------
 // code -> fp16 operands.  A code c enters the MFMA as the fp16 subnormal with
@@ -126,13 +133,6 @@ __device__ inline void topk_merge(float (&L)[TOPK], const float (&O)[TOPK]) {
   cswap(L[0], L[2]); cswap(L[1], L[3]); cswap(L[4], L[6]); cswap(L[5], L[7]);
   cswap(L[0], L[1]); cswap(L[2], L[3]); cswap(L[4], L[5]); cswap(L[6], L[7]);
 }
-__device__ inline void topk_merge_xor(float (&L)[TOPK], int m) {
-  float O[TOPK];
-#pragma unroll
-  for (int i = 0; i < TOPK; i++) O[i] = xorf(L[i], m);
-  topk_merge(L, O);
-}
-
 // ---------------------------------------------------------------------------
 struct AttnParams {
   DevState S;
@@ -204,11 +204,102 @@ __device__ inline float head_max(float v) {
   if constexpr (GP <= 8) v = fmaxf(v, dpp_f<0x128>(v));          // row_ror:8
   return max_swap32(max_swap16(v));
 }
+// Exact butterflies on VALU.  xchg<K> (K = 1, 2, 4, 8) is the value of lane
+// i ^ K: DPP quad permutations, a pair of bank-masked row shifts, a row
+// rotation by 8.  For K = 16, 32 a swap hands every lane both values of its
+// pair (even row / lower half first).  Sums, maxima and top-8 merges of a
+// pair are independent of operand order, so both partners get the same bits.
+template <int K>
+__device__ inline float xchg(float v) {
+  if constexpr (K == 1) return dpp_f<0xB1>(v);                   // quad_perm [1,0,3,2]
+  if constexpr (K == 2) return dpp_f<0x4E>(v);                   // quad_perm [2,3,0,1]
+  if constexpr (K == 4) {
+    int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x104, 0xf, 0x5, false);   // row_shl:4, banks 0, 2
+    t = __builtin_amdgcn_update_dpp(t, __builtin_bit_cast(int, v), 0x114, 0xf, 0xA, false);       // row_shr:4, banks 1, 3
+    return __builtin_bit_cast(float, t);
+  }
+  if constexpr (K == 8) return dpp_f<0x128>(v);                  // row_ror:8
+}
+template <int K>
+__device__ inline void swap_pair(float v, float& a, float& b) {
+  uint32_t x = __builtin_bit_cast(uint32_t, v), y;
+  if constexpr (K == 16) asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x), "=&v"(y));
+  else asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x), "=&v"(y));
+  a = __builtin_bit_cast(float, x);
+  b = __builtin_bit_cast(float, y);
+}
+template <int K>
+__device__ inline float pair_sum(float v) {
+  if constexpr (K <= 8) {
+    return v + xchg<K>(v);
+  } else {
+    float a, b;
+    swap_pair<K>(v, a, b);
+    return a + b;
+  }
+}
+template <int K>
+__device__ inline float pair_max(float v) {
+  if constexpr (K <= 8) {
+    return fmaxf(v, xchg<K>(v));
+  } else {
+    float a, b;
+    swap_pair<K>(v, a, b);
+    return fmaxf(a, b);
+  }
+}
+template <int K>
+__device__ inline void pair_topk(float (&L)[TOPK]) {
+  float O[TOPK];
+  if constexpr (K <= 8) {
+#pragma unroll
+    for (int i = 0; i < TOPK; i++) O[i] = xchg<K>(L[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < TOPK; i++) swap_pair<K>(L[i], L[i], O[i]);
+  }
+  topk_merge(L, O);
+}
 template <int GP>
 __device__ inline float head_sum(float v) {
-#pragma unroll
-  for (int o = GP; o < 64; o <<= 1) v += xorf(v, o);
-  return v;
+  if constexpr (GP <= 4) v = pair_sum<4>(v);
+  if constexpr (GP <= 8) v = pair_sum<8>(v);
+  return pair_sum<32>(pair_sum<16>(v));
+}
+template <int GP>
+__device__ inline void head_topk(float (&L)[TOPK]) {
+  if constexpr (GP <= 4) pair_topk<4>(L);
+  if constexpr (GP <= 8) pair_topk<8>(L);
+  pair_topk<16>(L);
+  pair_topk<32>(L);
+}
+// reductions over the first n lanes (the rest hold the neutral value),
+// broadcast from lane 0
+__device__ inline float first_lanes_sum(float v, int n) {
+  if (n > 1) v = pair_sum<1>(v);
+  if (n > 2) v = pair_sum<2>(v);
+  if (n > 4) v = pair_sum<4>(v);
+  if (n > 8) v = pair_sum<8>(v);
+  if (n > 16) v = pair_sum<16>(v);
+  if (n > 32) v = pair_sum<32>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+__device__ inline float first_lanes_max(float v, int n) {
+  if (n > 1) v = pair_max<1>(v);
+  if (n > 2) v = pair_max<2>(v);
+  if (n > 4) v = pair_max<4>(v);
+  if (n > 8) v = pair_max<8>(v);
+  if (n > 16) v = pair_max<16>(v);
+  if (n > 32) v = pair_max<32>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+__device__ inline void first_lanes_topk(float (&L)[TOPK], int n) {
+  if (n > 1) pair_topk<1>(L);
+  if (n > 2) pair_topk<2>(L);
+  if (n > 4) pair_topk<4>(L);
+  if (n > 8) pair_topk<8>(L);
+  if (n > 16) pair_topk<16>(L);
+  if (n > 32) pair_topk<32>(L);
 }
 
 // One step's data in registers: the K and V code chunks of the PK blocks
@@ -386,13 +477,15 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
 // Load step sigma of class C into a register buffer: lane l takes chunk l
 // of the K and V codes of each of the PK blocks, the metadata of its own
 // block's token quad and, with a window, its tokens' positions.  A last,
-// partial step repeats a live block (its mask is read as 0).
+// partial step repeats a live block (its mask is read as 0).  ls is the lane
+// whose addresses are used: the lane itself, or 0 in every lane for a padding
+// load (the same instructions, but one cache line that is already loaded).
 template <int D, int GS, bool WINDOW, int PK, int C>
 __device__ inline void load_step(Buf<D, GS, WINDOW, PK>& b, const uint8_t* pool_c, const int32_t* slot_c, int Hkv,
-                                 const int2* lv, int n, int sigma, int kvh, int lane) {
+                                 const int2* lv, int n, int sigma, int kvh, int lane, int ls) {
   constexpr int BITS = C == 0 ? 8 : (C == 1 ? 4 : 2);
   constexpr int NG = D / GS, CB = D * BITS / 32, CW = CB / 4, R = 128 * CB + 128 * NG, GP = 16 / PK;
-  const int lg = lane >> 4, jl = (lane & 15) / GP;
+  const int lg = ls >> 4, jl = (lane & 15) / GP;
   int ids[PK];
 #pragma unroll
   for (int j = 0; j < PK; j++) {
@@ -407,8 +500,8 @@ __device__ inline void load_step(Buf<D, GS, WINDOW, PK>& b, const uint8_t* pool_
 #pragma unroll
   for (int j = 0; j < PK; j++) {
     const uint8_t* rec = base + (int64_t)ids[j] * stride;
-    const uint8_t* kp = rec + lane * CB;
-    const uint8_t* vp = rec + 64 * CB + lane * CB;
+    const uint8_t* kp = rec + ls * CB;
+    const uint8_t* vp = rec + 64 * CB + ls * CB;
     if constexpr (CW % 4 == 0) {
 #pragma unroll
       for (int i = 0; i < CW / 4; i++) {
@@ -443,8 +536,9 @@ __device__ inline void load_step(Buf<D, GS, WINDOW, PK>& b, const uint8_t* pool_
 // class (compacted: id, mask), PK per step, steps dealt round-robin to the nw
 // waves.  Two register buffers alternate: the next step's loads are in flight
 // while the current step is computed, also across a class boundary.  Past the
-// last step a wave loads that step again (its lines are still in the L2), so
-// every path issues the same loads and the compiler's waits stay exact.
+// last step a wave issues the same load instructions with every lane on the
+// first line of the last step (one cached line), so every path issues the
+// same loads, the compiler's waits stay exact, and the padding is cheap.
 template <int D, int GS, bool WINDOW, int PK>
 __device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax, const int* nl, int kvh, int lo_pos,
                                  int lane, int w, int nw, bool head_ok, const half4_t (&qB)[D / 16],
@@ -467,10 +561,11 @@ __device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax
   const int32_t* slt2 = P.S.slot[2];
   const int Hkv = P.S.Hkv;
   auto load = [&](B& b, int g) {
+    const int ls = g < T ? lane : 0;
     g = g < T ? g : T - 1;
-    if (g < c1) load_step<D, GS, WINDOW, PK, 0>(b, pool0, slt0, Hkv, l0, n0, g, kvh, lane);
-    else if (g < c2) load_step<D, GS, WINDOW, PK, 1>(b, pool1, slt1, Hkv, l1, n1, g - c1, kvh, lane);
-    else load_step<D, GS, WINDOW, PK, 2>(b, pool2, slt2, Hkv, l2, n2, g - c2, kvh, lane);
+    if (g < c1) load_step<D, GS, WINDOW, PK, 0>(b, pool0, slt0, Hkv, l0, n0, g, kvh, lane, ls);
+    else if (g < c2) load_step<D, GS, WINDOW, PK, 1>(b, pool1, slt1, Hkv, l1, n1, g - c1, kvh, lane, ls);
+    else load_step<D, GS, WINDOW, PK, 2>(b, pool2, slt2, Hkv, l2, n2, g - c2, kvh, lane, ls);
   };
   auto mask_of = [&](const int2* lv, int n, int sigma) -> uint32_t {
     const int e = sigma * PK + jl;                  // this lane's block
@@ -512,7 +607,9 @@ struct Merged {
   float top[TOPK];
 };
 
-template <int D>
+// NMAX > 0: nrec <= NMAX, the accumulator reads of all records are issued
+// together and records without tokens are dropped by selects.
+template <int D, int NMAX = 0>
 __device__ inline void merge_records(const float* recs, int stride, int nrec, int lane, Merged& M) {
   float mr = -INFINITY, zr = 0.f, sr = 0.f, nr = 0.f;
   if (lane < nrec) {
@@ -520,50 +617,79 @@ __device__ inline void merge_records(const float* recs, int stride, int nrec, in
     nr = rec[D + 3];
     if (nr > 0.f) { mr = rec[D]; zr = rec[D + 1]; sr = rec[D + 2]; }
   }
-  float m = mr;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, xorf(m, o));
+  const float m = first_lanes_max(mr, nrec);
   const float sc = nr > 0.f ? exp2f(mr - m) : 0.f;
-  float Z = sc * zr, S2 = nr > 0.f ? sc * (sr + (mr - m) * zr) : 0.f, nn = nr;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) { Z += xorf(Z, o); S2 += xorf(S2, o); nn += xorf(nn, o); }
+  const float Z = first_lanes_sum(sc * zr, nrec);
+  const float S2 = first_lanes_sum(nr > 0.f ? sc * (sr + (mr - m) * zr) : 0.f, nrec);
+  const float nn = first_lanes_sum(nr, nrec);
 #pragma unroll
   for (int i = 0; i < TOPK; i++) M.top[i] = (lane < nrec && nr > 0.f) ? recs[(int64_t)lane * stride + D + 4 + i] : -INFINITY;
-  for (int o = 1; o < nrec; o <<= 1) topk_merge_xor(M.top, o);
+  first_lanes_topk(M.top, nrec);
   float a0 = 0.f, a1 = 0.f;
-  for (int r = 0; r < nrec; r++) {
-    const float f = __shfl(sc, r, 64);
-    if (f == 0.f) continue;
-    const float* rec = recs + (int64_t)r * stride;
-    a0 = fmaf(f, rec[lane], a0);
-    if (D > 64) a1 = fmaf(f, rec[lane + 64], a1);
+  if constexpr (NMAX > 0) {
+    float f[NMAX], x0[NMAX], x1[NMAX];
+#pragma unroll
+    for (int r = 0; r < NMAX; r++) {
+      const int rr = r < nrec ? r : 0;
+      const float fr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), rr));
+      f[r] = r < nrec ? fr : 0.f;
+      x0[r] = recs[(int64_t)rr * stride + lane];
+      x1[r] = D > 64 ? recs[(int64_t)rr * stride + lane + 64] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < NMAX; r++) {
+      a0 = f[r] != 0.f ? fmaf(f[r], x0[r], a0) : a0;
+      if (D > 64) a1 = f[r] != 0.f ? fmaf(f[r], x1[r], a1) : a1;
+    }
+  } else {
+    for (int r = 0; r < nrec; r++) {
+      const float f = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), r));
+      if (f == 0.f) continue;
+      const float* rec = recs + (int64_t)r * stride;
+      a0 = fmaf(f, rec[lane], a0);
+      if (D > 64) a1 = fmaf(f, rec[lane + 64], a1);
+    }
   }
   M.a0 = a0; M.a1 = a1; M.m = m; M.Z = Z; M.S2 = S2; M.n = (int)nn;
 }
 
-// Add the staged self token and the sink; write the output and statistics.
+// The staged self token of one query head: its logit (log2 units) and its V
+// row at dims lane and lane + 64.  Loaded in the prologue when the head's
+// wave is known, so that its latency hides behind the block loads.
+struct SelfTok {
+  float s2, v0, v1;
+};
 template <int D>
-__device__ inline void finalize_head(const AttnParams& P, int b, int hq, int lane, Merged M) {
+__device__ inline SelfTok load_self(const AttnParams& P, int b, int hq, int lane) {
   const DevState& S = P.S;
   const int G = S.Hq / S.Hkv, kvh = hq / G;
-  const float alpha = LOG2E / sqrtf((float)D);
+  const uint16_t* qr = P.q + ((int64_t)b * S.Hq + hq) * D;
+  const float* kr = P.k_self + ((int64_t)b * S.Hkv + kvh) * D;
+  const float* vr = P.v_self + ((int64_t)b * S.Hkv + kvh) * D;
+  float d = 0.f;
+  for (int i = lane; i < D; i += 64) d = fmaf(__builtin_bit_cast(float, (uint32_t)qr[i] << 16), kr[i], d);
+  d = pair_sum<32>(pair_sum<16>(pair_sum<8>(pair_sum<4>(pair_sum<2>(pair_sum<1>(d))))));
+  SelfTok t;
+  t.s2 = d * (LOG2E / sqrtf((float)D));
+  t.v0 = vr[lane];
+  t.v1 = D > 64 ? vr[lane + 64] : 0.f;
+  return t;
+}
+
+// Add the staged self token and the sink; write the output and statistics.
+template <int D>
+__device__ inline void finalize_head(const AttnParams& P, int b, int hq, int lane, Merged M, const SelfTok& self) {
+  const DevState& S = P.S;
   int n = M.n;
   if (P.k_self) {
-    const uint16_t* qr = P.q + ((int64_t)b * S.Hq + hq) * D;
-    const float* kr = P.k_self + ((int64_t)b * S.Hkv + kvh) * D;
-    float d = 0.f;
-    for (int i = lane; i < D; i += 64) d = fmaf(__builtin_bit_cast(float, (uint32_t)qr[i] << 16), kr[i], d);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) d += xorf(d, o);
-    const float self2 = d * alpha;
+    const float self2 = self.s2;
     const float m = fmaxf(M.m, self2);
     const float sc = M.n > 0 ? exp2f(M.m - m) : 0.f;
     const float ps = exp2f(self2 - m);
     M.S2 = sc * (M.S2 + (M.n > 0 ? (M.m - m) * M.Z : 0.f)) + ps * (self2 - m);
     M.Z = sc * M.Z + ps;
-    const float* vr = P.v_self + ((int64_t)b * S.Hkv + kvh) * D;
-    M.a0 = fmaf(ps, vr[lane], sc * M.a0);
-    if (D > 64) M.a1 = fmaf(ps, vr[lane + 64], sc * M.a1);
+    M.a0 = fmaf(ps, self.v0, sc * M.a0);
+    if (D > 64) M.a1 = fmaf(ps, self.v1, sc * M.a1);
     M.m = m;
     topk_insert(M.top, self2);
     n += 1;
@@ -603,7 +729,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   constexpr int RS = D + PART_X;                 // record stride (floats)
   // Dynamic LDS: first the raw block lists, last the waves' records; the live
   // lists are a static array.
-  extern __shared__ float lds[];
+  extern __shared__ __align__(16) float lds[];
   __shared__ int2 s_live[3 * TKV_MAX_BLOCKS];
   __shared__ int s_nlive[3];
   const DevState& S = P.S;
@@ -712,8 +838,24 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
     }
   }
   __syncthreads();
-  run_steps<D, GS, WINDOW, PK>(P, live, lmax, nlive, kvh, lo_pos, lane, w, nw, head_ok, qB, sumq, alpha * kCodeScale,
-                               st);
+  run_steps<D, GS, WINDOW, PK>(P, live, lmax, nlive, kvh, lo_pos, lane, w, nw, head_ok, qB, sumq,
+                               alpha * kCodeScale, st);
+  // The self token of this wave's first head (finalized here with one split):
+  // its reads are issued now, so that their latency overlaps the reductions
+  // and the record merge (the barriers below order LDS only).
+  const bool early_self = P.splits == 1 && P.k_self != nullptr && w < G;
+  float selfq[D / 64], selfk[D / 64], selfv[D / 64];
+  if (early_self) {
+    const uint16_t* qr = P.q + ((int64_t)b * S.Hq + kvh * G + w) * D;
+    const float* kr = P.k_self + ((int64_t)b * S.Hkv + kvh) * D;
+    const float* vr = P.v_self + ((int64_t)b * S.Hkv + kvh) * D;
+#pragma unroll
+    for (int i = 0; i < D / 64; i++) {
+      selfq[i] = __builtin_bit_cast(float, (uint32_t)qr[lane + 64 * i] << 16);
+      selfk[i] = kr[lane + 64 * i];
+      selfv[i] = vr[lane + 64 * i];
+    }
+  }
   // accumulator columns h and h + GP*i hold one head (block positions): sum
   // them into every column of the row (rotations inside the 16-lane row)
   if constexpr (PK > 1) {
@@ -733,9 +875,8 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
 #pragma unroll
   for (int gi = 0; gi < NG; gi++) st.zacc[gi] = head_sum<GP>(st.zacc[gi]);
   st.natt = (int)head_sum<GP>((float)st.natt);
-#pragma unroll
-  for (int o = GP; o < 64; o <<= 1) topk_merge_xor(st.top, o);
-  __syncthreads();                                // the raw lists' space takes the records
+  head_topk<GP>(st.top);
+  lds_barrier();                                  // the raw lists' space takes the records
   // lanes 16 lg + h (h < G) hold head h both in the accumulator's columns and,
   // after the sums above, in the packed layout (block 0)
   if (col_ok) {
@@ -743,8 +884,8 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
 #pragma unroll
     for (int n = 0; n < NT; n++) {
       const float z = st.zacc[(16 * n) / GS];
-#pragma unroll
-      for (int r = 0; r < 4; r++) rec[16 * n + 4 * lg + r] = st.acc[n][r] * kCodeScale + z;
+      *(float4*)(rec + 16 * n + 4 * lg) = make_float4(st.acc[n][0] * kCodeScale + z, st.acc[n][1] * kCodeScale + z,
+                                                      st.acc[n][2] * kCodeScale + z, st.acc[n][3] * kCodeScale + z);
     }
     if (lg == 0) {
       rec[D] = st.m2; rec[D + 1] = st.Z; rec[D + 2] = st.S2; rec[D + 3] = (float)st.natt;
@@ -752,14 +893,25 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
       for (int i = 0; i < TOPK; i++) rec[D + 4 + i] = st.top[i];
     }
   }
-  __syncthreads();
+  lds_barrier();
   // merge the waves' records; finalize here when the sequence is one split
   for (int hh = w; hh < G; hh += nw) {
     Merged M;
-    merge_records<D>(lds + (int64_t)hh * RS, G * RS, nw, lane, M);
+    merge_records<D, 8>(lds + (int64_t)hh * RS, G * RS, nw, lane, M);
     const int hq = kvh * G + hh;
     if (P.splits == 1) {
-      finalize_head<D>(P, b, hq, lane, M);
+      SelfTok self = {0.f, 0.f, 0.f};
+      if (hh == w && early_self) {
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < D / 64; i++) d = fmaf(selfq[i], selfk[i], d);
+        self.s2 = pair_sum<32>(pair_sum<16>(pair_sum<8>(pair_sum<4>(pair_sum<2>(pair_sum<1>(d)))))) * alpha;
+        self.v0 = selfv[0];
+        self.v1 = D > 64 ? selfv[D / 64 - 1] : 0.f;
+      } else if (P.k_self) {
+        self = load_self<D>(P, b, hq, lane);
+      }
+      finalize_head<D>(P, b, hq, lane, M, self);
     } else {
       float* rec = P.part + (((int64_t)b * S.Hq + hq) * P.splits + split) * RS;
       rec[lane] = M.a0;
@@ -784,9 +936,10 @@ __global__ __launch_bounds__(256) void k_combine(AttnParams P) {
   const int hq = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6), b = blockIdx.y;
   if (hq >= S.Hq) return;
   const float* recs = P.part + ((int64_t)b * S.Hq + hq) * P.splits * (D + PART_X);
+  const SelfTok self = P.k_self ? load_self<D>(P, b, hq, lane) : SelfTok{0.f, 0.f, 0.f};
   Merged M;
   merge_records<D>(recs, D + PART_X, P.splits, lane, M);
-  finalize_head<D>(P, b, hq, lane, M);
+  finalize_head<D>(P, b, hq, lane, M, self);
 }
 
 // ---------------------------------------------------------------------------
@@ -814,7 +967,7 @@ static int lds_bytes(const tkv_cache* c, int nw) {
   const int lists = 3 * c->S.max_blocks * 8;
   return recs > lists ? recs : lists;
 }
-static const int kStaticLds = 3 * TKV_MAX_BLOCKS * 8 + 16;
+static const int kStaticLds = 3 * TKV_MAX_BLOCKS * 8 + 16;      // live lists and counts
 
 void attn_plan(const tkv_cache* c, int batch, int num_splits, int* nw_out, int* splits_out) {
   const int units = batch * c->S.Hkv > 0 ? batch * c->S.Hkv : 1;
