@@ -147,20 +147,30 @@ static int64_t elem_bit(int64_t e, int bits) {
   return w * 32 + p * bits;
 }
 
+/* A code region holds 64 chunks.  A chunk of CB bytes is cut into units of
+   U = min(CB, 16) bytes; unit u of chunk k occupies bytes [(64u + k) U,
+   (64u + k + 1) U) of the region (for CB <= 16: chunk k at byte k*CB).
+   Bit `bit` of chunk k -> bit offset within the region. */
+static int64_t chunk_bit(const ora_layout *L, int c, int64_t k, int64_t bit) {
+  int64_t CB = chunk_bytes(L, c), U = CB < 16 ? CB : 16;
+  int64_t byte = bit / 8, u = byte / U;
+  return ((64 * u + k) * U + byte % U) * 8 + bit % 8;
+}
+
 /* K code of token t (0..15), dim d: chunk 16*lg + t, element gi*(g/4) + e',
    where gi = d / g, lg = (d % g) / (g/4), e' = d % (g/4). */
 static int64_t k_code_bit(const ora_layout *L, int c, int t, int d) {
   int g = L->group_size, q4 = g / 4;
   int gi = d / g, w = d % g, lg = w / q4, ep = w % q4;
   int64_t chunk = 16 * lg + t;
-  return chunk * chunk_bytes(L, c) * 8 + elem_bit((int64_t)gi * q4 + ep, CLASS_BITS[c]);
+  return chunk_bit(L, c, chunk, elem_bit((int64_t)gi * q4 + ep, CLASS_BITS[c]));
 }
 
 /* V code of token t = 4q + r, dim d = 16n + i: chunk 16*q + i, element 4n + r. */
 static int64_t v_code_bit(const ora_layout *L, int c, int t, int d) {
   int q = t / 4, r = t % 4, n = d / 16, i = d % 16;
   int64_t chunk = 16 * q + i;
-  return codes_bytes(L, c) * 8 + chunk * chunk_bytes(L, c) * 8 + elem_bit((int64_t)n * 4 + r, CLASS_BITS[c]);
+  return codes_bytes(L, c) * 8 + chunk_bit(L, c, chunk, elem_bit((int64_t)n * 4 + r, CLASS_BITS[c]));
 }
 
 /* byte offset of the (scale, zero) fp16 pair of token t, group gi, tensor kv (0=K, 1=V) */

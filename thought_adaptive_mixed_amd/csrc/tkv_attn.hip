@@ -503,9 +503,11 @@ __device__ inline void load_step(Buf<D, GS, WINDOW, PK>& b, const uint8_t* pool_
     const uint8_t* kp = rec + ls * CB;
     const uint8_t* vp = rec + 64 * CB + ls * CB;
     if constexpr (CW % 4 == 0) {
+      // 16-byte unit i of chunk l sits at byte (64 i + l) 16 of the region
 #pragma unroll
       for (int i = 0; i < CW / 4; i++) {
-        const uint4 x = ((const uint4*)kp)[i], y = ((const uint4*)vp)[i];
+        const uint4 x = *(const uint4*)(rec + (64 * i + ls) * 16);
+        const uint4 y = *(const uint4*)(rec + 64 * CB + (64 * i + ls) * 16);
         b.kw[j][4 * i] = x.x; b.kw[j][4 * i + 1] = x.y; b.kw[j][4 * i + 2] = x.z; b.kw[j][4 * i + 3] = x.w;
         b.vw[j][4 * i] = y.x; b.vw[j][4 * i + 1] = y.y; b.vw[j][4 * i + 2] = y.z; b.vw[j][4 * i + 3] = y.w;
       }

@@ -80,26 +80,35 @@ __host__ __device__ inline int32_t* scr_moves(int32_t* s, int max_seqs) {       
 }
 
 // ---------------------------------------------------------------------------
-// Code placement inside a (block, KV head) record.  Codes of one lane chunk
-// sit in 32-bit words of W = 32/bits codes: even elements in the low
-// half-word, odd elements in the high half-word, so one AND-OR with
-// 0x64006400 turns a pair of codes into two fp16 values 1024 + code.
+// Code placement inside a (block, KV head) record.  Each of the K and V code
+// regions holds 64 lane chunks of CB = D*bits/32 bytes.  Codes of a chunk sit
+// in 32-bit words of W = 32/bits codes: even elements in the low half-word,
+// odd elements in the high half-word, so that a shift and mask (or a byte
+// permute) puts a pair of codes into the two halves of an MFMA operand word.
+// A chunk is stored in units of U = min(CB, 16) bytes, unit u of chunk k at
+// byte (64u + k) U of its region: lane l's u-th 16-byte load then reads one
+// contiguous kilobyte across the 64 lanes.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int elem_bit(int e, int bits) {
   int W = 32 / bits, w = e / W, f = e % W;
   return w * 32 + ((f >> 1) + (f & 1) * (W >> 1)) * bits;
 }
+// byte b of chunk k of a region of chunks of CB bytes -> byte within the region
+__host__ __device__ inline int chunk_byte(int CB, int k, int b) {
+  const int U = CB < 16 ? CB : 16;
+  return (64 * (b / U) + k) * U + b % U;
+}
 // K: token t, dim d -> chunk 16*lg + t, element gi*(g/4) + e'
 __host__ __device__ inline int k_code_bit(int D, int g, int bits, int t, int d) {
   int q4 = g >> 2, gi = d / g, w = d % g, lg = w / q4, ep = w % q4;
-  int chunk = 16 * lg + t;
-  return chunk * (D * bits / 32) * 8 + elem_bit(gi * q4 + ep, bits);
+  int chunk = 16 * lg + t, eb = elem_bit(gi * q4 + ep, bits);
+  return chunk_byte(D * bits / 32, chunk, eb >> 3) * 8 + (eb & 7);
 }
 // V: token t = 4q + r, dim d = 16n + i -> chunk 16*q + i, element 4n + r
 __host__ __device__ inline int v_code_bit(int D, int bits, int t, int d) {
   int q = t >> 2, r = t & 3, n = d >> 4, i = d & 15;
-  int chunk = 16 * q + i;
-  return 64 * (D * bits / 32) * 8 + chunk * (D * bits / 32) * 8 + elem_bit(4 * n + r, bits);
+  int chunk = 16 * q + i, eb = elem_bit(4 * n + r, bits);
+  return 64 * (D * bits / 32) * 8 + chunk_byte(D * bits / 32, chunk, eb >> 3) * 8 + (eb & 7);
 }
 __host__ __device__ inline int meta_byte(int D, int g, int bits, int kv, int t, int gi) {
   int NG = D / g;

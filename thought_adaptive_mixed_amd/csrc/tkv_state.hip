@@ -430,7 +430,7 @@ __device__ void quant_row_wave(const DevState& S, int c, int blk, int t, int h, 
         const int d = (e / q4) * g + lg * q4 + (e % q4);
         word |= (uint32_t)codes[d] << (((f >> 1) + (f & 1) * (W >> 1)) * bits);
       }
-      *(uint32_t*)(base + (16 * lg + t) * CB + w * 4) = word;
+      *(uint32_t*)(base + chunk_byte(CB, 16 * lg + t, w * 4)) = word;
     }
   } else {
     // chunk 16*q + i, element 4n + r: token t = 4q + r, dim d = 16n + i
@@ -438,11 +438,11 @@ __device__ void quant_row_wave(const DevState& S, int c, int blk, int t, int h, 
     uint8_t* vbase = base + 64 * CB;
     for (int l = lane; l < 16 * wpc; l += 64) {
       const int i = l / wpc, w = l % wpc;
-      uint8_t* ch = vbase + (16 * q + i) * CB;
+      uint8_t* wb = vbase + chunk_byte(CB, 16 * q + i, w * 4);     // word w of chunk 16q + i
       if (bits == 8) {
         // word w holds dim n = w for tokens r = 0..3: our byte is field r
         const int f = r, p = (f >> 1) + (f & 1) * 2;
-        ch[w * 4 + p] = codes[16 * w + i];
+        wb[p] = codes[16 * w + i];
       } else {
         uint32_t mask = 0, val = 0;
         for (int f = 0; f < W; f++) {
@@ -452,7 +452,7 @@ __device__ void quant_row_wave(const DevState& S, int c, int blk, int t, int h, 
           mask |= ((1u << bits) - 1u) << (p * bits);
           val |= (uint32_t)codes[16 * (e >> 2) + i] << (p * bits);
         }
-        uint32_t* wp = (uint32_t*)ch + w;
+        uint32_t* wp = (uint32_t*)wb;
         atomicAnd(wp, ~mask);
         atomicOr(wp, val);
       }
