@@ -174,79 +174,14 @@ __device__ inline float pack_lane(float dst, float src) {
                                                                __builtin_bit_cast(int, src), 0x110 + GP * J, 0xf,
                                                                BANKS, false));
 }
-// max / sum over the lanes holding one head's values in the packed layout
-// (lanes h + GP*i of every row).  The max runs on VALU cross-lane moves only:
-// DPP row rotations by 4 and 8 inside a 16-lane row, then the gfx950 swaps of
-// row pairs (v_permlane16_swap) and wave halves (v_permlane32_swap).  A swap
-// of a value with a copy of itself leaves the even rows (lower half) in one
-// register and the odd rows (upper half) in the other, in every lane, so the
-// max of the two registers is the exact reduction over the pair.  The swap is
-// written as one asm block together with the copy (and the two wait states a
-// permlane needs after a VALU write): given the same value twice, the
-// compiler's builtin folds the two results into one.
-template <int CTRL>
-__device__ inline float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
-}
-__device__ inline float max_swap16(float v) {
-  uint32_t a = __builtin_bit_cast(uint32_t, v), b;
-  asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "=&v"(b));
-  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
-}
-__device__ inline float max_swap32(float v) {
-  uint32_t a = __builtin_bit_cast(uint32_t, v), b;
-  asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "=&v"(b));
-  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
-}
+// max over the lanes holding one head's values in the packed layout (lanes
+// h + GP*i of every row): DPP row rotations by 4 and 8 inside a 16-lane row,
+// then the row-pair and wave-half swaps.
 template <int GP>
 __device__ inline float head_max(float v) {
   if constexpr (GP <= 4) v = fmaxf(v, dpp_f<0x124>(v));          // row_ror:4
   if constexpr (GP <= 8) v = fmaxf(v, dpp_f<0x128>(v));          // row_ror:8
-  return max_swap32(max_swap16(v));
-}
-// Exact butterflies on VALU.  xchg<K> (K = 1, 2, 4, 8) is the value of lane
-// i ^ K: DPP quad permutations, a pair of bank-masked row shifts, a row
-// rotation by 8.  For K = 16, 32 a swap hands every lane both values of its
-// pair (even row / lower half first).  Sums, maxima and top-8 merges of a
-// pair are independent of operand order, so both partners get the same bits.
-template <int K>
-__device__ inline float xchg(float v) {
-  if constexpr (K == 1) return dpp_f<0xB1>(v);                   // quad_perm [1,0,3,2]
-  if constexpr (K == 2) return dpp_f<0x4E>(v);                   // quad_perm [2,3,0,1]
-  if constexpr (K == 4) {
-    int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x104, 0xf, 0x5, false);   // row_shl:4, banks 0, 2
-    t = __builtin_amdgcn_update_dpp(t, __builtin_bit_cast(int, v), 0x114, 0xf, 0xA, false);       // row_shr:4, banks 1, 3
-    return __builtin_bit_cast(float, t);
-  }
-  if constexpr (K == 8) return dpp_f<0x128>(v);                  // row_ror:8
-}
-template <int K>
-__device__ inline void swap_pair(float v, float& a, float& b) {
-  uint32_t x = __builtin_bit_cast(uint32_t, v), y;
-  if constexpr (K == 16) asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x), "=&v"(y));
-  else asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x), "=&v"(y));
-  a = __builtin_bit_cast(float, x);
-  b = __builtin_bit_cast(float, y);
-}
-template <int K>
-__device__ inline float pair_sum(float v) {
-  if constexpr (K <= 8) {
-    return v + xchg<K>(v);
-  } else {
-    float a, b;
-    swap_pair<K>(v, a, b);
-    return a + b;
-  }
-}
-template <int K>
-__device__ inline float pair_max(float v) {
-  if constexpr (K <= 8) {
-    return fmaxf(v, xchg<K>(v));
-  } else {
-    float a, b;
-    swap_pair<K>(v, a, b);
-    return fmaxf(a, b);
-  }
+  return pair_max<32>(pair_max<16>(v));
 }
 template <int K>
 __device__ inline void pair_topk(float (&L)[TOPK]) {

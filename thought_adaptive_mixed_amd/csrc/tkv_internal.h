@@ -116,6 +116,62 @@ __host__ __device__ inline int meta_byte(int D, int g, int bits, int kv, int t, 
 }
 
 // Sticky error word.
+// ---------------------------------------------------------------------------
+// Exact cross-lane butterflies on VALU (no LDS round trip).  xchg<K> (K = 1,
+// 2, 4, 8) is the value of lane i ^ K: DPP quad permutations, a pair of
+// bank-masked row shifts, a row rotation by 8.  For K = 16, 32 swap_pair hands
+// every lane both values of its pair (even row / lower half first) through
+// the gfx950 v_permlane16_swap / v_permlane32_swap, written as one asm block
+// with the copy: given the same value as both operands, the compiler's builtin
+// folds its two results into one.  The block also holds the two wait states a
+// permlane needs after a VALU write.  Sums, minima, maxima and top-k merges of
+// a pair do not depend on operand order, so both partners get the same bits.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+template <int K>
+__device__ inline float xchg(float v) {
+  if constexpr (K == 1) return dpp_f<0xB1>(v);                   // quad_perm [1,0,3,2]
+  if constexpr (K == 2) return dpp_f<0x4E>(v);                   // quad_perm [2,3,0,1]
+  if constexpr (K == 4) {
+    int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x104, 0xf, 0x5, false);   // row_shl:4, banks 0, 2
+    t = __builtin_amdgcn_update_dpp(t, __builtin_bit_cast(int, v), 0x114, 0xf, 0xA, false);       // row_shr:4, banks 1, 3
+    return __builtin_bit_cast(float, t);
+  }
+  if constexpr (K == 8) return dpp_f<0x128>(v);                  // row_ror:8
+}
+template <int K>
+__device__ inline void swap_pair(float v, float& a, float& b) {
+  uint32_t x = __builtin_bit_cast(uint32_t, v), y;
+  if constexpr (K == 16) asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x), "=&v"(y));
+  else asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x), "=&v"(y));
+  a = __builtin_bit_cast(float, x);
+  b = __builtin_bit_cast(float, y);
+}
+
+template <int K>
+__device__ inline float pair_sum(float v) {
+  if constexpr (K <= 8) {
+    return v + xchg<K>(v);
+  } else {
+    float a, b;
+    swap_pair<K>(v, a, b);
+    return a + b;
+  }
+}
+template <int K>
+__device__ inline float pair_max(float v) {
+  if constexpr (K <= 8) {
+    return fmaxf(v, xchg<K>(v));
+  } else {
+    float a, b;
+    swap_pair<K>(v, a, b);
+    return fmaxf(a, b);
+  }
+}
+
 __device__ inline void record_error(int32_t* hdr, int code, int seq) {
   atomicOr(&hdr[H_EKIND], 1 << (-code));
   atomicMin(&hdr[H_EMINSEQ], seq);

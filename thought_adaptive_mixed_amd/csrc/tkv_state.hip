@@ -390,6 +390,21 @@ __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+template <int K>
+__device__ inline void minmax_level(float& mn, float& mx) {
+  if constexpr (K <= 8) {
+    const float a = xchg<K>(mn), b = xchg<K>(mx);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  } else {
+    float m0, m1, x0, x1;
+    swap_pair<K>(mn, m0, m1);
+    swap_pair<K>(mx, x0, x1);
+    mn = m1 < m0 ? m1 : m0;
+    mx = x1 > x0 ? x1 : x0;
+  }
+}
+
 template <int E>
 __device__ void quant_row_wave(const DevState& S, int c, int blk, int t, int h, int kv, int lane, const float (&x)[E],
                                uint8_t* codes /* per-wave LDS, D bytes */) {
@@ -400,11 +415,14 @@ __device__ void quant_row_wave(const DevState& S, int c, int blk, int t, int h, 
   float mn = x[0], mx = x[0];
 #pragma unroll
   for (int e = 1; e < E; e++) { mn = x[e] < mn ? x[e] : mn; mx = x[e] > mx ? x[e] : mx; }
-  for (int o = 1; o < lpg; o <<= 1) {
-    const float a = __shfl_xor(mn, o, 64), b = __shfl_xor(mx, o, 64);
-    mn = a < mn ? a : mn;
-    mx = b > mx ? b : mx;
-  }
+  // butterfly over the group's lpg lanes (exact; a zero extremum may keep
+  // either sign, which no result depends on)
+  if (lpg > 1) minmax_level<1>(mn, mx);
+  if (lpg > 2) minmax_level<2>(mn, mx);
+  if (lpg > 4) minmax_level<4>(mn, mx);
+  if (lpg > 8) minmax_level<8>(mn, mx);
+  if (lpg > 16) minmax_level<16>(mn, mx);
+  if (lpg > 32) minmax_level<32>(mn, mx);
   // (the sign of a zero extremum cannot change the scale, the zero-point or any code)
   const float levels = (float)((1 << bits) - 1);
   const float range = mx - mn;
@@ -1167,7 +1185,9 @@ __global__ __launch_bounds__(256) void k_classify(int batch, int Hq, const float
       v = kind == 0 ? st[1] : 1.0f - st[2];
     }
     const int m = Hq - h0 < 64 ? Hq - h0 : 64;
-    for (int j = 0; j < m; j++) sum = sum + __shfl(v, j, 64);
+    // the terms in head order; v_readlane (no LDS round trip per term)
+    for (int j = 0; j < m; j++)
+      sum = sum + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
   }
   const float score = sum / (float)Hq;
   if (lane == 0) labels[b] = score <= tT ? (uint8_t)TKV_T : (score >= tE ? (uint8_t)TKV_E : (uint8_t)TKV_R);
