@@ -56,7 +56,6 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 // v_exp_f32 directly: no denormal-range fixup (weights below 2^-126 are 0)
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ inline float xorf(float v, int m) { return __shfl_xor(v, m, 64); }
 __device__ inline uint32_t rdlane(uint32_t v, int l) { return (uint32_t)__builtin_amdgcn_readlane((int)v, l); }
 // work-group barrier that orders LDS only: global reads in flight (the
 // padding loads past a wave's last step, the self token) are not waited for
@@ -664,8 +663,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   constexpr int NT = D / 16;
   constexpr int GP = 16 / PK;
   constexpr int RS = D + PART_X;                 // record stride (floats)
-  // Dynamic LDS: first the raw block lists, last the waves' records; the live
-  // lists are a static array.
+  // Dynamic LDS: the waves' records; the live block lists are a static array.
   extern __shared__ __align__(16) float lds[];
   __shared__ int2 s_live[3 * TKV_MAX_BLOCKS];
   __shared__ int s_nlive[3];
@@ -679,42 +677,16 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   const bool head_ok = hp < G;
   const int s = P.seq_ids[b];
   const bool seq_ok = s >= 0 && s < S.max_seqs;
-  int2* lst = (int2*)lds;                                 // [3][lmax], before any slot is filled
-  const int lmax = S.max_blocks;
-  int2* live = s_live;                                    // [3][lmax]
-  int* nlive = s_nlive;
-  // query B operand: column h, k = 4lg + e <-> dim gi*GS + lg*(GS/4) + 4mm + e
-  half4_t qB[NG * KM];
-  float sumq[NG];
+  // Query rows, read now and converted after the block lists (so that their
+  // latency overlaps the list reads).  Lane (h, lg) holds the query of the
+  // head of its packed column, h mod GP (zero for a padding column).
+  uint4 qraw[NG][GS / 32];
   {
-    const uint16_t* qr = P.q + ((int64_t)b * S.Hq + (int64_t)kvh * G + (col_ok ? h : 0)) * D;
+    const uint16_t* qr = P.q + ((int64_t)b * S.Hq + (int64_t)kvh * G + (head_ok ? hp : 0)) * D;
 #pragma unroll
-    for (int gi = 0; gi < NG; gi++) {
-      const uint4* src = (const uint4*)(qr + gi * GS + lg * (GS / 4));
-      uint32_t wq[GS / 8];
+    for (int gi = 0; gi < NG; gi++)
 #pragma unroll
-      for (int i = 0; i < GS / 32; i++) {
-        uint4 v = src[i];
-        wq[4 * i] = v.x; wq[4 * i + 1] = v.y; wq[4 * i + 2] = v.z; wq[4 * i + 3] = v.w;
-      }
-      float sq = 0.f;
-#pragma unroll
-      for (int mm = 0; mm < KM; mm++) {
-        half4_t v;
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int j = 4 * mm + e;
-          const uint32_t bits = (j & 1) ? (wq[j >> 1] & 0xFFFF0000u) : (wq[j >> 1] << 16);
-          const float x = col_ok ? __builtin_bit_cast(float, bits) : 0.f;
-          v[e] = (_Float16)x;
-          sq += (float)v[e];
-        }
-        qB[gi * KM + mm] = v;
-      }
-      sq += xorf(sq, 16);
-      sq += xorf(sq, 32);
-      sumq[gi] = __shfl(sq, hp, 64) * kCodeUnit;   // the packed lane's head, in code units
-    }
+      for (int i = 0; i < GS / 32; i++) qraw[gi][i] = ((const uint4*)(qr + gi * GS + lg * (GS / 4)))[i];
   }
   const float alpha = LOG2E / sqrtf((float)D);
   AttnState<D, GS> st;
@@ -725,54 +697,82 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   st.m2 = -INFINITY; st.Z = 0.f; st.S2 = 0.f; st.natt = 0;
 #pragma unroll
   for (int i = 0; i < TOPK; i++) st.top[i] = -INFINITY;
-  // the split's block ids and masks, all three classes, into LDS
-  int ncls[3] = {0, 0, 0};
+  // The split's live blocks of each class, into LDS, in list order: wave c
+  // (the waves in turn when there are fewer than three) takes class c's
+  // block-table entries 64 at a time, reads their block records and keeps,
+  // by ballot, those with a valid token (and, with a window, a position
+  // inside it).  A wave's first 64 entries of its own class are read
+  // together with the sequence record, before the split's range is known.
   const int lo_pos = WINDOW ? P.q_pos[b] - P.window + 1 : 0;
+  const int lmax = S.max_blocks;
+  int2* live = s_live;                                    // [3][lmax]
+  int* nlive = s_nlive;
   if (seq_ok) {
     const int32_t* q = S.seq + (int64_t)s * TKV_SEQ_W;
+    const int32_t* bt = S.btab + (int64_t)s * 3 * lmax;
+    const int spec = w < 3 && lane < lmax ? bt[w * lmax + lane] : 0;
     const int nb0 = q[Q_NBLK + 0], nb1 = q[Q_NBLK + 1], nb2 = q[Q_NBLK + 2];
     // byte-balanced split of [8-bit | 4-bit | 2-bit] block lists (< 2^31 bytes per sequence)
     const int w0 = (int)S.bh_bytes[0], w1 = (int)S.bh_bytes[1], w2 = (int)S.bh_bytes[2];
     const int P1 = nb0 * w0, P2 = P1 + nb1 * w1, W = P2 + nb2 * w2;
     const int lo = (int)((int64_t)W * split / P.splits), hi = (int)((int64_t)W * (split + 1) / P.splits);
-    const int32_t* bt = S.btab + (int64_t)s * 3 * S.max_blocks;
-    int j0s[3], j1s[3];
-    const int off[3] = {0, P1, P2}, wb[3] = {w0, w1, w2}, nb[3] = {nb0, nb1, nb2};
-#pragma unroll
-    for (int c = 0; c < 3; c++) {
-      const int a = lo - off[c], z = hi - off[c];
-      j0s[c] = a <= 0 ? 0 : min(nb[c], (a + wb[c] - 1) / wb[c]);
-      j1s[c] = z <= 0 ? 0 : min(nb[c], (z + wb[c] - 1) / wb[c]);
-      ncls[c] = j1s[c] > j0s[c] ? j1s[c] - j0s[c] : 0;
-    }
-    const int tot = ncls[0] + ncls[1] + ncls[2];
-    for (int e = threadIdx.x; e < tot; e += blockDim.x) {
-      const int c = e < ncls[0] ? 0 : (e < ncls[0] + ncls[1] ? 1 : 2);
-      const int i = e - (c == 0 ? 0 : (c == 1 ? ncls[0] : ncls[0] + ncls[1]));
-      const int id = bt[c * S.max_blocks + j0s[c] + i];
-      const int2 rec = *(const int2*)(pick3(S.blk, c) + (int64_t)id * TKV_BLK_W);
-      int m = rec.x;
-      if (WINDOW && rec.y < lo_pos) m = 0;
-      lst[c * lmax + i] = make_int2(id, m);
-    }
-  }
-  __syncthreads();
-  // keep the live blocks (mask != 0), in order
-  if (w == 0) {
     const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
-#pragma unroll
-    for (int c = 0; c < 3; c++) {
+    for (int c = w; c < 3; c += nw) {
+      const int off = c == 0 ? 0 : (c == 1 ? P1 : P2);
+      const int wb = c == 0 ? w0 : (c == 1 ? w1 : w2);
+      const int nbc = c == 0 ? nb0 : (c == 1 ? nb1 : nb2);
+      const int a = lo - off, z = hi - off;
+      const int j0 = a <= 0 ? 0 : min(nbc, (a + wb - 1) / wb);
+      const int j1 = z <= 0 ? 0 : min(nbc, (z + wb - 1) / wb);
+      const int32_t* blk = pick3(S.blk, c);
       int cnt = 0;
-      for (int b0 = 0; b0 < ncls[c]; b0 += 64) {
-        const int e = b0 + lane;
-        const int2 v = e < ncls[c] ? lst[c * lmax + e] : make_int2(0, 0);
-        const bool lv = v.y != 0;
-        const uint64_t m = __builtin_amdgcn_ballot_w64(lv);
-        if (lv) live[c * lmax + cnt + __popcll(m & lt)] = v;
-        cnt += __popcll(m);
+      for (int j = j0; j < j1; j += 64) {
+        const int jj = j + lane;
+        const bool in = jj < j1;
+        int id = 0, m = 0;
+        if (in) {
+          id = (j == 0 && c == w) ? spec : bt[c * lmax + jj];
+          const int2 rec = *(const int2*)(blk + (int64_t)id * TKV_BLK_W);
+          m = rec.x;
+          if (WINDOW && rec.y < lo_pos) m = 0;
+        }
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(m != 0);
+        if (m != 0) live[c * lmax + cnt + __popcll(bal & lt)] = make_int2(id, m);
+        cnt += __popcll(bal);
       }
       if (lane == 0) nlive[c] = cnt;
     }
+  } else {
+    for (int c = w; c < 3; c += nw)
+      if (lane == 0) nlive[c] = 0;
+  }
+  // query B operand: qB[gi*KM + mm][e] of lane (h, lg) holds dim
+  // gi*GS + lg*(GS/4) + 4mm + e of column h's head; and sum(q) per group (over
+  // the four lane groups of the column), in code units
+  half4_t qB[NG * KM];
+  float sumq[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; gi++) {
+    uint32_t wq[GS / 8];
+#pragma unroll
+    for (int i = 0; i < GS / 32; i++) {
+      wq[4 * i] = qraw[gi][i].x; wq[4 * i + 1] = qraw[gi][i].y; wq[4 * i + 2] = qraw[gi][i].z; wq[4 * i + 3] = qraw[gi][i].w;
+    }
+    float sq = 0.f;
+#pragma unroll
+    for (int mm = 0; mm < KM; mm++) {
+      half4_t v;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int j = 4 * mm + e;
+        const uint32_t bits = (j & 1) ? (wq[j >> 1] & 0xFFFF0000u) : (wq[j >> 1] << 16);
+        const float x = head_ok ? __builtin_bit_cast(float, bits) : 0.f;
+        v[e] = (_Float16)x;
+        sq += (float)v[e];
+      }
+      qB[gi * KM + mm] = v;
+    }
+    sumq[gi] = pair_sum<32>(pair_sum<16>(sq)) * kCodeUnit;
   }
   __syncthreads();
   run_steps<D, GS, WINDOW, PK>(P, live, lmax, nlive, kvh, lo_pos, lane, w, nw, head_ok, qB, sumq,
@@ -813,7 +813,6 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   for (int gi = 0; gi < NG; gi++) st.zacc[gi] = head_sum<GP>(st.zacc[gi]);
   st.natt = (int)head_sum<GP>((float)st.natt);
   head_topk<GP>(st.top);
-  lds_barrier();                                  // the raw lists' space takes the records
   // lanes 16 lg + h (h < G) hold head h both in the accumulator's columns and,
   // after the sums above, in the packed layout (block 0)
   if (col_ok) {
@@ -896,13 +895,10 @@ static int pack_of(const tkv_cache* c, int G) {
   return G <= 8 && (c->S.D == 64 || c->S.D / c->S.g <= 2) ? 2 : 1;
 }
 
-// dynamic LDS: the raw block lists, later the waves' records; the live lists
-// are static
+// dynamic LDS: the waves' records (the live block lists are static)
 static int lds_bytes(const tkv_cache* c, int nw) {
   const int D = c->S.D, G = c->S.Hq / c->S.Hkv;
-  const int recs = nw * G * (D + PART_X) * (int)sizeof(float);
-  const int lists = 3 * c->S.max_blocks * 8;
-  return recs > lists ? recs : lists;
+  return nw * G * (D + PART_X) * (int)sizeof(float);
 }
 static const int kStaticLds = 3 * TKV_MAX_BLOCKS * 8 + 16;      // live lists and counts
 
