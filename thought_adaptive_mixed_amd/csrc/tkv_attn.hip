@@ -107,6 +107,11 @@ __device__ inline half4_t operand4(const uint32_t* words, int e0) {
 __device__ inline half8_t cat8(half4_t a, half4_t b) {
   return (half8_t){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
+// v (k) or zeros (!k)
+__device__ inline half4_t keep4(half4_t v, bool k) {
+  const uint2 u = __builtin_bit_cast(uint2, v);
+  return __builtin_bit_cast(half4_t, make_uint2(k ? u.x : 0u, k ? u.y : 0u));
+}
 // v_mfma_f32_16x16x32_f16: k = 8 * (lane / 16) + e in both operands
 __device__ inline float4_t mfma32(half8_t a, half8_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -251,44 +256,41 @@ struct Buf {
 
 template <int D, int GS, int BITS, bool WINDOW, int PK>
 __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj, int lo_pos,
-                                    int lane, bool head_ok, const half4_t (&qB)[D / 16], const float (&sumq)[D / GS],
+                                    int lane, bool head_ok, const half4_t (&qB)[D / 16],
+                                    const half8_t (&qK)[PK > 1 ? PK / 2 : 1][D / 16], const float (&sumq)[D / GS],
                                     float alpha, AttnState<D, GS>& st) {
   constexpr int NG = D / GS;
   constexpr int KM = GS / 16;
   constexpr int NT = D / 16;
   constexpr int GP = 16 / PK;
   const int lg = lane >> 4, jl = (lane & 15) / GP;
-  // S^T = K Q^T per block and group (16x16x32: a lane's 16 elements of a
-  // group are two 8-element k slices); the PK blocks packed side by side
+  // S^T = K Q^T per group, the PK blocks packed side by side.  PK = 1: a
+  // lane's 16 elements of a group are two 8-element k slices.  PK > 1: a k
+  // slice holds the same 4 elements of blocks 2p and 2p+1, and the query
+  // operand qK[p] of a lane is zero outside its own block's half, so column
+  // h receives block h / GP's logits directly.
   float4_t spk[NG];
-#pragma unroll
-  for (int j = 0; j < PK; j++) {
-    float4_t sj[NG];
+  if constexpr (PK == 1) {
 #pragma unroll
     for (int gi = 0; gi < NG; gi++) {
-      sj[gi] = (float4_t){0.f, 0.f, 0.f, 0.f};
+      spk[gi] = (float4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mm = 0; mm < KM; mm += 2)
-        sj[gi] = mfma32(cat8(operand4<BITS>(b.kw[j], gi * (GS / 4) + 4 * mm),
-                             operand4<BITS>(b.kw[j], gi * (GS / 4) + 4 * mm + 4)),
-                        cat8(qB[gi * KM + mm], qB[gi * KM + mm + 1]), sj[gi]);
+        spk[gi] = mfma32(cat8(operand4<BITS>(b.kw[0], gi * (GS / 4) + 4 * mm),
+                              operand4<BITS>(b.kw[0], gi * (GS / 4) + 4 * mm + 4)),
+                         cat8(qB[gi * KM + mm], qB[gi * KM + mm + 1]), spk[gi]);
     }
-    if (j == 0) {
+  } else {
 #pragma unroll
-      for (int gi = 0; gi < NG; gi++) spk[gi] = sj[gi];
-    } else {
+    for (int gi = 0; gi < NG; gi++) {
+      spk[gi] = (float4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int gi = 0; gi < NG; gi++)
+      for (int p = 0; p < PK / 2; p++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-          if constexpr (PK > 1) {
-            if (j == 1) spk[gi][r] = pack_lane<GP, 1>(spk[gi][r], sj[gi][r]);
-            if constexpr (PK > 2) {
-              if (j == 2) spk[gi][r] = pack_lane<GP, 2>(spk[gi][r], sj[gi][r]);
-              if (j == 3) spk[gi][r] = pack_lane<GP, 3>(spk[gi][r], sj[gi][r]);
-            }
-          }
-        }
+        for (int mm = 0; mm < KM; mm++)
+          spk[gi] = mfma32(cat8(operand4<BITS>(b.kw[2 * p], gi * (GS / 4) + 4 * mm),
+                                operand4<BITS>(b.kw[2 * p + 1], gi * (GS / 4) + 4 * mm)),
+                           qK[p][gi * KM + mm], spk[gi]);
     }
   }
   // this lane's block (mask mj) and token quad (lg)
@@ -385,18 +387,14 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
     // lane keeps its own block's half of the slice and zeroes the other, so
     // accumulator column h collects head h % GP over the blocks at position
     // h / GP of every step; the positions are summed once at the end.
-    auto keep = [](half4_t v, bool k) -> half4_t {
-      const uint2 u = __builtin_bit_cast(uint2, v);
-      return __builtin_bit_cast(half4_t, make_uint2(k ? u.x : 0u, k ? u.y : 0u));
-    };
 #pragma unroll
     for (int jp = 0; jp < PK; jp += 2) {
       const bool k0 = jl == jp, k1 = jl == jp + 1;
       half8_t bh[NG], bl[NG];
 #pragma unroll
       for (int gi = 0; gi < NG; gi++) {
-        bh[gi] = cat8(keep(pbh[gi], k0), keep(pbh[gi], k1));
-        bl[gi] = cat8(keep(pbl[gi], k0), keep(pbl[gi], k1));
+        bh[gi] = cat8(keep4(pbh[gi], k0), keep4(pbh[gi], k1));
+        bl[gi] = cat8(keep4(pbl[gi], k0), keep4(pbl[gi], k1));
       }
 #pragma unroll
       for (int n = 0; n < NT; n++) {
@@ -478,7 +476,8 @@ __device__ inline void load_step(Buf<D, GS, WINDOW, PK>& b, const uint8_t* pool_
 template <int D, int GS, bool WINDOW, int PK>
 __device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax, const int* nl, int kvh, int lo_pos,
                                  int lane, int w, int nw, bool head_ok, const half4_t (&qB)[D / 16],
-                                 const float (&sumq)[D / GS], float alpha, AttnState<D, GS>& st) {
+                                 const half8_t (&qK)[PK > 1 ? PK / 2 : 1][D / 16], const float (&sumq)[D / GS],
+                                 float alpha, AttnState<D, GS>& st) {
   typedef Buf<D, GS, WINDOW, PK> B;
   constexpr int GP = 16 / PK;
   const int jl = (lane & 15) / GP;
@@ -509,11 +508,14 @@ __device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax
   };
   auto comp = [&](const B& b, int g) {
     if (g < c1)
-      compute_step<D, GS, 8, WINDOW, PK>(b, mask_of(l0, n0, g), lo_pos, lane, head_ok, qB, sumq, alpha, st);
+      compute_step<D, GS, 8, WINDOW, PK>(b, mask_of(l0, n0, g), lo_pos, lane, head_ok, qB, qK, sumq, alpha,
+                                          st);
     else if (g < c2)
-      compute_step<D, GS, 4, WINDOW, PK>(b, mask_of(l1, n1, g - c1), lo_pos, lane, head_ok, qB, sumq, alpha, st);
+      compute_step<D, GS, 4, WINDOW, PK>(b, mask_of(l1, n1, g - c1), lo_pos, lane, head_ok, qB, qK, sumq, alpha,
+                                          st);
     else
-      compute_step<D, GS, 2, WINDOW, PK>(b, mask_of(l2, n2, g - c2), lo_pos, lane, head_ok, qB, sumq, alpha, st);
+      compute_step<D, GS, 2, WINDOW, PK>(b, mask_of(l2, n2, g - c2), lo_pos, lane, head_ok, qB, qK, sumq, alpha,
+                                          st);
   };
   int g = w;
   if (g >= T) return;
@@ -774,8 +776,18 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
     }
     sumq[gi] = pair_sum<32>(pair_sum<16>(sq)) * kCodeUnit;
   }
+  // K-side operands for packed blocks: pair p keeps the lane's query in the
+  // half of the k slice that holds its own block (2p or 2p+1)
+  half8_t qK[PK > 1 ? PK / 2 : 1][NG * KM];
+  if constexpr (PK > 1) {
+    const int jq = (lane & 15) / GP;
+#pragma unroll
+    for (int p2 = 0; p2 < PK / 2; p2++)
+#pragma unroll
+      for (int i = 0; i < NG * KM; i++) qK[p2][i] = cat8(keep4(qB[i], jq == 2 * p2), keep4(qB[i], jq == 2 * p2 + 1));
+  }
   __syncthreads();
-  run_steps<D, GS, WINDOW, PK>(P, live, lmax, nlive, kvh, lo_pos, lane, w, nw, head_ok, qB, sumq,
+  run_steps<D, GS, WINDOW, PK>(P, live, lmax, nlive, kvh, lo_pos, lane, w, nw, head_ok, qB, qK, sumq,
                                alpha * kCodeScale, st);
   // The self token of this wave's first head (finalized here with one split):
   // its reads are issued now, so that their latency overlaps the reductions
