@@ -350,10 +350,11 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
       if (s2[r] > thr) topk_insert(st.top, s2[r]);
   }
   // P' = p sV per group as fp16 hi + lo (packed layout), and the zero-point
-  // term.  A masked token has p = 0, but its slot may never have been written
-  // (the tail of an open block, the block repeated to pad a last step): its
-  // fp16 scale and zero-point are cleared so that no stale NaN or inf pattern
-  // reaches the products.
+  // term.  A masked token has p = 0 and finite metadata: pools are cleared
+  // when the cache is created, so a slot never written (the tail of an open
+  // block, the block repeated to pad a last step) holds zeros.  p sV is an fma
+  // with a +0 addend (one mixed-precision op; a zero's sign cannot matter in
+  // sums into the accumulator).
   half4_t pbh[NG], pbl[NG];
 #pragma unroll
   for (int gi = 0; gi < NG; gi++) {
@@ -361,8 +362,8 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
     float z = st.zacc[gi];
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      const uint32_t m = ((vb >> r) & 1u) ? b.mv[r * NG + gi] : 0u;
-      pv[r] = p[r] * h_lo(m);
+      const uint32_t m = b.mv[r * NG + gi];
+      pv[r] = fmaf(p[r], h_lo(m), 0.f);
       z = fmaf(p[r], h_hi(m), z);
     }
     st.zacc[gi] = z;
