@@ -922,7 +922,10 @@ void attn_plan(const tkv_cache* c, int batch, int num_splits, int* nw_out, int* 
   int splits = num_splits;
   if (splits <= 0) {
     splits = (kTargetWaves + units * nw - 1) / (units * nw);
-    const int cap = (3 * c->S.max_blocks) / (4 * nw) > 1 ? (3 * c->S.max_blocks) / (4 * nw) : 1;
+    // at most as many splits as give each wave about four steps when the
+    // block lists are full (more would leave waves idle and add a combine)
+    const int pk = pack_of(c, c->S.Hq / c->S.Hkv);
+    const int cap = (3 * c->S.max_blocks) / (4 * nw * pk) > 1 ? (3 * c->S.max_blocks) / (4 * nw * pk) : 1;
     if (splits > cap) splits = cap;
     if (splits > 64) splits = 64;
     if (splits < 1) splits = 1;
