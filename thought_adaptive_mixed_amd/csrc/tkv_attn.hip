@@ -56,7 +56,6 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 // v_exp_f32 directly: no denormal-range fixup (weights below 2^-126 are 0)
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ inline uint32_t rdlane(uint32_t v, int l) { return (uint32_t)__builtin_amdgcn_readlane((int)v, l); }
 // work-group barrier that orders LDS only: global reads in flight (the
 // padding loads past a wave's last step, the self token) are not waited for
 __device__ inline void lds_barrier() {
@@ -166,18 +165,6 @@ struct AttnState {
 __device__ inline float h_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFF)); }
 __device__ inline float h_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
-// ---------------------------------------------------------------------------
-// Packing of the PK blocks of a step (GP = 16 / PK lanes per block and row):
-// lanes [GP*J, GP*J + GP) of each row take block J's lanes [0, GP) (row shift
-// right, only the target banks written).
-// ---------------------------------------------------------------------------
-template <int GP, int J>
-__device__ inline float pack_lane(float dst, float src) {
-  constexpr int BANKS = ((1 << (GP / 4)) - 1) << ((GP / 4) * J);
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, dst),
-                                                               __builtin_bit_cast(int, src), 0x110 + GP * J, 0xf,
-                                                               BANKS, false));
-}
 // max over the lanes holding one head's values in the packed layout (lanes
 // h + GP*i of every row): DPP row rotations by 4 and 8 inside a 16-lane row,
 // then the row-pair and wave-half swaps.
