@@ -354,7 +354,7 @@ static void vacate(const ora_layout *L, ora_state *S, int c, int slot) {
 /* kv_append_quant: tokens applied one by one in list order.               */
 /* k, v: fp32 [n][Hkv][D].  slot_out (nullable): (class << 28) | slot, or  */
 /* -1 for a token that was not stored.                                     */
-/* Segments (TBE bullet, "thought segments"): a maximal run of             */
+/* Segments (TBE bullet: eviction acts on runs of one thought type): a maximal run of */
 /* consecutively appended tokens of one sequence with the same type (and   */
 /* the same precision class, should the open segment have been downgraded).*/
 /* Failure rules (per call): a token whose sequence already failed in this */
