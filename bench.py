@@ -308,7 +308,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8/4/2 codes as exact f16, f16 MFMA, f32 accumulate",
+        "dtype": "f16 MFMA (int8/4/2 codes as exact fp16 subnormals), f32 accumulate",
         "data": "synthetic",
         "config": {"workload": "llama8b-like reasoning decode, one layer: B32, Hq32/Hkv8, D128, g64, "
                                "16k generated tokens/seq, 10% budget (1638 retained), R/E/T 8/4/2-bit, "
