@@ -12,7 +12,9 @@
 // dropped) are taken PK at a time, steps dealt round-robin to the waves.  A
 // wave holds two steps of records (codes and metadata of PK blocks) in
 // registers: the loads of the next step are in flight while the current one
-// is computed.  Per 16-token block, lane l takes chunk l of the K codes and
+// is computed.  The codes are read through one buffer resource per block
+// record (scalar base, constant lane offset); the query operands, the same
+// for every step, are read from LDS.  Per 16-token block, lane l takes chunk l of the K codes and
 // chunk l of the V codes (D*bits/32 bytes each), which puts the codes straight
 // into MFMA operand layout (v_mfma_f32_16x16x32_f16; k = 8 (lane / 16) + e):
 //   S^T[t][h] = sum_d K[t][d] Q[h][d]     A = K codes, two 8-dim halves of a
@@ -159,6 +161,7 @@ struct AttnState {
   float zacc[NG];
   float m2, Z, S2;
   float top[TOPK];
+  float thr;                   // head-wide 8th-best of the top lists
   int natt;
 };
 
@@ -244,7 +247,7 @@ struct Buf {
 template <int D, int GS, int BITS, bool WINDOW, int PK>
 __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj, int lo_pos,
                                     int lane, bool head_ok, const half4_t (&qB)[D / 16],
-                                    const half8_t (&qK)[PK > 1 ? PK / 2 : 1][D / 16], const float (&sumq)[D / GS],
+                                    const half8_t* qk_lds, const float (&sumq)[D / GS],
                                     float alpha, AttnState<D, GS>& st) {
   constexpr int NG = D / GS;
   constexpr int KM = GS / 16;
@@ -256,6 +259,12 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
   // slice holds the same 4 elements of blocks 2p and 2p+1, and the query
   // operand qK[p] of a lane is zero outside its own block's half, so column
   // h receives block h / GP's logits directly.
+  // The query operands are read from LDS at every step (kept in registers
+  // they would hold 4 or 8 VGPRs per 16 dims through the whole loop); the
+  // empty asm makes the lane offset opaque so the reads stay in the loop.
+  int qoff = lane * 16;
+  asm volatile("" : "+v"(qoff));
+  const char* qrow = (const char*)qk_lds + qoff;
   float4_t spk[NG];
   if constexpr (PK == 1) {
 #pragma unroll
@@ -265,7 +274,7 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
       for (int mm = 0; mm < KM; mm += 2)
         spk[gi] = mfma32(cat8(operand4<BITS>(b.kw[0], gi * (GS / 4) + 4 * mm),
                               operand4<BITS>(b.kw[0], gi * (GS / 4) + 4 * mm + 4)),
-                         cat8(qB[gi * KM + mm], qB[gi * KM + mm + 1]), spk[gi]);
+                         *(const half8_t*)(qrow + ((gi * KM + mm) / 2) * 1024), spk[gi]);
     }
   } else {
 #pragma unroll
@@ -277,7 +286,7 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
         for (int mm = 0; mm < KM; mm++)
           spk[gi] = mfma32(cat8(operand4<BITS>(b.kw[2 * p], gi * (GS / 4) + 4 * mm),
                                 operand4<BITS>(b.kw[2 * p + 1], gi * (GS / 4) + 4 * mm)),
-                           qK[p][gi * KM + mm], spk[gi]);
+                           *(const half8_t*)(qrow + (p * (D / 16) + gi * KM + mm) * 1024), spk[gi]);
     }
   }
   // this lane's block (mask mj) and token quad (lg)
@@ -302,11 +311,12 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
     s2[r] = ((vb >> r) & 1u) ? x * alpha : -INFINITY;
     lmax = fmaxf(lmax, s2[r]);
   }
-  const float bm = head_max<GP>(lmax);
-  // lazy rescale: raise the running max only when a step exceeds it by SLACK
-  const bool grow = bm > st.m2 + SLACK;
-  if (__builtin_amdgcn_ballot_w64(grow)) {
-    if (grow) {
+  // lazy rescale: raise the running max only when a step exceeds it by
+  // SLACK.  A head's running max is held by all its lanes, so a lane's own
+  // values decide whether any head grows; the head-wide max is only formed then.
+  if (__builtin_amdgcn_ballot_w64(lmax > st.m2 + SLACK)) {
+    const float bm = head_max<GP>(lmax);
+    if (bm > st.m2 + SLACK) {
       if (st.m2 == -INFINITY) {
         st.Z = 0.f; st.S2 = 0.f;
       } else {
@@ -329,12 +339,13 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
     st.Z += p[r];
     st.S2 = fmaf(p[r], fmaxf(t, -200.f), st.S2);
   }
-  // top-8: only values above the head-wide 8th-best bound can enter
-  const float thr = head_max<GP>(st.top[TOPK - 1]);
-  if (__builtin_amdgcn_ballot_w64(lmax > thr)) {
+  // top-8: only values above the head-wide 8th-best bound can enter (the
+  // bound changes only when values enter, so it is formed only then)
+  if (__builtin_amdgcn_ballot_w64(lmax > st.thr)) {
 #pragma unroll
     for (int r = 0; r < 4; r++)
-      if (s2[r] > thr) topk_insert(st.top, s2[r]);
+      if (s2[r] > st.thr) topk_insert(st.top, s2[r]);
+    st.thr = head_max<GP>(st.top[TOPK - 1]);
   }
   // P' = p sV per group as fp16 hi + lo (packed layout), and the zero-point
   // term.  A masked token has p = 0 and finite metadata: pools are cleared
@@ -397,50 +408,57 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
 // Load step sigma of class C into a register buffer: lane l takes chunk l
 // of the K and V codes of each of the PK blocks, the metadata of its own
 // block's token quad and, with a window, its tokens' positions.  A last,
-// partial step repeats a live block (its mask is read as 0).  ls is the lane
-// whose addresses are used: the lane itself, or 0 in every lane for a padding
-// load (the same instructions, but one cache line that is already loaded).
+// partial step repeats a live block (its mask is read as 0).  The codes are
+// read through a buffer resource per block record (base address in scalar
+// registers, the lane's offset a constant), so no per-lane address arithmetic
+// is spent on them; a padding step past the wave's last one gives its records
+// zero length, and its code loads then return zeros without touching memory.
+// The metadata and positions of a padding step are read from the first line
+// of the repeated block in every lane (one cached line).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kRawBufferWord3 = 0x00020000;     // gfx9 raw buffer: 32-bit elements, no swizzle
 template <int D, int GS, bool WINDOW, int PK, int C>
-__device__ inline void load_step(Buf<D, GS, WINDOW, PK>& b, const uint8_t* pool_c, const int32_t* slot_c, int Hkv,
-                                 const int2* lv, int n, int sigma, int kvh, int lane, int ls) {
+__device__ inline void load_step(Buf<D, GS, WINDOW, PK>& b, const uint8_t* pool_kvh, int64_t stride,
+                                 const int32_t* slot_c, const int2* lv, int n, int sigma, int lane, bool pad) {
   constexpr int BITS = C == 0 ? 8 : (C == 1 ? 4 : 2);
   constexpr int NG = D / GS, CB = D * BITS / 32, CW = CB / 4, R = 128 * CB + 128 * NG, GP = 16 / PK;
-  const int lg = ls >> 4, jl = (lane & 15) / GP;
+  const int lg = lane >> 4, jl = (lane & 15) / GP;
   int ids[PK];
 #pragma unroll
   for (int j = 0; j < PK; j++) {
     const int e = sigma * PK + j;
     ids[j] = __builtin_amdgcn_readfirstlane(lv[e < n ? e : n - 1].x);
   }
-  int idj = ids[0];                                 // this lane's block
-#pragma unroll
-  for (int j = 1; j < PK; j++) idj = jl == j ? ids[j] : idj;
-  const uint8_t* base = pool_c + (int64_t)kvh * R;
-  const int64_t stride = (int64_t)Hkv * R;
 #pragma unroll
   for (int j = 0; j < PK; j++) {
-    const uint8_t* rec = base + (int64_t)ids[j] * stride;
-    const uint8_t* kp = rec + ls * CB;
-    const uint8_t* vp = rec + 64 * CB + ls * CB;
+    const uint8_t* rec = pool_kvh + (int64_t)ids[j] * stride;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, pad ? 0 : R, kRawBufferWord3);
     if constexpr (CW % 4 == 0) {
       // 16-byte unit i of chunk l sits at byte (64 i + l) 16 of the region
 #pragma unroll
       for (int i = 0; i < CW / 4; i++) {
-        const uint4 x = *(const uint4*)(rec + (64 * i + ls) * 16);
-        const uint4 y = *(const uint4*)(rec + 64 * CB + (64 * i + ls) * 16);
-        b.kw[j][4 * i] = x.x; b.kw[j][4 * i + 1] = x.y; b.kw[j][4 * i + 2] = x.z; b.kw[j][4 * i + 3] = x.w;
-        b.vw[j][4 * i] = y.x; b.vw[j][4 * i + 1] = y.y; b.vw[j][4 * i + 2] = y.z; b.vw[j][4 * i + 3] = y.w;
+        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + 1024 * i, 0, 0);
+        const u32x4_t y = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + 1024 * i + 64 * CB, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; e++) { b.kw[j][4 * i + e] = x[e]; b.vw[j][4 * i + e] = y[e]; }
       }
     } else if constexpr (CW == 2) {
-      const uint2 x = *(const uint2*)kp, y = *(const uint2*)vp;
-      b.kw[j][0] = x.x; b.kw[j][1] = x.y; b.vw[j][0] = y.x; b.vw[j][1] = y.y;
+      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * 8, 0, 0);
+      const u32x2_t y = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * 8 + 64 * CB, 0, 0);
+      b.kw[j][0] = x[0]; b.kw[j][1] = x[1]; b.vw[j][0] = y[0]; b.vw[j][1] = y[1];
     } else {
-      b.kw[j][0] = *(const uint32_t*)kp; b.vw[j][0] = *(const uint32_t*)vp;
+      b.kw[j][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, 0);
+      b.vw[j][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4 + 64 * CB, 0, 0);
     }
   }
-  const uint8_t* rj = base + (int64_t)idj * stride + 128 * CB;
-  const uint4* mkp = (const uint4*)(rj + lg * 16 * NG);
-  const uint4* mvp = (const uint4*)(rj + 64 * NG + lg * 16 * NG);
+  int idj = ids[0];                                 // this lane's block
+#pragma unroll
+  for (int j = 1; j < PK; j++) idj = (jl == j && !pad) ? ids[j] : idj;
+  const int lq = pad ? 0 : lg;
+  const uint8_t* rj = pool_kvh + (int64_t)idj * stride + 128 * CB;
+  const uint4* mkp = (const uint4*)(rj + lq * 16 * NG);
+  const uint4* mvp = (const uint4*)(rj + 64 * NG + lq * 16 * NG);
 #pragma unroll
   for (int i = 0; i < NG; i++) {
     const uint4 x = mkp[i], y = mvp[i];
@@ -448,7 +466,7 @@ __device__ inline void load_step(Buf<D, GS, WINDOW, PK>& b, const uint8_t* pool_
     b.mv[4 * i] = y.x; b.mv[4 * i + 1] = y.y; b.mv[4 * i + 2] = y.z; b.mv[4 * i + 3] = y.w;
   }
   if constexpr (WINDOW) {
-    const int4* pr = (const int4*)(slot_c + ((int64_t)idj * TKV_BS + 4 * lg) * 2);
+    const int4* pr = (const int4*)(slot_c + ((int64_t)idj * TKV_BS + 4 * lq) * 2);
     const int4 x = pr[0], y = pr[1];
     b.pos[0] = x.x; b.pos[1] = x.z; b.pos[2] = y.x; b.pos[3] = y.z;
   }
@@ -458,18 +476,21 @@ __device__ inline void load_step(Buf<D, GS, WINDOW, PK>& b, const uint8_t* pool_
 // class (compacted: id, mask), PK per step, steps dealt round-robin to the nw
 // waves.  Two register buffers alternate: the next step's loads are in flight
 // while the current step is computed, also across a class boundary.  Past the
-// last step a wave issues the same load instructions with every lane on the
-// first line of the last step (one cached line), so every path issues the
-// same loads, the compiler's waits stay exact, and the padding is cheap.
+// last step a wave issues the same load instructions (code loads of
+// zero-length records, metadata from one cached line), so every path issues
+// the same loads, the compiler's waits stay exact, and the padding is cheap.
 template <int D, int GS, bool WINDOW, int PK>
 __device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax, const int* nl, int kvh, int lo_pos,
                                  int lane, int w, int nw, bool head_ok, const half4_t (&qB)[D / 16],
-                                 const half8_t (&qK)[PK > 1 ? PK / 2 : 1][D / 16], const float (&sumq)[D / GS],
+                                 const half8_t* qk_lds, const float (&sumq)[D / GS],
                                  float alpha, AttnState<D, GS>& st) {
   typedef Buf<D, GS, WINDOW, PK> B;
   constexpr int GP = 16 / PK;
   const int jl = (lane & 15) / GP;
-  const int n0 = nl[0], n1 = nl[1], n2 = nl[2];
+  // wave-uniform (read from LDS, so the compiler cannot tell): the step
+  // index, the class branches and the block addresses stay scalar
+  const int n0 = __builtin_amdgcn_readfirstlane(nl[0]), n1 = __builtin_amdgcn_readfirstlane(nl[1]),
+            n2 = __builtin_amdgcn_readfirstlane(nl[2]);
   const int c1 = (n0 + PK - 1) / PK, c2 = c1 + (n1 + PK - 1) / PK, T = c2 + (n2 + PK - 1) / PK;
   const int2* l0 = live;
   const int2* l1 = live + lmax;
@@ -482,13 +503,17 @@ __device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax
   const int32_t* slt0 = P.S.slot[0];
   const int32_t* slt1 = P.S.slot[1];
   const int32_t* slt2 = P.S.slot[2];
-  const int Hkv = P.S.Hkv;
+  const int64_t Hkv = P.S.Hkv;
+  const int64_t R0 = P.S.bh_bytes[0], R1 = P.S.bh_bytes[1], R2 = P.S.bh_bytes[2];
+  const uint8_t* pk0 = pool0 + kvh * R0;
+  const uint8_t* pk1 = pool1 + kvh * R1;
+  const uint8_t* pk2 = pool2 + kvh * R2;
   auto load = [&](B& b, int g) {
-    const int ls = g < T ? lane : 0;
-    g = g < T ? g : T - 1;
-    if (g < c1) load_step<D, GS, WINDOW, PK, 0>(b, pool0, slt0, Hkv, l0, n0, g, kvh, lane, ls);
-    else if (g < c2) load_step<D, GS, WINDOW, PK, 1>(b, pool1, slt1, Hkv, l1, n1, g - c1, kvh, lane, ls);
-    else load_step<D, GS, WINDOW, PK, 2>(b, pool2, slt2, Hkv, l2, n2, g - c2, kvh, lane, ls);
+    const bool pad = g >= T;
+    g = pad ? T - 1 : g;
+    if (g < c1) load_step<D, GS, WINDOW, PK, 0>(b, pk0, Hkv * R0, slt0, l0, n0, g, lane, pad);
+    else if (g < c2) load_step<D, GS, WINDOW, PK, 1>(b, pk1, Hkv * R1, slt1, l1, n1, g - c1, lane, pad);
+    else load_step<D, GS, WINDOW, PK, 2>(b, pk2, Hkv * R2, slt2, l2, n2, g - c2, lane, pad);
   };
   auto mask_of = [&](const int2* lv, int n, int sigma) -> uint32_t {
     const int e = sigma * PK + jl;                  // this lane's block
@@ -496,29 +521,42 @@ __device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax
   };
   auto comp = [&](const B& b, int g) {
     if (g < c1)
-      compute_step<D, GS, 8, WINDOW, PK>(b, mask_of(l0, n0, g), lo_pos, lane, head_ok, qB, qK, sumq, alpha,
+      compute_step<D, GS, 8, WINDOW, PK>(b, mask_of(l0, n0, g), lo_pos, lane, head_ok, qB, qk_lds, sumq, alpha,
                                           st);
     else if (g < c2)
-      compute_step<D, GS, 4, WINDOW, PK>(b, mask_of(l1, n1, g - c1), lo_pos, lane, head_ok, qB, qK, sumq, alpha,
+      compute_step<D, GS, 4, WINDOW, PK>(b, mask_of(l1, n1, g - c1), lo_pos, lane, head_ok, qB, qk_lds, sumq, alpha,
                                           st);
     else
-      compute_step<D, GS, 2, WINDOW, PK>(b, mask_of(l2, n2, g - c2), lo_pos, lane, head_ok, qB, qK, sumq, alpha,
+      compute_step<D, GS, 2, WINDOW, PK>(b, mask_of(l2, n2, g - c2), lo_pos, lane, head_ok, qB, qk_lds, sumq, alpha,
                                           st);
   };
   int g = w;
   if (g >= T) return;
+  // The two waves of a SIMD compete for issue and the arbiter favours the
+  // older one; a wave lowers its priority as it advances through its steps,
+  // so the one behind is favoured and the pair ends closer together.
+  const int Tw = (T - w + nw - 1) / nw;          // this wave's steps
+  int k = 0;
+  auto set_priority = [&]() {
+    const int lv = 3 - (4 * k) / Tw;
+    if (lv >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (lv == 2) __builtin_amdgcn_s_setprio(2);
+    else if (lv == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  };
   B A, Bn;
   load(A, g);
   while (true) {
     load(Bn, g + nw);
-    comp(A, g);
+    set_priority(); comp(A, g); k++;
     g += nw;
     if (g >= T) break;
     load(A, g + nw);
-    comp(Bn, g);
+    set_priority(); comp(Bn, g); k++;
     g += nw;
     if (g >= T) break;
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // ---------------------------------------------------------------------------
@@ -659,7 +697,8 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   __shared__ int s_nlive[3];
   const DevState& S = P.S;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  // the wave index is uniform across its lanes: say so to the compiler
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nw = blockDim.x >> 6;
   const int lg = lane >> 4, h = lane & 15;
   const int G = S.Hq / S.Hkv;
   const bool col_ok = h < G;                     // MFMA column h is a real head
@@ -687,6 +726,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   st.m2 = -INFINITY; st.Z = 0.f; st.S2 = 0.f; st.natt = 0;
 #pragma unroll
   for (int i = 0; i < TOPK; i++) st.top[i] = -INFINITY;
+  st.thr = -INFINITY;
   // The split's live blocks of each class, into LDS, in list order: wave c
   // (the waves in turn when there are fewer than three) takes class c's
   // block-table entries 64 at a time, reads their block records and keeps,
@@ -764,18 +804,26 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
     }
     sumq[gi] = pair_sum<32>(pair_sum<16>(sq)) * kCodeUnit;
   }
-  // K-side operands for packed blocks: pair p keeps the lane's query in the
-  // half of the k slice that holds its own block (2p or 2p+1)
-  half8_t qK[PK > 1 ? PK / 2 : 1][NG * KM];
-  if constexpr (PK > 1) {
-    const int jq = (lane & 15) / GP;
+  // K-side query operands in LDS, identical in every wave (wave 0 stores
+  // them), [k slice][lane].  One block per step: 16 dims per k slice.  Packed
+  // blocks: pair p keeps the lane's query in the half of the k slice that
+  // holds its own block (2p or 2p+1), [pair][16 dims][lane].
+  __shared__ half8_t s_qk[(PK > 1 ? PK / 2 : 1) * NT * 64];
+  if (w == 0) {
+    if constexpr (PK == 1) {
 #pragma unroll
-    for (int p2 = 0; p2 < PK / 2; p2++)
+      for (int i = 0; i < NT; i += 2) s_qk[(i / 2) * 64 + lane] = cat8(qB[i], qB[i + 1]);
+    } else {
+      const int jq = (lane & 15) / GP;
 #pragma unroll
-      for (int i = 0; i < NG * KM; i++) qK[p2][i] = cat8(keep4(qB[i], jq == 2 * p2), keep4(qB[i], jq == 2 * p2 + 1));
+      for (int p2 = 0; p2 < PK / 2; p2++)
+#pragma unroll
+        for (int i = 0; i < NT; i++)
+          s_qk[(p2 * NT + i) * 64 + lane] = cat8(keep4(qB[i], jq == 2 * p2), keep4(qB[i], jq == 2 * p2 + 1));
+    }
   }
   __syncthreads();
-  run_steps<D, GS, WINDOW, PK>(P, live, lmax, nlive, kvh, lo_pos, lane, w, nw, head_ok, qB, qK, sumq,
+  run_steps<D, GS, WINDOW, PK>(P, live, lmax, nlive, kvh, lo_pos, lane, w, nw, head_ok, qB, s_qk, sumq,
                                alpha * kCodeScale, st);
   // The self token of this wave's first head (finalized here with one split):
   // its reads are issued now, so that their latency overlaps the reductions
@@ -900,7 +948,7 @@ static int lds_bytes(const tkv_cache* c, int nw) {
   const int D = c->S.D, G = c->S.Hq / c->S.Hkv;
   return nw * G * (D + PART_X) * (int)sizeof(float);
 }
-static const int kStaticLds = 3 * TKV_MAX_BLOCKS * 8 + 16;      // live lists and counts
+static const int kStaticLds = 3 * TKV_MAX_BLOCKS * 8 + 16 + 8192;   // live lists and counts, query operands
 
 void attn_plan(const tkv_cache* c, int batch, int num_splits, int* nw_out, int* splits_out) {
   const int units = batch * c->S.Hkv > 0 ? batch * c->S.Hkv : 1;
