@@ -72,6 +72,8 @@ def lib():
         L.ora_evict.argtypes = [P, P, C.c_int, P, P, P, P]; L.ora_evict.restype = None
         L.ora_plan_budget.argtypes = [P, P, C.c_int, P, C.c_int, C.c_int, C.c_int, P, P, P, P]
         L.ora_plan_budget.restype = C.c_int
+        L.ora_plan_anneal.argtypes = [P, P, C.c_int, P, C.c_int, C.c_int, P, P, P, P]
+        L.ora_plan_anneal.restype = C.c_int
         L.ora_seq_reset.argtypes = [P, P, C.c_int, P]; L.ora_seq_reset.restype = None
         L.ora_attention.argtypes = [P, P, C.c_int, P, P, P, P, P, P, C.c_int, C.c_int, P, P, P]
         L.ora_attention.restype = None
@@ -199,6 +201,14 @@ class OracleCache:
         ok = np.zeros(max_ops, np.int32); ob = np.zeros(max_ops, np.uint8)
         m = lib().ora_plan_budget(C.byref(self.L._c), C.byref(self._state), seq_ids.size, _p(seq_ids),
                                   int(num), int(den), int(max_ops), _p(os_), _p(og), _p(ok), _p(ob))
+        return os_[:m], og[:m], ok[:m], ob[:m]
+
+    def plan_anneal(self, seq_ids, r0, max_ops):
+        seq_ids = _arr(seq_ids, np.int32)
+        os_ = np.zeros(max_ops, np.int32); og = np.zeros(max_ops, np.int32)
+        ok = np.zeros(max_ops, np.int32); ob = np.zeros(max_ops, np.uint8)
+        m = lib().ora_plan_anneal(C.byref(self.L._c), C.byref(self._state), seq_ids.size, _p(seq_ids),
+                                  int(r0), int(max_ops), _p(os_), _p(og), _p(ok), _p(ob))
         return os_[:m], og[:m], ok[:m], ob[:m]
 
     def seq_reset(self, seq_ids):

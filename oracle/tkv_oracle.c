@@ -533,6 +533,45 @@ int ora_plan_budget(const ora_layout *L, ora_state *S, int n, const int32_t *seq
   return m;
 }
 
+/* ---------------------------------------------------------------------- */
+/* Annealing schedule of TBE (Methodology, TBE bullet: once a Transition  */
+/* thought is detected, tokens of the earlier, less critical Reasoning or  */
+/* Execution segments are evicted progressively on an annealing schedule   */
+/* of the retention, e.g. 64, then 32, then 16, at segment granularity;    */
+/* lay summary "Astuce B": a small safety net of Transition thoughts is    */
+/* always kept).  Reading: a T event is the opening of a T segment; an R   */
+/* or E segment followed by e >= 1 T segments has retention cap            */
+/* r0 / 2^(e-1) (integer halving, 0 once halved to nothing), and keeps its */
+/* cap newest retained tokens; T segments are never planned.  The cap      */
+/* depends only on the segment table, so planning twice gives no new ops.  */
+/* Ops (s, k, keep_n = cap, bits 0) in list order of the sequences and     */
+/* segment order; at most max_ops are written and counted.                 */
+/* ---------------------------------------------------------------------- */
+int ora_plan_anneal(const ora_layout *L, ora_state *S, int n, const int32_t *seq_ids, int r0, int max_ops,
+                    int32_t *op_seq, int32_t *op_seg, int32_t *op_keep, uint8_t *op_bits) {
+  int m = 0;
+  for (int i = 0; i < n; i++) {
+    int s = seq_ids[i];
+    if (s < 0 || s >= L->max_seqs) continue;
+    int32_t *q = SEQ(L, S, s);
+    int nseg = q[Q_NSEG];
+    for (int k = 0; k < nseg; k++) {
+      int32_t *g = SEGR(L, S, s, k);
+      if (g[G_TYPE] == 2 || g[G_NRET] == 0) continue;
+      int events = 0;                       /* T segments opened after segment k */
+      for (int j = k + 1; j < nseg; j++)
+        if (SEGR(L, S, s, j)[G_TYPE] == 2) events++;
+      if (events == 0) continue;
+      int cap = r0;
+      for (int e = 1; e < events && cap > 0; e++) cap /= 2;
+      if (g[G_NRET] > cap && m < max_ops) {
+        op_seq[m] = s; op_seg[m] = k; op_keep[m] = cap; op_bits[m] = 0; m++;
+      }
+    }
+  }
+  return m;
+}
+
 /* Return the sequences' blocks to the global stacks (list order, classes
    in order, blocks in block-list order) and clear their records. */
 void ora_seq_reset(const ora_layout *L, ora_state *S, int n, const int32_t *seq_ids) {

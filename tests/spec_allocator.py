@@ -153,6 +153,25 @@ class Spec:
                     self.free[c].insert(0, blk)
             del self.seqs[s]
 
+    def anneal(self, seq_list, r0, max_ops):
+        """TBE annealing: walking a sequence's segments from the newest back,
+        every T segment passed is one more event for the older segments; an R
+        or E segment seen after e >= 1 events keeps r0 // 2**(e-1) tokens."""
+        ops = []
+        for s in seq_list:
+            if not (0 <= s < self.max_seqs):
+                continue
+            segs = self._seq(s)["segs"]
+            found, events = [], 0
+            for k in reversed(range(len(segs))):
+                g = segs[k]
+                if g["type"] == 2:
+                    events += 1
+                elif events and g["nret"] > r0 // 2 ** (events - 1):
+                    found.append((s, k, r0 // 2 ** (events - 1), 0))
+            ops.extend(reversed(found))
+        return ops[:max_ops]
+
     def plan(self, seq_list, num, den, max_ops):
         ops = []
         for s in seq_list:

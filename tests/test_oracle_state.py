@@ -170,6 +170,15 @@ def run_program(prog, pools, max_seqs, max_blocks, max_segs, order, seed):
             if want:
                 oc.evict(*[list(x) for x in zip(*want)])
                 sp.evict(want)
+        elif kind == "N":
+            seqs, r0 = step[1], step[2]
+            got = oc.plan_anneal(seqs, r0, 16)
+            want = sp.anneal(seqs, r0, 16)
+            assert list(zip(*[a.tolist() for a in got])) == want
+            if want:
+                oc.evict(*[list(x) for x in zip(*want)])
+                sp.evict(want)
+            assert not len(oc.plan_anneal(seqs, r0, 16)[0]) or len(want) == 16, "planning again gives no ops"
         else:
             oc.seq_reset(step[1]); sp.reset(step[1])
         compare(oc, sp)
@@ -186,6 +195,69 @@ def test_brute_force_against_spec(seed):
     for rep in range(12):
         prog = random_program(rng, 2, 8)
         run_program(prog, pools, 2, 2, 5, order, seed * 100 + rep)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_anneal_brute_force_against_spec(seed):
+    """Random programs with annealing plans (applied at once) inserted."""
+    rng = np.random.default_rng(1000 + seed)
+    pools = (3, 3, 2) if seed % 2 else (2, 3, 3)
+    for rep in range(10):
+        prog = random_program(rng, 2, 8)
+        for _ in range(3):
+            at = int(rng.integers(0, len(prog) + 1))
+            r0 = int(rng.choice([0, 1, 2, 3, 4, 5, 64]))
+            prog.insert(at, ("N", [int(s) for s in rng.permutation(2)], r0))
+        run_program(prog, pools, 2, 2, 6, None, seed * 100 + rep)
+
+
+def anneal_cache(types_and_lengths, pools=(8, 8, 8)):
+    L = oracle.OracleLayout(1, 1, 64, 32, pools, 1, 16, 32)
+    oc = oracle.OracleCache(L)
+    types = [t for t, n in types_and_lengths for _ in range(n)]
+    kv = np.zeros((len(types), 1, 64), np.float32)
+    oc.append([0] * len(types), range(len(types)), types, kv, kv)
+    assert oc.error()[0] == 0
+    return oc
+
+
+def test_anneal_hand_example():
+    """Segments R100 E50 T5 R80 T3 E40(open), r0 = 64.  Segments 0 and 1 have
+    seen two T segments open after them: cap 64/2 = 32, so they keep 32; segment
+    3 has seen one: cap 64, keeps 64 of 80; T segments and the open E segment
+    (no T after it) get nothing."""
+    oc = anneal_cache([(0, 100), (1, 50), (2, 5), (0, 80), (2, 3), (1, 40)], pools=(16, 16, 8))
+    ops = oc.plan_anneal([0], 64, 8)
+    assert list(zip(*[a.tolist() for a in ops])) == [(0, 0, 32, 0), (0, 1, 32, 0), (0, 3, 64, 0)]
+    oc.evict(*ops)
+    assert [int(x) for x in oc.segments(0)[:, 5]] == [32, 32, 5, 64, 3, 40]
+    assert oc.seq_record(0)[8] == 32 + 32 + 5 + 64 + 3 + 40
+    assert len(oc.plan_anneal([0], 64, 8)[0]) == 0          # idempotent
+
+
+def test_anneal_schedule_matches_pages_example():
+    """tests/golden/anneal_schedule.txt: the retention after the e-th
+    Transition event, starting from the pages' 64 -> 32 -> 16 and halving on.
+    One R segment of 100 tokens, then e T segments separated by 1-token E
+    segments; after each event the plan trims the R segment to the schedule."""
+    rows = [tuple(int(x) for x in ln.split()) for ln in open(__file__.rsplit("/", 1)[0] + "/golden/anneal_schedule.txt")
+            if ln.strip() and not ln.startswith("#")]
+    segs = [(0, 100)]
+    oc = anneal_cache(segs, pools=(8, 8, 8))
+    pos = 100
+    kv = np.zeros((1, 1, 64), np.float32)
+    for events, cap in rows:
+        oc.append([0], [pos], [2], kv, kv); pos += 1         # a T segment opens: one more event
+        oc.append([0], [pos], [1], kv, kv); pos += 1         # and closes
+        ops = oc.plan_anneal([0], 64, 8)
+        nret = int(oc.segments(0)[0, 5])
+        if nret > cap:
+            assert list(zip(*[a.tolist() for a in ops])) == [(0, 0, cap, 0)], (events, cap)
+            oc.evict(*ops)
+        else:
+            assert len(ops[0]) == 0
+        assert int(oc.segments(0)[0, 5]) == min(100, cap), (events, cap)
+    assert int(oc.segments(0)[0, 5]) == 0
 
 
 def test_pool_exhaustion_leaves_failed_sequence_untouched():
