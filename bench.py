@@ -3,7 +3,10 @@
 One step = one pass of the whole path over one batch: paged decode attention
 over the mixed-precision, hole-bearing cache (with the staged self token) ->
 thought_classify -> kv_append_quant of the new token at its label's precision
--> kv_plan_budget (token budget ladder) -> kv_evict_segment.  Workload: the
+-> kv_plan_budget (token budget ladder) -> kv_evict_segment.  With
+--policy anneal the ladder is replaced by kv_plan_anneal (the TBE annealing
+schedule of the retention, r0 = 64 by default), applied to the built state
+until it plans nothing before anything is timed.  Workload: the
 Llama-8B-like reasoning-decode layer (B32, Hq32/Hkv8, D128, g64, 16k generated
 tokens per sequence, 10% budget -> 1638 retained, R/E/T 8/4/2-bit) with
 planted-temperature queries, synthetic data.
@@ -130,10 +133,11 @@ def measured_traffic():
     return float(j["traffic_bytes_per_launch"]) if h.hexdigest() == j["source_sha256"] else None
 
 
-def cpu_baseline(w, state, ch, n_seq, budget_s=12.0, max_reps=1000):
+def cpu_baseline(w, state, ch, n_seq, budget_s=12.0, max_reps=1000, policy="ladder", r0=64):
     """The oracle as it stands, on a sample of n_seq sequences of the same
     workload: one full step (attention with the self token, classify, append,
-    ladder, evict) per repetition, on all host cores the process may use."""
+    ladder or annealing plan, evict) per repetition, on all host cores the
+    process may use."""
     import oracle
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import helpers
@@ -151,7 +155,10 @@ def cpu_baseline(w, state, ch, n_seq, budget_s=12.0, max_reps=1000):
         out, st, na = oc.attention(sel, p, q[:n_seq], k_self=k[:n_seq], v_self=v[:n_seq])
         lab = oracle.classify(st.astype(np.float32), *ch.tau)
         oc.append(sel, p, lab, k[:n_seq], v[:n_seq])
-        ops = oc.plan_budget(sel, ch.budget[0], ch.budget[1], 256)
+        if policy == "anneal":
+            ops = oc.plan_anneal(sel, r0, 256)
+        else:
+            ops = oc.plan_budget(sel, ch.budget[0], ch.budget[1], 256)
         if ops[0].size:
             oc.evict(*ops)
         tokens += int(na.sum())
@@ -161,7 +168,7 @@ def cpu_baseline(w, state, ch, n_seq, budget_s=12.0, max_reps=1000):
     dt = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     return {"value": tokens / dt, "unit": "KV tokens/s", "cores": min(threads, cores), "kind": "oracle",
-            "sample": f"{reps} full steps (attention+classify+append+ladder+evict) on {n_seq} of "
+            "sample": f"{reps} full steps (attention+classify+append+{policy}+evict) on {n_seq} of "
                       f"{w.seq_ids.size} sequences of the same cache, fp64 attention, {dt:.1f} s"}
 
 
@@ -172,6 +179,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=6)
     ap.add_argument("--copies", type=int, default=0, help="state copies (0 = enough for > 1 GiB)")
     ap.add_argument("--cpu-seqs", type=int, default=32)
+    ap.add_argument("--policy", choices=("ladder", "anneal"), default="ladder",
+                    help="eviction planner of the step: the token-budget ladder, or the TBE annealing schedule")
+    ap.add_argument("--r0", type=int, default=64, help="first retention of the annealing schedule")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-only", action="store_true", help="time only the attention call (diagnostic)")
     ap.add_argument("--torch-events", action="store_true", help="time with torch's default events (diagnostic)")
@@ -189,6 +199,7 @@ def main():
     from thought_adaptive_mixed_amd import binding, synth
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import helpers
+    dv0 = lambda a: helpers.dev(a, np.int32)
 
     total_steps = args.warmup + args.steps
     log("[bench] building workload")
@@ -203,6 +214,18 @@ def main():
     log(f"[bench] state {state_bytes / 1e6:.1f} MB, {R} copies")
     c0 = helpers.build_gpu(w)
     torch.cuda.synchronize()
+    if args.policy == "anneal":
+        # the built state has never been annealed: apply the schedule until it plans nothing
+        m_all = L.max_tokens_per_call
+        t_ops = [torch.zeros(m_all, dtype=torch.int32, device="cuda") for _ in range(3)]
+        t_bits = torch.zeros(m_all, dtype=torch.uint8, device="cuda")
+        t_n = torch.zeros(1, dtype=torch.int32, device="cuda")
+        for _ in range(1000):
+            c0.plan_anneal(dv0(w.seq_ids), args.r0, m_all, t_n, *t_ops, t_bits)
+            c0.evict(*t_ops, t_bits, n_ops_dev=t_n, n_ops=m_all)
+            if int(t_n.item()) == 0:
+                break
+        torch.cuda.synchronize()
     state = c0.export()
     caches = [c0] + [binding.Cache(helpers.gpu_layout(L), w.block_order) for _ in range(R - 1)]
     for c in caches[1:]:
@@ -214,11 +237,15 @@ def main():
     # inputs for every step, resident on the device
     dv = helpers.dev
     seq_d = dv(w.seq_ids, np.int32)
-    steps_in = []
-    for s in range(total_steps):
-        q, k, v, pos = ch.step_inputs(s)
-        pos = (w.q_pos + s // R).astype(np.int32)       # each copy advances one position per step it serves
-        steps_in.append((dv(q, np.uint16), dv(k, np.float32), dv(v, np.float32), dv(pos, np.int32)))
+    # Step s runs on copy s % R, and it is that copy's (s // R)-th decode step:
+    # each copy replays the same decode sequence (positions, planted thought
+    # types, new tokens), so every copy sees the planted segment process as
+    # one cache would, not every R-th step of it.
+    per_copy = []
+    for i in range((total_steps + R - 1) // R):
+        q, k, v, pos = ch.step_inputs(i)
+        per_copy.append((dv(q, np.uint16), dv(k, np.float32), dv(v, np.float32), dv(pos, np.int32)))
+    steps_in = [per_copy[s // R] for s in range(total_steps)]
     Hq, D = L.num_q_heads, L.head_dim
     out = torch.empty(B, Hq, D, dtype=torch.float32, device="cuda")
     stats = torch.empty(B, Hq, 3, dtype=torch.float32, device="cuda")
@@ -243,8 +270,10 @@ def main():
         calls_b.append([
             binding.classify(stats, ch.tau[0], ch.tau[1], labels, stream=sh, prepare=True),
             c.append(seq_d, pos, labels, k, v, stream=sh, prepare=True),
-            c.plan_budget(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, o_seq, o_seg, o_keep, o_bits,
-                          stream=sh, prepare=True),
+            (c.plan_anneal(seq_d, args.r0, max_ops, n_ops, o_seq, o_seg, o_keep, o_bits, stream=sh, prepare=True)
+             if args.policy == "anneal" else
+             c.plan_budget(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, o_seq, o_seg, o_keep, o_bits,
+                           stream=sh, prepare=True)),
             c.evict(o_seq, o_seg, o_keep, o_bits, n_ops_dev=n_ops, n_ops=max_ops, stream=sh, prepare=True),
         ])
 
@@ -311,8 +340,12 @@ def main():
         "dtype": "f16 MFMA (int8/4/2 codes as exact fp16 subnormals), f32 accumulate",
         "data": "synthetic",
         "config": {"workload": "llama8b-like reasoning decode, one layer: B32, Hq32/Hkv8, D128, g64, "
-                               "16k generated tokens/seq, 10% budget (1638 retained), R/E/T 8/4/2-bit, "
-                               "planted-temperature queries; step = attention+classify+append+ladder+evict",
+                               + ("16k generated tokens/seq, 10% budget (1638 retained), R/E/T 8/4/2-bit, "
+                                  "planted-temperature queries; step = attention+classify+append+ladder+evict"
+                                  if args.policy == "ladder" else
+                                  f"16k generated tokens/seq, R/E/T 8/4/2-bit, TBE annealing schedule "
+                                  f"(r0 {args.r0}) applied to the built state, planted-temperature queries; "
+                                  f"step = attention+classify+append+anneal+evict"),
                    "batch": B, "copies": R, "attended_per_step": tokens / args.steps,
                    "launch": "eager, one stream"},
         "attn_ms": attn_avg,
@@ -324,7 +357,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(w, state, ch, args.cpu_seqs)
+        result["cpu_baseline"] = cpu_baseline(w, state, ch, args.cpu_seqs, policy=args.policy, r0=args.r0)
     print(json.dumps(result), flush=True)
 
 

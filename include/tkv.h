@@ -154,7 +154,8 @@ int kv_append_quant(tkv_cache* c, int32_t n, const int32_t* seq_ids, const int32
  *   frees the old slots.  new_bits 0 keeps the precision.
  *   A segment may appear in one op per call.  Arrays have n_ops entries; when
  *   n_ops_dev (device i32, nullable) is given, only its first *n_ops_dev <=
- *   n_ops ops are applied (for op lists written by kv_plan_budget).
+ *   n_ops ops are applied (for op lists written by kv_plan_budget or
+ *   kv_plan_anneal).
  *   Device errors: ENOSEG (unknown or fully evicted segment), EINVAL (bad
  *   keep_n/new_bits, repeated segment), ENOMEM (no room for the downgrade). */
 int kv_evict_segment(tkv_cache* c, int32_t n_ops, const int32_t* n_ops_dev, const int32_t* seq_ids,
@@ -173,6 +174,27 @@ int kv_evict_segment(tkv_cache* c, int32_t n_ops, const int32_t* n_ops_dev, cons
 int kv_plan_budget(tkv_cache* c, int32_t n, const int32_t* seq_ids, int32_t budget_num,
                    int32_t budget_den, int32_t max_ops, int32_t* n_ops_dev, int32_t* op_seq,
                    int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t stream);
+
+/* kv_plan_anneal -- the annealing schedule of TBE (TBE bullet: once a
+ * Transition thought is detected, the earlier Reasoning/Execution segments are
+ * evicted progressively, the retention shrinking on a schedule such as 64, 32,
+ * 16; segment granularity; the lay summary's "Astuce B" keeps a small safety
+ * net of Transition thoughts).  For each listed sequence (ids outside
+ * [0, max_seqs) are skipped) and each of its R or E segments with retained
+ * tokens: e = the number of T segments opened after it; when e >= 1 its cap
+ * is r0 halved e-1 times (integer halving: 64, 32, 16, ..., 1, 0 for r0 =
+ * 64), and a segment holding more retained tokens than its cap gets the op
+ * (seq, segment, keep_n = cap, new_bits = 0).  T segments are never planned.
+ * The plan depends only on the segment tables, so planning again after
+ * applying it gives no ops.  Ops in list order of the sequences, segments in
+ * order; at most max_ops (<= max_tokens_per_call) are written to op_*
+ * (device arrays of max_ops entries) and their count to *n_ops_dev; feed them
+ * to kv_evict_segment with n_ops_dev.  A sequence listed twice is planned
+ * twice (kv_evict_segment then rejects the repeated segments).
+ *   EINVAL: n or max_ops out of range, r0 < 0, or a required pointer is NULL. */
+int kv_plan_anneal(tkv_cache* c, int32_t n, const int32_t* seq_ids, int32_t r0, int32_t max_ops,
+                   int32_t* n_ops_dev, int32_t* op_seq, int32_t* op_seg, int32_t* op_keep,
+                   uint8_t* op_bits, hipStream_t stream);
 
 /* paged_decode_attn -- one decode step of attention over the mixed-precision,
  * hole-bearing cache (abstract: a kernel extending PagedAttention that reuses

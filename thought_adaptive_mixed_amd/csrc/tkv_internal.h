@@ -228,6 +228,8 @@ int launch_evict(tkv_cache* c, int n_ops, const int32_t* n_ops_dev, const int32_
                  const int32_t* keep_n, const uint8_t* new_bits, hipStream_t st);
 int launch_plan(tkv_cache* c, int n, const int32_t* seq_ids, int num, int den, int max_ops, int32_t* n_ops_dev,
                 int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st);
+int launch_anneal(tkv_cache* c, int n, const int32_t* seq_ids, int r0, int max_ops, int32_t* n_ops_dev,
+                  int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st);
 int launch_seq_reset(tkv_cache* c, int n, const int32_t* seq_ids, hipStream_t st);
 int launch_classify(int batch, int Hq, const float* stats, float tau_T, float tau_E, int kind, uint8_t* labels,
                     hipStream_t st);

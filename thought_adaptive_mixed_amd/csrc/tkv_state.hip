@@ -1119,6 +1119,92 @@ int launch_plan(tkv_cache* c, int n, const int32_t* seq_ids, int num, int den, i
 }
 
 // ---------------------------------------------------------------------------
+// Annealing schedule of TBE (Methodologie, TBE bullet: on a Transition thought
+// the earlier Reasoning/Execution segments are evicted progressively, the
+// retention shrinking on a schedule such as 64, 32, 16; the lay summary keeps
+// a small safety net of Transition thoughts).  An R or E segment with e >= 1
+// T segments opened after it is capped at r0 halved e-1 times and keeps its
+// cap newest retained tokens; T segments are never planned.  One wave per
+// listed sequence walks its segment table 64 records at a time: a ballot over
+// the T records gives the total, a running prefix of it gives each record's
+// count of later T segments, and a ballot over the over-cap records places
+// the ops in segment order.  A first walk counts each sequence's ops, a scan
+// over the list places them, a second walk writes them.
+// ---------------------------------------------------------------------------
+__device__ int anneal_wave(const DevState& S, int s, int r0, int base, int max_ops, int32_t* os, int32_t* og,
+                           int32_t* ok, uint8_t* ob, bool write, int lane) {
+  if (s < 0 || s >= S.max_seqs) return 0;
+  const int32_t* q = S.seq + (int64_t)s * TKV_SEQ_W;
+  const int nseg = __builtin_amdgcn_readfirstlane(q[Q_NSEG]);
+  const int32_t* segs = S.segt + (int64_t)s * S.max_segs * TKV_SEG_W;
+  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  int total_t = 0;
+  for (int b0 = 0; b0 < nseg; b0 += 64) {
+    const int k = b0 + lane;
+    const bool t = k < nseg && segs[(int64_t)k * TKV_SEG_W + G_TYPE] == TKV_T;
+    total_t += __popcll(__builtin_amdgcn_ballot_w64(t));
+  }
+  if (total_t == 0) return 0;
+  int m = 0, seen_t = 0;                          // T segments in earlier chunks
+  for (int b0 = 0; b0 < nseg; b0 += 64) {
+    const int k = b0 + lane;
+    int type = TKV_T, nret = 0;
+    if (k < nseg) {
+      const int32_t* g = segs + (int64_t)k * TKV_SEG_W;
+      type = g[G_TYPE];
+      nret = g[G_NRET];
+    }
+    const uint64_t tb = __builtin_amdgcn_ballot_w64(k < nseg && type == TKV_T);
+    const int later = total_t - seen_t - __popcll(tb & (lt | (1ull << lane)));  // T segments after k
+    const int sh = later - 1 < 31 ? later - 1 : 31;
+    const int cap = later >= 1 ? (r0 >> sh) : 0;
+    const bool take = k < nseg && type != TKV_T && later >= 1 && nret > cap;
+    const uint64_t tm = __builtin_amdgcn_ballot_w64(take);
+    if (take && write) {
+      const int at = base + m + __popcll(tm & lt);
+      if (at < max_ops) { os[at] = s; og[at] = k; ok[at] = cap; ob[at] = 0; }
+    }
+    m += __popcll(tm);
+    seen_t += __popcll(tb);
+  }
+  return m;
+}
+
+__global__ __launch_bounds__(WG) void k_anneal(DevState S, int n, const int32_t* seq_ids, int r0, int max_ops,
+                                               int32_t* n_ops, int32_t* os, int32_t* og, int32_t* ok, uint8_t* ob) {
+  __shared__ int s_cnt[TKV_MAX_TOK];         // ops of each listed sequence
+  __shared__ int s_base[TKV_MAX_TOK];        // their first op's index
+  __shared__ int s_tmp[48];
+  const int tid = threadIdx.x, NT = blockDim.x, wv = tid >> 6, lane = tid & 63, NW = NT >> 6;
+  for (int i = wv; i < n; i += NW) {
+    const int s = __builtin_amdgcn_readfirstlane(seq_ids[i]);
+    const int m = anneal_wave(S, s, r0, 0, 0, os, og, ok, ob, false, lane);
+    if (lane == 0) s_cnt[i] = m;
+  }
+  __syncthreads();
+  const int per = (n + NT - 1) / NT;
+  const int lo = tid * per, hi = min(n, lo + per);
+  int v[3] = {0, 0, 0}, ex[3], tot[3];
+  for (int i = lo; i < hi; i++) v[0] += s_cnt[i];
+  wg_scan3(v, ex, tot, s_tmp);
+  for (int i = lo, run = ex[0]; i < hi; i++) { s_base[i] = run; run += s_cnt[i]; }
+  __syncthreads();
+  for (int i = wv; i < n; i += NW) {
+    if (s_cnt[i] == 0 || s_base[i] >= max_ops) continue;
+    const int s = __builtin_amdgcn_readfirstlane(seq_ids[i]);
+    anneal_wave(S, s, r0, s_base[i], max_ops, os, og, ok, ob, true, lane);
+  }
+  if (tid == 0) *n_ops = tot[0] < max_ops ? tot[0] : max_ops;
+}
+
+int launch_anneal(tkv_cache* c, int n, const int32_t* seq_ids, int r0, int max_ops, int32_t* n_ops_dev,
+                  int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st) {
+  const int nt = n < 1 ? 64 : (n >= WG / 64 ? WG : 64 * n);
+  k_anneal<<<1, nt, 0, st>>>(c->S, n, seq_ids, r0, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits);
+  return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
+}
+
+// ---------------------------------------------------------------------------
 // Sequence reset: blocks back to the global stacks in list order.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(WG) void k_seq_reset(DevState S, int n, const int32_t* seq_ids) {
