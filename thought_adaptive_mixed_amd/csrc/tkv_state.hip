@@ -518,6 +518,7 @@ int launch_append(tkv_cache* c, int n, const int32_t* seq_ids, const int32_t* po
 // order (list, offset, count) and its number of downgrades.
 // ---------------------------------------------------------------------------
 #define ST_APPLY 4u       // s_st: bits 0-1 target class, bit 2 = apply
+#define ST_DUP 8u         // s_st bit 3: an earlier op of the sequence names the same segment
 
 __device__ void evict_walk(const DevState& S, int s, const SeqRec& rec, int cnt, const uint16_t* lst,
                            const int32_t* seg_ids, const int32_t* keep_n, const uint8_t* new_bits,
@@ -530,12 +531,11 @@ __device__ void evict_walk(const DevState& S, int s, const SeqRec& rec, int cnt,
     const int j = lst[r];
     // the final pass repeats the last simulated walk: it only records errors
     // and leaves the per-op results (and the pop indices packed with them) alone
-    if (!final_pass) { s_ni[j] = 0; s_st[j] = 0; }
+    if (!final_pass) { s_ni[j] = 0; s_st[j] &= ST_DUP; }
     if (failed) continue;
     const int k = seg_ids[j];
     if (k < 0 || k >= nseg) { failed = 1; code = TKV_ENOSEG; continue; }
-    int dup = 0;
-    for (int r2 = 0; r2 < r; r2++) if (seg_ids[lst[r2]] == k) { dup = 1; break; }
+    const int dup = (s_st[j] & ST_DUP) != 0;
     const int nb = new_bits[j];
     const int sr = s_segrec[j];
     const int c = sr >> 14, gb = class_bits(c);
@@ -561,7 +561,7 @@ __device__ void evict_walk(const DevState& S, int s, const SeqRec& rec, int cnt,
       nslot.add(c2, TKV_BS * nd - keep);
       nslot.add(c, keep);
     }
-    if (!final_pass) { s_ni[j] = nd; s_st[j] = (uint8_t)(c2 | ST_APPLY); }
+    if (!final_pass) { s_ni[j] = nd; s_st[j] = (uint8_t)((s_st[j] & ST_DUP) | c2 | ST_APPLY); }
     ndown += down;
   }
   if (final_pass) {
@@ -620,6 +620,14 @@ __global__ __launch_bounds__(WG) void k_evict_plan(DevState S, int n_cap, const 
   if (tid == 0) misc[3] = n;
   __syncthreads();
   const int n_valid = group_by_seq(n, S.max_seqs, s_seq, s_cnt, s_off, s_list, s_tmp);
+  // repeated segments, flagged once for the walks below (an op per thread,
+  // against the earlier ops of its sequence)
+  for (int p = tid; p < n_valid; p += NT) {
+    const int j = s_list[p], k = seg_ids[j];
+    for (int p2 = s_off[s_seq[j]]; p2 < p; p2++)
+      if (seg_ids[s_list[p2]] == k) { s_st[j] = ST_DUP; break; }
+  }
+  __syncthreads();
   const int my_cnt = walker ? s_cnt[tid] : 0;
   const uint16_t* my_list = s_list + (walker ? s_off[tid] : 0);
   int ndown = 0;
@@ -777,6 +785,119 @@ __global__ __launch_bounds__(RQ_THREADS) void k_requant(DevState S) {
   }
 }
 
+// Evict, part 2, the ops of one sequence without downgrades, each class in
+// one scan.  Ops of one class touch only that class's slots and stack, and a
+// sequence's segments hold disjoint position ranges, so: map each op's
+// segment to the op, gather the valid slots of those segments with one scan of
+// the class's blocks into a bitmap over the union of the ops' position ranges,
+// rank every slot by position (bitmap prefix counts), and evict the oldest
+// m - keep of each op; an op's evicted slots go on the stack after those of
+// the earlier ops of its class (list order), in ascending position order.
+// The result is the one of applying the ops one after another.
+#define EVB_MAXOPS 256          // ops of one sequence handled by the class-wise path
+__device__ void evict_classwise(const DevState& S, int s, int cnt, const int32_t* recs, int32_t* q, const int32_t* bt,
+                                int32_t* st, int32_t* s_pos, int32_t* s_slot, int32_t* s_segop, uint32_t* s_bm,
+                                int32_t* s_bpre, int* s_tmp, int* s_cnt) {
+  __shared__ int s_m[EVB_MAXOPS], s_ev[EVB_MAXOPS], s_base[EVB_MAXOPS], s_rk0[EVB_MAXOPS];
+  __shared__ int s_evtot;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_evtot = 0;
+  for (int c = 0; c < 3; c++) {
+    // the class's ops: union of their position ranges (the same in every thread)
+    int lo = TKV_INF, hi = -1, nop = 0;
+    for (int r = 0; r < cnt; r++) {
+      const int4 o0 = *(const int4*)(recs + 8 * r), o1 = *(const int4*)(recs + 8 * r + 4);
+      if (!(o0.x & 1) || ((o0.x >> 4) & 3) != c) continue;
+      lo = min(lo, o1.z);
+      hi = max(hi, o1.z + o1.w - 1);
+      nop++;
+    }
+    if (nop == 0) continue;
+    const int span = hi - lo + 1, nbw = (span + 31) >> 5;
+    for (int k = tid; k < S.max_segs; k += EV_THREADS) s_segop[k] = -1;
+    for (int w = tid; w < nbw; w += EV_THREADS) s_bm[w] = 0;
+    for (int r = tid; r < cnt; r += EV_THREADS) s_m[r] = 0;
+    if (tid == 0) *s_cnt = 0;
+    __syncthreads();
+    for (int r = tid; r < cnt; r += EV_THREADS) {
+      const int4 o0 = *(const int4*)(recs + 8 * r);
+      if ((o0.x & 1) && ((o0.x >> 4) & 3) == c) s_segop[o0.y] = r;
+    }
+    __syncthreads();
+    // gather: (position offset | op << 15, slot) of every valid slot of a target segment
+    const int nbk = q[Q_NBLK + c];
+    for (int x = tid; x < nbk * TKV_BS; x += EV_THREADS) {
+      const int blk = bt[c * S.max_blocks + x / TKV_BS], t = x % TKV_BS;
+      const int mask = pick3(S.blk, c)[(int64_t)blk * TKV_BLK_W];
+      const int2 sr = *(const int2*)(pick3(S.slot, c) + ((int64_t)blk * TKV_BS + t) * 2);
+      if (!((mask >> t) & 1) || sr.y < 0 || sr.y >= S.max_segs) continue;
+      const int r = s_segop[sr.y];
+      if (r < 0) continue;
+      const int4 o1 = *(const int4*)(recs + 8 * r + 4);
+      if ((unsigned)(sr.x - o1.z) >= (unsigned)o1.w) continue;       // not on a consistent state
+      const int at = atomicAdd(s_cnt, 1);
+      if (at >= EV_MAXSLOT) continue;
+      const int off = sr.x - lo;
+      s_pos[at] = off | (r << 15);
+      s_slot[at] = blk * TKV_BS + t;
+      atomicOr(&s_bm[off >> 5], 1u << (off & 31));
+      atomicAdd(&s_m[r], 1);
+    }
+    __syncthreads();
+    const int m = *s_cnt < EV_MAXSLOT ? *s_cnt : EV_MAXSLOT;
+    // exclusive prefix of the bitmap words' popcounts
+    {
+      int pc[EV_BMW / EV_THREADS], v[3] = {0, 0, 0}, ex[3], tot[3];
+#pragma unroll
+      for (int u = 0; u < EV_BMW / EV_THREADS; u++) {
+        const int w = tid * (EV_BMW / EV_THREADS) + u;
+        pc[u] = w < nbw ? __popc(s_bm[w]) : 0;
+        v[0] += pc[u];
+      }
+      wg_scan3(v, ex, tot, s_tmp);
+      int run = ex[0];
+#pragma unroll
+      for (int u = 0; u < EV_BMW / EV_THREADS; u++) {
+        s_bpre[tid * (EV_BMW / EV_THREADS) + u] = run;
+        run += pc[u];
+      }
+    }
+    __syncthreads();
+    // per op in list order: kept and evicted counts, stack offset, rank of its first position
+    if (tid == 0) {
+      int run = q[Q_NSLOT + c], evc = 0;
+      for (int r = 0; r < cnt; r++) {
+        const int4 o0 = *(const int4*)(recs + 8 * r), o1 = *(const int4*)(recs + 8 * r + 4);
+        if (!(o0.x & 1) || ((o0.x >> 4) & 3) != c) continue;
+        const int mr = s_m[r];
+        const int keep = o0.z < mr ? o0.z : mr;
+        const int off = o1.z - lo;
+        s_ev[r] = mr - keep;
+        s_base[r] = run;
+        s_rk0[r] = s_bpre[off >> 5] + __popc(s_bm[off >> 5] & ((1u << (off & 31)) - 1u));
+        run += mr - keep;
+        evc += mr - keep;
+        S.segt[((int64_t)s * S.max_segs + o0.y) * TKV_SEG_W + G_NRET] = keep;
+      }
+      q[Q_NSLOT + c] = run;
+      s_evtot += evc;
+    }
+    __syncthreads();
+    int32_t* stc = st + (int64_t)c * S.max_blocks * TKV_BS;
+    for (int a = tid; a < m; a += EV_THREADS) {
+      const int off = s_pos[a] & 0x7FFF, r = s_pos[a] >> 15;
+      const int rk = s_bpre[off >> 5] + __popc(s_bm[off >> 5] & ((1u << (off & 31)) - 1u)) - s_rk0[r];
+      if (rk >= s_ev[r]) continue;
+      const int sl = s_slot[a];
+      atomicAnd(&pick3(S.blk, c)[(int64_t)(sl / TKV_BS) * TKV_BLK_W], ~(1 << (sl % TKV_BS)));
+      stc[s_base[r] + rk] = sl;
+    }
+    __threadfence_block();
+    __syncthreads();
+  }
+  if (tid == 0) q[Q_NRET] -= s_evtot;
+}
+
 __global__ __launch_bounds__(EV_THREADS) void k_evict_apply(DevState S) {
   __shared__ int32_t s_pos[EV_MAXSLOT];
   __shared__ int32_t s_slot[EV_MAXSLOT];
@@ -806,6 +927,31 @@ __global__ __launch_bounds__(EV_THREADS) void k_evict_apply(DevState S) {
   // reads from, so they are re-quantized here, in op order.
   const bool defer = ndown <= 1;
   int nmoves = 0;
+  // Several ops and no downgrade: each class in one scan (below); otherwise
+  // (or when a bound of that path is exceeded) the ops one after another.
+  if (ndown == 0 && cnt > 1 && cnt <= EVB_MAXOPS && S.max_segs <= EV_MAXSLOT) {
+    __shared__ int s_ok;
+    if (tid == 0) {
+      int ok = 1;
+      for (int c = 0; c < 3 && ok; c++) {
+        int lo = TKV_INF, hi = -1;
+        for (int r = 0; r < cnt; r++) {
+          const int4 o0 = *(const int4*)(recs + 8 * r), o1 = *(const int4*)(recs + 8 * r + 4);
+          if (!(o0.x & 1) || ((o0.x >> 4) & 3) != c) continue;
+          lo = min(lo, o1.z);
+          hi = max(hi, o1.z + o1.w - 1);
+        }
+        if (hi >= lo && hi - lo + 1 > EV_BMW * 32) ok = 0;
+      }
+      s_ok = ok;
+    }
+    __syncthreads();
+    if (s_ok) {
+      evict_classwise(S, s, cnt, recs, q, bt, st, s_pos, s_slot, s_rank, s_bm, s_bpre, s_tmp, &s_cnt);
+      if (tid == 0) scr_mcnt(S.scratch)[s] = 0;
+      return;
+    }
+  }
   for (int r0 = 0; r0 < cnt; r0++) {
     const int4 o0 = *(const int4*)(recs + 8 * r0), o1 = *(const int4*)(recs + 8 * r0 + 4);
     if (!(o0.x & 1)) continue;
