@@ -74,6 +74,8 @@ def lib():
         L.ora_plan_budget.restype = C.c_int
         L.ora_plan_anneal.argtypes = [P, P, C.c_int, P, C.c_int, C.c_int, P, P, P, P]
         L.ora_plan_anneal.restype = C.c_int
+        L.ora_compact.argtypes = [P, P, C.c_int, P]; L.ora_compact.restype = None
+        L.ora_token_rows.argtypes = [P, P, C.c_int, C.c_int, C.c_int, P, P]; L.ora_token_rows.restype = None
         L.ora_seq_reset.argtypes = [P, P, C.c_int, P]; L.ora_seq_reset.restype = None
         L.ora_attention.argtypes = [P, P, C.c_int, P, P, P, P, P, P, C.c_int, C.c_int, P, P, P]
         L.ora_attention.restype = None
@@ -211,6 +213,10 @@ class OracleCache:
                                   int(r0), int(max_ops), _p(os_), _p(og), _p(ok), _p(ob))
         return os_[:m], og[:m], ok[:m], ob[:m]
 
+    def compact(self, seq_ids):
+        seq_ids = _arr(seq_ids, np.int32)
+        lib().ora_compact(C.byref(self.L._c), C.byref(self._state), seq_ids.size, _p(seq_ids))
+
     def seq_reset(self, seq_ids):
         seq_ids = _arr(seq_ids, np.int32)
         lib().ora_seq_reset(C.byref(self.L._c), C.byref(self._state), seq_ids.size, _p(seq_ids))
@@ -246,6 +252,28 @@ class OracleCache:
         n = int(self.seq_record(s)[6])
         base = s * L.max_segments_per_seq * SEG_W
         return self.bufs["segt"][base:base + n * SEG_W].reshape(n, SEG_W)
+
+    def token_rows(self, s):
+        """{position: fp32 [2][Hkv][D] K and V rows} of the retained tokens of sequence s."""
+        L = self.L
+        q = self.seq_record(s)
+        H, D = L.num_kv_heads, L.head_dim
+        out = {}
+        for c in range(3):
+            bt = self.bufs["btab"][(s * 3 + c) * L.max_blocks_per_seq:][:int(q[c])]
+            for blk in bt:
+                mask = int(self.bufs[f"blk{c}"][int(blk) * 4])
+                for t in range(16):
+                    if not (mask >> t) & 1:
+                        continue
+                    slot = int(blk) * 16 + t
+                    rows = np.zeros((2, H, D), np.float32)
+                    for h in range(H):
+                        k = np.zeros(D, np.float32); v = np.zeros(D, np.float32)
+                        lib().ora_token_rows(C.byref(L._c), C.byref(self._state), c, slot, h, _p(k), _p(v))
+                        rows[0, h], rows[1, h] = k, v
+                    out[int(self.bufs[f"slot{c}"][slot * 2])] = rows
+        return out
 
     def error(self):
         h = self.bufs["hdr"]

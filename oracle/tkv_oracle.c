@@ -305,6 +305,13 @@ static void load_token_f32(const ora_layout *L, ora_state *S, int c, int blk, in
   }
 }
 
+/* The fp32 rows (K then V) of the token in slot `slot` of class c, head h
+   (test access to stored tokens). */
+void ora_token_rows(const ora_layout *L, ora_state *S, int c, int slot, int head, float *k, float *v) {
+  load_token_f32(L, S, c, slot / BS, slot % BS, head, 0, k);
+  load_token_f32(L, S, c, slot / BS, slot % BS, head, 1, v);
+}
+
 /* Dequantize one code exactly in fp64. */
 static double deq64(const ora_layout *L, ora_state *S, int c, int blk, int t, int head, int kv, int d) {
   uint8_t *bh = block_head(L, S, c, blk, head);
@@ -570,6 +577,119 @@ int ora_plan_anneal(const ora_layout *L, ora_state *S, int n, const int32_t *seq
     }
   }
   return m;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Gather compaction: the baseline that in-place reuse avoids (abstract:   */
+/* the kernel reuses evicted tokens' slots, so no compaction is needed;    */
+/* Continuous Thinking bullet).  Reading: for each listed sequence (an id  */
+/* listed again is compacted once, at its first listing) and each class    */
+/* holding blocks, its m retained tokens are copied bit for bit, in       */
+/* position order, into ceil(m/16) blocks popped from the class's global   */
+/* stack (token i into slot i % 16 of the (i/16)-th popped block); those   */
+/* blocks become the class's block list and the free-slot stack becomes    */
+/* the empty tail of the last one (lowest slot on top).  All pops of the   */
+/* call come first, in list order; then the old blocks of every compacted  */
+/* sequence go back to their global stacks (sequences in list order,       */
+/* classes in order, blocks in list order, records cleared), so no copy    */
+/* reads a block written in the same call.  A sequence that does not find  */
+/* all its blocks fails with ENOMEM and is left untouched; after the first */
+/* such failure of a class, every later sequence needing blocks of that    */
+/* class fails too.  Ids outside [0, max_seqs): EINVAL.                    */
+/* ---------------------------------------------------------------------- */
+static int32_t token_pos(ora_state *S, int c, int slot) { return S->slot[c][slot * SLOT_W]; }
+
+static void copy_token(const ora_layout *L, ora_state *S, int c, int src, int dst) {
+  int D = L->head_dim, NG = D / L->group_size, bits = CLASS_BITS[c];
+  for (int h = 0; h < L->num_kv_heads; h++) {
+    uint8_t *sb = block_head(L, S, c, src / BS, h), *db = block_head(L, S, c, dst / BS, h);
+    int ts = src % BS, td = dst % BS;
+    for (int d = 0; d < D; d++) {
+      put_code(db, k_code_bit(L, c, td, d), bits, get_code(sb, k_code_bit(L, c, ts, d), bits));
+      put_code(db, v_code_bit(L, c, td, d), bits, get_code(sb, v_code_bit(L, c, ts, d), bits));
+    }
+    for (int kv = 0; kv < 2; kv++)
+      for (int gi = 0; gi < NG; gi++) memcpy(db + meta_off(L, c, kv, td, gi), sb + meta_off(L, c, kv, ts, gi), 4);
+  }
+}
+
+void ora_compact(const ora_layout *L, ora_state *S, int n, const int32_t *seq_ids) {
+  int MB = L->max_blocks_per_seq;
+  char *seen = calloc((size_t)L->max_seqs, 1);
+  int32_t *plan_s = malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+  int32_t *newb = malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1) * 3 * MB);
+  int32_t *slots = malloc(sizeof(int32_t) * (size_t)MB * BS);
+  int dry[3] = {0, 0, 0}, np = 0;
+  /* pops, in list order */
+  for (int i = 0; i < n; i++) {
+    int s = seq_ids[i];
+    if (s < 0 || s >= L->max_seqs) { record_error(S, ORA_EINVAL, s < 0 ? 0x7fffffff : s); continue; }
+    if (seen[s]) continue;
+    seen[s] = 1;
+    int32_t *q = SEQ(L, S, s);
+    int need[3], ok = 1;
+    for (int c = 0; c < 3; c++) {
+      int m = 0;
+      for (int j = 0; j < q[Q_NBLK + c]; j++) {
+        int mask = S->blk[c][BTAB(L, S, s, c)[j] * BLK_W];
+        for (int t = 0; t < BS; t++) m += (mask >> t) & 1;
+      }
+      need[c] = (m + BS - 1) / BS;
+    }
+    for (int c = 0; c < 3; c++)
+      if (need[c] > 0 && (dry[c] || need[c] > S->hdr[H_FREE + c])) { dry[c] = 1; ok = 0; }
+    if (!ok) { record_error(S, ORA_ENOMEM, s); continue; }
+    int32_t *nb = newb + (int64_t)np * 3 * MB;
+    for (int c = 0; c < 3; c++)
+      for (int j = 0; j < need[c]; j++) nb[c * MB + j] = S->freestk[c][--S->hdr[H_FREE + c]];
+    plan_s[np++] = s;
+  }
+  /* copies: each class's retained tokens in position order into the popped blocks */
+  int32_t *oldb = malloc(sizeof(int32_t) * (size_t)(np > 0 ? np : 1) * 3 * MB);
+  int32_t *oldn = malloc(sizeof(int32_t) * (size_t)(np > 0 ? np : 1) * 3);
+  for (int p = 0; p < np; p++) {
+    int s = plan_s[p];
+    int32_t *q = SEQ(L, S, s), *nb = newb + (int64_t)p * 3 * MB;
+    for (int c = 0; c < 3; c++) {
+      int32_t *bt = BTAB(L, S, s, c);
+      int nold = q[Q_NBLK + c];
+      oldn[p * 3 + c] = nold;
+      memcpy(oldb + ((int64_t)p * 3 + c) * MB, bt, sizeof(int32_t) * (size_t)nold);
+      if (nold == 0) continue;
+      int m = 0;
+      for (int j = 0; j < nold; j++) {
+        int blk = bt[j], mask = S->blk[c][blk * BLK_W];
+        for (int t = 0; t < BS; t++) if ((mask >> t) & 1) slots[m++] = blk * BS + t;
+      }
+      for (int a = 1; a < m; a++) {            /* insertion sort by position */
+        int32_t x = slots[a]; int b = a - 1;
+        while (b >= 0 && token_pos(S, c, slots[b]) > token_pos(S, c, x)) { slots[b + 1] = slots[b]; b--; }
+        slots[b + 1] = x;
+      }
+      int need = (m + BS - 1) / BS;
+      for (int i = 0; i < m; i++) {
+        int dst = nb[c * MB + i / BS] * BS + i % BS;
+        copy_token(L, S, c, slots[i], dst);
+        occupy(L, S, c, dst, token_pos(S, c, slots[i]), S->slot[c][slots[i] * SLOT_W + 1]);
+      }
+      for (int j = 0; j < need; j++) { bt[j] = nb[c * MB + j]; S->blk[c][bt[j] * BLK_W + 2] = s; }
+      q[Q_NBLK + c] = need;
+      q[Q_NSLOT + c] = 0;
+      if (m % BS) {
+        int32_t *st = SSTK(L, S, s, c);
+        for (int t = BS - 1; t >= m % BS; t--) st[q[Q_NSLOT + c]++] = bt[need - 1] * BS + t;
+      }
+    }
+  }
+  /* pushes: the old blocks back, records cleared */
+  for (int p = 0; p < np; p++)
+    for (int c = 0; c < 3; c++)
+      for (int j = 0; j < oldn[p * 3 + c]; j++) {
+        int blk = oldb[((int64_t)p * 3 + c) * MB + j];
+        S->blk[c][blk * BLK_W + 0] = 0; S->blk[c][blk * BLK_W + 1] = -1; S->blk[c][blk * BLK_W + 2] = -1;
+        S->freestk[c][S->hdr[H_FREE + c]++] = blk;
+      }
+  free(oldb); free(oldn); free(slots); free(newb); free(plan_s); free(seen);
 }
 
 /* Return the sequences' blocks to the global stacks (list order, classes

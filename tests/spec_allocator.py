@@ -142,6 +142,51 @@ class Spec:
             seg["nret"] = keep
             q["nret"] -= ev
 
+    def compact(self, seqs):
+        """Gather compaction: for each sequence (its first listing only) and
+        each class it holds blocks of, its retained tokens, oldest first, are
+        placed 16 to a block in blocks taken from the class's free list; the
+        tail of the last such block is the new free-slot stack.  The old blocks
+        are released only after every listed sequence has taken its blocks."""
+        dry = [False] * 3
+        done, plans = set(), []
+        for s in seqs:
+            if not (0 <= s < self.max_seqs):
+                self._err(EINVAL, s if s >= 0 else 0x7FFFFFFF); continue
+            if s in done:
+                continue
+            done.add(s)
+            q = self._seq(s)
+            toks = [sorted(self.slot[(c, b * BS + t)] for b in q["blocks"][c] for t in self.block[(c, b)]["valid"])
+                    for c in range(3)]
+            need = [-(-len(toks[c]) // BS) for c in range(3)]
+            short = [c for c in range(3) if need[c] and (dry[c] or need[c] > len(self.free[c]))]
+            for c in short:
+                dry[c] = True
+            if short:
+                self._err(ENOMEM, s); continue
+            plans.append((s, toks, [[self.free[c].pop(0) for _ in range(need[c])] for c in range(3)]))
+        released = []
+        for s, toks, fresh in plans:
+            q = self._seq(s)
+            for c in range(3):
+                if not q["blocks"][c]:
+                    continue
+                released.append((c, q["blocks"][c]))
+                for j, blk in enumerate(fresh[c]):
+                    part = toks[c][BS * j:BS * (j + 1)]
+                    self.block[(c, blk)] = {"valid": set(range(len(part))), "maxpos": max(p for p, _ in part),
+                                            "owner": s}
+                    for t, rec in enumerate(part):
+                        self.slot[(c, blk * BS + t)] = rec
+                q["blocks"][c] = list(fresh[c])
+                used = len(toks[c]) % BS
+                q["stack"][c] = [fresh[c][-1] * BS + t for t in range(BS - 1, used - 1, -1)] if used else []
+        for c, blocks in released:
+            for blk in blocks:
+                del self.block[(c, blk)]
+                self.free[c].insert(0, blk)
+
     def reset(self, seqs):
         for s in seqs:
             if not (0 <= s < self.max_seqs):

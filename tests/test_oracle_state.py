@@ -170,6 +170,8 @@ def run_program(prog, pools, max_seqs, max_blocks, max_segs, order, seed):
             if want:
                 oc.evict(*[list(x) for x in zip(*want)])
                 sp.evict(want)
+        elif kind == "C":
+            oc.compact(step[1]); sp.compact(step[1])
         elif kind == "N":
             seqs, r0 = step[1], step[2]
             got = oc.plan_anneal(seqs, r0, 16)
@@ -209,6 +211,87 @@ def test_anneal_brute_force_against_spec(seed):
             r0 = int(rng.choice([0, 1, 2, 3, 4, 5, 64]))
             prog.insert(at, ("N", [int(s) for s in rng.permutation(2)], r0))
         run_program(prog, pools, 2, 2, 6, None, seed * 100 + rep)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_compact_brute_force_against_spec(seed):
+    """Random programs with gather compactions (lists with repeats and bad
+    ids) inserted; small pools so that compactions also run out of blocks."""
+    rng = np.random.default_rng(2000 + seed)
+    pools = (3, 3, 3) if seed % 2 else (2, 3, 2)
+    order = [rng.permutation(p).astype(np.int32) for p in pools] if seed % 3 == 0 else None
+    for rep in range(10):
+        prog = random_program(rng, 2, 8)
+        for _ in range(3):
+            at = int(rng.integers(0, len(prog) + 1))
+            lst = [int(x) for x in rng.integers(-1, 3, int(rng.integers(0, 4)))]
+            prog.insert(at, ("C", lst))
+        run_program(prog, pools, 2, 2, 6, order, seed * 100 + rep)
+
+
+def test_compact_hand_example():
+    """Seq 0: 40 R tokens (3 blocks of class 0), the middle 20 evicted (via a
+    3-segment layout R20 E2 R20 after which the first R segment keeps 10).  30
+    tokens remain in class 0 -> 2 fresh blocks, full then 14; the tail slots 14
+    and 15 of the second form the stack with slot 14 on top; the 3 old blocks
+    go back, the last of them on top."""
+    L = oracle.OracleLayout(1, 1, 64, 32, (8, 4, 4), 1, 8, 8)
+    oc = oracle.OracleCache(L)
+    types = [0] * 20 + [1] * 2 + [0] * 20
+    kv = np.random.default_rng(3).standard_normal((42, 1, 64)).astype(np.float32)
+    oc.append([0] * 42, range(42), types, kv, kv)
+    oc.evict([0], [0], [10], [0])                 # segment 0 keeps its 10 newest (positions 10..19)
+    before = oc.attention([0], [42], np.zeros((1, 1, 64), np.uint16) + 0x3F80)
+    old_blocks = oc.bufs["btab"][:3].copy()
+    free0 = int(oc.bufs["hdr"][0])
+    fresh = oc.bufs["free0"][free0 - 2:free0][::-1].copy()   # the two blocks popped next
+    oc.compact([0, 0])
+    q = oc.seq_record(0)
+    assert q[0] == 2 and q[3] == 2 and oc.error()[0] == 0
+    bt = oc.bufs["btab"][:2]
+    assert bt.tolist() == fresh.tolist()
+    blk = oc.bufs["blk0"].reshape(-1, 4)
+    assert blk[bt[0], 0] == 0xFFFF and blk[bt[1], 0] == (1 << 14) - 1
+    pos = oc.bufs["slot0"].reshape(-1, 16, 2)[:, :, 0]
+    assert pos[bt[0]].tolist() == list(range(10, 20)) + list(range(22, 28))
+    assert pos[bt[1], :14].tolist() == list(range(28, 42))
+    assert blk[bt[0], 1] == 27 and blk[bt[1], 1] == 41
+    assert oc.bufs["sstk"][:2].tolist() == [int(bt[1]) * 16 + 15, int(bt[1]) * 16 + 14]
+    assert int(oc.bufs["hdr"][0]) == free0 - 2 + 3
+    assert oc.bufs["free0"][free0 - 2:free0 + 1].tolist() == old_blocks.tolist()
+    for b in old_blocks:
+        assert blk[b].tolist()[:3] == [0, -1, -1]
+    after = oc.attention([0], [42], np.zeros((1, 1, 64), np.uint16) + 0x3F80)
+    np.testing.assert_allclose(after[0], before[0], rtol=1e-12, atol=1e-14)
+    assert after[2].tolist() == before[2].tolist() == [32]
+    check_invariants(oc)
+
+
+def test_compact_keeps_attention_and_rows():
+    """On a churned multi-sequence state: compaction moves bits, so every
+    token's dequantized K and V rows (found by position) are unchanged and the
+    attention of every sequence equals the one before (fp64, another order)."""
+    from thought_adaptive_mixed_amd import synth
+    import helpers
+    import dataclasses
+    w = synth.small_static(seed=85, B=3, Hq=8, Hkv=2, D=64, g=32, permute=False)
+    w.layout = dataclasses.replace(w.layout, pool_blocks=tuple(2 * p for p in w.layout.pool_blocks))
+    oc = helpers.build_oracle(w)
+    seqs = [int(s) for s in w.seq_ids]
+    before = oc.attention(w.seq_ids, w.q_pos, w.q_bf16)
+    rows0 = {s: oc.token_rows(s) for s in seqs}
+    oc.compact(seqs[::-1])
+    assert oc.error()[0] == 0
+    after = oc.attention(w.seq_ids, w.q_pos, w.q_bf16)
+    np.testing.assert_allclose(after[0], before[0], rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(after[1], before[1], rtol=1e-11, atol=1e-13)
+    assert after[2].tolist() == before[2].tolist()
+    for s in seqs:
+        r1 = oc.token_rows(s)
+        assert r1.keys() == rows0[s].keys()
+        for p in r1:
+            assert np.array_equal(r1[p], rows0[s][p]), (s, p)
+    check_invariants(oc)
 
 
 def anneal_cache(types_and_lengths, pools=(8, 8, 8)):
