@@ -6,7 +6,11 @@ thought_classify -> kv_append_quant of the new token at its label's precision
 -> kv_plan_budget (token budget ladder) -> kv_evict_segment.  With
 --policy anneal the ladder is replaced by kv_plan_anneal (the TBE annealing
 schedule of the retention, r0 = 64 by default), applied to the built state
-until it plans nothing before anything is timed.  Workload: the
+until it plans nothing before anything is timed.  With --compact every step
+also compacts the sequences it evicted from (tkv_compact, the gather-
+compaction baseline that in-place slot reuse avoids), after every sequence
+was compacted once before timing.  --workload churn256 runs the B256 decode
+loop (lengths 4k..32k, 5% budget) instead of the default.  Workload: the
 Llama-8B-like reasoning-decode layer (B32, Hq32/Hkv8, D128, g64, 16k generated
 tokens per sequence, 10% budget -> 1638 retained, R/E/T 8/4/2-bit) with
 planted-temperature queries, synthetic data.
@@ -133,7 +137,7 @@ def measured_traffic():
     return float(j["traffic_bytes_per_launch"]) if h.hexdigest() == j["source_sha256"] else None
 
 
-def cpu_baseline(w, state, ch, n_seq, budget_s=12.0, max_reps=1000, policy="ladder", r0=64):
+def cpu_baseline(w, state, ch, n_seq, budget_s=12.0, max_reps=1000, policy="ladder", r0=64, compact=False):
     """The oracle as it stands, on a sample of n_seq sequences of the same
     workload: one full step (attention with the self token, classify, append,
     ladder or annealing plan, evict) per repetition, on all host cores the
@@ -161,6 +165,8 @@ def cpu_baseline(w, state, ch, n_seq, budget_s=12.0, max_reps=1000, policy="ladd
             ops = oc.plan_budget(sel, ch.budget[0], ch.budget[1], 256)
         if ops[0].size:
             oc.evict(*ops)
+            if compact:
+                oc.compact(ops[0])
         tokens += int(na.sum())
         reps += 1
         if time.perf_counter() - t0 > budget_s or reps >= max_reps:
@@ -168,8 +174,26 @@ def cpu_baseline(w, state, ch, n_seq, budget_s=12.0, max_reps=1000, policy="ladd
     dt = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     return {"value": tokens / dt, "unit": "KV tokens/s", "cores": min(threads, cores), "kind": "oracle",
-            "sample": f"{reps} full steps (attention+classify+append+{policy}+evict) on {n_seq} of "
+            "sample": f"{reps} full steps (attention+classify+append+{policy}+evict"
+                      f"{'+compact' if compact else ''}) on {n_seq} of "
                       f"{w.seq_ids.size} sequences of the same cache, fp64 attention, {dt:.1f} s"}
+
+
+def workload_name(args):
+    if args.workload == "llama8b":
+        head = "llama8b-like reasoning decode, one layer: B32, Hq32/Hkv8, D128, g64, "
+        if args.policy == "ladder":
+            body = ("16k generated tokens/seq, 10% budget (1638 retained), R/E/T 8/4/2-bit, "
+                    "planted-temperature queries; step = attention+classify+append+ladder+evict")
+        else:
+            body = (f"16k generated tokens/seq, R/E/T 8/4/2-bit, TBE annealing schedule (r0 {args.r0}) applied "
+                    f"to the built state, planted-temperature queries; step = attention+classify+append+anneal+evict")
+    else:
+        head = "B256 reasoning decode loop, one layer: Hq32/Hkv8, D128, g64, "
+        body = ("lengths U{4k..32k}, 5% budget, R/E/T 8/4/2-bit, planted-temperature queries; step = "
+                "attention+classify+append+" + ("ladder" if args.policy == "ladder" else f"anneal (r0 {args.r0})")
+                + "+evict")
+    return head + body + ("+compact (gather-compaction baseline, dense start)" if args.compact else "")
 
 
 def main():
@@ -182,6 +206,10 @@ def main():
     ap.add_argument("--policy", choices=("ladder", "anneal"), default="ladder",
                     help="eviction planner of the step: the token-budget ladder, or the TBE annealing schedule")
     ap.add_argument("--r0", type=int, default=64, help="first retention of the annealing schedule")
+    ap.add_argument("--compact", action="store_true",
+                    help="compact the sequences each step evicted from (gather-compaction baseline)")
+    ap.add_argument("--workload", choices=("llama8b", "churn256"), default="llama8b",
+                    help="the llama8b-like layer (B32, 16k, 10%% budget) or the B256 decode loop (4k..32k, 5%% budget)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-only", action="store_true", help="time only the attention call (diagnostic)")
     ap.add_argument("--torch-events", action="store_true", help="time with torch's default events (diagnostic)")
@@ -204,7 +232,7 @@ def main():
     total_steps = args.warmup + args.steps
     log("[bench] building workload")
     t0 = time.time()
-    ch = synth.bench_cycle(steps=total_steps)
+    ch = synth.bench_cycle(steps=total_steps) if args.workload == "llama8b" else synth.churn(steps=total_steps)
     w = ch.base
     L = w.layout
     B = w.seq_ids.size
@@ -225,6 +253,11 @@ def main():
             c0.evict(*t_ops, t_bits, n_ops_dev=t_n, n_ops=m_all)
             if int(t_n.item()) == 0:
                 break
+        torch.cuda.synchronize()
+    if args.compact:
+        # start dense: every sequence compacted once (one per call, so each needs only its own room)
+        for s in w.seq_ids:
+            c0.compact(dv0([s]))
         torch.cuda.synchronize()
     state = c0.export()
     caches = [c0] + [binding.Cache(helpers.gpu_layout(L), w.block_order) for _ in range(R - 1)]
@@ -275,7 +308,7 @@ def main():
              c.plan_budget(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, o_seq, o_seg, o_keep, o_bits,
                            stream=sh, prepare=True)),
             c.evict(o_seq, o_seg, o_keep, o_bits, n_ops_dev=n_ops, n_ops=max_ops, stream=sh, prepare=True),
-        ])
+        ] + ([c.compact(o_seq, n_dev=n_ops, n=max_ops, stream=sh, prepare=True)] if args.compact else []))
 
     # Steps are launched eagerly on torch's current stream: on this stack a
     # replayed HIP graph per step measured slower than direct launches.  The
@@ -339,25 +372,22 @@ def main():
         "vs_baseline": None,
         "dtype": "f16 MFMA (int8/4/2 codes as exact fp16 subnormals), f32 accumulate",
         "data": "synthetic",
-        "config": {"workload": "llama8b-like reasoning decode, one layer: B32, Hq32/Hkv8, D128, g64, "
-                               + ("16k generated tokens/seq, 10% budget (1638 retained), R/E/T 8/4/2-bit, "
-                                  "planted-temperature queries; step = attention+classify+append+ladder+evict"
-                                  if args.policy == "ladder" else
-                                  f"16k generated tokens/seq, R/E/T 8/4/2-bit, TBE annealing schedule "
-                                  f"(r0 {args.r0}) applied to the built state, planted-temperature queries; "
-                                  f"step = attention+classify+append+anneal+evict"),
+        "config": {"workload": workload_name(args),
                    "batch": B, "copies": R, "attended_per_step": tokens / args.steps,
                    "launch": "eager, one stream"},
         "attn_ms": attn_avg,
         "attn_kv_tokens_per_s": (tokens / args.steps) / (attn_avg * 1e-3),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic() if (args.workload == "llama8b" and args.policy == "ladder"
+                                                       and not args.compact) else None,
                      "kernel": "k_attn (paged_decode_attn; one launch per step)",
                      "bytes_per_launch": abytes_step},
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(w, state, ch, args.cpu_seqs, policy=args.policy, r0=args.r0)
+        result["cpu_baseline"] = cpu_baseline(w, state, ch, args.cpu_seqs, policy=args.policy, r0=args.r0,
+                                              compact=args.compact)
     print(json.dumps(result), flush=True)
 
 

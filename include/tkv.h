@@ -196,6 +196,28 @@ int kv_plan_anneal(tkv_cache* c, int32_t n, const int32_t* seq_ids, int32_t r0, 
                    int32_t* n_ops_dev, int32_t* op_seq, int32_t* op_seg, int32_t* op_keep,
                    uint8_t* op_bits, hipStream_t stream);
 
+/* tkv_compact -- gather compaction, the baseline that in-place slot reuse
+ * makes unnecessary (abstract: the kernel reuses evicted tokens' slots and so
+ * eliminates compaction; Continuous Thinking bullet).  For each listed
+ * sequence (an id listed again is compacted once; with n_dev, device i32,
+ * nullable, only the first *n_dev <= n ids are read, so the seq_ids of an op
+ * list written by a planner can be passed as they are) and each class it
+ * holds blocks of: its m retained tokens are copied bit for bit, in position
+ * order, into ceil(m/16) blocks popped from the class's global stack (token i
+ * into slot i % 16 of the (i/16)-th popped block), which become its block
+ * list; its free-slot stack becomes the empty tail of the last of them (lowest
+ * slot on top).  All pops of the call come first (list order), then the old
+ * blocks of every compacted sequence return to the global stacks (list
+ * order, classes in order, blocks in list order).  Segments, lengths and
+ * counts are unchanged; attention over the compacted cache reads the same
+ * tokens.  Scratch (inside the cache's scratch buffer) carries the plan
+ * between the three kernels of the call.
+ *   Device errors: EINVAL (id outside [0, max_seqs)), ENOMEM (a sequence that
+ *   does not find all its blocks is left untouched; after the first such
+ *   failure of a class every later sequence needing that class fails too).
+ *   EINVAL: n < 0 or n > max_tokens_per_call, or seq_ids NULL with n > 0. */
+int tkv_compact(tkv_cache* c, int32_t n, const int32_t* n_dev, const int32_t* seq_ids, hipStream_t stream);
+
 /* paged_decode_attn -- one decode step of attention over the mixed-precision,
  * hole-bearing cache (abstract: a kernel extending PagedAttention that reuses
  * evicted slots), with the sparsity statistics that assign the thought type

@@ -161,6 +161,12 @@ extern "C" int kv_plan_anneal(tkv_cache* c, int32_t n, const int32_t* seq_ids, i
   return launch_anneal(c, n, seq_ids, r0, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits, stream);
 }
 
+extern "C" int tkv_compact(tkv_cache* c, int32_t n, const int32_t* n_dev, const int32_t* seq_ids, hipStream_t stream) {
+  if (!c || n < 0 || n > c->S.max_tokens || (n > 0 && !seq_ids)) return TKV_EINVAL;
+  c->last_stream = stream;
+  return launch_compact(c, n, n_dev, seq_ids, stream);
+}
+
 extern "C" size_t tkv_attn_workspace(const tkv_cache* c, int32_t batch, int32_t num_splits) {
   if (!c || batch < 0) return 0;
   int nw, s;

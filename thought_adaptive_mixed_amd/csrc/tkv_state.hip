@@ -1351,6 +1351,352 @@ int launch_anneal(tkv_cache* c, int n, const int32_t* seq_ids, int r0, int max_o
 }
 
 // ---------------------------------------------------------------------------
+// Gather compaction, the baseline that in-place reuse avoids (abstract: the
+// kernel reuses evicted tokens' slots, eliminating compaction; Continuous
+// Thinking bullet).  For each listed sequence (first listing only) and class
+// holding blocks, the m retained tokens are copied bit for bit, in position
+// order, into ceil(m/16) blocks popped from the class's global stack (token i
+// into slot i % 16 of the (i/16)-th popped block), which become its block
+// list; its free-slot stack becomes the empty tail of the last one (lowest
+// slot on top).  All pops of the call come first (list order), then every
+// compacted sequence's old blocks go back (list order, classes in order,
+// blocks in list order, records cleared).  A sequence that does not find all
+// its blocks fails with ENOMEM, untouched; after the first such failure of a
+// class, every later sequence needing blocks of that class fails too.
+//   k_compact_plan: first listings, token counts (a wave per sequence), the
+//     list-order pops (one thread: the failure rule is a chain), the pushes'
+//     places, and the offsets of the copy tasks (one per new block).
+//   k_compact_copy: a fixed grid of work-groups walks the tasks.  A task
+//     ranks the class's retained tokens by position (a bitmap over their
+//     positions and its prefix counts), takes the 16 of its block and writes
+//     the block: K chunks hold one token each and are copied word for word; a
+//     V word holds the codes of a token quad and is assembled field by field;
+//     metadata words are per (token, group); then the new slots' and block's
+//     records.  Sources are old blocks, destinations popped ones: no block is
+//     both read and written, and the block lists are not touched yet.
+//   k_compact_push: the new block lists and slot stacks, then the old blocks
+//     onto the global stacks and the stack heights.
+// Scratch: per item {seq or -1, pop top[3], push base[3]}; per (item, class)
+// the task offsets; per sequence its old block lists [3][max_blocks], their
+// lengths [3] and its token counts [3], in its move area.
+// ---------------------------------------------------------------------------
+#define CMP_BMW 2048          // position bitmap words of the ranking: spans up to 65536 positions
+__device__ inline int32_t* cmp_old(const DevState& S, int s, int c) {
+  return scr_moves(S.scratch, S.max_seqs) + (int64_t)s * S.max_blocks * TKV_BS * 2 + c * S.max_blocks;
+}
+__device__ inline int32_t* cmp_counts(const DevState& S, int s) {       // [0..2] old lengths, [3..5] tokens
+  return scr_moves(S.scratch, S.max_seqs) + (int64_t)s * S.max_blocks * TKV_BS * 2 + 3 * S.max_blocks;
+}
+__device__ inline int32_t* cmp_tasks(const DevState& S) { return S.scratch + TKV_MAX_TOK; }   // [3 * MAX_TOK + 1]
+
+__device__ inline int eff_count(int n_cap, const int32_t* n_dev) {
+  if (!n_dev) return n_cap;
+  const int m = *n_dev;
+  return m < n_cap ? (m < 0 ? 0 : m) : n_cap;
+}
+
+__global__ __launch_bounds__(WG) void k_compact_plan(DevState S, int n_cap, const int32_t* n_dev,
+                                                     const int32_t* seq_ids) {
+  __shared__ int s_first[TKV_MAX_SEQS];
+  __shared__ int16_t s_m[TKV_MAX_TOK][3];
+  const int tid = threadIdx.x, NT = blockDim.x, wv = tid >> 6, lane = tid & 63, NW = NT >> 6;
+  const int n = eff_count(n_cap, n_dev);
+  for (int s = tid; s < S.max_seqs; s += NT) s_first[s] = TKV_INF;
+  __syncthreads();
+  for (int i = tid; i < n; i += NT) {
+    const int s = seq_ids[i];
+    if (s >= 0 && s < S.max_seqs) atomicMin(&s_first[s], i);
+  }
+  __syncthreads();
+  // retained tokens per class of each first listing (a wave per item)
+  for (int i = wv; i < n; i += NW) {
+    const int s = __builtin_amdgcn_readfirstlane(seq_ids[i]);
+    if (s < 0 || s >= S.max_seqs || s_first[s] != i) continue;
+    const int32_t* q = S.seq + (int64_t)s * TKV_SEQ_W;
+    for (int c = 0; c < 3; c++) {
+      const int nb = q[Q_NBLK + c];
+      int m = 0;
+      for (int j = lane; j < nb; j += 64)
+        m += __popc((uint32_t)pick3(S.blk, c)[(int64_t)S.btab[((int64_t)s * 3 + c) * S.max_blocks + j] * TKV_BLK_W] &
+                    0xFFFFu);
+      m = wave_total(wave_incl_scan(m));
+      if (lane == 0) s_m[i][c] = (int16_t)m;
+    }
+  }
+  int32_t* recs = scr_oprec(S.scratch);
+  for (int i = tid; i < n_cap; i += NT) recs[8 * i] = -1;
+  __syncthreads();
+  if (tid == 0) {
+    int avail[3], cum[3] = {0, 0, 0}, pushed[3] = {0, 0, 0}, tasks = 0;
+    bool dry[3] = {false, false, false};
+    for (int c = 0; c < 3; c++) avail[c] = S.hdr[H_FREE + c];
+    int32_t* pre = cmp_tasks(S);
+    for (int i = 0; i < n; i++) {
+      const int s = seq_ids[i];
+      int need[3] = {0, 0, 0};
+      bool planned = false;
+      if (s < 0 || s >= S.max_seqs) {
+        record_error(S.hdr, TKV_EINVAL, s < 0 ? TKV_INF : s);
+      } else if (s_first[s] == i) {
+        bool ok = true;
+        for (int c = 0; c < 3; c++) {
+          need[c] = (s_m[i][c] + TKV_BS - 1) / TKV_BS;
+          if (need[c] > 0 && (dry[c] || need[c] > avail[c] - cum[c])) { dry[c] = true; ok = false; }
+        }
+        if (!ok) record_error(S.hdr, TKV_ENOMEM, s);
+        planned = ok;
+      }
+      if (planned) {
+        recs[8 * i] = s;
+        int32_t* cn = cmp_counts(S, s);
+        for (int c = 0; c < 3; c++) {
+          recs[8 * i + 1 + c] = avail[c] - 1 - cum[c];
+          cum[c] += need[c];
+          cn[3 + c] = s_m[i][c];
+        }
+      }
+      for (int c = 0; c < 3; c++) {
+        pre[3 * i + c] = tasks;
+        tasks += planned ? need[c] : 0;
+      }
+    }
+    pre[3 * n] = tasks;
+    // pushes start where the pops ended
+    for (int i = 0; i < n; i++) {
+      const int s = recs[8 * i];
+      if (s < 0) continue;
+      const int32_t* q = S.seq + (int64_t)s * TKV_SEQ_W;
+      int32_t* cn = cmp_counts(S, s);
+      for (int c = 0; c < 3; c++) {
+        recs[8 * i + 4 + c] = avail[c] - cum[c] + pushed[c];
+        cn[c] = q[Q_NBLK + c];
+        pushed[c] += q[Q_NBLK + c];
+      }
+    }
+    int32_t* misc = scr_misc(S.scratch);
+    for (int c = 0; c < 3; c++) misc[8 + c] = avail[c] - cum[c] + pushed[c];
+  }
+}
+
+template <int BITS>
+__device__ void compact_copy_block(const DevState& S, int c, int newb, int cnt, const int32_t* src_slot, int tid) {
+  constexpr int W = 32 / BITS;
+  const int D = S.D, g = S.g, NG = D / g, CB = D * BITS / 32, CW = CB / 4;
+  const int64_t R = pick3(S.bh_bytes, c);
+  uint8_t* pool = pick3(S.pool, c);
+  const int nk = 16 * 4 * CW, nv = 4 * 16 * CW, nm = 16 * 2 * NG, per_head = nk + nv + nm;
+  for (int x = tid; x < S.Hkv * per_head; x += EV_THREADS) {
+    const int h = x / per_head;
+    int u = x % per_head;
+    uint8_t* dst = pool + ((int64_t)newb * S.Hkv + h) * R;
+    if (u < nk) {                              // K chunk word: one token
+      const int td = u / (4 * CW), lg = (u / CW) % 4, wc = u % CW;
+      if (td >= cnt) continue;
+      const int src = src_slot[td], ts = src % TKV_BS;
+      const uint8_t* sr = pool + ((int64_t)(src / TKV_BS) * S.Hkv + h) * R;
+      *(uint32_t*)(dst + chunk_byte(CB, 16 * lg + td, 4 * wc)) = *(const uint32_t*)(sr + chunk_byte(CB, 16 * lg + ts, 4 * wc));
+    } else if ((u -= nk) < nv) {               // V word: a token quad, field by field
+      const int qd = u / (16 * CW), i = (u / CW) % 16, wc = u % CW;
+      uint32_t out = 0;
+      for (int r = 0; r < 4; r++) {
+        const int td = 4 * qd + r;
+        if (td >= cnt) break;
+        const int src = src_slot[td], ts = src % TKV_BS, qs = ts >> 2, rs = ts & 3;
+        const uint8_t* sr = pool + ((int64_t)(src / TKV_BS) * S.Hkv + h) * R;
+        const uint32_t w = *(const uint32_t*)(sr + 64 * CB + chunk_byte(CB, 16 * qs + i, 4 * wc));
+        for (int nn = 0; nn < W / 4; nn++) {
+          const int fs = 4 * nn + rs, fd = 4 * nn + r;
+          const int ps = (fs >> 1) + (fs & 1) * (W >> 1), pd = (fd >> 1) + (fd & 1) * (W >> 1);
+          out |= ((w >> (ps * BITS)) & ((1u << BITS) - 1u)) << (pd * BITS);
+        }
+      }
+      *(uint32_t*)(dst + 64 * CB + chunk_byte(CB, 16 * qd + i, 4 * wc)) = out;
+    } else {                                   // metadata word
+      u -= nv;
+      const int td = u / (2 * NG), kv = (u / NG) % 2, gi = u % NG;
+      if (td >= cnt) continue;
+      const int src = src_slot[td], ts = src % TKV_BS;
+      const uint8_t* sr = pool + ((int64_t)(src / TKV_BS) * S.Hkv + h) * R;
+      *(uint32_t*)(dst + meta_byte(D, g, BITS, kv, td, gi)) = *(const uint32_t*)(sr + meta_byte(D, g, BITS, kv, ts, gi));
+    }
+  }
+}
+
+#define CMP_GRID 1024
+__global__ __launch_bounds__(EV_THREADS) void k_compact_copy(DevState S, int n_cap, const int32_t* n_dev) {
+  __shared__ uint32_t s_bm[CMP_BMW];
+  __shared__ int32_t s_bpre[CMP_BMW];
+  __shared__ int32_t s_pos[EV_MAXSLOT];        // the sort fallback (span above the bitmap)
+  __shared__ int32_t s_slot[EV_MAXSLOT];
+  __shared__ int32_t s_src[TKV_BS], s_spos[TKV_BS];
+  __shared__ int s_tmp[48];
+  __shared__ int s_lo, s_hi, s_cnt;
+  const int tid = threadIdx.x;
+  const int n = eff_count(n_cap, n_dev);
+  const int32_t* pre = cmp_tasks(S);
+  const int total = pre[3 * n];
+  const int32_t* recs = scr_oprec(S.scratch);
+  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+    // the (item, class) of task t: last k with pre[k] <= t (tasks exist only for planned items)
+    int lo = 0, hi = 3 * n;
+    while (hi - lo > 1) { const int mid = (lo + hi) >> 1; if (pre[mid] <= t) lo = mid; else hi = mid; }
+    const int i = lo / 3, c = lo % 3, j = t - pre[lo];
+    const int s = recs[8 * i];
+    const int32_t* q = S.seq + (int64_t)s * TKV_SEQ_W;
+    const int32_t* bt = S.btab + ((int64_t)s * 3 + c) * S.max_blocks;
+    const int nold = q[Q_NBLK + c], m = cmp_counts(S, s)[3 + c];
+    const int cnt = min(TKV_BS, m - TKV_BS * j);
+    const int32_t* blkc = pick3(S.blk, c);
+    const int32_t* slotc = pick3(S.slot, c);
+    // position range of the class's retained tokens
+    if (tid == 0) { s_lo = TKV_INF; s_hi = -1; s_cnt = 0; }
+    __syncthreads();
+    int my_lo = TKV_INF, my_hi = -1;
+    for (int x = tid; x < nold * TKV_BS; x += EV_THREADS) {
+      const int blk = bt[x / TKV_BS], tt = x % TKV_BS;
+      if (!((blkc[(int64_t)blk * TKV_BLK_W] >> tt) & 1)) continue;
+      const int p = slotc[((int64_t)blk * TKV_BS + tt) * 2];
+      my_lo = min(my_lo, p); my_hi = max(my_hi, p);
+    }
+    if (my_hi >= 0) { atomicMin(&s_lo, my_lo); atomicMax(&s_hi, my_hi); }
+    __syncthreads();
+    const int P0 = s_lo, span = s_hi - s_lo + 1;
+    if (span <= CMP_BMW * 32) {
+      // rank by position: bitmap of the positions, prefix counts of its words
+      const int nbw = (span + 31) >> 5;
+      for (int w = tid; w < CMP_BMW; w += EV_THREADS) s_bm[w] = 0;
+      __syncthreads();
+      for (int x = tid; x < nold * TKV_BS; x += EV_THREADS) {
+        const int blk = bt[x / TKV_BS], tt = x % TKV_BS;
+        if (!((blkc[(int64_t)blk * TKV_BLK_W] >> tt) & 1)) continue;
+        const int off = slotc[((int64_t)blk * TKV_BS + tt) * 2] - P0;
+        atomicOr(&s_bm[off >> 5], 1u << (off & 31));
+      }
+      __syncthreads();
+      {
+        int pc[CMP_BMW / EV_THREADS], v[3] = {0, 0, 0}, ex[3], tot[3];
+#pragma unroll
+        for (int u = 0; u < CMP_BMW / EV_THREADS; u++) {
+          const int w = tid * (CMP_BMW / EV_THREADS) + u;
+          pc[u] = w < nbw ? __popc(s_bm[w]) : 0;
+          v[0] += pc[u];
+        }
+        wg_scan3(v, ex, tot, s_tmp);
+        int run = ex[0];
+#pragma unroll
+        for (int u = 0; u < CMP_BMW / EV_THREADS; u++) {
+          s_bpre[tid * (CMP_BMW / EV_THREADS) + u] = run;
+          run += pc[u];
+        }
+      }
+      __syncthreads();
+      for (int x = tid; x < nold * TKV_BS; x += EV_THREADS) {
+        const int blk = bt[x / TKV_BS], tt = x % TKV_BS;
+        if (!((blkc[(int64_t)blk * TKV_BLK_W] >> tt) & 1)) continue;
+        const int p = slotc[((int64_t)blk * TKV_BS + tt) * 2], off = p - P0;
+        const int rk = s_bpre[off >> 5] + __popc(s_bm[off >> 5] & ((1u << (off & 31)) - 1u)) - TKV_BS * j;
+        if (rk >= 0 && rk < cnt) { s_src[rk] = blk * TKV_BS + tt; s_spos[rk] = p; }
+      }
+    } else {
+      // a span above the bitmap: gather and sort
+      for (int x = tid; x < nold * TKV_BS; x += EV_THREADS) {
+        const int blk = bt[x / TKV_BS], tt = x % TKV_BS;
+        if (!((blkc[(int64_t)blk * TKV_BLK_W] >> tt) & 1)) continue;
+        const int at = atomicAdd(&s_cnt, 1);
+        s_pos[at] = slotc[((int64_t)blk * TKV_BS + tt) * 2];
+        s_slot[at] = blk * TKV_BS + tt;
+      }
+      __syncthreads();
+      lds_sort_pairs(s_pos, s_slot, min(s_cnt, EV_MAXSLOT), tid, EV_THREADS);
+      if (tid < cnt) { s_src[tid] = s_slot[TKV_BS * j + tid]; s_spos[tid] = s_pos[TKV_BS * j + tid]; }
+    }
+    __syncthreads();
+    const int newb = pick3(S.freestk, c)[recs[8 * i + 1 + c] - j];
+    if (c == 0) compact_copy_block<8>(S, c, newb, cnt, s_src, tid);
+    else if (c == 1) compact_copy_block<4>(S, c, newb, cnt, s_src, tid);
+    else compact_copy_block<2>(S, c, newb, cnt, s_src, tid);
+    // the new slots' records and the new block's record
+    int32_t* slotw = pick3(S.slot, c);
+    if (tid < cnt) {
+      slotw[((int64_t)newb * TKV_BS + tid) * 2] = s_spos[tid];
+      slotw[((int64_t)newb * TKV_BS + tid) * 2 + 1] = slotc[(int64_t)s_src[tid] * 2 + 1];
+    }
+    if (tid == 0) {
+      int32_t* r = pick3(S.blk, c) + (int64_t)newb * TKV_BLK_W;
+      r[0] = (int)((1u << cnt) - 1u);
+      r[1] = s_spos[cnt - 1];
+      r[2] = s;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(WG) void k_compact_push(DevState S, int n_cap, const int32_t* n_dev) {
+  const int tid = threadIdx.x, NT = blockDim.x;
+  const int n = eff_count(n_cap, n_dev);
+  const int32_t* recs = scr_oprec(S.scratch);
+  // 1. save the old block lists
+  for (int i = 0; i < n; i++) {
+    const int s = recs[8 * i];
+    if (s < 0) continue;
+    const int32_t* cn = cmp_counts(S, s);
+    for (int c = 0; c < 3; c++) {
+      const int32_t* bt = S.btab + ((int64_t)s * 3 + c) * S.max_blocks;
+      int32_t* oldl = cmp_old(S, s, c);
+      for (int j = tid; j < cn[c]; j += NT) oldl[j] = bt[j];
+    }
+  }
+  __syncthreads();
+  // 2. the new block lists (popped entries, read before the pushes overwrite
+  //    them) and slot stacks of the classes that held blocks
+  for (int i = 0; i < n; i++) {
+    const int s = recs[8 * i];
+    if (s < 0) continue;
+    const int32_t* cn = cmp_counts(S, s);
+    int32_t* q = S.seq + (int64_t)s * TKV_SEQ_W;
+    for (int c = 0; c < 3; c++) {
+      if (cn[c] == 0) continue;
+      const int m = cn[3 + c], need = (m + TKV_BS - 1) / TKV_BS;
+      const int used = m % TKV_BS, tail = used ? TKV_BS - used : 0;
+      int32_t* bt = S.btab + ((int64_t)s * 3 + c) * S.max_blocks;
+      const int32_t* fs = pick3(S.freestk, c);
+      for (int j = tid; j < need; j += NT) bt[j] = fs[recs[8 * i + 1 + c] - j];
+      if (tail) {
+        const int last = fs[recs[8 * i + 1 + c] - (need - 1)];
+        int32_t* st = S.sstk + ((int64_t)s * 3 + c) * S.max_blocks * TKV_BS;
+        for (int k = tid; k < tail; k += NT) st[k] = last * TKV_BS + (TKV_BS - 1 - k);
+      }
+      if (tid == 0) { q[Q_NBLK + c] = need; q[Q_NSLOT + c] = tail; }
+    }
+  }
+  __syncthreads();
+  // 3. the old blocks back onto the global stacks, records cleared
+  for (int i = 0; i < n; i++) {
+    const int s = recs[8 * i];
+    if (s < 0) continue;
+    const int32_t* cn = cmp_counts(S, s);
+    for (int c = 0; c < 3; c++) {
+      const int32_t* oldl = cmp_old(S, s, c);
+      for (int j = tid; j < cn[c]; j += NT) {
+        const int b = oldl[j];
+        int32_t* r = pick3(S.blk, c) + (int64_t)b * TKV_BLK_W;
+        r[0] = 0; r[1] = -1; r[2] = -1;
+        pick3(S.freestk, c)[recs[8 * i + 4 + c] + j] = b;
+      }
+    }
+  }
+  if (tid < 3) S.hdr[H_FREE + tid] = scr_misc(S.scratch)[8 + tid];
+}
+
+int launch_compact(tkv_cache* c, int n, const int32_t* n_dev, const int32_t* seq_ids, hipStream_t st) {
+  if (n == 0) return TKV_OK;
+  k_compact_plan<<<1, WG, 0, st>>>(c->S, n, n_dev, seq_ids);
+  k_compact_copy<<<CMP_GRID, EV_THREADS, 0, st>>>(c->S, n, n_dev);
+  k_compact_push<<<1, WG, 0, st>>>(c->S, n, n_dev);
+  return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
+}
+
+// ---------------------------------------------------------------------------
 // Sequence reset: blocks back to the global stacks in list order.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(WG) void k_seq_reset(DevState S, int n, const int32_t* seq_ids) {
