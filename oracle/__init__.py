@@ -44,7 +44,7 @@ class _Layout(C.Structure):
     _fields_ = [("num_kv_heads", C.c_int32), ("num_q_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("group_size", C.c_int32), ("bits", C.c_int32 * 3), ("pool_blocks", C.c_int32 * 3),
                 ("max_seqs", C.c_int32), ("max_blocks_per_seq", C.c_int32),
-                ("max_segments_per_seq", C.c_int32)]
+                ("max_segments_per_seq", C.c_int32), ("num_layers", C.c_int32)]
 
 
 class _State(C.Structure):
@@ -77,7 +77,7 @@ def lib():
         L.ora_compact.argtypes = [P, P, C.c_int, P]; L.ora_compact.restype = None
         L.ora_token_rows.argtypes = [P, P, C.c_int, C.c_int, C.c_int, P, P]; L.ora_token_rows.restype = None
         L.ora_seq_reset.argtypes = [P, P, C.c_int, P]; L.ora_seq_reset.restype = None
-        L.ora_attention.argtypes = [P, P, C.c_int, P, P, P, P, P, P, C.c_int, C.c_int, P, P, P]
+        L.ora_attention.argtypes = [P, P, C.c_int, P, P, P, P, P, P, C.c_int, C.c_int, C.c_int, P, P, P]
         L.ora_attention.restype = None
         L.ora_classify.argtypes = [C.c_int, C.c_int, P, C.c_float, C.c_float, C.c_int, P]
         L.ora_classify.restype = None
@@ -122,16 +122,18 @@ def quantize_group(x: np.ndarray, bits: int):
 # ---------------------------------------------------------------------------
 class OracleLayout:
     def __init__(self, num_kv_heads, num_q_heads, head_dim, group_size, pool_blocks,
-                 max_seqs, max_blocks_per_seq, max_segments_per_seq, bits=(8, 4, 2)):
+                 max_seqs, max_blocks_per_seq, max_segments_per_seq, bits=(8, 4, 2), num_layers=1):
         self.num_kv_heads, self.num_q_heads = int(num_kv_heads), int(num_q_heads)
         self.head_dim, self.group_size = int(head_dim), int(group_size)
         self.bits = tuple(int(b) for b in bits)
         self.pool_blocks = tuple(int(p) for p in pool_blocks)
         self.max_seqs, self.max_blocks_per_seq = int(max_seqs), int(max_blocks_per_seq)
         self.max_segments_per_seq = int(max_segments_per_seq)
+        self.num_layers = max(1, int(num_layers))
+        self.stored_heads = self.num_kv_heads * self.num_layers
         self._c = _Layout(self.num_kv_heads, self.num_q_heads, self.head_dim, self.group_size,
                           (C.c_int32 * 3)(*self.bits), (C.c_int32 * 3)(*self.pool_blocks),
-                          self.max_seqs, self.max_blocks_per_seq, self.max_segments_per_seq)
+                          self.max_seqs, self.max_blocks_per_seq, self.max_segments_per_seq, self.num_layers)
 
     def block_head_bytes(self, c: int) -> int:
         return int(lib().ora_block_head_bytes(C.byref(self._c), c))
@@ -149,7 +151,7 @@ class OracleCache:
         self.bufs = {}
         for c in range(3):
             P = L.pool_blocks[c]
-            self.bufs[f"pool{c}"] = np.zeros(P * L.num_kv_heads * L.block_head_bytes(c), np.uint8)
+            self.bufs[f"pool{c}"] = np.zeros(P * L.stored_heads * L.block_head_bytes(c), np.uint8)
             self.bufs[f"blk{c}"] = np.zeros(P * BLK_W, np.int32)
             self.bufs[f"slot{c}"] = np.zeros(P * BS * SLOT_W, np.int32)
             self.bufs[f"free{c}"] = np.zeros(P, np.int32)
@@ -221,7 +223,7 @@ class OracleCache:
         seq_ids = _arr(seq_ids, np.int32)
         lib().ora_seq_reset(C.byref(self.L._c), C.byref(self._state), seq_ids.size, _p(seq_ids))
 
-    def attention(self, seq_ids, q_pos, q_bf16, k_self=None, v_self=None, sinks=None, window=0, topk=8):
+    def attention(self, seq_ids, q_pos, q_bf16, k_self=None, v_self=None, sinks=None, window=0, topk=8, layer=0):
         L = self.L
         seq_ids = _arr(seq_ids, np.int32); q_pos = _arr(q_pos, np.int32)
         q_bf16 = _arr(q_bf16, np.uint16)
@@ -231,8 +233,8 @@ class OracleCache:
         stats = np.zeros((B, L.num_q_heads, 3), np.float64)
         n_att = np.zeros(B, np.int32)
         lib().ora_attention(C.byref(L._c), C.byref(self._state), B, _p(seq_ids), _p(q_pos), _p(q_bf16),
-                            _p(k_self), _p(v_self), _p(sinks), int(window), int(topk), _p(out), _p(stats),
-                            _p(n_att))
+                            _p(k_self), _p(v_self), _p(sinks), int(window), int(topk), int(layer), _p(out),
+                            _p(stats), _p(n_att))
         return out, stats, n_att
 
     # -- state views -----------------------------------------------------------
@@ -257,7 +259,7 @@ class OracleCache:
         """{position: fp32 [2][Hkv][D] K and V rows} of the retained tokens of sequence s."""
         L = self.L
         q = self.seq_record(s)
-        H, D = L.num_kv_heads, L.head_dim
+        H, D = L.stored_heads, L.head_dim
         out = {}
         for c in range(3):
             bt = self.bufs["btab"][(s * 3 + c) * L.max_blocks_per_seq:][:int(q[c])]

@@ -58,6 +58,7 @@ typedef struct {
   int32_t bits[3];               /* bits for thought type R, E, T */
   int32_t pool_blocks[3];
   int32_t max_seqs, max_blocks_per_seq, max_segments_per_seq;
+  int32_t num_layers;            /* layers sharing block tables and eviction; 0 counts as 1 */
 } ora_layout;
 
 typedef struct {
@@ -131,10 +132,13 @@ static double bf16_to_f64(uint16_t b) {
 static int64_t chunk_bytes(const ora_layout *L, int c) { return (int64_t)L->head_dim * CLASS_BITS[c] / 32; }
 static int64_t codes_bytes(const ora_layout *L, int c) { return 64 * chunk_bytes(L, c); }
 static int64_t meta_bytes(const ora_layout *L) { return (int64_t)BS * (L->head_dim / L->group_size) * 4; }
+/* KV heads stored per block: every layer's (the layers share block tables,
+   segments and eviction, so a token's rows of all layers sit in one slot). */
+int ora_stored_heads(const ora_layout *L) { return L->num_kv_heads * (L->num_layers > 1 ? L->num_layers : 1); }
 int64_t ora_block_head_bytes(const ora_layout *L, int c) { return 2 * codes_bytes(L, c) + 2 * meta_bytes(L); }
 
 static uint8_t *block_head(const ora_layout *L, ora_state *S, int c, int blk, int head) {
-  return S->pool[c] + ((int64_t)blk * L->num_kv_heads + head) * ora_block_head_bytes(L, c);
+  return S->pool[c] + ((int64_t)blk * ora_stored_heads(L) + head) * ora_block_head_bytes(L, c);
 }
 
 /* Bit offset of element e within a chunk of `bits`-wide codes.  Codes are
@@ -359,7 +363,7 @@ static void vacate(const ora_layout *L, ora_state *S, int c, int slot) {
 
 /* ---------------------------------------------------------------------- */
 /* kv_append_quant: tokens applied one by one in list order.               */
-/* k, v: fp32 [n][Hkv][D].  slot_out (nullable): (class << 28) | slot, or  */
+/* k, v: fp32 [n][L][Hkv][D].  slot_out (nullable): (class << 28) | slot, or */
 /* -1 for a token that was not stored.                                     */
 /* Segments (TBE bullet: eviction acts on runs of one thought type): a maximal run of */
 /* consecutively appended tokens of one sequence with the same type (and   */
@@ -372,7 +376,7 @@ static void vacate(const ora_layout *L, ora_state *S, int c, int slot) {
 /* ---------------------------------------------------------------------- */
 void ora_append(const ora_layout *L, ora_state *S, int n, const int32_t *seq_ids, const int32_t *pos,
                 const uint8_t *thought, const float *k, const float *v, int32_t *slot_out) {
-  int H = L->num_kv_heads, D = L->head_dim;
+  int H = ora_stored_heads(L), D = L->head_dim;
   char *failed = calloc((size_t)L->max_seqs, 1);
   int dry[3] = {0, 0, 0};
   for (int i = 0; i < n; i++) {
@@ -444,7 +448,7 @@ static int segment_slots(const ora_layout *L, ora_state *S, int s, int k, int c,
 /* ---------------------------------------------------------------------- */
 void ora_evict(const ora_layout *L, ora_state *S, int n_ops, const int32_t *seq_ids, const int32_t *seg_ids,
                const int32_t *keep_n, const uint8_t *new_bits) {
-  int H = L->num_kv_heads, D = L->head_dim;
+  int H = ora_stored_heads(L), D = L->head_dim;
   char *failed = calloc((size_t)L->max_seqs, 1);
   int dry[3] = {0, 0, 0};
   int32_t *slots = malloc(sizeof(int32_t) * (size_t)L->max_blocks_per_seq * BS);
@@ -601,7 +605,7 @@ static int32_t token_pos(ora_state *S, int c, int slot) { return S->slot[c][slot
 
 static void copy_token(const ora_layout *L, ora_state *S, int c, int src, int dst) {
   int D = L->head_dim, NG = D / L->group_size, bits = CLASS_BITS[c];
-  for (int h = 0; h < L->num_kv_heads; h++) {
+  for (int h = 0; h < ora_stored_heads(L); h++) {
     uint8_t *sb = block_head(L, S, c, src / BS, h), *db = block_head(L, S, c, dst / BS, h);
     int ts = src % BS, td = dst % BS;
     for (int d = 0; d < D; d++) {
@@ -712,6 +716,7 @@ void ora_seq_reset(const ora_layout *L, ora_state *S, int n, const int32_t *seq_
 
 /* ---------------------------------------------------------------------- */
 /* Attention in fp64 over the current state.                               */
+/* One layer per call: the rows of layer `layer` (stored head layer*Hkv+j).*/
 /* For batch entry b (sequence seq_ids[b], query position t = q_pos[b])    */
 /* and query head h (KV head h / (Hq/Hkv)): the attended set A holds every */
 /* valid slot of the sequence in all three classes with pos >= t - W + 1   */
@@ -724,7 +729,7 @@ void ora_seq_reset(const ora_layout *L, ora_state *S, int n, const int32_t *seq_
 /* ---------------------------------------------------------------------- */
 void ora_attention(const ora_layout *L, ora_state *S, int batch, const int32_t *seq_ids, const int32_t *q_pos,
                    const uint16_t *qbf, const float *k_self, const float *v_self, const float *sinks,
-                   int window, int topk, double *out, double *stats, int32_t *n_attended) {
+                   int window, int topk, int layer, double *out, double *stats, int32_t *n_attended) {
   int Hq = L->num_q_heads, Hkv = L->num_kv_heads, D = L->head_dim, G = Hq / Hkv;
   #pragma omp parallel for schedule(dynamic, 1)
   for (int bh = 0; bh < batch * Hkv; bh++) {
@@ -744,8 +749,8 @@ void ora_attention(const ora_layout *L, ora_state *S, int batch, const int32_t *
           int ps = S->slot[c][(blk * BS + tt) * SLOT_W];
           if (window > 0 && ps < t - window + 1) continue;
           for (int d = 0; d < D; d++) {
-            K[(int64_t)n * D + d] = deq64(L, S, c, blk, tt, j, 0, d);
-            V[(int64_t)n * D + d] = deq64(L, S, c, blk, tt, j, 1, d);
+            K[(int64_t)n * D + d] = deq64(L, S, c, blk, tt, layer * Hkv + j, 0, d);
+            V[(int64_t)n * D + d] = deq64(L, S, c, blk, tt, layer * Hkv + j, 1, d);
           }
           n++;
         }

@@ -12,7 +12,7 @@ BS = 16
 def oracle_layout(L: synth.Layout):
     import oracle
     return oracle.OracleLayout(L.num_kv_heads, L.num_q_heads, L.head_dim, L.group_size, L.pool_blocks,
-                               L.max_seqs, L.max_blocks_per_seq, L.max_segments_per_seq, L.bits)
+                               L.max_seqs, L.max_blocks_per_seq, L.max_segments_per_seq, L.bits, L.num_layers)
 
 
 def build_oracle(w: synth.Workload):
@@ -34,7 +34,7 @@ def gpu_layout(L: synth.Layout):
     from thought_adaptive_mixed_amd import binding
     return binding.make_layout(L.num_kv_heads, L.num_q_heads, L.head_dim, L.group_size, L.pool_blocks,
                                L.max_seqs, L.max_blocks_per_seq, L.max_segments_per_seq, L.max_tokens_per_call,
-                               L.bits)
+                               L.bits, L.num_layers)
 
 
 def dev(a, dtype=None):
@@ -100,9 +100,10 @@ def compare_states(L: synth.Layout, g: dict, o: dict, label=""):
         gs, os_ = g[f"slot{c}"].reshape(P, 16, 2), o[f"slot{c}"].reshape(P, 16, 2)
         assert np.array_equal(gs[valid], os_[valid]), f"{label} slot records class {c}"
         # pools: differing bits must all lie outside valid tokens' bits
-        R = g[f"pool{c}"].size // (P * L.num_kv_heads)
-        gp = g[f"pool{c}"].reshape(P, L.num_kv_heads, R)
-        op = o[f"pool{c}"].reshape(P, L.num_kv_heads, R)
+        H = L.num_kv_heads * L.num_layers             # every layer's heads are stored per block
+        R = g[f"pool{c}"].size // (P * H)
+        gp = g[f"pool{c}"].reshape(P, H, R)
+        op = o[f"pool{c}"].reshape(P, H, R)
         diff = gp ^ op
         rows = np.nonzero(diff.reshape(P, -1).any(1))[0]
         if rows.size:

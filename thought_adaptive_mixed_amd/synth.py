@@ -62,6 +62,7 @@ class Layout:
     max_segments_per_seq: int
     max_tokens_per_call: int = 4096
     bits: Tuple[int, int, int] = (8, 4, 2)
+    num_layers: int = 1                  # layers sharing block tables and eviction
 
 
 @dataclasses.dataclass
@@ -106,7 +107,7 @@ class Workload:
 
 def draw_kv(seed, n, layout: Layout, outlier_k, outlier_v):
     rng = np.random.default_rng(list(seed))
-    H, D = layout.num_kv_heads, layout.head_dim
+    H, D = layout.num_kv_heads * layout.num_layers, layout.head_dim     # every layer's rows
     k = rng.standard_normal((n, H * D), dtype=np.float32)
     v = rng.standard_normal((n, H * D), dtype=np.float32)
     if outlier_k is not None and outlier_k.size:
@@ -363,6 +364,28 @@ def small_static(seed=77, B=3, Hq=8, Hkv=2, D=128, g=64, L=900, frac=0.3, sinks=
     w = _static("small", seed, B, Hq, Hkv, D, g, lengths, n, permute=permute, sinks=sinks, windows=windows,
                 max_call=256, slack_blocks=4)
     return w
+
+
+def layered(w: Workload, num_layers: int) -> Workload:
+    """The workload with num_layers layers sharing its block tables: the same
+    appends, evictions and queries, K/V rows drawn for every layer, the
+    outlier channels repeated in each layer."""
+    H, D = w.layout.num_kv_heads, w.layout.head_dim
+    w = dataclasses.replace(w, layout=dataclasses.replace(w.layout, num_layers=num_layers))
+    if w.outlier_k is not None and w.outlier_k.size:
+        w.outlier_k = np.concatenate([w.outlier_k + l * H * D for l in range(num_layers)])
+        w.outlier_v = np.concatenate([w.outlier_v + l * H * D for l in range(num_layers)])
+    return w
+
+
+def layer_queries(w: Workload, layer: int, beta=1.0) -> np.ndarray:
+    """Seeded bf16 queries [B][Hq][D] of one layer (layer 0: the workload's own)."""
+    if layer == 0:
+        return w.q_bf16
+    L = w.layout
+    rng = np.random.default_rng([w.seed, 50000 + layer])
+    return queries(rng, w.seq_ids.size, L.num_q_heads, L.head_dim,
+                   np.full(w.seq_ids.size, beta, np.float32))
 
 
 # ---------------------------------------------------------------------------
