@@ -24,6 +24,7 @@ Prints ONE JSON line (see the fields below).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -180,6 +181,11 @@ def cpu_baseline(w, state, ch, n_seq, budget_s=12.0, max_reps=1000, policy="ladd
 
 
 def workload_name(args):
+    return workload_name_1(args) + (f"; {args.layers} layers per step sharing the block tables (each layer holds the "
+                                    f"one-layer state's records)" if args.layers > 1 else "")
+
+
+def workload_name_1(args):
     if args.workload == "llama8b":
         head = "llama8b-like reasoning decode, one layer: B32, Hq32/Hkv8, D128, g64, "
         if args.policy == "ladder":
@@ -208,6 +214,8 @@ def main():
     ap.add_argument("--r0", type=int, default=64, help="first retention of the annealing schedule")
     ap.add_argument("--compact", action="store_true",
                     help="compact the sequences each step evicted from (gather-compaction baseline)")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="layers per decode step sharing the block tables (the one-layer state replicated)")
     ap.add_argument("--workload", choices=("llama8b", "churn256"), default="llama8b",
                     help="the llama8b-like layer (B32, 16k, 10%% budget) or the B256 decode loop (4k..32k, 5%% budget)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -260,10 +268,28 @@ def main():
             c0.compact(dv0([s]))
         torch.cuda.synchronize()
     state = c0.export()
-    caches = [c0] + [binding.Cache(helpers.gpu_layout(L), w.block_order) for _ in range(R - 1)]
-    for c in caches[1:]:
-        c.import_(state)
-    tok_c, blk_c = state_class_tokens(state, L)
+    NL = max(1, args.layers)
+    if NL > 1:
+        # every layer of the layered cache holds the one-layer state's records (same bytes and work per layer)
+        state1 = state
+        state = dict(state1)
+        for cc in range(3):
+            P = L.pool_blocks[cc]
+            state[f"pool{cc}"] = np.repeat(state1[f"pool{cc}"].reshape(P, 1, -1), NL, axis=1).ravel()
+        del c0
+        L = dataclasses.replace(L, num_layers=NL)
+        sizes = binding.buffer_sizes(helpers.gpu_layout(L))
+        R = args.copies or max(2, math.ceil((1 << 30) / sum(sizes[:-1])))
+        caches = [binding.Cache(helpers.gpu_layout(L), w.block_order) for _ in range(R)]
+        for c in caches:
+            c.import_(state)
+        log(f"[bench] {NL} layers: state {sum(sizes[:-1]) / 1e6:.1f} MB, {R} copies")
+        state = state1
+    else:
+        caches = [c0] + [binding.Cache(helpers.gpu_layout(L), w.block_order) for _ in range(R - 1)]
+        for c in caches[1:]:
+            c.import_(state)
+    tok_c, blk_c = state_class_tokens(state, dataclasses.replace(L, num_layers=1))
     abytes, kvbytes = algorithmic_bytes(tok_c, blk_c, L, B)
     log(f"[bench] built in {time.time() - t0:.1f} s; algorithmic bytes per attention call {abytes / 1e6:.2f} MB")
 
@@ -277,13 +303,16 @@ def main():
     per_copy = []
     for i in range((total_steps + R - 1) // R):
         q, k, v, pos = ch.step_inputs(i)
-        per_copy.append((dv(q, np.uint16), dv(k, np.float32), dv(v, np.float32), dv(pos, np.int32)))
+        # with layers: each layer attends with the same query and self-token rows; the append takes every layer's
+        kl, vl = np.tile(k, (1, NL, 1)), np.tile(v, (1, NL, 1))
+        per_copy.append((dv(q, np.uint16), dv(k, np.float32), dv(v, np.float32), dv(pos, np.int32),
+                         dv(kl, np.float32) if NL > 1 else None, dv(vl, np.float32) if NL > 1 else None))
     steps_in = [per_copy[s // R] for s in range(total_steps)]
     Hq, D = L.num_q_heads, L.head_dim
     out = torch.empty(B, Hq, D, dtype=torch.float32, device="cuda")
-    stats = torch.empty(B, Hq, 3, dtype=torch.float32, device="cuda")
+    stats = torch.empty(B, NL, Hq, 3, dtype=torch.float32, device="cuda")   # every layer's rows of a step
     n_att = torch.zeros(total_steps, B, dtype=torch.int32, device="cuda")   # one row per step
-    ws = torch.empty(c0.workspace_bytes(B), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(caches[0].workspace_bytes(B), 16), dtype=torch.uint8, device="cuda")
     labels = torch.empty(B, dtype=torch.uint8, device="cuda")
     max_ops = 256
     n_ops = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -297,12 +326,13 @@ def main():
     calls_a, calls_b = [], []
     for s in range(total_steps):
         c = caches[s % R]
-        q, k, v, pos = steps_in[s]
-        calls_a.append(c.attention(seq_d, pos, q, out, ws, stats=stats, n_attended=n_att[s], k_self=k, v_self=v,
-                                   stream=sh, prepare=True))
+        q, k, v, pos, kl, vl = steps_in[s]
+        calls_a.append([c.attention(seq_d, pos, q, out, ws, stats=stats[:, l], n_attended=n_att[s], k_self=k,
+                                    v_self=v, layer=l, stats_stride=NL * Hq * 3, stream=sh, prepare=True)
+                        for l in range(NL)])
         calls_b.append([
-            binding.classify(stats, ch.tau[0], ch.tau[1], labels, stream=sh, prepare=True),
-            c.append(seq_d, pos, labels, k, v, stream=sh, prepare=True),
+            binding.classify(stats.view(B, NL * Hq, 3), ch.tau[0], ch.tau[1], labels, stream=sh, prepare=True),
+            c.append(seq_d, pos, labels, kl if NL > 1 else k, vl if NL > 1 else v, stream=sh, prepare=True),
             (c.plan_anneal(seq_d, args.r0, max_ops, n_ops, o_seq, o_seg, o_keep, o_bits, stream=sh, prepare=True)
              if args.policy == "anneal" else
              c.plan_budget(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, o_seq, o_seg, o_keep, o_bits,
@@ -315,7 +345,8 @@ def main():
     # attention launch is bracketed by events on the same stream.
     def step(s):
         ev.record(2 * s, sh)
-        calls_a[s]()
+        for f in calls_a[s]:
+            f()
         ev.record(2 * s + 1, sh)
         if not args.attn_only:
             for f in calls_b[s]:
@@ -351,14 +382,15 @@ def main():
     errs = [c.get_error() for c in caches]
     if any(e[0] for e in errs):
         log(f"[bench] WARNING device errors: {errs}")
-    tokens = int(n_att[args.warmup:].sum().item())
+    tokens1 = int(n_att[args.warmup:].sum().item())        # one layer's attended tokens
+    tokens = tokens1 * NL                                   # KV tokens attended over all layers
     ms_step = ms_total / args.steps
-    attn_avg = float(np.mean(attn_ms))
+    attn_avg = float(np.mean(attn_ms))                      # every layer's attention of a step
     # the cache changes a little from step to step (appends, evictions): scale
     # the KV part of the byte count by the attended tokens actually seen
     init_tokens = int(tok_c[:B].sum())
-    abytes_step = abytes - kvbytes + kvbytes * (tokens / args.steps) / max(init_tokens, 1)
-    achieved = abytes_step / (attn_avg * 1e-3) / 1e9
+    abytes_step = abytes - kvbytes + kvbytes * (tokens1 / args.steps) / max(init_tokens, 1)
+    achieved = abytes_step / (attn_avg / NL * 1e-3) / 1e9
     result = {
         "metric": METRIC,
         "value": tokens / (ms_total * 1e-3),
@@ -374,14 +406,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload_name(args),
                    "batch": B, "copies": R, "attended_per_step": tokens / args.steps,
-                   "launch": "eager, one stream"},
+                   "launch": "eager, one stream", **({"layers": NL} if NL > 1 else {})},
         "attn_ms": attn_avg,
         "attn_kv_tokens_per_s": (tokens / args.steps) / (attn_avg * 1e-3),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic() if (args.workload == "llama8b" and args.policy == "ladder"
-                                                       and not args.compact) else None,
-                     "kernel": "k_attn (paged_decode_attn; one launch per step)",
+                                                       and not args.compact and NL == 1) else None,
+                     "kernel": "k_attn (paged_decode_attn; one launch per layer and step)",
                      "bytes_per_launch": abytes_step},
     }
     if not args.no_cpu_baseline:

@@ -34,9 +34,11 @@
  * State format (the buffers, all little-endian):
  *   Three precision classes c = 0, 1, 2 hold 8-, 4- and 2-bit codes.  Each
  *   class has a pool of `pool_blocks[c]` blocks; a block holds 16 token slots
- *   of every KV head.  Slot id = block * 16 + slot-in-block.
- *   POOLc  u8  [pool_blocks[c]][Hkv][R_c] with R_c = 4*D*bits_c + 128*(D/g):
- *          per (block, KV head): K codes (64 chunks of D*bits/32 bytes), V
+ *   of every layer and KV head (the L layers share block tables, segments and
+ *   eviction: a token is stored, evicted, moved for all layers at once).  Slot
+ *   id = block * 16 + slot-in-block.
+ *   POOLc  u8  [pool_blocks[c]][L][Hkv][R_c] with R_c = 4*D*bits_c + 128*(D/g):
+ *          per (block, layer, KV head): K codes (64 chunks of D*bits/32 bytes), V
  *          codes (64 chunks), K meta, V meta.  Meta = fp16 (scale, zero) per
  *          (token, group), token-major.  K code of token t, dim d: chunk
  *          16*lg + t, element gi*(g/4) + e' with gi = d/g, lg = (d%g)/(g/4),
@@ -103,6 +105,7 @@ typedef struct {
   int32_t max_blocks_per_seq;     /* per class, 1..256                         */
   int32_t max_segments_per_seq;   /* >= 1                                      */
   int32_t max_tokens_per_call;    /* bound on items per append/evict/plan call, 1..4096 */
+  int32_t num_layers;             /* L: layers sharing the block tables, 1..64 (0 counts as 1) */
 } tkv_layout;
 
 /* Byte sizes of the TKV_NUM_BUFFERS buffers for layout L_h.  EINVAL for a
@@ -130,10 +133,10 @@ int tkv_seq_reset(tkv_cache* c, int32_t n, const int32_t* seq_ids, hipStream_t s
  * token overwrites an evicted slot of its precision class in place).
  *   seq_ids i32[n], positions i32[n] (strictly increasing per sequence, at
  *   least the sequence's length), thought u8[n] (TKV_R/E/T), k and v fp32
- *   [n][Hkv][D] rows.  Tokens are applied in list order: each pops its
- *   (sequence, class) free-slot stack, refilled with a fresh block from the
- *   class's global stack when empty; each (token, head, tensor, group of g
- *   dims) is quantized to bits_c asymmetric codes with an fp16 scale
+ *   [n][L][Hkv][D] rows (every layer's rows of the token).  Tokens are
+ *   applied in list order: each pops its (sequence, class) free-slot stack,
+ *   refilled with a fresh block from the class's global stack when empty;
+ *   each (token, layer, head, tensor, group of g dims) is quantized to bits_c asymmetric codes with an fp16 scale
  *   (max-min)/(2^bits-1) and fp16 zero-point min, codes rounded half-even and
  *   clamped.  A token opens a new segment when its type differs from the open
  *   segment's (or that segment was downgraded).
@@ -221,13 +224,18 @@ int tkv_compact(tkv_cache* c, int32_t n, const int32_t* n_dev, const int32_t* se
 /* paged_decode_attn -- one decode step of attention over the mixed-precision,
  * hole-bearing cache (abstract: a kernel extending PagedAttention that reuses
  * evicted slots), with the sparsity statistics that assign the thought type
- * (thought decomposition bullets).  For batch entry b and query head h (KV
- * head h / (Hq/Hkv)): attend every valid slot of sequence seq_ids[b] in all
+ * (thought decomposition bullets).  One layer per call (`layer`): for batch
+ * entry b and query head h (KV head h / (Hq/Hkv) of that layer): attend every valid slot of sequence seq_ids[b] in all
  * three classes (with position >= q_pos[b] - window + 1 when window > 0) plus
  * the unquantized self token when k_self is given; logits q.k/sqrt(D);
  * out = sum e^(l-m) v / (sum e^(l-m) + [sinks] e^(sinks[h]-m)).
  * Statistics over the tokens only (sink excluded): H = -sum p ln p, H/ln n
- * (0 if n < 2), and the mass of the min(topk, n) largest p. */
+ * (0 if n < 2), and the mass of the min(topk, n) largest p.  With
+ * stats_stride = L*Hq*3 and stats advanced by layer*Hq*3, the L calls of a
+ * step fill one [batch][L][Hq][3] array that thought_classify can average
+ * over all layers (num_q_heads = L*Hq).
+ *   EINVAL (besides the shapes): layer outside [0, L), stats_stride neither 0
+ *   nor >= Hq*3. */
 typedef struct {
   int32_t batch;              /* entries, <= max_seqs                              */
   const int32_t* seq_ids;     /* i32[batch]                                        */
@@ -244,6 +252,8 @@ typedef struct {
   int32_t* n_attended;        /* nullable i32[batch]                               */
   void* workspace;            /* >= tkv_attn_workspace(c, batch, num_splits) bytes; nullable when that is 0 */
   size_t workspace_bytes;
+  int32_t layer;              /* 0..L-1: the layer whose K/V are attended                  */
+  int32_t stats_stride;       /* floats between batch entries of stats; 0 = Hq*3, else >= Hq*3 */
 } tkv_attn_args;
 
 /* Workspace bytes paged_decode_attn needs for `batch` entries and the given

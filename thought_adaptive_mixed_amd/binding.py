@@ -33,7 +33,8 @@ class Layout(C.Structure):
     _fields_ = [("num_kv_heads", C.c_int32), ("num_q_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("group_size", C.c_int32), ("bits", C.c_int32 * 3), ("pool_blocks", C.c_int32 * 3),
                 ("max_seqs", C.c_int32), ("max_blocks_per_seq", C.c_int32),
-                ("max_segments_per_seq", C.c_int32), ("max_tokens_per_call", C.c_int32)]
+                ("max_segments_per_seq", C.c_int32), ("max_tokens_per_call", C.c_int32),
+                ("num_layers", C.c_int32)]
 
 
 class AttnArgs(C.Structure):
@@ -41,7 +42,8 @@ class AttnArgs(C.Structure):
                 ("k_self", C.c_void_p), ("v_self", C.c_void_p), ("sinks", C.c_void_p),
                 ("window", C.c_int32), ("topk", C.c_int32), ("num_splits", C.c_int32),
                 ("out", C.c_void_p), ("stats", C.c_void_p), ("n_attended", C.c_void_p),
-                ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
+                ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t), ("layer", C.c_int32),
+                ("stats_stride", C.c_int32)]
 
 
 class TkvError(RuntimeError):
@@ -141,10 +143,10 @@ def _issue(fn, args, what, prepare, keep=None):
 
 
 def make_layout(num_kv_heads, num_q_heads, head_dim, group_size, pool_blocks, max_seqs, max_blocks_per_seq,
-                max_segments_per_seq, max_tokens_per_call=4096, bits=(8, 4, 2)) -> Layout:
+                max_segments_per_seq, max_tokens_per_call=4096, bits=(8, 4, 2), num_layers=1) -> Layout:
     return Layout(num_kv_heads, num_q_heads, head_dim, group_size, (C.c_int32 * 3)(*bits),
                   (C.c_int32 * 3)(*pool_blocks), max_seqs, max_blocks_per_seq, max_segments_per_seq,
-                  max_tokens_per_call)
+                  max_tokens_per_call, num_layers)
 
 
 def buffer_sizes(layout: Layout):
@@ -228,10 +230,11 @@ class Cache:
         return int(self.L.tkv_attn_workspace(self.h, int(batch), int(num_splits)))
 
     def attention(self, seq_ids, q_pos, q, out, workspace, stats=None, n_attended=None, k_self=None, v_self=None,
-                  sinks=None, window=0, topk=8, num_splits=0, *, stream=None, prepare=False):
+                  sinks=None, window=0, topk=8, num_splits=0, layer=0, stats_stride=0, *, stream=None, prepare=False):
         a = AttnArgs(int(seq_ids.numel()), _ptr(seq_ids), _ptr(q_pos), _ptr(q), _ptr(k_self), _ptr(v_self),
                      _ptr(sinks), int(window), int(topk), int(num_splits), _ptr(out), _ptr(stats), _ptr(n_attended),
-                     _ptr(workspace), int(workspace.numel() * workspace.element_size()))
+                     _ptr(workspace), int(workspace.numel() * workspace.element_size()), int(layer),
+                     int(stats_stride))
         args = (self.h, C.byref(a), _stream(stream))
         return _issue(self.L.paged_decode_attn, args, "paged_decode_attn", prepare, keep=a)
 
@@ -257,7 +260,8 @@ class Cache:
 
 
 def classify(stats, tau_T, tau_E, labels_out, score_kind=0, *, stream=None, prepare=False):
-    B, Hq = int(stats.shape[0]), int(stats.shape[1])
+    B = int(stats.shape[0])
+    Hq = int(stats.numel()) // (3 * B) if B else 0          # every head of every layer in the rows
     args = (B, Hq, _ptr(stats), C.c_float(tau_T), C.c_float(tau_E), int(score_kind), _ptr(labels_out),
             _stream(stream))
     return _issue(load().thought_classify, args, "thought_classify", prepare)

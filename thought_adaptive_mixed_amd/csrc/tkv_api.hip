@@ -22,6 +22,7 @@ static int layout_ok(const tkv_layout* L) {
   if (L->max_blocks_per_seq < 1 || L->max_blocks_per_seq > TKV_MAX_BLOCKS) return 0;
   if (L->max_segments_per_seq < 1) return 0;
   if (L->max_tokens_per_call < 1 || L->max_tokens_per_call > TKV_MAX_TOK) return 0;
+  if (L->num_layers < 0 || L->num_layers > 64) return 0;
   return 1;
 }
 
@@ -33,7 +34,8 @@ extern "C" int tkv_buffer_sizes(const tkv_layout* L, size_t sizes[TKV_NUM_BUFFER
   if (!layout_ok(L) || !sizes) return TKV_EINVAL;
   for (int c = 0; c < 3; c++) {
     const size_t P = (size_t)L->pool_blocks[c];
-    sizes[TKV_BUF_POOL0 + c] = P * L->num_kv_heads * (size_t)bh_bytes(L, c);
+    sizes[TKV_BUF_POOL0 + c] = P * (size_t)(L->num_layers > 1 ? L->num_layers : 1) * L->num_kv_heads *
+                               (size_t)bh_bytes(L, c);
     sizes[TKV_BUF_BLK0 + c] = P * TKV_BLK_W * 4;
     sizes[TKV_BUF_SLOT0 + c] = P * TKV_BS * TKV_SLOT_W * 4;
     sizes[TKV_BUF_FREE0 + c] = P * 4;
@@ -96,6 +98,8 @@ extern "C" int tkv_create(const tkv_layout* L, void* const bufs[TKV_NUM_BUFFERS]
   S.scratch = (int32_t*)bufs[TKV_BUF_SCRATCH];
   S.Hkv = L->num_kv_heads; S.Hq = L->num_q_heads; S.D = L->head_dim; S.g = L->group_size;
   S.NG = L->head_dim / L->group_size;
+  S.NL = L->num_layers > 1 ? L->num_layers : 1;
+  S.Hst = S.NL * S.Hkv;
   S.max_seqs = L->max_seqs; S.max_blocks = L->max_blocks_per_seq; S.max_segs = L->max_segments_per_seq;
   S.max_tokens = L->max_tokens_per_call;
   c->last_stream = stream;
@@ -178,6 +182,8 @@ extern "C" int paged_decode_attn(tkv_cache* c, const tkv_attn_args* a, hipStream
   if (!c || !a) return TKV_EINVAL;
   if (a->batch < 0 || a->batch > c->S.max_seqs) return TKV_EINVAL;
   if (a->topk < 1 || a->topk > 8 || a->window < 0 || a->num_splits < 0 || a->num_splits > 64) return TKV_EINVAL;
+  if (a->layer < 0 || a->layer >= c->S.NL) return TKV_EINVAL;
+  if (a->stats_stride != 0 && a->stats_stride < c->S.Hq * 3) return TKV_EINVAL;
   if (a->batch > 0 && (!a->seq_ids || !a->q_pos || !a->q || !a->out)) return TKV_EINVAL;
   if ((a->k_self == nullptr) != (a->v_self == nullptr)) return TKV_EINVAL;
   int nw, s;

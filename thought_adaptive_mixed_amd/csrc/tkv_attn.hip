@@ -148,6 +148,8 @@ struct AttnParams {
   const float* v_self;
   const float* sinks;
   int window, splits, topk;
+  int layer;                   // the layer attended: KV heads layer*Hkv.. of each block
+  int stats_stride;            // floats between batch entries of stats
   float* part;                 // [batch][Hq][splits][D + PART_X]
   float* out;
   float* stats;
@@ -503,17 +505,19 @@ __device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax
   const int32_t* slt0 = P.S.slot[0];
   const int32_t* slt1 = P.S.slot[1];
   const int32_t* slt2 = P.S.slot[2];
-  const int64_t Hkv = P.S.Hkv;
+  // a block stores every layer's KV heads: this layer's head kvh is head
+  // layer*Hkv + kvh of Hst per block
+  const int64_t Hst = P.S.Hst, hk = (int64_t)P.layer * P.S.Hkv + kvh;
   const int64_t R0 = P.S.bh_bytes[0], R1 = P.S.bh_bytes[1], R2 = P.S.bh_bytes[2];
-  const uint8_t* pk0 = pool0 + kvh * R0;
-  const uint8_t* pk1 = pool1 + kvh * R1;
-  const uint8_t* pk2 = pool2 + kvh * R2;
+  const uint8_t* pk0 = pool0 + hk * R0;
+  const uint8_t* pk1 = pool1 + hk * R1;
+  const uint8_t* pk2 = pool2 + hk * R2;
   auto load = [&](B& b, int g) {
     const bool pad = g >= T;
     g = pad ? T - 1 : g;
-    if (g < c1) load_step<D, GS, WINDOW, PK, 0>(b, pk0, Hkv * R0, slt0, l0, n0, g, lane, pad);
-    else if (g < c2) load_step<D, GS, WINDOW, PK, 1>(b, pk1, Hkv * R1, slt1, l1, n1, g - c1, lane, pad);
-    else load_step<D, GS, WINDOW, PK, 2>(b, pk2, Hkv * R2, slt2, l2, n2, g - c2, lane, pad);
+    if (g < c1) load_step<D, GS, WINDOW, PK, 0>(b, pk0, Hst * R0, slt0, l0, n0, g, lane, pad);
+    else if (g < c2) load_step<D, GS, WINDOW, PK, 1>(b, pk1, Hst * R1, slt1, l1, n1, g - c1, lane, pad);
+    else load_step<D, GS, WINDOW, PK, 2>(b, pk2, Hst * R2, slt2, l2, n2, g - c2, lane, pad);
   };
   auto mask_of = [&](const int2* lv, int n, int sigma) -> uint32_t {
     const int e = sigma * PK + jl;                  // this lane's block
@@ -659,7 +663,7 @@ __device__ inline void finalize_head(const AttnParams& P, int b, int hq, int lan
     n += 1;
   }
   float* out = P.out + ((int64_t)b * S.Hq + hq) * D;
-  float* st = P.stats ? P.stats + ((int64_t)b * S.Hq + hq) * 3 : nullptr;
+  float* st = P.stats ? P.stats + (int64_t)b * P.stats_stride + hq * 3 : nullptr;
   if (n == 0) {
     out[lane] = 0.f;
     if (D > 64) out[lane + 64] = 0.f;
@@ -1009,6 +1013,7 @@ int launch_attention(tkv_cache* c, const tkv_attn_args* a, int nw, int splits, h
   P.S = c->S; P.seq_ids = a->seq_ids; P.q_pos = a->q_pos; P.q = a->q;
   P.k_self = a->k_self; P.v_self = a->v_self; P.sinks = a->sinks;
   P.window = a->window; P.splits = splits; P.topk = a->topk;
+  P.layer = a->layer; P.stats_stride = a->stats_stride ? a->stats_stride : c->S.Hq * 3;
   P.part = (float*)a->workspace; P.out = a->out; P.stats = a->stats; P.n_attended = a->n_attended;
   const int D = c->S.D, g = c->S.g, lds = lds_bytes(c, nw);
   const bool win = a->window > 0;

@@ -36,6 +36,7 @@ struct DevState {
   int32_t* segt;
   int32_t* scratch;
   int Hkv, Hq, D, g, NG;
+  int NL, Hst;                    // layers; KV heads stored per block (NL * Hkv)
   int type_class[3];              // class index for thought type R, E, T
   int pool_blocks[3];
   int max_seqs, max_blocks, max_segs, max_tokens;

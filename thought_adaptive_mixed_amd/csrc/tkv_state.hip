@@ -431,7 +431,7 @@ __device__ void quant_row_wave(const DevState& S, int c, int blk, int t, int h, 
   const float sf = f16_bits_to_f32(sh), zf = f16_bits_to_f32(zh);
 #pragma unroll
   for (int e = 0; e < E; e++) codes[lane * E + e] = (uint8_t)quant_code(x[e], sf, zf, bits);
-  uint8_t* base = pick3(S.pool, c) + ((int64_t)blk * S.Hkv + h) * pick3(S.bh_bytes, c);
+  uint8_t* base = pick3(S.pool, c) + ((int64_t)blk * S.Hst + h) * pick3(S.bh_bytes, c);
   if ((lane * E) % g == 0) *(uint32_t*)(base + meta_byte(D, g, bits, kv, t, gi)) = (uint32_t)sh | ((uint32_t)zh << 16);
   wave_lds_sync();
   const int W = 32 / bits;
@@ -484,12 +484,12 @@ __global__ __launch_bounds__(256) void k_append_store(DevState S, int n, const f
   __shared__ uint8_t s_codes[4][128];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + wv;
-  if (row >= (int64_t)n * S.Hkv * 2) return;
+  if (row >= (int64_t)n * S.Hst * 2) return;
   const int kv = (int)(row & 1);
-  const int h = (int)((row >> 1) % S.Hkv);
-  const int i = (int)((row >> 1) / S.Hkv);
+  const int h = (int)((row >> 1) % S.Hst);
+  const int i = (int)((row >> 1) / S.Hst);
   // the row's values do not depend on the slot: read them first
-  const float* src = (kv ? v : k) + ((int64_t)i * S.Hkv + h) * S.D + lane * E;
+  const float* src = (kv ? v : k) + ((int64_t)i * S.Hst + h) * S.D + lane * E;
   float x[E];
 #pragma unroll
   for (int e = 0; e < E; e++) x[e] = src[e];
@@ -503,7 +503,7 @@ int launch_append(tkv_cache* c, int n, const int32_t* seq_ids, const int32_t* po
                   const float* k, const float* v, int32_t* slot_out, hipStream_t st) {
   if (n == 0) return TKV_OK;
   k_append_alloc<<<1, walker_threads(c->S.max_seqs), 0, st>>>(c->S, n, seq_ids, pos, thought, slot_out);
-  const int64_t rows = (int64_t)n * c->S.Hkv * 2;
+  const int64_t rows = (int64_t)n * c->S.Hst * 2;
   const int blocks = (int)((rows + 3) / 4);
   if (c->S.D == 128) k_append_store<2><<<blocks, 256, 0, st>>>(c->S, n, k, v);
   else k_append_store<1><<<blocks, 256, 0, st>>>(c->S, n, k, v);
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(WG) void k_evict_plan(DevState S, int n_cap, const 
 __device__ float deq_code(const DevState& S, int c, int blk, int t, int h, int kv, int d) {
 #pragma clang fp contract(off)
   const int bits = class_bits(c);
-  const uint8_t* base = pick3(S.pool, c) + ((int64_t)blk * S.Hkv + h) * pick3(S.bh_bytes, c);
+  const uint8_t* base = pick3(S.pool, c) + ((int64_t)blk * S.Hst + h) * pick3(S.bh_bytes, c);
   int bit = kv ? v_code_bit(S.D, bits, t, d) : k_code_bit(S.D, S.g, bits, t, d);
   uint32_t word = *(const uint32_t*)(base + ((bit >> 5) << 2));
   unsigned code = (word >> (bit & 31)) & ((1u << bits) - 1u);
@@ -771,11 +771,11 @@ __global__ __launch_bounds__(RQ_THREADS) void k_requant(DevState S) {
   for (int i = lo; i < hi; i++) { s_off[i] = run; run += mcnt[i]; }
   if (tid == 0) s_off[S.max_seqs] = tot[0];
   __syncthreads();
-  const int total_rows = tot[0] * S.Hkv * 2;
+  const int total_rows = tot[0] * S.Hst * 2;
   const int wv = tid >> 6, lane = tid & 63;
   const int nwaves = gridDim.x * (RQ_THREADS / 64);
   for (int row = blockIdx.x * (RQ_THREADS / 64) + wv; row < total_rows; row += nwaves) {
-    const int kv = row & 1, h = (row >> 1) % S.Hkv, mv = (row >> 1) / S.Hkv;
+    const int kv = row & 1, h = (row >> 1) % S.Hst, mv = (row >> 1) / S.Hst;
     // sequence owning move mv: last s with s_off[s] <= mv
     int a = 0, b = S.max_seqs;
     while (b - a > 1) { const int mid = (a + b) >> 1; if (s_off[mid] <= mv) a = mid; else b = mid; }
@@ -1046,8 +1046,8 @@ __global__ __launch_bounds__(EV_THREADS) void k_evict_apply(DevState S) {
         nmoves += keep;
       } else {
         const int wv = tid >> 6, lane = tid & 63;
-        for (int row = wv; row < keep * S.Hkv * 2; row += EV_THREADS / 64) {
-          const int kv = row & 1, h = (row >> 1) % S.Hkv, p = (row >> 1) / S.Hkv;
+        for (int row = wv; row < keep * S.Hst * 2; row += EV_THREADS / 64) {
+          const int kv = row & 1, h = (row >> 1) % S.Hst, p = (row >> 1) / S.Hst;
           int ns;
           if (p < S0) ns = st2[S0 - 1 - p];
           else { int pp = p - S0; ns = bt[c2 * S.max_blocks + nbk2 + pp / TKV_BS] * TKV_BS + pp % TKV_BS; }
@@ -1485,15 +1485,15 @@ __device__ void compact_copy_block(const DevState& S, int c, int newb, int cnt, 
   const int64_t R = pick3(S.bh_bytes, c);
   uint8_t* pool = pick3(S.pool, c);
   const int nk = 16 * 4 * CW, nv = 4 * 16 * CW, nm = 16 * 2 * NG, per_head = nk + nv + nm;
-  for (int x = tid; x < S.Hkv * per_head; x += EV_THREADS) {
+  for (int x = tid; x < S.Hst * per_head; x += EV_THREADS) {
     const int h = x / per_head;
     int u = x % per_head;
-    uint8_t* dst = pool + ((int64_t)newb * S.Hkv + h) * R;
+    uint8_t* dst = pool + ((int64_t)newb * S.Hst + h) * R;
     if (u < nk) {                              // K chunk word: one token
       const int td = u / (4 * CW), lg = (u / CW) % 4, wc = u % CW;
       if (td >= cnt) continue;
       const int src = src_slot[td], ts = src % TKV_BS;
-      const uint8_t* sr = pool + ((int64_t)(src / TKV_BS) * S.Hkv + h) * R;
+      const uint8_t* sr = pool + ((int64_t)(src / TKV_BS) * S.Hst + h) * R;
       *(uint32_t*)(dst + chunk_byte(CB, 16 * lg + td, 4 * wc)) = *(const uint32_t*)(sr + chunk_byte(CB, 16 * lg + ts, 4 * wc));
     } else if ((u -= nk) < nv) {               // V word: a token quad, field by field
       const int qd = u / (16 * CW), i = (u / CW) % 16, wc = u % CW;
@@ -1502,7 +1502,7 @@ __device__ void compact_copy_block(const DevState& S, int c, int newb, int cnt, 
         const int td = 4 * qd + r;
         if (td >= cnt) break;
         const int src = src_slot[td], ts = src % TKV_BS, qs = ts >> 2, rs = ts & 3;
-        const uint8_t* sr = pool + ((int64_t)(src / TKV_BS) * S.Hkv + h) * R;
+        const uint8_t* sr = pool + ((int64_t)(src / TKV_BS) * S.Hst + h) * R;
         const uint32_t w = *(const uint32_t*)(sr + 64 * CB + chunk_byte(CB, 16 * qs + i, 4 * wc));
         for (int nn = 0; nn < W / 4; nn++) {
           const int fs = 4 * nn + rs, fd = 4 * nn + r;
@@ -1516,7 +1516,7 @@ __device__ void compact_copy_block(const DevState& S, int c, int newb, int cnt, 
       const int td = u / (2 * NG), kv = (u / NG) % 2, gi = u % NG;
       if (td >= cnt) continue;
       const int src = src_slot[td], ts = src % TKV_BS;
-      const uint8_t* sr = pool + ((int64_t)(src / TKV_BS) * S.Hkv + h) * R;
+      const uint8_t* sr = pool + ((int64_t)(src / TKV_BS) * S.Hst + h) * R;
       *(uint32_t*)(dst + meta_byte(D, g, BITS, kv, td, gi)) = *(const uint32_t*)(sr + meta_byte(D, g, BITS, kv, ts, gi));
     }
   }
