@@ -44,7 +44,7 @@ class _Layout(C.Structure):
     _fields_ = [("num_kv_heads", C.c_int32), ("num_q_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("group_size", C.c_int32), ("bits", C.c_int32 * 3), ("pool_blocks", C.c_int32 * 3),
                 ("max_seqs", C.c_int32), ("max_blocks_per_seq", C.c_int32),
-                ("max_segments_per_seq", C.c_int32), ("num_layers", C.c_int32)]
+                ("max_segments_per_seq", C.c_int32), ("num_layers", C.c_int32), ("code_format", C.c_int32)]
 
 
 class _State(C.Structure):
@@ -67,6 +67,8 @@ def lib():
         L.ora_f16_to_f64.argtypes = [C.c_uint16]; L.ora_f16_to_f64.restype = C.c_double
         L.ora_block_head_bytes.argtypes = [P, C.c_int]; L.ora_block_head_bytes.restype = C.c_int64
         L.ora_quantize_group.argtypes = [P, C.c_int, C.c_int, P, P, P]; L.ora_quantize_group.restype = None
+        L.ora_quantize_group_fmt.argtypes = [C.c_int, P, C.c_int, P, P]; L.ora_quantize_group_fmt.restype = None
+        L.ora_code_value.argtypes = [C.c_int, C.c_int, C.c_uint]; L.ora_code_value.restype = C.c_double
         L.ora_init.argtypes = [P, P, P]; L.ora_init.restype = None
         L.ora_append.argtypes = [P, P, C.c_int, P, P, P, P, P, P]; L.ora_append.restype = None
         L.ora_evict.argtypes = [P, P, C.c_int, P, P, P, P]; L.ora_evict.restype = None
@@ -117,12 +119,28 @@ def quantize_group(x: np.ndarray, bits: int):
     return codes, int(s[0]), int(z[0])
 
 
+def quantize_group_fmt(x: np.ndarray, c: int):
+    """Float / ternary quantizer of class c (0 FP8 E4M3, 1 FP4 E2M1, 2 ternary):
+    codes and the fp16 scale bits (the zero-point is 0)."""
+    x = np.ascontiguousarray(x, np.float32)
+    codes = np.zeros(x.size, np.uint32)
+    s = np.zeros(1, np.uint16)
+    lib().ora_quantize_group_fmt(c, _p(x), x.size, _p(codes), _p(s))
+    return codes, int(s[0])
+
+
+def code_value(code_format: int, c: int, code: int) -> float:
+    """The value a stored code stands for, before scale and zero-point."""
+    return float(lib().ora_code_value(code_format, c, code))
+
+
 # ---------------------------------------------------------------------------
 # state
 # ---------------------------------------------------------------------------
 class OracleLayout:
     def __init__(self, num_kv_heads, num_q_heads, head_dim, group_size, pool_blocks,
-                 max_seqs, max_blocks_per_seq, max_segments_per_seq, bits=(8, 4, 2), num_layers=1):
+                 max_seqs, max_blocks_per_seq, max_segments_per_seq, bits=(8, 4, 2), num_layers=1,
+                 code_format=0):
         self.num_kv_heads, self.num_q_heads = int(num_kv_heads), int(num_q_heads)
         self.head_dim, self.group_size = int(head_dim), int(group_size)
         self.bits = tuple(int(b) for b in bits)
@@ -131,9 +149,11 @@ class OracleLayout:
         self.max_segments_per_seq = int(max_segments_per_seq)
         self.num_layers = max(1, int(num_layers))
         self.stored_heads = self.num_kv_heads * self.num_layers
+        self.code_format = int(code_format)
         self._c = _Layout(self.num_kv_heads, self.num_q_heads, self.head_dim, self.group_size,
                           (C.c_int32 * 3)(*self.bits), (C.c_int32 * 3)(*self.pool_blocks),
-                          self.max_seqs, self.max_blocks_per_seq, self.max_segments_per_seq, self.num_layers)
+                          self.max_seqs, self.max_blocks_per_seq, self.max_segments_per_seq, self.num_layers,
+                          self.code_format)
 
     def block_head_bytes(self, c: int) -> int:
         return int(lib().ora_block_head_bytes(C.byref(self._c), c))

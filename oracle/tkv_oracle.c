@@ -59,6 +59,7 @@ typedef struct {
   int32_t pool_blocks[3];
   int32_t max_seqs, max_blocks_per_seq, max_segments_per_seq;
   int32_t num_layers;            /* layers sharing block tables and eviction; 0 counts as 1 */
+  int32_t code_format;           /* 0: integer codes; 1: FP8 E4M3 / FP4 E2M1 / ternary by class */
 } ora_layout;
 
 typedef struct {
@@ -150,6 +151,11 @@ static int64_t elem_bit(int64_t e, int bits) {
   int64_t p = (f >> 1) + (f & 1) * (W / 2);
   return w * 32 + p * bits;
 }
+/* Float and ternary codes (code_format 1) sit in their words in element
+   order, least significant field first. */
+static int64_t elem_bit_of(const ora_layout *L, int64_t e, int bits) {
+  return L->code_format ? e * bits : elem_bit(e, bits);
+}
 
 /* A code region holds 64 chunks.  A chunk of CB bytes is cut into units of
    U = min(CB, 16) bytes; unit u of chunk k occupies bytes [(64u + k) U,
@@ -167,14 +173,14 @@ static int64_t k_code_bit(const ora_layout *L, int c, int t, int d) {
   int g = L->group_size, q4 = g / 4;
   int gi = d / g, w = d % g, lg = w / q4, ep = w % q4;
   int64_t chunk = 16 * lg + t;
-  return chunk_bit(L, c, chunk, elem_bit((int64_t)gi * q4 + ep, CLASS_BITS[c]));
+  return chunk_bit(L, c, chunk, elem_bit_of(L, (int64_t)gi * q4 + ep, CLASS_BITS[c]));
 }
 
 /* V code of token t = 4q + r, dim d = 16n + i: chunk 16*q + i, element 4n + r. */
 static int64_t v_code_bit(const ora_layout *L, int c, int t, int d) {
   int q = t / 4, r = t % 4, n = d / 16, i = d % 16;
   int64_t chunk = 16 * q + i;
-  return codes_bytes(L, c) * 8 + chunk_bit(L, c, chunk, elem_bit((int64_t)n * 4 + r, CLASS_BITS[c]));
+  return codes_bytes(L, c) * 8 + chunk_bit(L, c, chunk, elem_bit_of(L, (int64_t)n * 4 + r, CLASS_BITS[c]));
 }
 
 /* byte offset of the (scale, zero) fp16 pair of token t, group gi, tensor kv (0=K, 1=V) */
@@ -274,6 +280,95 @@ void ora_quantize_group(const float *x, int n, int bits, unsigned *codes, uint16
   *s16 = sh; *z16 = zh;
 }
 
+/* ---------------------------------------------------------------------- */
+/* Float and ternary codes (code_format 1; TBQ bullet: 8-bit FP8 for       */
+/* Reasoning tokens, a 4-bit float for Execution, 2-bit ternary for        */
+/* Transition).  Symmetric, one fp16 scale per group, zero-point 0.        */
+/*   FP8 E4M3 (class 0): s = fp16(amax / 448); code = E4M3 of x / s,       */
+/*     round to nearest even, saturated at +-448.                          */
+/*   FP4 E2M1 (class 1): s = fp16(amax / 6); code = E2M1 of x / s, round   */
+/*     to nearest, ties to the even mantissa, saturated at +-6.            */
+/*   Ternary (class 2), the rule of Ternary Weight Networks (Li, Zhang,    */
+/*     Liu 2016): threshold 0.7 * mean |x|; t = sign(x) where |x| exceeds  */
+/*     it, else 0; s = fp16(mean |x| over the nonzero t).  Sums are        */
+/*     pairwise over index halves.  Codes 0 -> 00, +1 -> 01, -1 -> 11.     */
+/* A zero scale gives all-zero codes; zero and -0 codes are +0.            */
+/* ---------------------------------------------------------------------- */
+static double e4m3_value(unsigned c) {
+  int e = (c >> 3) & 15, m = c & 7;
+  double v = e ? ldexp(1.0 + m / 8.0, e - 7) : ldexp(m / 8.0, -6);
+  return (c & 0x80) ? -v : v;
+}
+static double e2m1_value(unsigned c) {
+  int e = (c >> 1) & 3, m = c & 1;
+  double v = e ? ldexp(1.0 + m / 2.0, e - 1) : m * 0.5;
+  return (c & 8) ? -v : v;
+}
+static double ternary_value(unsigned c) { return c == 1 ? 1.0 : (c == 3 ? -1.0 : 0.0); }
+
+static unsigned e4m3_code(float y) {
+  double a = fabs((double)y);
+  unsigned mag;
+  if (a >= 448.0) mag = 0x7E;
+  else if (a < ldexp(1.0, -6)) mag = (unsigned)nearbyint(a * 512.0);          /* subnormal steps of 2^-9 */
+  else {
+    int E; frexp(a, &E); E -= 1;                                              /* 2^E <= a < 2^(E+1) */
+    double q = (ldexp(a, -E) - 1.0) * 8.0;
+    int m = (int)nearbyint(q);
+    if (m == 8) { m = 0; E += 1; }
+    mag = (unsigned)(((E + 7) << 3) | m);
+  }
+  return mag == 0 ? 0 : mag | (y < 0.0f ? 0x80u : 0u);
+}
+static unsigned e2m1_code(float y) {
+  double a = fabs((double)y);
+  unsigned mag;
+  if (a >= 6.0) mag = 7;
+  else if (a < 1.0) mag = (unsigned)nearbyint(a * 2.0);                       /* 0, 0.5, 1 */
+  else {
+    int E; frexp(a, &E); E -= 1;
+    double q = (ldexp(a, -E) - 1.0) * 2.0;
+    int m = (int)nearbyint(q);
+    if (m == 2) { m = 0; E += 1; }
+    mag = (unsigned)(((E + 1) << 1) | m);
+  }
+  return mag == 0 ? 0 : mag | (y < 0.0f ? 8u : 0u);
+}
+static float pairwise_sum(const float *x, int n) {
+  return n == 1 ? x[0] : pairwise_sum(x, n / 2) + pairwise_sum(x + n / 2, n / 2);
+}
+
+void ora_quantize_group_fmt(int c, const float *x, int n, unsigned *codes, uint16_t *s16) {
+  float a[256];
+  float amax = 0.0f;
+  for (int i = 0; i < n; i++) { a[i] = fabsf(x[i]); if (a[i] > amax) amax = a[i]; }
+  uint16_t sh;
+  if (c == 2) {
+    float thr = 0.7f * (pairwise_sum(a, n) / (float)n);
+    float kept[256]; int cnt = 0;
+    for (int i = 0; i < n; i++) { int on = x[i] > thr || x[i] < -thr; kept[i] = on ? a[i] : 0.0f; cnt += on; }
+    sh = cnt ? ora_f32_to_f16(pairwise_sum(kept, n) / (float)cnt) : 0;
+    for (int i = 0; i < n; i++)
+      codes[i] = sh == 0 ? 0 : (x[i] > thr ? 1u : (x[i] < -thr ? 3u : 0u));
+  } else {
+    sh = ora_f32_to_f16(amax / (c == 0 ? 448.0f : 6.0f));
+    float sf = f16_to_f32(sh);
+    for (int i = 0; i < n; i++)
+      codes[i] = sh == 0 ? 0 : (c == 0 ? e4m3_code(x[i] / sf) : e2m1_code(x[i] / sf));
+  }
+  if (sh == 0x8000u) sh = 0;
+  *s16 = sh;
+}
+/* value of a stored code, before the group's scale and zero-point */
+static double code_value(const ora_layout *L, int c, unsigned code) {
+  if (!L->code_format) return (double)code;
+  return c == 0 ? e4m3_value(code) : (c == 1 ? e2m1_value(code) : ternary_value(code));
+}
+double ora_code_value(int code_format, int c, unsigned code) {
+  ora_layout L; memset(&L, 0, sizeof L); L.code_format = code_format;
+  return code_value(&L, c, code);
+}
+
 /* Quantize one token's K and V rows of one KV head into block-head memory. */
 static void store_token(const ora_layout *L, ora_state *S, int c, int blk, int t, int head,
                         const float *krow, const float *vrow) {
@@ -283,7 +378,8 @@ static void store_token(const ora_layout *L, ora_state *S, int c, int blk, int t
   for (int kv = 0; kv < 2; kv++) {
     const float *row = kv ? vrow : krow;
     for (int gi = 0; gi < NG; gi++) {
-      ora_quantize_group(row + gi * g, g, bits, codes, &sh, &zh);
+      if (L->code_format) { ora_quantize_group_fmt(c, row + gi * g, g, codes, &sh); zh = 0; }
+      else ora_quantize_group(row + gi * g, g, bits, codes, &sh, &zh);
       for (int j = 0; j < g; j++) {
         int d = gi * g + j;
         int64_t bit = kv ? v_code_bit(L, c, t, d) : k_code_bit(L, c, t, d);
@@ -304,7 +400,7 @@ static void load_token_f32(const ora_layout *L, ora_state *S, int c, int blk, in
     uint8_t *m = bh + meta_off(L, c, kv, t, gi);
     float sf = f16_to_f32(get_u16(m)), zf = f16_to_f32(get_u16(m + 2));
     unsigned code = get_code(bh, kv ? v_code_bit(L, c, t, d) : k_code_bit(L, c, t, d), bits);
-    float prod = sf * (float)code;          /* exact: 11-bit by <=8-bit significands */
+    float prod = sf * (float)code_value(L, c, code);   /* exact: 11-bit by <=8-bit significands */
     row[d] = prod + zf;
   }
 }
@@ -321,7 +417,7 @@ static double deq64(const ora_layout *L, ora_state *S, int c, int blk, int t, in
   uint8_t *bh = block_head(L, S, c, blk, head);
   uint8_t *m = bh + meta_off(L, c, kv, t, d / L->group_size);
   unsigned code = get_code(bh, kv ? v_code_bit(L, c, t, d) : k_code_bit(L, c, t, d), CLASS_BITS[c]);
-  return ora_f16_to_f64(get_u16(m)) * (double)code + ora_f16_to_f64(get_u16(m + 2));
+  return ora_f16_to_f64(get_u16(m)) * code_value(L, c, code) + ora_f16_to_f64(get_u16(m + 2));
 }
 
 /* ---------------------------------------------------------------------- */

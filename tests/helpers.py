@@ -12,7 +12,8 @@ BS = 16
 def oracle_layout(L: synth.Layout):
     import oracle
     return oracle.OracleLayout(L.num_kv_heads, L.num_q_heads, L.head_dim, L.group_size, L.pool_blocks,
-                               L.max_seqs, L.max_blocks_per_seq, L.max_segments_per_seq, L.bits, L.num_layers)
+                               L.max_seqs, L.max_blocks_per_seq, L.max_segments_per_seq, L.bits, L.num_layers,
+                               L.code_format)
 
 
 def build_oracle(w: synth.Workload):
@@ -34,7 +35,7 @@ def gpu_layout(L: synth.Layout):
     from thought_adaptive_mixed_amd import binding
     return binding.make_layout(L.num_kv_heads, L.num_q_heads, L.head_dim, L.group_size, L.pool_blocks,
                                L.max_seqs, L.max_blocks_per_seq, L.max_segments_per_seq, L.max_tokens_per_call,
-                               L.bits, L.num_layers)
+                               L.bits, L.num_layers, L.code_format)
 
 
 def dev(a, dtype=None):
@@ -62,10 +63,10 @@ def _templates(L, c):
     """Per slot-in-block t: byte masks of the bits token t owns in one
     (block, KV head) record (K codes, V codes, K and V meta)."""
     import oracle
-    key = (L.head_dim, L.group_size, c)
+    key = (L.head_dim, L.group_size, c, L.code_format)
     if key in _TEMPLATES:
         return _TEMPLATES[key]
-    ol = oracle.OracleLayout(1, 1, L.head_dim, L.group_size, (1, 1, 1), 1, 1, 1)
+    ol = oracle.OracleLayout(1, 1, L.head_dim, L.group_size, (1, 1, 1), 1, 1, 1, code_format=L.code_format)
     R = ol.block_head_bytes(c)
     bits = (8, 4, 2)[c]
     NG = L.head_dim // L.group_size

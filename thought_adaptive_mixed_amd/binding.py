@@ -34,7 +34,7 @@ class Layout(C.Structure):
                 ("group_size", C.c_int32), ("bits", C.c_int32 * 3), ("pool_blocks", C.c_int32 * 3),
                 ("max_seqs", C.c_int32), ("max_blocks_per_seq", C.c_int32),
                 ("max_segments_per_seq", C.c_int32), ("max_tokens_per_call", C.c_int32),
-                ("num_layers", C.c_int32)]
+                ("num_layers", C.c_int32), ("code_format", C.c_int32)]
 
 
 class AttnArgs(C.Structure):
@@ -143,10 +143,11 @@ def _issue(fn, args, what, prepare, keep=None):
 
 
 def make_layout(num_kv_heads, num_q_heads, head_dim, group_size, pool_blocks, max_seqs, max_blocks_per_seq,
-                max_segments_per_seq, max_tokens_per_call=4096, bits=(8, 4, 2), num_layers=1) -> Layout:
+                max_segments_per_seq, max_tokens_per_call=4096, bits=(8, 4, 2), num_layers=1,
+                code_format=0) -> Layout:
     return Layout(num_kv_heads, num_q_heads, head_dim, group_size, (C.c_int32 * 3)(*bits),
                   (C.c_int32 * 3)(*pool_blocks), max_seqs, max_blocks_per_seq, max_segments_per_seq,
-                  max_tokens_per_call, num_layers)
+                  max_tokens_per_call, num_layers, code_format)
 
 
 def buffer_sizes(layout: Layout):

@@ -63,6 +63,7 @@ class Layout:
     max_tokens_per_call: int = 4096
     bits: Tuple[int, int, int] = (8, 4, 2)
     num_layers: int = 1                  # layers sharing block tables and eviction
+    code_format: int = 0                 # 0 integer codes; 1 FP8 E4M3 / FP4 E2M1 / ternary
 
 
 @dataclasses.dataclass
