@@ -67,7 +67,8 @@ def lib():
         L.ora_f16_to_f64.argtypes = [C.c_uint16]; L.ora_f16_to_f64.restype = C.c_double
         L.ora_block_head_bytes.argtypes = [P, C.c_int]; L.ora_block_head_bytes.restype = C.c_int64
         L.ora_quantize_group.argtypes = [P, C.c_int, C.c_int, P, P, P]; L.ora_quantize_group.restype = None
-        L.ora_quantize_group_fmt.argtypes = [C.c_int, P, C.c_int, P, P]; L.ora_quantize_group_fmt.restype = None
+        L.ora_quantize_group_fmt.argtypes = [C.c_int, P, C.c_int, P, P, P]
+        L.ora_quantize_group_fmt.restype = None
         L.ora_code_value.argtypes = [C.c_int, C.c_int, C.c_uint]; L.ora_code_value.restype = C.c_double
         L.ora_init.argtypes = [P, P, P]; L.ora_init.restype = None
         L.ora_append.argtypes = [P, P, C.c_int, P, P, P, P, P, P]; L.ora_append.restype = None
@@ -121,12 +122,13 @@ def quantize_group(x: np.ndarray, bits: int):
 
 def quantize_group_fmt(x: np.ndarray, c: int):
     """Float / ternary quantizer of class c (0 FP8 E4M3, 1 FP4 E2M1, 2 ternary):
-    codes and the fp16 scale bits (the zero-point is 0)."""
+    codes and the fp16 scale and zero-point bits (zero-point 0 for the float
+    classes, -scale for ternary, whose codes are t + 1)."""
     x = np.ascontiguousarray(x, np.float32)
     codes = np.zeros(x.size, np.uint32)
-    s = np.zeros(1, np.uint16)
-    lib().ora_quantize_group_fmt(c, _p(x), x.size, _p(codes), _p(s))
-    return codes, int(s[0])
+    s = np.zeros(1, np.uint16); z = np.zeros(1, np.uint16)
+    lib().ora_quantize_group_fmt(c, _p(x), x.size, _p(codes), _p(s), _p(z))
+    return codes, int(s[0]), int(z[0])
 
 
 def code_value(code_format: int, c: int, code: int) -> float:

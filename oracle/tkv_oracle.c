@@ -151,10 +151,11 @@ static int64_t elem_bit(int64_t e, int bits) {
   int64_t p = (f >> 1) + (f & 1) * (W / 2);
   return w * 32 + p * bits;
 }
-/* Float and ternary codes (code_format 1) sit in their words in element
-   order, least significant field first. */
+/* Float codes (code_format 1, 8- and 4-bit classes) sit in their words in
+   element order, least significant field first; ternary codes, which are
+   integers on a three-level grid, keep the integer order. */
 static int64_t elem_bit_of(const ora_layout *L, int64_t e, int bits) {
-  return L->code_format ? e * bits : elem_bit(e, bits);
+  return (L->code_format && bits > 2) ? e * bits : elem_bit(e, bits);
 }
 
 /* A code region holds 64 chunks.  A chunk of CB bytes is cut into units of
@@ -291,8 +292,10 @@ void ora_quantize_group(const float *x, int n, int bits, unsigned *codes, uint16
 /*   Ternary (class 2), the rule of Ternary Weight Networks (Li, Zhang,    */
 /*     Liu 2016): threshold 0.7 * mean |x|; t = sign(x) where |x| exceeds  */
 /*     it, else 0; s = fp16(mean |x| over the nonzero t).  Sums are        */
-/*     pairwise over index halves.  Codes 0 -> 00, +1 -> 01, -1 -> 11.     */
-/* A zero scale gives all-zero codes; zero and -0 codes are +0.            */
+/*     pairwise over index halves.  Stored as the integer code t + 1 with  */
+/*     zero-point -s, so x^ = s * code + zero as for integer codes.        */
+/* A zero scale gives all-zero codes and zero-point; zero and -0 float     */
+/* codes are +0.                                                           */
 /* ---------------------------------------------------------------------- */
 static double e4m3_value(unsigned c) {
   int e = (c >> 3) & 15, m = c & 7;
@@ -304,7 +307,6 @@ static double e2m1_value(unsigned c) {
   double v = e ? ldexp(1.0 + m / 2.0, e - 1) : m * 0.5;
   return (c & 8) ? -v : v;
 }
-static double ternary_value(unsigned c) { return c == 1 ? 1.0 : (c == 3 ? -1.0 : 0.0); }
 
 static unsigned e4m3_code(float y) {
   double a = fabs((double)y);
@@ -338,7 +340,7 @@ static float pairwise_sum(const float *x, int n) {
   return n == 1 ? x[0] : pairwise_sum(x, n / 2) + pairwise_sum(x + n / 2, n / 2);
 }
 
-void ora_quantize_group_fmt(int c, const float *x, int n, unsigned *codes, uint16_t *s16) {
+void ora_quantize_group_fmt(int c, const float *x, int n, unsigned *codes, uint16_t *s16, uint16_t *z16) {
   float a[256];
   float amax = 0.0f;
   for (int i = 0; i < n; i++) { a[i] = fabsf(x[i]); if (a[i] > amax) amax = a[i]; }
@@ -349,7 +351,7 @@ void ora_quantize_group_fmt(int c, const float *x, int n, unsigned *codes, uint1
     for (int i = 0; i < n; i++) { int on = x[i] > thr || x[i] < -thr; kept[i] = on ? a[i] : 0.0f; cnt += on; }
     sh = cnt ? ora_f32_to_f16(pairwise_sum(kept, n) / (float)cnt) : 0;
     for (int i = 0; i < n; i++)
-      codes[i] = sh == 0 ? 0 : (x[i] > thr ? 1u : (x[i] < -thr ? 3u : 0u));
+      codes[i] = sh == 0 ? 0 : (x[i] > thr ? 2u : (x[i] < -thr ? 0u : 1u));
   } else {
     sh = ora_f32_to_f16(amax / (c == 0 ? 448.0f : 6.0f));
     float sf = f16_to_f32(sh);
@@ -358,11 +360,12 @@ void ora_quantize_group_fmt(int c, const float *x, int n, unsigned *codes, uint1
   }
   if (sh == 0x8000u) sh = 0;
   *s16 = sh;
+  *z16 = (c == 2 && sh) ? (uint16_t)(sh ^ 0x8000u) : 0;
 }
 /* value of a stored code, before the group's scale and zero-point */
 static double code_value(const ora_layout *L, int c, unsigned code) {
-  if (!L->code_format) return (double)code;
-  return c == 0 ? e4m3_value(code) : (c == 1 ? e2m1_value(code) : ternary_value(code));
+  if (!L->code_format || c == 2) return (double)code;
+  return c == 0 ? e4m3_value(code) : e2m1_value(code);
 }
 double ora_code_value(int code_format, int c, unsigned code) {
   ora_layout L; memset(&L, 0, sizeof L); L.code_format = code_format;
@@ -378,7 +381,7 @@ static void store_token(const ora_layout *L, ora_state *S, int c, int blk, int t
   for (int kv = 0; kv < 2; kv++) {
     const float *row = kv ? vrow : krow;
     for (int gi = 0; gi < NG; gi++) {
-      if (L->code_format) { ora_quantize_group_fmt(c, row + gi * g, g, codes, &sh); zh = 0; }
+      if (L->code_format) ora_quantize_group_fmt(c, row + gi * g, g, codes, &sh, &zh);
       else ora_quantize_group(row + gi * g, g, bits, codes, &sh, &zh);
       for (int j = 0; j < g; j++) {
         int d = gi * g + j;

@@ -45,8 +45,8 @@ def test_e2m1_decode_every_code():
     for c in range(16):
         v = E2M1[c & 7] * (-1 if c & 8 else 1)
         assert oracle.code_value(1, 1, c) == v
-    assert [oracle.code_value(1, 2, c) for c in range(4)] == [0.0, 1.0, 0.0, -1.0]
-    # code_format 0 codes are their own values
+    # ternary codes are integers (t + 1, with zero-point -scale), as are code_format 0 codes
+    assert [oracle.code_value(1, 2, c) for c in range(3)] == [0.0, 1.0, 2.0]
     assert oracle.code_value(0, 0, 200) == 200.0
 
 
@@ -73,8 +73,8 @@ def test_e4m3_encode_matches_torch_at_unit_scale(kind):
     for i in range(0, y.size, 63):
         x = np.concatenate([[448.0], y[i:i + 63]]).astype(np.float32)
         x = np.pad(x, (0, 64 - x.size))
-        codes, s = oracle.quantize_group_fmt(x, 0)
-        assert s == 0x3C00
+        codes, s, z = oracle.quantize_group_fmt(x, 0)
+        assert s == 0x3C00 and z == 0
         assert np.array_equal(codes, torch_e4m3_bits(x)), kind
 
 
@@ -85,7 +85,8 @@ def test_e4m3_scaled_groups_match_torch():
     for trial in range(300):
         n = (32, 64)[trial % 2]
         x = (rng.standard_normal(n) * 10.0 ** rng.uniform(-4, 3)).astype(np.float32)
-        codes, s = oracle.quantize_group_fmt(x, 0)
+        codes, s, z = oracle.quantize_group_fmt(x, 0)
+        assert z == 0
         sf = np.float32(f16(s))
         assert s == oracle.f32_to_f16_bits(float(np.float32(np.abs(x).max()) / np.float32(448)))
         y = (x / sf).astype(np.float32)
@@ -100,7 +101,7 @@ def test_e4m3_saturates_when_scale_rounds_down():
     s = f16(oracle.f32_to_f16_bits(float(amax / np.float32(448))))
     assert amax / np.float32(s) > 448
     x = np.zeros(32, np.float32); x[3] = amax; x[4] = -amax
-    codes, _ = oracle.quantize_group_fmt(x, 0)
+    codes, _, _ = oracle.quantize_group_fmt(x, 0)
     assert codes[3] == 0x7E and codes[4] == 0xFE
 
 
@@ -123,7 +124,8 @@ def test_e2m1_encode_brute_force():
             x = np.concatenate([[6.0], rng.choice(np.concatenate([ties, -ties]), n - 1)]).astype(np.float32)
         else:
             x = (rng.standard_normal(n) * 10.0 ** rng.uniform(-4, 3)).astype(np.float32)
-        codes, s = oracle.quantize_group_fmt(x, 1)
+        codes, s, z = oracle.quantize_group_fmt(x, 1)
+        assert z == 0
         sf = np.float32(f16(s))
         assert s == oracle.f32_to_f16_bits(float(np.float32(np.abs(x).max()) / np.float32(6)))
         want = [brute_e2m1(np.float32(v / sf)) for v in x]
@@ -145,7 +147,7 @@ def test_float_grid_roundtrip(c):
         v = rng.choice(vals, g)
         v[rng.integers(g)] = top * (1 if rng.integers(2) else -1)
         x = (s * v).astype(np.float32)
-        codes, sh = oracle.quantize_group_fmt(x, c)
+        codes, sh, _ = oracle.quantize_group_fmt(x, c)
         assert f16(sh) == s
         back = np.array([f16(sh) * oracle.code_value(1, c, int(k)) for k in codes])
         assert np.array_equal(back, x.astype(np.float64)), trial
@@ -153,11 +155,12 @@ def test_float_grid_roundtrip(c):
 
 def test_ternary_hand_example():
     """By hand: mean |x| = 8.3/8 = 1.0375, threshold 0.72625; the four
-    entries beyond it keep their signs; s = (2 + 1.5 + 3 + 1)/4 = 1.875."""
+    entries beyond it keep their signs; s = (2 + 1.5 + 3 + 1)/4 = 1.875;
+    codes t + 1, zero-point -1.875."""
     x = np.array([0.1, -2.0, 0.5, 1.5, -0.2, 0.0, 3.0, -1.0], np.float32)
-    codes, s = oracle.quantize_group_fmt(x, 2)
-    assert codes.tolist() == [0, 3, 0, 1, 0, 0, 1, 3]
-    assert f16(s) == 1.875
+    codes, s, z = oracle.quantize_group_fmt(x, 2)
+    assert codes.tolist() == [1, 0, 1, 2, 1, 1, 2, 0]
+    assert f16(s) == 1.875 and f16(z) == -1.875
 
 
 def test_ternary_rule_and_least_squares_scale():
@@ -171,9 +174,10 @@ def test_ternary_rule_and_least_squares_scale():
         thr = 0.7 * np.abs(x.astype(np.float64)).mean()
         if np.min(np.abs(np.abs(x) - thr)) < 1e-4 * thr:
             continue
-        codes, s = oracle.quantize_group_fmt(x, 2)
+        codes, s, z = oracle.quantize_group_fmt(x, 2)
         t = np.where(x > thr, 1, np.where(x < -thr, -1, 0))
-        assert codes.tolist() == [{0: 0, 1: 1, -1: 3}[int(v)] for v in t], trial
+        assert codes.tolist() == (t + 1).tolist(), trial
+        assert z == s ^ 0x8000
         opt = np.linalg.lstsq(t[:, None].astype(np.float64), x.astype(np.float64), rcond=None)[0][0]
         assert abs(f16(s) - opt) <= 2.0 ** -11 * abs(opt) * 1.01, trial
 
@@ -181,20 +185,22 @@ def test_ternary_rule_and_least_squares_scale():
 def test_ternary_symmetry_and_degenerate_groups():
     rng = np.random.default_rng(16)
     x = rng.standard_normal(64).astype(np.float32)
-    c1, s1 = oracle.quantize_group_fmt(x, 2)
-    c2, s2 = oracle.quantize_group_fmt(-x, 2)
-    assert s1 == s2 and c2.tolist() == [{0: 0, 1: 3, 3: 1}[int(c)] for c in c1]
+    c1, s1, _ = oracle.quantize_group_fmt(x, 2)
+    c2, s2, _ = oracle.quantize_group_fmt(-x, 2)
+    assert s1 == s2 and c2.tolist() == (2 - c1).tolist()
     for c in range(3):
         z = np.zeros(32, np.float32)
-        assert oracle.quantize_group_fmt(z, c)[1] == 0 and not oracle.quantize_group_fmt(z, c)[0].any()
+        codes, sh, zh = oracle.quantize_group_fmt(z, c)
+        assert sh == 0 and zh == 0 and not codes.any()
         z[7] = -0.0
-        assert oracle.quantize_group_fmt(z, c)[1] == 0
+        assert oracle.quantize_group_fmt(z, c)[1:] == (0, 0)
 
 
 @pytest.mark.parametrize("D,g", [(64, 32), (128, 64)])
 def test_page_format_packing_is_natural_and_a_bijection(D, g):
     """code_format 1 keeps the chunk layout of code_format 0 (the same chunk
-    and word for every code) and orders the fields of a word by element."""
+    and word for every code) and orders the fields of a word by element for
+    the float classes; ternary codes keep the integer order."""
     L0 = oracle.OracleLayout(1, 1, D, g, (1, 1, 1), 1, 1, 1)
     L1 = oracle.OracleLayout(1, 1, D, g, (1, 1, 1), 1, 1, 1, code_format=1)
     for c, bits in enumerate((8, 4, 2)):
@@ -203,12 +209,12 @@ def test_page_format_packing_is_natural_and_a_bijection(D, g):
             for t in range(16):
                 for d in range(D):
                     b0, b1 = L0.code_bit(c, kv, t, d), L1.code_bit(c, kv, t, d)
-                    assert b0 // 32 == b1 // 32
+                    assert b0 // 32 == b1 // 32 and (c < 2 or b0 == b1)
                     used[b1:b1 + bits] += 1
         assert np.all(used == 1)
         # K codes of one token: consecutive dims of a quarter-group in consecutive fields
         q4 = g // 4
-        for d in range(0, D, q4):
+        for d in range(0, D, q4) if c < 2 else []:
             bs = [L1.code_bit(c, 0, 0, d + e) for e in range(q4)]
             per_word = 32 // bits
             for e in range(1, q4):
@@ -220,16 +226,15 @@ def format_rows(rng, types, H, D, g, c_of_type):
     """Rows exactly representable in each token's page format (grid values
     times a power-of-two scale, the largest magnitude present per group)."""
     out = np.zeros((len(types), H, D), np.float32)
-    tabs = {c: np.array([oracle.code_value(1, c, k) for k in range(1 << (8, 4, 2)[c])
-                         if not (c == 0 and k & 0x7F == 0x7F)]) for c in range(3)}
+    tabs = {c: np.array([oracle.code_value(1, c, k) for k in range(1 << (8, 4)[c])
+                         if not (c == 0 and k & 0x7F == 0x7F)]) for c in range(2)}
+    tabs[2] = np.array([-1.0, 0.0, 1.0])         # the ternary grid in units of the scale
     tops = {0: 448.0, 1: 6.0, 2: 1.0}
     for i, y in enumerate(types):
         c = c_of_type[int(y)]
         for h in range(H):
             for gi in range(D // g):
                 v = rng.choice(tabs[c], g)
-                if c == 2:
-                    v = rng.choice([-1.0, 1.0], g)      # every entry beyond the threshold
                 v[rng.integers(g)] = tops[c]
                 out[i, h, gi * g:(gi + 1) * g] = 2.0 ** int(rng.integers(-8, -2)) * v
     return out
@@ -274,9 +279,9 @@ def test_page_format_downgrade_requantizes_reconstruction():
     rows = oc.token_rows(0)
     for pos in range(3):
         for gi in range(2):
-            c4, s4 = oracle.quantize_group_fmt(x[pos, 0, gi * 32:(gi + 1) * 32], 1)
+            c4, s4, _ = oracle.quantize_group_fmt(x[pos, 0, gi * 32:(gi + 1) * 32], 1)
             xr = np.array([np.float32(f16(s4)) * np.float32(oracle.code_value(1, 1, int(k))) for k in c4],
                           np.float32)
-            c2, s2 = oracle.quantize_group_fmt(xr, 2)
-            want = np.array([np.float32(f16(s2)) * np.float32(oracle.code_value(1, 2, int(k))) for k in c2])
+            c2, s2, z2 = oracle.quantize_group_fmt(xr, 2)
+            want = np.array([np.float32(f16(s2)) * np.float32(k) + np.float32(f16(z2)) for k in c2], np.float32)
             assert np.array_equal(rows[pos][0][0, gi * 32:(gi + 1) * 32], want)
