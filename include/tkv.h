@@ -46,6 +46,25 @@
  *          element 4n+r.  Within a chunk, codes sit in 32-bit words of 32/bits
  *          codes; the low half-word holds the word's even elements and the high
  *          half-word its odd elements, least significant field first.
+ *          With code_format 1 the 8- and 4-bit (float) codes sit in element
+ *          order instead (element j of a word in bits j*bits..).
+ *   Code formats (ThinKV technical summary, "Methodology", TBQ bullet: FP8
+ *   or NVFP4 for Reasoning tokens, ternary for Transition tokens).  Per
+ *   (token, group) of g dims with fp16 scale s and zero z:
+ *     code_format 0, every class: asymmetric integer, s = (max-min)/(2^b-1),
+ *          z = min, code = round-to-nearest-even((x - z)/s) clamped; x^ = s*code + z.
+ *     code_format 1, class 0: FP8 E4M3 (bias 7, subnormals, no infinities),
+ *          s = amax/448, z = 0, code = E4M3(x/s) rounded to nearest even and
+ *          saturated at +-448; x^ = s*value(code).
+ *     code_format 1, class 1: FP4 E2M1 (values 0, .5, 1, 1.5, 2, 3, 4, 6),
+ *          s = amax/6, z = 0, nearest with ties to the even code, saturated;
+ *          x^ = s*value(code).
+ *     code_format 1, class 2: ternary by the rule of Ternary Weight Networks
+ *          (Li, Zhang, Liu 2016): threshold 0.7*mean|x|, t = sign(x) beyond it
+ *          else 0, s = mean |x| over the nonzero t (the sums pairwise over
+ *          index halves); stored as the integer code t + 1 with z = -s, so
+ *          x^ = s*code + z as for integer codes.
+ *     A zero scale stores all-zero codes and zero; a -0 scale or zero is stored as +0.
  *   BLKc   i32 [pool_blocks[c]][4]   {valid mask (bit t = slot t), max position
  *          ever stored, owner sequence, 0}; a free block is {0, -1, -1, 0}.
  *   SLOTc  i32 [pool_blocks[c]*16][2] {position, segment id} (valid slots).
@@ -106,6 +125,8 @@ typedef struct {
   int32_t max_segments_per_seq;   /* >= 1                                      */
   int32_t max_tokens_per_call;    /* bound on items per append/evict/plan call, 1..4096 */
   int32_t num_layers;             /* L: layers sharing the block tables, 1..64 (0 counts as 1) */
+  int32_t code_format;            /* 0: asymmetric integer codes; 1: the class's float or ternary
+                                     format (8-bit FP8 E4M3, 4-bit FP4 E2M1, 2-bit ternary) */
 } tkv_layout;
 
 /* Byte sizes of the TKV_NUM_BUFFERS buffers for layout L_h.  EINVAL for a

@@ -23,6 +23,7 @@ static int layout_ok(const tkv_layout* L) {
   if (L->max_segments_per_seq < 1) return 0;
   if (L->max_tokens_per_call < 1 || L->max_tokens_per_call > TKV_MAX_TOK) return 0;
   if (L->num_layers < 0 || L->num_layers > 64) return 0;
+  if (L->code_format != 0 && L->code_format != 1) return 0;
   return 1;
 }
 
@@ -100,6 +101,7 @@ extern "C" int tkv_create(const tkv_layout* L, void* const bufs[TKV_NUM_BUFFERS]
   S.NG = L->head_dim / L->group_size;
   S.NL = L->num_layers > 1 ? L->num_layers : 1;
   S.Hst = S.NL * S.Hkv;
+  S.fmt = L->code_format;
   S.max_seqs = L->max_seqs; S.max_blocks = L->max_blocks_per_seq; S.max_segs = L->max_segments_per_seq;
   S.max_tokens = L->max_tokens_per_call;
   c->last_stream = stream;

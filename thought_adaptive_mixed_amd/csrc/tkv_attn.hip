@@ -94,15 +94,38 @@ __device__ inline uint32_t code_pair(uint32_t w, int p) {
     return (w >> (p * BITS)) & M;
   }
 }
-template <int BITS>
+// Elements e0 .. e0+3 (e0 a multiple of 4) of a lane's chunk as an fp16
+// quad.  Integer codes (FMT 0, and ternary codes in either format): the
+// subnormals above.  Float codes (FMT 1): the FP8 E4M3 or FP4 E2M1 values
+// themselves, converted pairwise to fp32 by the hardware and packed to fp16,
+// both exact (E4M3 and E2M1 values are fp16 values); the codes of a word sit
+// in element order.
+template <int BITS, int FMT>
 __device__ inline half4_t operand4(const uint32_t* words, int e0) {
   constexpr int W = 32 / BITS;
   const uint32_t w = words[e0 / W];
-  const int p = (e0 % W) >> 1;
-  const half2_t a = __builtin_bit_cast(half2_t, code_pair<BITS>(w, p));
-  const half2_t b = __builtin_bit_cast(half2_t, code_pair<BITS>(w, p + 1));
-  half4_t r = {a[0], a[1], b[0], b[1]};
-  return r;
+  if constexpr (FMT == 1 && BITS == 8) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);          // bytes 0, 1
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);           // bytes 2, 3
+    const half2_t lo = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(a[0], a[1]));
+    const half2_t hi = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(b[0], b[1]));
+    return (half4_t){lo[0], lo[1], hi[0], hi[1]};
+  } else if constexpr (FMT == 1 && BITS == 4) {
+    const bool up = (e0 % W) != 0;                                    // elements 4..7 of the word: bytes 2, 3
+    const auto a = up ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2)
+                      : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const auto b = up ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3)
+                      : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const half2_t lo = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(a[0], a[1]));
+    const half2_t hi = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(b[0], b[1]));
+    return (half4_t){lo[0], lo[1], hi[0], hi[1]};
+  } else {
+    const int p = (e0 % W) >> 1;
+    const half2_t a = __builtin_bit_cast(half2_t, code_pair<BITS>(w, p));
+    const half2_t b = __builtin_bit_cast(half2_t, code_pair<BITS>(w, p + 1));
+    half4_t r = {a[0], a[1], b[0], b[1]};
+    return r;
+  }
 }
 
 __device__ inline half8_t cat8(half4_t a, half4_t b) {
@@ -164,6 +187,7 @@ struct AttnState {
   float m2, Z, S2;
   float top[TOPK];
   float thr;                   // head-wide 8th-best of the top lists
+  float vunit;                 // value of one accumulator unit (2^24 once integer codes entered, else 1)
   int natt;
 };
 
@@ -246,7 +270,7 @@ struct Buf {
   int pos[WINDOW ? 4 : 1];
 };
 
-template <int D, int GS, int BITS, bool WINDOW, int PK>
+template <int D, int GS, int BITS, int FMT, bool WINDOW, int PK>
 __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj, int lo_pos,
                                     int lane, bool head_ok, const half4_t (&qB)[D / 16],
                                     const half8_t* qk_lds, const float (&sumq)[D / GS],
@@ -274,8 +298,8 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
       spk[gi] = (float4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mm = 0; mm < KM; mm += 2)
-        spk[gi] = mfma32(cat8(operand4<BITS>(b.kw[0], gi * (GS / 4) + 4 * mm),
-                              operand4<BITS>(b.kw[0], gi * (GS / 4) + 4 * mm + 4)),
+        spk[gi] = mfma32(cat8(operand4<BITS, FMT>(b.kw[0], gi * (GS / 4) + 4 * mm),
+                              operand4<BITS, FMT>(b.kw[0], gi * (GS / 4) + 4 * mm + 4)),
                          *(const half8_t*)(qrow + ((gi * KM + mm) / 2) * 1024), spk[gi]);
     }
   } else {
@@ -286,8 +310,8 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
       for (int p = 0; p < PK / 2; p++)
 #pragma unroll
         for (int mm = 0; mm < KM; mm++)
-          spk[gi] = mfma32(cat8(operand4<BITS>(b.kw[2 * p], gi * (GS / 4) + 4 * mm),
-                                operand4<BITS>(b.kw[2 * p + 1], gi * (GS / 4) + 4 * mm)),
+          spk[gi] = mfma32(cat8(operand4<BITS, FMT>(b.kw[2 * p], gi * (GS / 4) + 4 * mm),
+                                operand4<BITS, FMT>(b.kw[2 * p + 1], gi * (GS / 4) + 4 * mm)),
                            *(const half8_t*)(qrow + (p * (D / 16) + gi * KM + mm) * 1024), spk[gi]);
     }
   }
@@ -378,7 +402,7 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
   if constexpr (PK == 1) {
 #pragma unroll
     for (int n = 0; n < NT; n++) {
-      const half4_t a = operand4<BITS>(b.vw[0], 4 * n);
+      const half4_t a = operand4<BITS, FMT>(b.vw[0], 4 * n);
       st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pbh[(16 * n) / GS], st.acc[n], 0, 0, 0);
       st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pbl[(16 * n) / GS], st.acc[n], 0, 0, 0);
     }
@@ -399,7 +423,7 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
       }
 #pragma unroll
       for (int n = 0; n < NT; n++) {
-        const half8_t a = cat8(operand4<BITS>(b.vw[jp], 4 * n), operand4<BITS>(b.vw[jp + 1], 4 * n));
+        const half8_t a = cat8(operand4<BITS, FMT>(b.vw[jp], 4 * n), operand4<BITS, FMT>(b.vw[jp + 1], 4 * n));
         st.acc[n] = mfma32(a, bh[(16 * n) / GS], st.acc[n]);
         st.acc[n] = mfma32(a, bl[(16 * n) / GS], st.acc[n]);
       }
@@ -481,7 +505,7 @@ __device__ inline void load_step(Buf<D, GS, WINDOW, PK>& b, const uint8_t* pool_
 // last step a wave issues the same load instructions (code loads of
 // zero-length records, metadata from one cached line), so every path issues
 // the same loads, the compiler's waits stay exact, and the padding is cheap.
-template <int D, int GS, bool WINDOW, int PK>
+template <int D, int GS, bool WINDOW, int PK, int FMT>
 __device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax, const int* nl, int kvh, int lo_pos,
                                  int lane, int w, int nw, bool head_ok, const half4_t (&qB)[D / 16],
                                  const half8_t* qk_lds, const float (&sumq)[D / GS],
@@ -523,16 +547,30 @@ __device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax
     const int e = sigma * PK + jl;                  // this lane's block
     return e < n ? (uint32_t)lv[e].y : 0u;
   };
+  // alpha is the logit factor for operands in integer code units (2^-24);
+  // float codes enter with their own values.  A wave's steps go through the
+  // classes in order, so with float codes its accumulator holds plain values
+  // until its first ternary (integer-coded) step, where it is brought to code
+  // units once (exact: a power of two).
+  const float alpha_f = FMT ? alpha * kCodeUnit : alpha;
   auto comp = [&](const B& b, int g) {
     if (g < c1)
-      compute_step<D, GS, 8, WINDOW, PK>(b, mask_of(l0, n0, g), lo_pos, lane, head_ok, qB, qk_lds, sumq, alpha,
-                                          st);
+      compute_step<D, GS, 8, FMT, WINDOW, PK>(b, mask_of(l0, n0, g), lo_pos, lane, head_ok, qB, qk_lds, sumq,
+                                               alpha_f, st);
     else if (g < c2)
-      compute_step<D, GS, 4, WINDOW, PK>(b, mask_of(l1, n1, g - c1), lo_pos, lane, head_ok, qB, qk_lds, sumq, alpha,
-                                          st);
-    else
-      compute_step<D, GS, 2, WINDOW, PK>(b, mask_of(l2, n2, g - c2), lo_pos, lane, head_ok, qB, qk_lds, sumq, alpha,
-                                          st);
+      compute_step<D, GS, 4, FMT, WINDOW, PK>(b, mask_of(l1, n1, g - c1), lo_pos, lane, head_ok, qB, qk_lds, sumq,
+                                               alpha_f, st);
+    else {
+      if constexpr (FMT == 1) {
+        if (st.vunit != kCodeScale) {
+#pragma unroll
+          for (int n = 0; n < D / 16; n++) st.acc[n] *= kCodeUnit;
+          st.vunit = kCodeScale;
+        }
+      }
+      compute_step<D, GS, 2, 0, WINDOW, PK>(b, mask_of(l2, n2, g - c2), lo_pos, lane, head_ok, qB, qk_lds, sumq,
+                                             alpha, st);
+    }
   };
   int g = w;
   if (g >= T) return;
@@ -688,7 +726,7 @@ __device__ inline void finalize_head(const AttnParams& P, int b, int hq, int lan
   if (P.n_attended && hq == 0 && lane == 0) P.n_attended[b] = n;
 }
 
-template <int D, int GS, bool WINDOW, int PK>
+template <int D, int GS, bool WINDOW, int PK, int FMT>
 __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   constexpr int NG = D / GS;
   constexpr int KM = GS / 16;
@@ -731,6 +769,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
 #pragma unroll
   for (int i = 0; i < TOPK; i++) st.top[i] = -INFINITY;
   st.thr = -INFINITY;
+  st.vunit = FMT ? 1.0f : kCodeScale;
   // The split's live blocks of each class, into LDS, in list order: wave c
   // (the waves in turn when there are fewer than three) takes class c's
   // block-table entries 64 at a time, reads their block records and keeps,
@@ -827,8 +866,8 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
     }
   }
   __syncthreads();
-  run_steps<D, GS, WINDOW, PK>(P, live, lmax, nlive, kvh, lo_pos, lane, w, nw, head_ok, qB, s_qk, sumq,
-                               alpha * kCodeScale, st);
+  run_steps<D, GS, WINDOW, PK, FMT>(P, live, lmax, nlive, kvh, lo_pos, lane, w, nw, head_ok, qB, s_qk, sumq,
+                                    alpha * kCodeScale, st);
   // The self token of this wave's first head (finalized here with one split):
   // its reads are issued now, so that their latency overlaps the reductions
   // and the record merge (the barriers below order LDS only).
@@ -872,8 +911,9 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
 #pragma unroll
     for (int n = 0; n < NT; n++) {
       const float z = st.zacc[(16 * n) / GS];
-      *(float4*)(rec + 16 * n + 4 * lg) = make_float4(st.acc[n][0] * kCodeScale + z, st.acc[n][1] * kCodeScale + z,
-                                                      st.acc[n][2] * kCodeScale + z, st.acc[n][3] * kCodeScale + z);
+      const float u = st.vunit;
+      *(float4*)(rec + 16 * n + 4 * lg) = make_float4(st.acc[n][0] * u + z, st.acc[n][1] * u + z,
+                                                      st.acc[n][2] * u + z, st.acc[n][3] * u + z);
     }
     if (lg == 0) {
       rec[D] = st.m2; rec[D + 1] = st.Z; rec[D + 2] = st.S2; rec[D + 3] = (float)st.natt;
@@ -978,31 +1018,31 @@ size_t attn_workspace_bytes(const tkv_cache* c, int batch, int splits) {
   return (size_t)batch * c->S.Hq * splits * (c->S.D + PART_X) * sizeof(float);
 }
 
-template <int D, int GS, bool W, int PK>
+template <int D, int GS, bool W, int PK, int FMT>
 static void launch_one(const AttnParams& P, dim3 grid, int nw, int lds, hipStream_t st) {
   static bool attr_set = false;            // dynamic LDS above 64 KiB must be allowed once per kernel
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)k_attn<D, GS, W, PK>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)k_attn<D, GS, W, PK, FMT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               kMaxLds - kStaticLds);
     attr_set = true;
   }
-  k_attn<D, GS, W, PK><<<grid, 64 * nw, lds, st>>>(P);
+  k_attn<D, GS, W, PK, FMT><<<grid, 64 * nw, lds, st>>>(P);
 }
 
-template <int D, int GS>
+template <int D, int GS, int FMT>
 static void launch_attn_t(const AttnParams& P, int batch, int Hkv, int Hq, int nw, int lds, bool window, int pk,
                           hipStream_t st) {
   dim3 grid(P.splits, Hkv, batch);
   constexpr int PK2 = D == 64 || D / GS <= 2 ? 2 : 1;   // (pack_of returns 2 only with at most two groups at D = 128)
   constexpr int PK4 = D == 64 ? 4 : PK2;                // (and 4 only for D = 64)
   if (window) {
-    if (pk == 4) launch_one<D, GS, true, PK4>(P, grid, nw, lds, st);
-    else if (pk == 2) launch_one<D, GS, true, PK2>(P, grid, nw, lds, st);
-    else launch_one<D, GS, true, 1>(P, grid, nw, lds, st);
+    if (pk == 4) launch_one<D, GS, true, PK4, FMT>(P, grid, nw, lds, st);
+    else if (pk == 2) launch_one<D, GS, true, PK2, FMT>(P, grid, nw, lds, st);
+    else launch_one<D, GS, true, 1, FMT>(P, grid, nw, lds, st);
   } else {
-    if (pk == 4) launch_one<D, GS, false, PK4>(P, grid, nw, lds, st);
-    else if (pk == 2) launch_one<D, GS, false, PK2>(P, grid, nw, lds, st);
-    else launch_one<D, GS, false, 1>(P, grid, nw, lds, st);
+    if (pk == 4) launch_one<D, GS, false, PK4, FMT>(P, grid, nw, lds, st);
+    else if (pk == 2) launch_one<D, GS, false, PK2, FMT>(P, grid, nw, lds, st);
+    else launch_one<D, GS, false, 1, FMT>(P, grid, nw, lds, st);
   }
   if (P.splits > 1) k_combine<D><<<dim3((Hq + 3) / 4, batch), 256, 0, st>>>(P);
 }
@@ -1018,9 +1058,17 @@ int launch_attention(tkv_cache* c, const tkv_attn_args* a, int nw, int splits, h
   const int D = c->S.D, g = c->S.g, lds = lds_bytes(c, nw);
   const bool win = a->window > 0;
   const int pk = pack_of(c, c->S.Hq / c->S.Hkv);
-  if (D == 128 && g == 64) launch_attn_t<128, 64>(P, a->batch, c->S.Hkv, c->S.Hq, nw, lds, win, pk, st);
-  else if (D == 128 && g == 32) launch_attn_t<128, 32>(P, a->batch, c->S.Hkv, c->S.Hq, nw, lds, win, pk, st);
-  else if (D == 64 && g == 64) launch_attn_t<64, 64>(P, a->batch, c->S.Hkv, c->S.Hq, nw, lds, win, pk, st);
-  else launch_attn_t<64, 32>(P, a->batch, c->S.Hkv, c->S.Hq, nw, lds, win, pk, st);
+  const int B = a->batch, Hkv = c->S.Hkv, Hq = c->S.Hq;
+  if (c->S.fmt == 0) {
+    if (D == 128 && g == 64) launch_attn_t<128, 64, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+    else if (D == 128 && g == 32) launch_attn_t<128, 32, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+    else if (D == 64 && g == 64) launch_attn_t<64, 64, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+    else launch_attn_t<64, 32, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+  } else {
+    if (D == 128 && g == 64) launch_attn_t<128, 64, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+    else if (D == 128 && g == 32) launch_attn_t<128, 32, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+    else if (D == 64 && g == 64) launch_attn_t<64, 64, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+    else launch_attn_t<64, 32, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+  }
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }

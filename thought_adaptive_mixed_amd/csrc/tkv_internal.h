@@ -37,6 +37,7 @@ struct DevState {
   int32_t* scratch;
   int Hkv, Hq, D, g, NG;
   int NL, Hst;                    // layers; KV heads stored per block (NL * Hkv)
+  int fmt;                        // code format: 0 integer, 1 FP8 / FP4 / ternary
   int type_class[3];              // class index for thought type R, E, T
   int pool_blocks[3];
   int max_seqs, max_blocks, max_segs, max_tokens;
@@ -88,11 +89,17 @@ __host__ __device__ inline int32_t* scr_moves(int32_t* s, int max_seqs) {       
 // permute) puts a pair of codes into the two halves of an MFMA operand word.
 // A chunk is stored in units of U = min(CB, 16) bytes, unit u of chunk k at
 // byte (64u + k) U of its region: lane l's u-th 16-byte load then reads one
-// contiguous kilobyte across the 64 lanes.
+// contiguous kilobyte across the 64 lanes.  Float codes (format 1, the 8- and
+// 4-bit classes) sit in element order instead: the hardware's packed
+// conversions take consecutive fields of a word.  Ternary codes are integers.
 // ---------------------------------------------------------------------------
-__host__ __device__ inline int elem_bit(int e, int bits) {
+__host__ __device__ inline int natural_order(int fmt, int c) { return fmt && c < 2; }
+__host__ __device__ inline int field_pos(int f, int W, int nat) {
+  return nat ? f : (f >> 1) + (f & 1) * (W >> 1);
+}
+__host__ __device__ inline int elem_bit(int e, int bits, int nat) {
   int W = 32 / bits, w = e / W, f = e % W;
-  return w * 32 + ((f >> 1) + (f & 1) * (W >> 1)) * bits;
+  return w * 32 + field_pos(f, W, nat) * bits;
 }
 // byte b of chunk k of a region of chunks of CB bytes -> byte within the region
 __host__ __device__ inline int chunk_byte(int CB, int k, int b) {
@@ -100,15 +107,15 @@ __host__ __device__ inline int chunk_byte(int CB, int k, int b) {
   return (64 * (b / U) + k) * U + b % U;
 }
 // K: token t, dim d -> chunk 16*lg + t, element gi*(g/4) + e'
-__host__ __device__ inline int k_code_bit(int D, int g, int bits, int t, int d) {
+__host__ __device__ inline int k_code_bit(int D, int g, int bits, int nat, int t, int d) {
   int q4 = g >> 2, gi = d / g, w = d % g, lg = w / q4, ep = w % q4;
-  int chunk = 16 * lg + t, eb = elem_bit(gi * q4 + ep, bits);
+  int chunk = 16 * lg + t, eb = elem_bit(gi * q4 + ep, bits, nat);
   return chunk_byte(D * bits / 32, chunk, eb >> 3) * 8 + (eb & 7);
 }
 // V: token t = 4q + r, dim d = 16n + i -> chunk 16*q + i, element 4n + r
-__host__ __device__ inline int v_code_bit(int D, int bits, int t, int d) {
+__host__ __device__ inline int v_code_bit(int D, int bits, int nat, int t, int d) {
   int q = t >> 2, r = t & 3, n = d >> 4, i = d & 15;
-  int chunk = 16 * q + i, eb = elem_bit(4 * n + r, bits);
+  int chunk = 16 * q + i, eb = elem_bit(4 * n + r, bits, nat);
   return 64 * (D * bits / 32) * 8 + chunk_byte(D * bits / 32, chunk, eb >> 3) * 8 + (eb & 7);
 }
 __host__ __device__ inline int meta_byte(int D, int g, int bits, int kv, int t, int gi) {
@@ -219,6 +226,62 @@ __device__ inline unsigned quant_code(float x, float sf, float zf, int bits) {
   r = r < 0.0f ? 0.0f : r;
   r = r > top ? top : r;
   return (unsigned)r;
+}
+
+// ---------------------------------------------------------------------------
+// Float and ternary codes (format 1), per (token, group) with one fp16 scale:
+// class 0 FP8 E4M3 (scale amax/448), class 1 FP4 E2M1 (scale amax/6), both
+// rounded to nearest even and saturated, zero-point 0; class 2 ternary by the
+// Ternary Weight Networks rule (threshold 0.7 mean|x|, scale the mean |x| of
+// the entries beyond it), stored as the integer code t + 1 with zero-point
+// -scale.
+// The encoders work on the fp32 bit pattern: a value below the smallest
+// normal of the format is a multiple of its subnormal step, rounded as an
+// integer; above, the mantissa is cut to the format's width with round to
+// nearest even (a carry into the exponent is the integer add itself).
+// ---------------------------------------------------------------------------
+__device__ inline unsigned e4m3_encode(float y) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, y);
+  const uint32_t a = u & 0x7FFFFFFFu, sgn = (u >> 24) & 0x80u;
+  unsigned mag;
+  if (a >= 0x43E00000u) mag = 0x7E;                                   // |y| >= 448
+  else if (a < 0x3C800000u) {                                         // |y| < 2^-6: steps of 2^-9
+    mag = (unsigned)__builtin_rintf(__builtin_bit_cast(float, a) * 512.0f);
+  } else {
+    // rebias 127 -> 7 and keep 3 mantissa bits, rounding the 20 dropped bits to nearest even
+    const uint32_t r = a - (120u << 23);
+    const uint32_t keep = r >> 20, rest = r & 0xFFFFFu;
+    mag = keep + ((rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ? 1u : 0u);
+  }
+  return mag ? (mag | sgn) : 0u;
+}
+__device__ inline unsigned e2m1_encode(float y) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, y);
+  const uint32_t a = u & 0x7FFFFFFFu, sgn = (u >> 28) & 0x8u;
+  unsigned mag;
+  if (a >= 0x40C00000u) mag = 7;                                      // |y| >= 6
+  else if (a < 0x3F800000u) {                                         // |y| < 1: steps of 1/2
+    mag = (unsigned)__builtin_rintf(__builtin_bit_cast(float, a) * 2.0f);
+  } else {
+    const uint32_t r = a - (126u << 23);                              // rebias 127 -> 1
+    const uint32_t keep = r >> 22, rest = r & 0x3FFFFFu;
+    mag = keep + ((rest > 0x200000u || (rest == 0x200000u && (keep & 1u))) ? 1u : 0u);
+  }
+  return mag ? (mag | sgn) : 0u;
+}
+// value of a float code of class c (0 or 1) in format 1, before the scale
+__device__ inline float fmt_value(int c, unsigned code) {
+  if (c == 0) {
+    const unsigned e = (code >> 3) & 15u, m = code & 7u;
+    const float v = e ? __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    return (code & 0x80u) ? -v : v;
+  }
+  if (c == 1) {
+    const unsigned e = (code >> 1) & 3u, m = code & 1u;
+    const float v = e ? __builtin_bit_cast(float, ((e + 126u) << 23) | (m << 22)) : (float)m * 0.5f;
+    return (code & 8u) ? -v : v;
+  }
+  return (float)code;
 }
 
 // Launchers (state kernels)

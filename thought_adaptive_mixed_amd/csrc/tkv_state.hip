@@ -424,19 +424,65 @@ __device__ void quant_row_wave(const DevState& S, int c, int blk, int t, int h, 
   if (lpg > 16) minmax_level<16>(mn, mx);
   if (lpg > 32) minmax_level<32>(mn, mx);
   // (the sign of a zero extremum cannot change the scale, the zero-point or any code)
-  const float levels = (float)((1 << bits) - 1);
-  const float range = mx - mn;
-  const float s32 = range / levels;
-  const uint16_t sh = f16_bits_rne(s32), zh = f16_bits_rne(mn);
-  const float sf = f16_bits_to_f32(sh), zf = f16_bits_to_f32(zh);
+  uint16_t sh, zh = 0;
+  if (S.fmt == 0) {
+    const float levels = (float)((1 << bits) - 1);
+    const float range = mx - mn;
+    const float s32 = range / levels;
+    sh = f16_bits_rne(s32);
+    zh = f16_bits_rne(mn);
+    const float sf = f16_bits_to_f32(sh), zf = f16_bits_to_f32(zh);
 #pragma unroll
-  for (int e = 0; e < E; e++) codes[lane * E + e] = (uint8_t)quant_code(x[e], sf, zf, bits);
+    for (int e = 0; e < E; e++) codes[lane * E + e] = (uint8_t)quant_code(x[e], sf, zf, bits);
+  } else if (c < 2) {
+    // FP8 / FP4: scale fp16(amax / largest finite value); codes of x / scale
+    const float amax = mx > -mn ? mx : -mn;
+    sh = f16_bits_rne(amax / (c == 0 ? 448.0f : 6.0f));
+    const float sf = f16_bits_to_f32(sh);
+#pragma unroll
+    for (int e = 0; e < E; e++)
+      codes[lane * E + e] = (uint8_t)(sh == 0 ? 0u : (c == 0 ? e4m3_encode(x[e] / sf) : e2m1_encode(x[e] / sf)));
+  } else {
+    // ternary, stored as the integer code t + 1 with zero-point -scale: sums
+    // pairwise over index halves, i.e. the lane's own elements first, then
+    // butterfly levels 1, 2, 4, ... over the group's lanes
+    float sa = __builtin_fabsf(x[0]);
+#pragma unroll
+    for (int e = 1; e < E; e++) sa = sa + __builtin_fabsf(x[e]);
+    if (lpg > 1) sa = pair_sum<1>(sa);
+    if (lpg > 2) sa = pair_sum<2>(sa);
+    if (lpg > 4) sa = pair_sum<4>(sa);
+    if (lpg > 8) sa = pair_sum<8>(sa);
+    if (lpg > 16) sa = pair_sum<16>(sa);
+    if (lpg > 32) sa = pair_sum<32>(sa);
+    const float thr = 0.7f * (sa / (float)g);
+    float sk = 0.0f, nk = 0.0f;
+    unsigned t[E];
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+      t[e] = x[e] > thr ? 2u : (x[e] < -thr ? 0u : 1u);
+      const float k = t[e] != 1u ? __builtin_fabsf(x[e]) : 0.0f;
+      sk = e ? sk + k : k;
+      nk += t[e] != 1u ? 1.0f : 0.0f;
+    }
+    if (lpg > 1) { sk = pair_sum<1>(sk); nk = pair_sum<1>(nk); }
+    if (lpg > 2) { sk = pair_sum<2>(sk); nk = pair_sum<2>(nk); }
+    if (lpg > 4) { sk = pair_sum<4>(sk); nk = pair_sum<4>(nk); }
+    if (lpg > 8) { sk = pair_sum<8>(sk); nk = pair_sum<8>(nk); }
+    if (lpg > 16) { sk = pair_sum<16>(sk); nk = pair_sum<16>(nk); }
+    if (lpg > 32) { sk = pair_sum<32>(sk); nk = pair_sum<32>(nk); }
+    sh = nk > 0.0f ? f16_bits_rne(sk / nk) : (uint16_t)0;
+    zh = sh ? (uint16_t)(sh ^ 0x8000u) : (uint16_t)0;
+#pragma unroll
+    for (int e = 0; e < E; e++) codes[lane * E + e] = (uint8_t)(sh == 0 ? 0u : t[e]);
+  }
   uint8_t* base = pick3(S.pool, c) + ((int64_t)blk * S.Hst + h) * pick3(S.bh_bytes, c);
   if ((lane * E) % g == 0) *(uint32_t*)(base + meta_byte(D, g, bits, kv, t, gi)) = (uint32_t)sh | ((uint32_t)zh << 16);
   wave_lds_sync();
   const int W = 32 / bits;
   const int CB = D * bits / 32;                // bytes per chunk
   const int wpc = CB / 4;                      // words per chunk
+  const int nat = natural_order(S.fmt, c);
   if (kv == 0) {
     // word l: chunk 16*lg + t, word w; element e = w*W + f holds dim (e/(g/4))*g + lg*(g/4) + e%(g/4)
     const int q4 = g / 4;
@@ -446,7 +492,7 @@ __device__ void quant_row_wave(const DevState& S, int c, int blk, int t, int h, 
       for (int f = 0; f < W; f++) {
         const int e = w * W + f;
         const int d = (e / q4) * g + lg * q4 + (e % q4);
-        word |= (uint32_t)codes[d] << (((f >> 1) + (f & 1) * (W >> 1)) * bits);
+        word |= (uint32_t)codes[d] << (field_pos(f, W, nat) * bits);
       }
       *(uint32_t*)(base + chunk_byte(CB, 16 * lg + t, w * 4)) = word;
     }
@@ -459,14 +505,14 @@ __device__ void quant_row_wave(const DevState& S, int c, int blk, int t, int h, 
       uint8_t* wb = vbase + chunk_byte(CB, 16 * q + i, w * 4);     // word w of chunk 16q + i
       if (bits == 8) {
         // word w holds dim n = w for tokens r = 0..3: our byte is field r
-        const int f = r, p = (f >> 1) + (f & 1) * 2;
+        const int p = field_pos(r, 4, nat);
         wb[p] = codes[16 * w + i];
       } else {
         uint32_t mask = 0, val = 0;
         for (int f = 0; f < W; f++) {
           const int e = w * W + f;
           if ((e & 3) != r) continue;
-          const int p = (f >> 1) + (f & 1) * (W >> 1);
+          const int p = field_pos(f, W, nat);
           mask |= ((1u << bits) - 1u) << (p * bits);
           val |= (uint32_t)codes[16 * (e >> 2) + i] << (p * bits);
         }
@@ -700,12 +746,13 @@ __device__ float deq_code(const DevState& S, int c, int blk, int t, int h, int k
 #pragma clang fp contract(off)
   const int bits = class_bits(c);
   const uint8_t* base = pick3(S.pool, c) + ((int64_t)blk * S.Hst + h) * pick3(S.bh_bytes, c);
-  int bit = kv ? v_code_bit(S.D, bits, t, d) : k_code_bit(S.D, S.g, bits, t, d);
+  const int nat = natural_order(S.fmt, c);
+  int bit = kv ? v_code_bit(S.D, bits, nat, t, d) : k_code_bit(S.D, S.g, bits, nat, t, d);
   uint32_t word = *(const uint32_t*)(base + ((bit >> 5) << 2));
   unsigned code = (word >> (bit & 31)) & ((1u << bits) - 1u);
   uint32_t m = *(const uint32_t*)(base + meta_byte(S.D, S.g, bits, kv, t, d / S.g));
   float sf = f16_bits_to_f32((uint16_t)(m & 0xFFFF)), zf = f16_bits_to_f32((uint16_t)(m >> 16));
-  float prod = sf * (float)code;
+  float prod = sf * (nat ? fmt_value(c, code) : (float)code);     // exact product
   return prod + zf;
 }
 
@@ -1482,6 +1529,7 @@ template <int BITS>
 __device__ void compact_copy_block(const DevState& S, int c, int newb, int cnt, const int32_t* src_slot, int tid) {
   constexpr int W = 32 / BITS;
   const int D = S.D, g = S.g, NG = D / g, CB = D * BITS / 32, CW = CB / 4;
+  const int nat = natural_order(S.fmt, c);
   const int64_t R = pick3(S.bh_bytes, c);
   uint8_t* pool = pick3(S.pool, c);
   const int nk = 16 * 4 * CW, nv = 4 * 16 * CW, nm = 16 * 2 * NG, per_head = nk + nv + nm;
@@ -1506,7 +1554,7 @@ __device__ void compact_copy_block(const DevState& S, int c, int newb, int cnt, 
         const uint32_t w = *(const uint32_t*)(sr + 64 * CB + chunk_byte(CB, 16 * qs + i, 4 * wc));
         for (int nn = 0; nn < W / 4; nn++) {
           const int fs = 4 * nn + rs, fd = 4 * nn + r;
-          const int ps = (fs >> 1) + (fs & 1) * (W >> 1), pd = (fd >> 1) + (fd & 1) * (W >> 1);
+          const int ps = field_pos(fs, W, nat), pd = field_pos(fd, W, nat);
           out |= ((w >> (ps * BITS)) & ((1u << BITS) - 1u)) << (pd * BITS);
         }
       }

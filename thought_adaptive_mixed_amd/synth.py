@@ -379,6 +379,13 @@ def layered(w: Workload, num_layers: int) -> Workload:
     return w
 
 
+def page_formats(w: Workload) -> Workload:
+    """The workload stored in the float / ternary code formats (FP8 E4M3 for
+    the 8-bit class, FP4 E2M1 for the 4-bit class, ternary for the 2-bit
+    class): the same calls and inputs."""
+    return dataclasses.replace(w, layout=dataclasses.replace(w.layout, code_format=1))
+
+
 def layer_queries(w: Workload, layer: int, beta=1.0) -> np.ndarray:
     """Seeded bf16 queries [B][Hq][D] of one layer (layer 0: the workload's own)."""
     if layer == 0:
