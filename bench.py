@@ -10,7 +10,8 @@ until it plans nothing before anything is timed.  With --compact every step
 also compacts the sequences it evicted from (tkv_compact, the gather-
 compaction baseline that in-place slot reuse avoids), after every sequence
 was compacted once before timing.  --workload churn256 runs the B256 decode
-loop (lengths 4k..32k, 5% budget) instead of the default.  Workload: the
+loop (lengths 4k..32k, 5% budget) instead of the default.  --formats page
+stores the classes as FP8 E4M3 / FP4 E2M1 / ternary codes.  Workload: the
 Llama-8B-like reasoning-decode layer (B32, Hq32/Hkv8, D128, g64, 16k generated
 tokens per sequence, 10% budget -> 1638 retained, R/E/T 8/4/2-bit) with
 planted-temperature queries, synthetic data.
@@ -181,8 +182,10 @@ def cpu_baseline(w, state, ch, n_seq, budget_s=12.0, max_reps=1000, policy="ladd
 
 
 def workload_name(args):
-    return workload_name_1(args) + (f"; {args.layers} layers per step sharing the block tables (each layer holds the "
-                                    f"one-layer state's records)" if args.layers > 1 else "")
+    return (workload_name_1(args)
+            + (f"; {args.layers} layers per step sharing the block tables (each layer holds the "
+               f"one-layer state's records)" if args.layers > 1 else "")
+            + ("; page code formats (R FP8 E4M3, E FP4 E2M1, T ternary)" if args.formats == "page" else ""))
 
 
 def workload_name_1(args):
@@ -218,6 +221,8 @@ def main():
                     help="layers per decode step sharing the block tables (the one-layer state replicated)")
     ap.add_argument("--workload", choices=("llama8b", "churn256"), default="llama8b",
                     help="the llama8b-like layer (B32, 16k, 10%% budget) or the B256 decode loop (4k..32k, 5%% budget)")
+    ap.add_argument("--formats", choices=("int", "page"), default="int",
+                    help="code formats of the 8/4/2-bit classes: asymmetric integer, or FP8 E4M3 / FP4 E2M1 / ternary")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-only", action="store_true", help="time only the attention call (diagnostic)")
     ap.add_argument("--torch-events", action="store_true", help="time with torch's default events (diagnostic)")
@@ -241,6 +246,8 @@ def main():
     log("[bench] building workload")
     t0 = time.time()
     ch = synth.bench_cycle(steps=total_steps) if args.workload == "llama8b" else synth.churn(steps=total_steps)
+    if args.formats == "page":
+        ch.base = synth.page_formats(ch.base)
     w = ch.base
     L = w.layout
     B = w.seq_ids.size
@@ -402,7 +409,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 MFMA (int8/4/2 codes as exact fp16 subnormals), f32 accumulate",
+        "dtype": ("f16 MFMA (int8/4/2 codes as exact fp16 subnormals), f32 accumulate" if args.formats == "int" else
+                  "f16 MFMA (FP8 E4M3 / FP4 E2M1 codes converted exactly to fp16, ternary codes as fp16 "
+                  "subnormals), f32 accumulate"),
         "data": "synthetic",
         "config": {"workload": workload_name(args),
                    "batch": B, "copies": R, "attended_per_step": tokens / args.steps,
@@ -412,7 +421,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic() if (args.workload == "llama8b" and args.policy == "ladder"
-                                                       and not args.compact and NL == 1) else None,
+                                                       and not args.compact and NL == 1
+                                                       and args.formats == "int") else None,
                      "kernel": "k_attn (paged_decode_attn; one launch per layer and step)",
                      "bytes_per_launch": abytes_step},
     }
