@@ -2,8 +2,9 @@
 
 One step = one pass of the whole path over one batch: paged decode attention
 over the mixed-precision, hole-bearing cache (with the staged self token) ->
-thought_classify -> kv_append_quant of the new token at its label's precision
--> kv_plan_budget (token budget ladder) -> kv_evict_segment.  With
+thought classification and kv_append_quant of the new token at its label's
+precision (one call, kv_classify_append) -> kv_plan_budget (token budget
+ladder) -> kv_evict_segment.  With
 --policy anneal the ladder is replaced by kv_plan_anneal (the TBE annealing
 schedule of the retention, r0 = 64 by default), applied to the built state
 until it plans nothing before anything is timed.  With --compact every step
@@ -338,8 +339,9 @@ def main():
                                     v_self=v, layer=l, stats_stride=NL * Hq * 3, stream=sh, prepare=True)
                         for l in range(NL)])
         calls_b.append([
-            binding.classify(stats.view(B, NL * Hq, 3), ch.tau[0], ch.tau[1], labels, stream=sh, prepare=True),
-            c.append(seq_d, pos, labels, kl if NL > 1 else k, vl if NL > 1 else v, stream=sh, prepare=True),
+            # classification of every layer's statistics rows, inside the append's allocation kernel
+            c.classify_append(seq_d, pos, stats.view(B, NL * Hq, 3), ch.tau[0], ch.tau[1], kl if NL > 1 else k,
+                              vl if NL > 1 else v, labels_out=labels, stream=sh, prepare=True),
             (c.plan_anneal(seq_d, args.r0, max_ops, n_ops, o_seq, o_seg, o_keep, o_bits, stream=sh, prepare=True)
              if args.policy == "anneal" else
              c.plan_budget(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, o_seq, o_seg, o_keep, o_bits,

@@ -167,6 +167,23 @@ int kv_append_quant(tkv_cache* c, int32_t n, const int32_t* seq_ids, const int32
                     const uint8_t* thought, const float* k, const float* v, int32_t* slot_out,
                     hipStream_t stream);
 
+/* kv_classify_append -- thought decomposition bullets (the attention
+ * sparsity of a decode step assigns the type of the token it produces) with
+ * the TBQ bullet (that token is then quantized at its type's precision): the
+ * same result as thought_classify(n, num_q_heads, stats, tau_T, tau_E,
+ * score_kind, labels) followed by kv_append_quant(c, n, seq_ids, positions,
+ * labels, k, v, slot_out), with the classification done inside the append's
+ * allocation kernel (one launch fewer).  Token i takes the label of row i of
+ * stats fp32 [n][num_q_heads][3] (the attention batch in token order; with
+ * several layers num_q_heads = L*Hq).  labels_out (nullable) u8[n] receives
+ * the labels taken.
+ *   EINVAL: n < 0 or n > max_tokens_per_call, num_q_heads < 1, score_kind
+ *   not 0 or 1, or a required pointer NULL. */
+int kv_classify_append(tkv_cache* c, int32_t n, const int32_t* seq_ids, const int32_t* positions,
+                       const float* stats, int32_t num_q_heads, float tau_T, float tau_E, int32_t score_kind,
+                       uint8_t* labels_out, const float* k, const float* v, int32_t* slot_out,
+                       hipStream_t stream);
+
 /* kv_evict_segment -- TBE bullet (progressive eviction at thought-segment
  * granularity; the retention schedule shrinks a segment step by step).
  *   Op i = (seq_ids[i], segment_ids[i], keep_n[i], new_bits[i]): keep the

@@ -24,7 +24,7 @@ NUM_BUFFERS = len(BUFFER_NAMES)
 BUFFER_DTYPES = {n: (np.uint8 if n.startswith("pool") else np.int32) for n in BUFFER_NAMES}
 
 # Entry points declared in include/tkv.h
-SYMBOLS = ["tkv_buffer_sizes", "tkv_create", "tkv_destroy", "tkv_seq_reset", "kv_append_quant",
+SYMBOLS = ["tkv_buffer_sizes", "tkv_create", "tkv_destroy", "tkv_seq_reset", "kv_append_quant", "kv_classify_append",
            "kv_evict_segment", "kv_plan_budget", "kv_plan_anneal", "tkv_compact", "tkv_attn_workspace", "paged_decode_attn",
            "thought_classify", "tkv_get_error", "tkv_export_state", "tkv_import_state", "tkv_strerror"]
 
@@ -69,6 +69,7 @@ def load(path: str = LIB_PATH):
     L.tkv_destroy.argtypes = [P]
     L.tkv_seq_reset.argtypes = [P, I, P, P]
     L.kv_append_quant.argtypes = [P, I, P, P, P, P, P, P, P]
+    L.kv_classify_append.argtypes = [P, I, P, P, P, I, C.c_float, C.c_float, I, P, P, P, P, P]
     L.kv_evict_segment.argtypes = [P, I, P, P, P, P, P, P]
     L.kv_plan_budget.argtypes = [P, I, P, I, I, I, P, P, P, P, P, P]
     L.kv_plan_anneal.argtypes = [P, I, P, I, I, P, P, P, P, P, P]
@@ -200,6 +201,16 @@ class Cache:
         args = (self.h, n, _ptr(seq_ids), _ptr(positions), _ptr(thought), _ptr(k), _ptr(v), _ptr(slot_out),
                 _stream(stream))
         return _issue(self.L.kv_append_quant, args, "kv_append_quant", prepare)
+
+    def classify_append(self, seq_ids, positions, stats, tau_T, tau_E, k, v, labels_out=None, score_kind=0,
+                        slot_out=None, *, stream=None, prepare=False):
+        """thought_classify of `stats` rows followed by kv_append_quant with those
+        labels, in one launch sequence (kv_classify_append)."""
+        n = int(seq_ids.numel())
+        heads = int(stats.numel()) // (3 * n) if n else 1     # every head of every layer in a row
+        args = (self.h, n, _ptr(seq_ids), _ptr(positions), _ptr(stats), heads, C.c_float(tau_T), C.c_float(tau_E),
+                int(score_kind), _ptr(labels_out), _ptr(k), _ptr(v), _ptr(slot_out), _stream(stream))
+        return _issue(self.L.kv_classify_append, args, "kv_classify_append", prepare)
 
     def evict(self, seq_ids, seg_ids, keep_n, new_bits, n_ops_dev=None, n_ops=None, *, stream=None, prepare=False):
         n = int(seq_ids.numel()) if n_ops is None else int(n_ops)

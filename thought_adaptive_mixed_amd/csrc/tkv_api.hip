@@ -137,6 +137,18 @@ extern "C" int kv_append_quant(tkv_cache* c, int32_t n, const int32_t* seq_ids, 
   return launch_append(c, n, seq_ids, positions, thought, k, v, slot_out, stream);
 }
 
+extern "C" int kv_classify_append(tkv_cache* c, int32_t n, const int32_t* seq_ids, const int32_t* positions,
+                                  const float* stats, int32_t num_q_heads, float tau_T, float tau_E,
+                                  int32_t score_kind, uint8_t* labels_out, const float* k, const float* v,
+                                  int32_t* slot_out, hipStream_t stream) {
+  if (!c || n < 0 || n > c->S.max_tokens) return TKV_EINVAL;
+  if (num_q_heads < 1 || (score_kind != 0 && score_kind != 1)) return TKV_EINVAL;
+  if (n > 0 && (!seq_ids || !positions || !stats || !k || !v)) return TKV_EINVAL;
+  c->last_stream = stream;
+  const ClassifyIn cl = {stats, num_q_heads, score_kind, tau_T, tau_E, labels_out};
+  return launch_append(c, n, seq_ids, positions, nullptr, k, v, slot_out, stream, &cl);
+}
+
 extern "C" int kv_evict_segment(tkv_cache* c, int32_t n_ops, const int32_t* n_ops_dev, const int32_t* seq_ids,
                                 const int32_t* segment_ids, const int32_t* keep_n, const uint8_t* new_bits,
                                 hipStream_t stream) {

@@ -21,9 +21,11 @@
 //                                         lane's 16 dims of a group per k slice
 //   O^T[d][h] += sum_t V[t][d] P'[t][h]   A = V codes, a lane's 4 tokens of two
 //                                         blocks per k slice
-// Codes enter the MFMA as fp16 subnormals (bit pattern = code, value code *
-// 2^-24), so the operand is the masked code word itself; products are exact
-// and the 2^24 is folded back in fp32.  The fp16 scales and zero-points are
+// Integer codes enter the MFMA as fp16 subnormals (8-bit code c as the bit
+// pattern c, value c * 2^-24; 4- and 2-bit codes at the top of the subnormal
+// mantissa, c * 2^-18 and c * 2^-16), so an operand is the masked (and
+// shifted) code word itself; products are exact and the power of two is
+// folded back in fp32, per class.  The fp16 scales and zero-points are
 // applied per (token, group) in fp32:
 //   logit = (sum_g sK * (q_g . c_g) + zK * sum(q_g)) / sqrt(D)
 //   out   = sum_t (p sV) c  +  sum_t p zV          (per group of dims)
@@ -48,6 +50,7 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 #define PART_X 16          // extra floats per partial record: m2, Z, S2, n, top8[8], pad
 #define TOPK 8
@@ -67,15 +70,22 @@ __device__ inline void lds_barrier() {
 }
 
 // ---------------------------------------------------------------------------
-// code -> fp16 operands.  A code c enters the MFMA as the fp16 subnormal with
-// bit pattern c, i.e. the value c * 2^-24: products with the fp16 queries or
+// code -> fp16 operands.  An integer code c enters the MFMA as an fp16
+// subnormal, the value c * 2^-kUnitExp: products with the fp16 queries or
 // probabilities are exact in fp32 and every partial sum is the plain code
-// product scaled by 2^-24, so the scale is folded back exactly afterwards
-// (into the logit factor on the K side, into the accumulator on the V side).
+// product times that power of two, folded back exactly afterwards (into the
+// logit factor on the K side, into the accumulator's unit on the V side).
 // ---------------------------------------------------------------------------
 typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 constexpr float kCodeUnit = 0x1p-24f;     // value of the fp16 subnormal with bit pattern 1
 constexpr float kCodeScale = 0x1p24f;
+// The 4- and 2-bit codes are placed at the top of the 10-bit subnormal
+// mantissa (bits 6..9 and 8..9), so that code 1 is 2^-18 and 2^-16: measured
+// on gfx950, the f16 MFMA loses precision on subnormal inputs whose leading
+// mantissa bits are zero (codes at bits 0..1 gave errors of 2.6e-4 of the
+// largest product, at bits 8..9 6e-7; 8-bit codes at bits 0..7 1e-5).
+template <int BITS>
+constexpr int kUnitExp = BITS == 8 ? 24 : (BITS == 4 ? 18 : 16);   // integer code 1 is 2^-kUnitExp
 // fields p and p + W/2 of word w (elements 2p, 2p+1 of the word), one per half
 template <int BITS>
 __device__ inline uint32_t code_pair(uint32_t w, int p) {
@@ -84,14 +94,10 @@ __device__ inline uint32_t code_pair(uint32_t w, int p) {
     const uint32_t sel = (uint32_t)p | (0x0cu << 8) | ((uint32_t)(p + 2) << 16) | (0x0cu << 24);
     return __builtin_amdgcn_perm(0u, w, sel);
   } else {
-    constexpr int W = 32 / BITS;
-    constexpr uint32_t M = ((1u << BITS) - 1u) * 0x00010001u;
-    if (p == W / 2 - 1) {
-      // the top field of each half: a packed 16-bit shift leaves nothing above it
-      const ushort2_t h = __builtin_bit_cast(ushort2_t, w) >> (ushort2_t){(unsigned short)(p * BITS), (unsigned short)(p * BITS)};
-      return __builtin_bit_cast(uint32_t, h);
-    }
-    return (w >> (p * BITS)) & M;
+    // field p of each half moved to bits 10-BITS .. 9 of that half
+    constexpr uint32_t M = (((1u << BITS) - 1u) << (10 - BITS)) * 0x00010001u;
+    const int sh = p * BITS - (10 - BITS);
+    return (sh >= 0 ? (w >> sh) : (w << -sh)) & M;
   }
 }
 // Elements e0 .. e0+3 (e0 a multiple of 4) of a lane's chunk as an fp16
@@ -187,7 +193,7 @@ struct AttnState {
   float m2, Z, S2;
   float top[TOPK];
   float thr;                   // head-wide 8th-best of the top lists
-  float vunit;                 // value of one accumulator unit (2^24 once integer codes entered, else 1)
+  float vunit;                 // value of one V-side accumulator unit (the unit of the class last computed)
   int natt;
 };
 
@@ -280,6 +286,9 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
   constexpr int NT = D / 16;
   constexpr int GP = 16 / PK;
   const int lg = lane >> 4, jl = (lane & 15) / GP;
+  // integer codes of this class are in units of 2^-kUnitExp; the zero-point
+  // term's sum of q (in units of 2^-24) is brought to the same unit
+  constexpr float kSumqScale = (FMT == 1 && BITS != 2) ? 1.0f : (float)(1u << (24 - kUnitExp<BITS>));
   // S^T = K Q^T per group, the PK blocks packed side by side.  PK = 1: a
   // lane's 16 elements of a group are two 8-element k slices.  PK > 1: a k
   // slice holds the same 4 elements of blocks 2p and 2p+1, and the query
@@ -324,6 +333,15 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
   }
   st.natt += __builtin_popcount(valid);
   const uint32_t vb = head_ok ? valid : 0u;
+  // (made opaque so that the three classes' scaled copies are not all held
+  // in registers across the loop)
+  float sq_c[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; gi++) {
+    float t = sumq[gi];
+    if constexpr (kSumqScale != 1.0f) asm volatile("" : "+v"(t));
+    sq_c[gi] = t * kSumqScale;
+  }
   float s2[4];
   float lmax = -INFINITY;
 #pragma unroll
@@ -332,7 +350,7 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
 #pragma unroll
     for (int gi = 0; gi < NG; gi++) {
       const uint32_t m = b.mk[r * NG + gi];
-      x = fmaf(h_lo(m), spk[gi][r], fmaf(h_hi(m), sumq[gi], x));
+      x = fmaf(h_lo(m), spk[gi][r], fmaf(h_hi(m), sq_c[gi], x));
     }
     s2[r] = ((vb >> r) & 1u) ? x * alpha : -INFINITY;
     lmax = fmaxf(lmax, s2[r]);
@@ -391,10 +409,15 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
       z = fmaf(p[r], h_hi(m), z);
     }
     st.zacc[gi] = z;
-    half2_t h01 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1]));
-    half2_t h23 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pv[2], pv[3]));
-    half2_t l01 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pv[0] - (float)h01[0], pv[1] - (float)h01[1]));
-    half2_t l23 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pv[2] - (float)h23[0], pv[3] - (float)h23[1]));
+    // round to nearest (v_cvt_pk_f16_f32): the residual of the hi part is
+    // exact in fp32, and the lo part's rounding error is unbiased.  Rounding
+    // toward zero made every term's error one-signed: with sharp attention the
+    // many small P' terms (whose lo part sits in the fp16 subnormal range,
+    // step 2^-24) then added up to ~2e-3 on large-valued channels.
+    const half2_t h01 = __builtin_convertvector((float2_t){pv[0], pv[1]}, half2_t);
+    const half2_t h23 = __builtin_convertvector((float2_t){pv[2], pv[3]}, half2_t);
+    const half2_t l01 = __builtin_convertvector((float2_t){pv[0] - (float)h01[0], pv[1] - (float)h01[1]}, half2_t);
+    const half2_t l23 = __builtin_convertvector((float2_t){pv[2] - (float)h23[0], pv[3] - (float)h23[1]}, half2_t);
     pbh[gi] = (half4_t){h01[0], h01[1], h23[0], h23[1]};
     pbl[gi] = (half4_t){l01[0], l01[1], l23[0], l23[1]};
   }
@@ -547,29 +570,36 @@ __device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax
     const int e = sigma * PK + jl;                  // this lane's block
     return e < n ? (uint32_t)lv[e].y : 0u;
   };
-  // alpha is the logit factor for operands in integer code units (2^-24);
-  // float codes enter with their own values.  A wave's steps go through the
-  // classes in order, so with float codes its accumulator holds plain values
-  // until its first ternary (integer-coded) step, where it is brought to code
-  // units once (exact: a power of two).
-  const float alpha_f = FMT ? alpha * kCodeUnit : alpha;
-  auto comp = [&](const B& b, int g) {
-    if (g < c1)
-      compute_step<D, GS, 8, FMT, WINDOW, PK>(b, mask_of(l0, n0, g), lo_pos, lane, head_ok, qB, qk_lds, sumq,
-                                               alpha_f, st);
-    else if (g < c2)
-      compute_step<D, GS, 4, FMT, WINDOW, PK>(b, mask_of(l1, n1, g - c1), lo_pos, lane, head_ok, qB, qk_lds, sumq,
-                                               alpha_f, st);
-    else {
-      if constexpr (FMT == 1) {
-        if (st.vunit != kCodeScale) {
+  // alpha is the logit factor for plain values.  The operands of a class are
+  // its codes in units of 2^-kUnitExp (integer codes) or the values themselves
+  // (float codes), so each class has its own logit factor, and the V-side
+  // accumulator has a unit too.  A wave's steps go through the classes in
+  // order: at its first step of a class with another unit, the accumulator is
+  // brought to that unit once (a power of two, exact), and st.vunit carries
+  // the unit to the epilogue.
+  constexpr float u0 = FMT ? 1.0f : (float)(1u << kUnitExp<8>);
+  constexpr float u1 = FMT ? 1.0f : (float)(1u << kUnitExp<4>);
+  constexpr float u2 = (float)(1u << kUnitExp<2>);
+  auto to_unit = [&](float u) {
+    if (st.vunit != u) {
+      const float f = st.vunit / u;
 #pragma unroll
-          for (int n = 0; n < D / 16; n++) st.acc[n] *= kCodeUnit;
-          st.vunit = kCodeScale;
-        }
-      }
+      for (int n = 0; n < D / 16; n++) st.acc[n] *= f;
+      st.vunit = u;
+    }
+  };
+  auto comp = [&](const B& b, int g) {
+    if (g < c1) {
+      compute_step<D, GS, 8, FMT, WINDOW, PK>(b, mask_of(l0, n0, g), lo_pos, lane, head_ok, qB, qk_lds, sumq,
+                                               alpha * u0, st);
+    } else if (g < c2) {
+      to_unit(u1);
+      compute_step<D, GS, 4, FMT, WINDOW, PK>(b, mask_of(l1, n1, g - c1), lo_pos, lane, head_ok, qB, qk_lds, sumq,
+                                               alpha * u1, st);
+    } else {
+      to_unit(u2);
       compute_step<D, GS, 2, 0, WINDOW, PK>(b, mask_of(l2, n2, g - c2), lo_pos, lane, head_ok, qB, qk_lds, sumq,
-                                             alpha, st);
+                                             alpha * u2, st);
     }
   };
   int g = w;
@@ -769,7 +799,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
 #pragma unroll
   for (int i = 0; i < TOPK; i++) st.top[i] = -INFINITY;
   st.thr = -INFINITY;
-  st.vunit = FMT ? 1.0f : kCodeScale;
+  st.vunit = FMT ? 1.0f : kCodeScale;        // the unit of the first class (8-bit codes)
   // The split's live blocks of each class, into LDS, in list order: wave c
   // (the waves in turn when there are fewer than three) takes class c's
   // block-table entries 64 at a time, reads their block records and keeps,
@@ -867,7 +897,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   }
   __syncthreads();
   run_steps<D, GS, WINDOW, PK, FMT>(P, live, lmax, nlive, kvh, lo_pos, lane, w, nw, head_ok, qB, s_qk, sumq,
-                                    alpha * kCodeScale, st);
+                                    alpha, st);
   // The self token of this wave's first head (finalized here with one split):
   // its reads are issued now, so that their latency overlaps the reductions
   // and the record merge (the barriers below order LDS only).

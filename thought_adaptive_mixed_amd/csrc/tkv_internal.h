@@ -284,10 +284,34 @@ __device__ inline float fmt_value(int c, unsigned code) {
   return (float)code;
 }
 
+// ---------------------------------------------------------------------------
+// Thought label of one batch entry from its statistics row (heads x {H,
+// H/ln n, M_k}): fp32 sum in head order of H/ln n (kind 0) or 1 - M_k (kind
+// 1), divided by the head count; T at or below tT, E at or above tE, else R.
+// ---------------------------------------------------------------------------
+struct ClassifyIn {
+  const float* stats;           // [n][heads][3]; null: the thought labels are an input
+  int heads, kind;
+  float tT, tE;
+  uint8_t* labels;              // nullable: the labels taken, [n]
+};
+__device__ inline uint32_t thought_label(float score, float tT, float tE) {
+  return score <= tT ? (uint32_t)TKV_T : (score >= tE ? (uint32_t)TKV_E : (uint32_t)TKV_R);
+}
+__device__ inline uint32_t classify_row(const float* row, const ClassifyIn& cl) {
+#pragma clang fp contract(off)
+  float sum = 0.0f;
+  for (int h = 0; h < cl.heads; h++) {
+    const float v = cl.kind == 0 ? row[3 * h + 1] : 1.0f - row[3 * h + 2];
+    sum = sum + v;
+  }
+  return thought_label(sum / (float)cl.heads, cl.tT, cl.tE);
+}
+
 // Launchers (state kernels)
 int launch_init(tkv_cache* c, hipStream_t st);
 int launch_append(tkv_cache* c, int n, const int32_t* seq_ids, const int32_t* pos, const uint8_t* thought,
-                  const float* k, const float* v, int32_t* slot_out, hipStream_t st);
+                  const float* k, const float* v, int32_t* slot_out, hipStream_t st, const ClassifyIn* cl = nullptr);
 int launch_evict(tkv_cache* c, int n_ops, const int32_t* n_ops_dev, const int32_t* seq_ids, const int32_t* seg_ids,
                  const int32_t* keep_n, const uint8_t* new_bits, hipStream_t st);
 int launch_plan(tkv_cache* c, int n, const int32_t* seq_ids, int num, int den, int max_ops, int32_t* n_ops_dev,

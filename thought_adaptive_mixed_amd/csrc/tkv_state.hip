@@ -295,7 +295,7 @@ __device__ void append_walk(const DevState& S, int s, SeqRec w, const C3& top, i
 }
 
 __global__ __launch_bounds__(WG) void k_append_alloc(DevState S, int n, const int32_t* seq_ids, const int32_t* pos,
-                                                     const uint8_t* thought, int32_t* slot_out) {
+                                                     const uint8_t* thought, int32_t* slot_out, ClassifyIn cl) {
   __shared__ __align__(16) uint16_t s_seq[TKV_MAX_TOK];
   __shared__ uint16_t s_list[TKV_MAX_TOK];
   __shared__ uint16_t s_idx[TKV_MAX_TOK];
@@ -313,7 +313,14 @@ __global__ __launch_bounds__(WG) void k_append_alloc(DevState S, int n, const in
   if (tid < 3) { dry_from[tid] = TKV_INF; avail[tid] = S.hdr[H_FREE + tid]; }
   for (int i = tid; i < n; i += NT) {
     const int s = seq_ids[i];
-    const uint32_t y = thought[i];
+    // the token's thought type: given, or classified here from its entry's statistics
+    uint32_t y;
+    if (cl.stats) {
+      y = classify_row(cl.stats + (int64_t)i * cl.heads * 3, cl);
+      if (cl.labels) cl.labels[i] = (uint8_t)y;
+    } else {
+      y = thought[i];
+    }
     const int p = pos[i];
     info[i] = -1;
     if (slot_out) slot_out[i] = -1;
@@ -546,9 +553,11 @@ __global__ __launch_bounds__(256) void k_append_store(DevState S, int n, const f
 }
 
 int launch_append(tkv_cache* c, int n, const int32_t* seq_ids, const int32_t* pos, const uint8_t* thought,
-                  const float* k, const float* v, int32_t* slot_out, hipStream_t st) {
+                  const float* k, const float* v, int32_t* slot_out, hipStream_t st, const ClassifyIn* cl) {
   if (n == 0) return TKV_OK;
-  k_append_alloc<<<1, walker_threads(c->S.max_seqs), 0, st>>>(c->S, n, seq_ids, pos, thought, slot_out);
+  const ClassifyIn none = {nullptr, 0, 0, 0.f, 0.f, nullptr};
+  k_append_alloc<<<1, walker_threads(c->S.max_seqs), 0, st>>>(c->S, n, seq_ids, pos, thought, slot_out,
+                                                              cl ? *cl : none);
   const int64_t rows = (int64_t)n * c->S.Hst * 2;
   const int blocks = (int)((rows + 3) / 4);
   if (c->S.D == 128) k_append_store<2><<<blocks, 256, 0, st>>>(c->S, n, k, v);
@@ -1816,7 +1825,7 @@ __global__ __launch_bounds__(256) void k_classify(int batch, int Hq, const float
       sum = sum + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
   }
   const float score = sum / (float)Hq;
-  if (lane == 0) labels[b] = score <= tT ? (uint8_t)TKV_T : (score >= tE ? (uint8_t)TKV_E : (uint8_t)TKV_R);
+  if (lane == 0) labels[b] = (uint8_t)thought_label(score, tT, tE);
 }
 
 int launch_classify(int batch, int Hq, const float* stats, float tau_T, float tau_E, int kind, uint8_t* labels,
