@@ -300,10 +300,21 @@ __device__ inline uint32_t thought_label(float score, float tT, float tE) {
 }
 __device__ inline uint32_t classify_row(const float* row, const ClassifyIn& cl) {
 #pragma clang fp contract(off)
+  // 16 heads' values are read together (independent loads in flight), then
+  // added in head order
+  const int off = cl.kind == 0 ? 1 : 2;
   float sum = 0.0f;
-  for (int h = 0; h < cl.heads; h++) {
-    const float v = cl.kind == 0 ? row[3 * h + 1] : 1.0f - row[3 * h + 2];
-    sum = sum + v;
+  int h = 0;
+  for (; h + 16 <= cl.heads; h += 16) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; j++) v[j] = row[3 * (h + j) + off];
+#pragma unroll
+    for (int j = 0; j < 16; j++) sum = sum + (cl.kind == 0 ? v[j] : 1.0f - v[j]);
+  }
+  for (; h < cl.heads; h++) {
+    const float v = row[3 * h + off];
+    sum = sum + (cl.kind == 0 ? v : 1.0f - v);
   }
   return thought_label(sum / (float)cl.heads, cl.tT, cl.tE);
 }
