@@ -4,7 +4,7 @@ One step = one pass of the whole path over one batch: paged decode attention
 over the mixed-precision, hole-bearing cache (with the staged self token) ->
 thought classification and kv_append_quant of the new token at its label's
 precision (one call, kv_classify_append) -> kv_plan_budget (token budget
-ladder) -> kv_evict_segment.  With
+ladder) -> kv_evict_segment (the two in one call, kv_plan_budget_evict).  With
 --policy anneal the ladder is replaced by kv_plan_anneal (the TBE annealing
 schedule of the retention, r0 = 64 by default), applied to the built state
 until it plans nothing before anything is timed.  With --compact every step
@@ -342,12 +342,13 @@ def main():
             # classification of every layer's statistics rows, inside the append's allocation kernel
             c.classify_append(seq_d, pos, stats.view(B, NL * Hq, 3), ch.tau[0], ch.tau[1], kl if NL > 1 else k,
                               vl if NL > 1 else v, labels_out=labels, stream=sh, prepare=True),
-            (c.plan_anneal(seq_d, args.r0, max_ops, n_ops, o_seq, o_seg, o_keep, o_bits, stream=sh, prepare=True)
+        ] + ([c.plan_anneal(seq_d, args.r0, max_ops, n_ops, o_seq, o_seg, o_keep, o_bits, stream=sh, prepare=True),
+              c.evict(o_seq, o_seg, o_keep, o_bits, n_ops_dev=n_ops, n_ops=max_ops, stream=sh, prepare=True)]
              if args.policy == "anneal" else
-             c.plan_budget(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, o_seq, o_seg, o_keep, o_bits,
-                           stream=sh, prepare=True)),
-            c.evict(o_seq, o_seg, o_keep, o_bits, n_ops_dev=n_ops, n_ops=max_ops, stream=sh, prepare=True),
-        ] + ([c.compact(o_seq, n_dev=n_ops, n=max_ops, stream=sh, prepare=True)] if args.compact else []))
+             # the ladder and the eviction's planning in one kernel (kv_plan_budget_evict)
+             [c.plan_budget_evict(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, o_seq, o_seg, o_keep, o_bits,
+                                  stream=sh, prepare=True)])
+          + ([c.compact(o_seq, n_dev=n_ops, n=max_ops, stream=sh, prepare=True)] if args.compact else []))
 
     # Steps are launched eagerly on torch's current stream: on this stack a
     # replayed HIP graph per step measured slower than direct launches.  The

@@ -216,6 +216,16 @@ int kv_plan_budget(tkv_cache* c, int32_t n, const int32_t* seq_ids, int32_t budg
                    int32_t budget_den, int32_t max_ops, int32_t* n_ops_dev, int32_t* op_seq,
                    int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t stream);
 
+/* kv_plan_budget_evict -- the same result as kv_plan_budget(c, n, seq_ids,
+ * budget_num, budget_den, max_ops, n_ops_dev, op_*) followed by
+ * kv_evict_segment(c, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits),
+ * with the ladder and the eviction's planning in one work-group (one launch
+ * fewer).  The op list is written to op_* and *n_ops_dev as by
+ * kv_plan_budget.  Errors as the two calls'. */
+int kv_plan_budget_evict(tkv_cache* c, int32_t n, const int32_t* seq_ids, int32_t budget_num, int32_t budget_den,
+                         int32_t max_ops, int32_t* n_ops_dev, int32_t* op_seq, int32_t* op_seg, int32_t* op_keep,
+                         uint8_t* op_bits, hipStream_t stream);
+
 /* kv_plan_anneal -- the annealing schedule of TBE (TBE bullet: once a
  * Transition thought is detected, the earlier Reasoning/Execution segments are
  * evicted progressively, the retention shrinking on a schedule such as 64, 32,

@@ -113,3 +113,52 @@ def test_classify_append_layers_and_kind():
         assert np.array_equal(la.cpu().numpy(), lb.cpu().numpy()), (kind, NL)
         assert len(set(la.cpu().numpy().tolist())) > 1
     helpers.compare_states(L, ga.export(), gb.export(), "fused vs two calls")
+
+
+def test_plan_budget_evict_lockstep():
+    """Decode loop on three caches: kv_plan_budget_evict, kv_plan_budget then
+    kv_evict_segment, and the oracle; op lists equal every step (device and
+    oracle), states every 8 steps, error words at the end."""
+    import torch
+    import oracle
+    ch = synth.small_churn(seed=98, steps=64)
+    w = ch.base
+    L = w.layout
+    say("[fused-plan] build")
+    oc = helpers.build_oracle(w)
+    ga = helpers.build_gpu(w)
+    gb = helpers.build_gpu(w)
+    dv = helpers.dev
+    seq_d = dv(w.seq_ids, np.int32)
+    max_ops = 64
+    bufs = {tag: [torch.zeros(1, dtype=torch.int32, device="cuda")] +
+                 [torch.zeros(max_ops, dtype=torch.int32, device="cuda") for _ in range(3)] +
+                 [torch.zeros(max_ops, dtype=torch.uint8, device="cuda")] for tag in ("a", "b")}
+    tT, tE = ch.tau
+    n_evict = n_down = 0
+    for s in range(ch.steps):
+        q, k, v, pos = ch.step_inputs(s)
+        ro, rs, rn = oc.attention(w.seq_ids, pos, q, k_self=k, v_self=v)
+        lab = oracle.classify(rs.astype(np.float32), tT, tE)
+        for g in (ga, gb):
+            g.append(seq_d, dv(pos, np.int32), dv(lab, np.uint8), dv(k, np.float32), dv(v, np.float32))
+        oc.append(w.seq_ids, pos, lab, k, v)
+        ga.plan_budget_evict(seq_d, ch.budget[0], ch.budget[1], max_ops, *bufs["a"])
+        gb.plan_budget(seq_d, ch.budget[0], ch.budget[1], max_ops, *bufs["b"])
+        gb.evict(*bufs["b"][1:], n_ops_dev=bufs["b"][0], n_ops=max_ops)
+        ops = oc.plan_budget(w.seq_ids, ch.budget[0], ch.budget[1], max_ops)
+        torch.cuda.synchronize()
+        m = int(bufs["a"][0].item())
+        assert m == int(bufs["b"][0].item()) == ops[0].size, f"op count step {s}"
+        for xa, xb, xo in zip(bufs["a"][1:], bufs["b"][1:], ops):
+            assert np.array_equal(xa.cpu().numpy()[:m], xo) and np.array_equal(xb.cpu().numpy()[:m], xo), s
+        if m:
+            oc.evict(*ops)
+            n_down += int((ops[3] == 2).sum()); n_evict += int((ops[3] == 0).sum())
+        if s % 8 == 7 or s == ch.steps - 1:
+            ea = ga.export()
+            helpers.compare_states(L, ea, gb.export(), f"fused plan vs two calls, step {s}")
+            helpers.compare_states(L, ea, oc.export(), f"fused plan vs oracle, step {s}")
+    say(f"[fused-plan] steps={ch.steps} evictions={n_evict} downgrades={n_down}")
+    assert n_evict > 0 and n_down > 0
+    assert ga.get_error() == gb.get_error() == oc.error()

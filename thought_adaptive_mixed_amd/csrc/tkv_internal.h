@@ -327,6 +327,8 @@ int launch_evict(tkv_cache* c, int n_ops, const int32_t* n_ops_dev, const int32_
                  const int32_t* keep_n, const uint8_t* new_bits, hipStream_t st);
 int launch_plan(tkv_cache* c, int n, const int32_t* seq_ids, int num, int den, int max_ops, int32_t* n_ops_dev,
                 int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st);
+int launch_plan_evict(tkv_cache* c, int n, const int32_t* seq_ids, int num, int den, int max_ops, int32_t* n_ops_dev,
+                      int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st);
 int launch_anneal(tkv_cache* c, int n, const int32_t* seq_ids, int r0, int max_ops, int32_t* n_ops_dev,
                   int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st);
 int launch_compact(tkv_cache* c, int n, const int32_t* n_dev, const int32_t* seq_ids, hipStream_t st);

@@ -626,9 +626,9 @@ __device__ void evict_walk(const DevState& S, int s, const SeqRec& rec, int cnt,
 }
 
 #define EV_STAGE 1024     // ops whose fields are staged in LDS
-__global__ __launch_bounds__(WG) void k_evict_plan(DevState S, int n_cap, const int32_t* n_dev, const int32_t* seq_ids,
-                                                   const int32_t* g_seg, const int32_t* g_keep,
-                                                   const uint8_t* g_bits) {
+__device__ __forceinline__ void evict_plan_body(const DevState& S, int n_cap, const int32_t* n_dev,
+                                                const int32_t* seq_ids, const int32_t* g_seg,
+                                                const int32_t* g_keep, const uint8_t* g_bits) {
   __shared__ __align__(16) uint16_t s_seq[TKV_MAX_TOK];
   __shared__ uint16_t s_list[TKV_MAX_TOK];
   __shared__ int32_t s_ni[TKV_MAX_TOK];       // fresh blocks an op needs | index of its first pop << 9
@@ -744,6 +744,11 @@ __global__ __launch_bounds__(WG) void k_evict_plan(DevState S, int n_cap, const 
     grp[2 * S.max_seqs + tid] = ndown;
   }
   if (tid < 3) { misc[tid] = avail[tid]; S.hdr[H_FREE + tid] = avail[tid] - total[tid]; }
+}
+__global__ __launch_bounds__(WG) void k_evict_plan(DevState S, int n_cap, const int32_t* n_dev, const int32_t* seq_ids,
+                                                   const int32_t* g_seg, const int32_t* g_keep,
+                                                   const uint8_t* g_bits) {
+  evict_plan_body(S, n_cap, n_dev, seq_ids, g_seg, g_keep, g_bits);
 }
 
 // Evict, part 2: one work-group per sequence applies its own ops in list order.
@@ -1258,8 +1263,9 @@ __device__ int ladder_wave(const DevState& S, int s, int num, int den, int base,
 }
 
 #define PL_STAGE_R 256     // over-budget sequences whose first ops are staged in LDS
-__global__ __launch_bounds__(WG) void k_plan(DevState S, int n, const int32_t* seq_ids, int num, int den, int max_ops,
-                                             int32_t* n_ops, int32_t* os, int32_t* og, int32_t* ok, uint8_t* ob) {
+__device__ __forceinline__ void plan_body(const DevState& S, int n, const int32_t* seq_ids, int num, int den,
+                                          int max_ops, int32_t* n_ops, int32_t* os, int32_t* og, int32_t* ok,
+                                          uint8_t* ob) {
   __shared__ uint16_t s_over[TKV_MAX_TOK];   // items over budget, in list order
   __shared__ int s_cnt[TKV_MAX_TOK];         // their op counts
   __shared__ int s_base[TKV_MAX_TOK];        // their first op's index
@@ -1311,12 +1317,36 @@ __global__ __launch_bounds__(WG) void k_plan(DevState S, int n, const int32_t* s
   }
   if (tid == 0) *n_ops = tot2[0] < max_ops ? tot2[0] : max_ops;
 }
+__global__ __launch_bounds__(WG) void k_plan(DevState S, int n, const int32_t* seq_ids, int num, int den, int max_ops,
+                                             int32_t* n_ops, int32_t* os, int32_t* og, int32_t* ok, uint8_t* ob) {
+  plan_body(S, n, seq_ids, num, den, max_ops, n_ops, os, og, ok, ob);
+}
 
 int launch_plan(tkv_cache* c, int n, const int32_t* seq_ids, int num, int den, int max_ops, int32_t* n_ops_dev,
                 int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st) {
   // a wave per listed sequence, up to 16 waves
   const int nt = n < 1 ? 64 : (n >= WG / 64 ? WG : 64 * n);
   k_plan<<<1, nt, 0, st>>>(c->S, n, seq_ids, num, den, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits);
+  return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
+}
+
+// The ladder and the first part of the eviction in one work-group: the op
+// list the ladder writes (global memory) is read back by the same
+// work-group after a barrier.  Then the eviction's apply and re-quantization
+// kernels as in kv_evict_segment.
+__global__ __launch_bounds__(WG) void k_plan_evict(DevState S, int n, const int32_t* seq_ids, int num, int den,
+                                                   int max_ops, int32_t* n_ops, int32_t* os, int32_t* og,
+                                                   int32_t* ok, uint8_t* ob) {
+  plan_body(S, n, seq_ids, num, den, max_ops, n_ops, os, og, ok, ob);
+  __syncthreads();
+  evict_plan_body(S, max_ops, n_ops, os, og, ok, ob);
+}
+int launch_plan_evict(tkv_cache* c, int n, const int32_t* seq_ids, int num, int den, int max_ops, int32_t* n_ops_dev,
+                      int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st) {
+  if (max_ops == 0) return launch_plan(c, n, seq_ids, num, den, 0, n_ops_dev, op_seq, op_seg, op_keep, op_bits, st);
+  k_plan_evict<<<1, WG, 0, st>>>(c->S, n, seq_ids, num, den, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits);
+  k_evict_apply<<<c->S.max_seqs, EV_THREADS, 0, st>>>(c->S);
+  k_requant<<<512, RQ_THREADS, 0, st>>>(c->S);
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
 
