@@ -29,7 +29,9 @@
  *     later items of that sequence in the same call are skipped, other
  *     sequences proceed, and a sticky error word records the kinds seen, the
  *     lowest sequence id involved and a count (tkv_get_error).
- *   - Inputs must be finite with magnitude below 2^15.
+ *   - Inputs must be finite: K/V rows with magnitude below 2^8 (the
+ *     attention feeds probability-weighted V scales of up to 2^8 times a
+ *     group's scale as fp16 operands), queries below 2^15.
  *
  * State format (the buffers, all little-endian):
  *   Three precision classes c = 0, 1, 2 hold 8-, 4- and 2-bit codes.  Each

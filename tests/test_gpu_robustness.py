@@ -99,3 +99,35 @@ def test_build_and_attention_are_deterministic():
     rb = gpu_attention(a, w.seq_ids, w.q_pos, w.q_bf16)
     for x, y in zip(ra, rb):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("formats", [False, True])
+def test_large_magnitude_inputs(formats):
+    """K/V rows up to ~200 in magnitude (the synthetic rows x6: the 1% outlier
+    channels reach the upper end of the input range the library states, below
+    2^8), with a downgrade and eviction history: state bit for bit, attention
+    finite and within the tolerances, with and without the self token and
+    splits."""
+    from test_gpu_parity import check_attention
+    import dataclasses
+    w = synth.small_static(seed=99, B=4, Hq=8, Hkv=2, D=128, g=64, L=1600)
+    if formats:
+        w = synth.page_formats(w)
+    base_kv = w.kv
+    w.kv = lambda call: tuple(x * np.float32(6.0) for x in base_kv(call))
+    L = w.layout
+    oc = helpers.build_oracle(w)
+    gc = helpers.build_gpu(w)
+    helpers.compare_states(L, gc.export(), oc.export(), "large magnitudes")
+    biggest = max(np.abs(base_kv(c)[0]).max() * 6 for c in w.calls if isinstance(c, synth.AppendCall))
+    assert 100.0 < biggest < 256.0, biggest
+    rng = np.random.default_rng(7)
+    ks = (rng.standard_normal((w.seq_ids.size, L.num_kv_heads, L.head_dim)) * 100).astype(np.float32)
+    vs = (rng.standard_normal((w.seq_ids.size, L.num_kv_heads, L.head_dim)) * 100).astype(np.float32)
+    for self_tok in (False, True):
+        for splits in (0, 3):
+            kw = dict(k_self=ks, v_self=vs) if self_tok else {}
+            say(f"[large] formats={formats} self={self_tok} splits={splits}")
+            got = gpu_attention(gc, w.seq_ids, w.q_pos, w.q_bf16, splits=splits, **kw)
+            check_attention(f"large formats={formats} self={self_tok} splits={splits}", got,
+                            oc.attention(w.seq_ids, w.q_pos, w.q_bf16, **kw))
