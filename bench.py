@@ -342,10 +342,10 @@ def main():
             # classification of every layer's statistics rows, inside the append's allocation kernel
             c.classify_append(seq_d, pos, stats.view(B, NL * Hq, 3), ch.tau[0], ch.tau[1], kl if NL > 1 else k,
                               vl if NL > 1 else v, labels_out=labels, stream=sh, prepare=True),
-        ] + ([c.plan_anneal(seq_d, args.r0, max_ops, n_ops, o_seq, o_seg, o_keep, o_bits, stream=sh, prepare=True),
-              c.evict(o_seq, o_seg, o_keep, o_bits, n_ops_dev=n_ops, n_ops=max_ops, stream=sh, prepare=True)]
+        ] + ([c.plan_anneal_evict(seq_d, args.r0, max_ops, n_ops, o_seq, o_seg, o_keep, o_bits, stream=sh,
+                                  prepare=True)]
              if args.policy == "anneal" else
-             # the ladder and the eviction's planning in one kernel (kv_plan_budget_evict)
+             # the planner and the eviction's planning in one kernel (kv_plan_budget_evict / kv_plan_anneal_evict)
              [c.plan_budget_evict(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, o_seq, o_seg, o_keep, o_bits,
                                   stream=sh, prepare=True)])
           + ([c.compact(o_seq, n_dev=n_ops, n=max_ops, stream=sh, prepare=True)] if args.compact else []))

@@ -249,6 +249,15 @@ int kv_plan_anneal(tkv_cache* c, int32_t n, const int32_t* seq_ids, int32_t r0, 
                    int32_t* n_ops_dev, int32_t* op_seq, int32_t* op_seg, int32_t* op_keep,
                    uint8_t* op_bits, hipStream_t stream);
 
+/* kv_plan_anneal_evict -- the same result as kv_plan_anneal(c, n, seq_ids,
+ * r0, max_ops, n_ops_dev, op_*) followed by kv_evict_segment(c, max_ops,
+ * n_ops_dev, op_seq, op_seg, op_keep, op_bits), with the plan and the
+ * eviction's planning in one work-group (one launch fewer).  Errors as the
+ * two calls'. */
+int kv_plan_anneal_evict(tkv_cache* c, int32_t n, const int32_t* seq_ids, int32_t r0, int32_t max_ops,
+                         int32_t* n_ops_dev, int32_t* op_seq, int32_t* op_seg, int32_t* op_keep,
+                         uint8_t* op_bits, hipStream_t stream);
+
 /* tkv_compact -- gather compaction, the baseline that in-place slot reuse
  * makes unnecessary (abstract: the kernel reuses evicted tokens' slots and so
  * eliminates compaction; Continuous Thinking bullet).  For each listed

@@ -163,3 +163,52 @@ def test_plan_budget_evict_lockstep(max_ops):
     say(f"[fused-plan] max_ops={max_ops} steps={ch.steps} evictions={n_evict} downgrades={n_down}")
     assert n_evict > 0 and (n_down > 0 or max_ops == 1)
     assert ga.get_error() == gb.get_error() == oc.error()
+
+
+def test_plan_anneal_evict_lockstep():
+    """Decode loop with the TBE annealing policy on three caches:
+    kv_plan_anneal_evict, kv_plan_anneal then kv_evict_segment, and the
+    oracle; op lists every step, states every 8 steps."""
+    import torch
+    import oracle
+    ch = synth.small_churn(seed=100, steps=64)
+    w = ch.base
+    L = w.layout
+    say("[fused-anneal] build")
+    oc = helpers.build_oracle(w)
+    ga = helpers.build_gpu(w)
+    gb = helpers.build_gpu(w)
+    dv = helpers.dev
+    seq_d = dv(w.seq_ids, np.int32)
+    max_ops = L.max_tokens_per_call
+    bufs = {tag: [torch.zeros(1, dtype=torch.int32, device="cuda")] +
+                 [torch.zeros(max_ops, dtype=torch.int32, device="cuda") for _ in range(3)] +
+                 [torch.zeros(max_ops, dtype=torch.uint8, device="cuda")] for tag in ("a", "b")}
+    tT, tE = ch.tau
+    n_ops_total = 0
+    for s in range(ch.steps):
+        q, k, v, pos = ch.step_inputs(s)
+        ro, rs, rn = oc.attention(w.seq_ids, pos, q, k_self=k, v_self=v)
+        lab = oracle.classify(rs.astype(np.float32), tT, tE)
+        for g in (ga, gb):
+            g.append(seq_d, dv(pos, np.int32), dv(lab, np.uint8), dv(k, np.float32), dv(v, np.float32))
+        oc.append(w.seq_ids, pos, lab, k, v)
+        ga.plan_anneal_evict(seq_d, 64, max_ops, *bufs["a"])
+        gb.plan_anneal(seq_d, 64, max_ops, *bufs["b"])
+        gb.evict(*bufs["b"][1:], n_ops_dev=bufs["b"][0], n_ops=max_ops)
+        ops = oc.plan_anneal(w.seq_ids, 64, max_ops)
+        torch.cuda.synchronize()
+        m = int(bufs["a"][0].item())
+        assert m == int(bufs["b"][0].item()) == ops[0].size, f"op count step {s}"
+        for xa, xb, xo in zip(bufs["a"][1:], bufs["b"][1:], ops):
+            assert np.array_equal(xa.cpu().numpy()[:m], xo) and np.array_equal(xb.cpu().numpy()[:m], xo), s
+        if m:
+            oc.evict(*ops)
+            n_ops_total += m
+        if s % 8 == 7 or s == ch.steps - 1:
+            ea = ga.export()
+            helpers.compare_states(L, ea, gb.export(), f"fused anneal vs two calls, step {s}")
+            helpers.compare_states(L, ea, oc.export(), f"fused anneal vs oracle, step {s}")
+    say(f"[fused-anneal] steps={ch.steps} ops={n_ops_total}")
+    assert n_ops_total > 0
+    assert ga.get_error() == gb.get_error() == oc.error()

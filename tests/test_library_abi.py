@@ -53,6 +53,7 @@ def test_null_handle_and_strerror():
     assert lib.kv_classify_append(None, 1, None, None, None, 4, C.c_float(0.3), C.c_float(0.8), 0, None, None,
                                   None, None, None) == binding.TKV_EINVAL
     assert lib.kv_plan_budget_evict(None, 1, None, 1, 10, 4, None, None, None, None, None, None) == binding.TKV_EINVAL
+    assert lib.kv_plan_anneal_evict(None, 1, None, 64, 4, None, None, None, None, None, None) == binding.TKV_EINVAL
     assert lib.thought_classify(-1, 4, None, C.c_float(0.3), C.c_float(0.8), 0, None, None) == binding.TKV_EINVAL
     assert lib.thought_classify(1, 4, None, C.c_float(0.3), C.c_float(0.8), 2, None, None) == binding.TKV_EINVAL
     assert binding.strerror(binding.TKV_ENOSEG) == "unknown or evicted segment"

@@ -25,7 +25,7 @@ BUFFER_DTYPES = {n: (np.uint8 if n.startswith("pool") else np.int32) for n in BU
 
 # Entry points declared in include/tkv.h
 SYMBOLS = ["tkv_buffer_sizes", "tkv_create", "tkv_destroy", "tkv_seq_reset", "kv_append_quant", "kv_classify_append",
-           "kv_evict_segment", "kv_plan_budget", "kv_plan_budget_evict", "kv_plan_anneal", "tkv_compact", "tkv_attn_workspace", "paged_decode_attn",
+           "kv_evict_segment", "kv_plan_budget", "kv_plan_budget_evict", "kv_plan_anneal", "kv_plan_anneal_evict", "tkv_compact", "tkv_attn_workspace", "paged_decode_attn",
            "thought_classify", "tkv_get_error", "tkv_export_state", "tkv_import_state", "tkv_strerror"]
 
 
@@ -74,6 +74,7 @@ def load(path: str = LIB_PATH):
     L.kv_plan_budget.argtypes = [P, I, P, I, I, I, P, P, P, P, P, P]
     L.kv_plan_budget_evict.argtypes = [P, I, P, I, I, I, P, P, P, P, P, P]
     L.kv_plan_anneal.argtypes = [P, I, P, I, I, P, P, P, P, P, P]
+    L.kv_plan_anneal_evict.argtypes = [P, I, P, I, I, P, P, P, P, P, P]
     L.tkv_compact.argtypes = [P, I, P, P, P]
     L.tkv_attn_workspace.argtypes = [P, I, I]; L.tkv_attn_workspace.restype = C.c_size_t
     L.paged_decode_attn.argtypes = [P, P, P]
@@ -231,6 +232,13 @@ class Cache:
         args = (self.h, int(seq_ids.numel()), _ptr(seq_ids), int(num), int(den), int(max_ops), _ptr(n_ops_dev),
                 _ptr(op_seq), _ptr(op_seg), _ptr(op_keep), _ptr(op_bits), _stream(stream))
         return _issue(self.L.kv_plan_budget_evict, args, "kv_plan_budget_evict", prepare)
+
+    def plan_anneal_evict(self, seq_ids, r0, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits, *, stream=None,
+                          prepare=False):
+        """plan_anneal followed by evict of the planned ops (kv_plan_anneal_evict)."""
+        args = (self.h, int(seq_ids.numel()), _ptr(seq_ids), int(r0), int(max_ops), _ptr(n_ops_dev), _ptr(op_seq),
+                _ptr(op_seg), _ptr(op_keep), _ptr(op_bits), _stream(stream))
+        return _issue(self.L.kv_plan_anneal_evict, args, "kv_plan_anneal_evict", prepare)
 
     def compact(self, seq_ids, n_dev=None, n=None, *, stream=None, prepare=False):
         k = int(seq_ids.numel()) if n is None else int(n)

@@ -190,6 +190,16 @@ extern "C" int kv_plan_anneal(tkv_cache* c, int32_t n, const int32_t* seq_ids, i
   return launch_anneal(c, n, seq_ids, r0, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits, stream);
 }
 
+extern "C" int kv_plan_anneal_evict(tkv_cache* c, int32_t n, const int32_t* seq_ids, int32_t r0, int32_t max_ops,
+                                    int32_t* n_ops_dev, int32_t* op_seq, int32_t* op_seg, int32_t* op_keep,
+                                    uint8_t* op_bits, hipStream_t stream) {
+  if (!c || n < 0 || n > c->S.max_tokens || r0 < 0 || max_ops < 0 || max_ops > c->S.max_tokens) return TKV_EINVAL;
+  if (!n_ops_dev || (n > 0 && !seq_ids) || (max_ops > 0 && (!op_seq || !op_seg || !op_keep || !op_bits)))
+    return TKV_EINVAL;
+  c->last_stream = stream;
+  return launch_anneal_evict(c, n, seq_ids, r0, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits, stream);
+}
+
 extern "C" int tkv_compact(tkv_cache* c, int32_t n, const int32_t* n_dev, const int32_t* seq_ids, hipStream_t stream) {
   if (!c || n < 0 || n > c->S.max_tokens || (n > 0 && !seq_ids)) return TKV_EINVAL;
   c->last_stream = stream;

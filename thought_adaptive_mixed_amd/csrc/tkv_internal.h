@@ -331,6 +331,8 @@ int launch_plan_evict(tkv_cache* c, int n, const int32_t* seq_ids, int num, int 
                       int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st);
 int launch_anneal(tkv_cache* c, int n, const int32_t* seq_ids, int r0, int max_ops, int32_t* n_ops_dev,
                   int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st);
+int launch_anneal_evict(tkv_cache* c, int n, const int32_t* seq_ids, int r0, int max_ops, int32_t* n_ops_dev,
+                        int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st);
 int launch_compact(tkv_cache* c, int n, const int32_t* n_dev, const int32_t* seq_ids, hipStream_t st);
 int launch_seq_reset(tkv_cache* c, int n, const int32_t* seq_ids, hipStream_t st);
 int launch_classify(int batch, int Hq, const float* stats, float tau_T, float tau_E, int kind, uint8_t* labels,

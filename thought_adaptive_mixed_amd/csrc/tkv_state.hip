@@ -1402,8 +1402,8 @@ __device__ int anneal_wave(const DevState& S, int s, int r0, int base, int max_o
   return m;
 }
 
-__global__ __launch_bounds__(WG) void k_anneal(DevState S, int n, const int32_t* seq_ids, int r0, int max_ops,
-                                               int32_t* n_ops, int32_t* os, int32_t* og, int32_t* ok, uint8_t* ob) {
+__device__ __forceinline__ void anneal_body(const DevState& S, int n, const int32_t* seq_ids, int r0, int max_ops,
+                                            int32_t* n_ops, int32_t* os, int32_t* og, int32_t* ok, uint8_t* ob) {
   __shared__ int s_cnt[TKV_MAX_TOK];         // ops of each listed sequence
   __shared__ int s_base[TKV_MAX_TOK];        // their first op's index
   __shared__ int s_tmp[48];
@@ -1429,10 +1429,32 @@ __global__ __launch_bounds__(WG) void k_anneal(DevState S, int n, const int32_t*
   if (tid == 0) *n_ops = tot[0] < max_ops ? tot[0] : max_ops;
 }
 
+__global__ __launch_bounds__(WG) void k_anneal(DevState S, int n, const int32_t* seq_ids, int r0, int max_ops,
+                                               int32_t* n_ops, int32_t* os, int32_t* og, int32_t* ok, uint8_t* ob) {
+  anneal_body(S, n, seq_ids, r0, max_ops, n_ops, os, og, ok, ob);
+}
+// The annealing plan and the first part of the eviction in one work-group
+// (as k_plan_evict for the budget ladder).
+__global__ __launch_bounds__(WG) void k_anneal_evict(DevState S, int n, const int32_t* seq_ids, int r0, int max_ops,
+                                                     int32_t* n_ops, int32_t* os, int32_t* og, int32_t* ok,
+                                                     uint8_t* ob) {
+  anneal_body(S, n, seq_ids, r0, max_ops, n_ops, os, og, ok, ob);
+  __syncthreads();
+  evict_plan_body(S, max_ops, n_ops, os, og, ok, ob);
+}
+
 int launch_anneal(tkv_cache* c, int n, const int32_t* seq_ids, int r0, int max_ops, int32_t* n_ops_dev,
                   int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st) {
   const int nt = n < 1 ? 64 : (n >= WG / 64 ? WG : 64 * n);
   k_anneal<<<1, nt, 0, st>>>(c->S, n, seq_ids, r0, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits);
+  return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
+}
+int launch_anneal_evict(tkv_cache* c, int n, const int32_t* seq_ids, int r0, int max_ops, int32_t* n_ops_dev,
+                        int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st) {
+  if (max_ops == 0) return launch_anneal(c, n, seq_ids, r0, 0, n_ops_dev, op_seq, op_seg, op_keep, op_bits, st);
+  k_anneal_evict<<<1, WG, 0, st>>>(c->S, n, seq_ids, r0, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits);
+  k_evict_apply<<<c->S.max_seqs, EV_THREADS, 0, st>>>(c->S);
+  k_requant<<<512, RQ_THREADS, 0, st>>>(c->S);
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
 
