@@ -2,7 +2,8 @@
 
 Method passage: ThinKV technical summary, "Methodologie" > TBQ bullet (group
 quantization of buffered tokens by thought category); the integer format with
-per-group fp16 scale and zero-point is the reading this build takes.
+per-group fp16 scale and zero-point is the reading the oracle follows (the page
+formats are pinned in test_oracle_formats.py).
 """
 import os
 
