@@ -4,28 +4,40 @@ One step = one pass of the whole path over one batch: paged decode attention
 over the mixed-precision, hole-bearing cache (with the staged self token) ->
 thought classification and kv_append_quant of the new token at its label's
 precision (one call, kv_classify_append) -> kv_plan_budget (token budget
-ladder) -> kv_evict_segment (the two in one call, kv_plan_budget_evict).  With
---policy anneal the ladder is replaced by kv_plan_anneal (the TBE annealing
-schedule of the retention, r0 = 64 by default), applied to the built state
-until it plans nothing before anything is timed.  With --compact every step
-also compacts the sequences it evicted from (tkv_compact, the gather-
-compaction baseline that in-place slot reuse avoids), after every sequence
-was compacted once before timing.  --workload churn256 runs the B256 decode
-loop (lengths 4k..32k, 5% budget) instead of the default.  --formats page
-stores the classes as FP8 E4M3 / FP4 E2M1 / ternary codes.  Workload: the
-Llama-8B-like reasoning-decode layer (B32, Hq32/Hkv8, D128, g64, 16k generated
-tokens per sequence, 10% budget -> 1638 retained, R/E/T 8/4/2-bit) with
-planted-temperature queries, synthetic data.
+ladder) -> kv_evict_segment (the two in one call, kv_plan_budget_evict).
 
-The state is replicated into enough copies to exceed the 256 MB Infinity Cache
-and consecutive steps rotate through them, so each step reads its cache from
-HBM.  All inputs are resident in HBM before the timed region.
+Default workload: the B256 eviction-churn decode loop (Hq32/Hkv8, D128, g64,
+starting lengths U{4k..32k}, 5% token budget, R/E/T 8/4/2-bit codes,
+planted-temperature queries), the largest configuration; --workload llama8b
+runs the same step on the Llama-8B-like layer (B32, 16k generated tokens, 10%
+budget).  Besides the step, the line carries:
+  - `configs`: the attention call alone on each static workload -- tiny (B1,
+    G1, D64), llama8b (B32, G4, D128), qwen14b (B64, G5, ragged lengths,
+    scattered block tables), gptoss20b (B128, G8, D64, sinks) with a 128-token
+    window and with full attention -- each timed as the median of 5
+    repetitions of 50 back-to-back launches, with its algorithmic bytes,
+    achieved GB/s and fraction of the 8 TB/s peak, and the oracle's rate on
+    the same state;
+  - `stream_read`: a plain 128-bit streaming read of a 2 GiB buffer in the
+    same process (the HBM read ceiling of this machine);
+  - `step_split_us`: per-call device time of the step (a second pass with
+    events between the calls).
+Options: --policy anneal (the TBE annealing schedule instead of the ladder),
+--compact (the gather-compaction baseline after every eviction), --layers N,
+--formats page (FP8 E4M3 / FP4 E2M1 / ternary codes).
 
-Prints ONE JSON line (see the fields below).
+Every state is replicated into enough copies to exceed the 256 MB Infinity
+Cache and consecutive launches rotate through them, so each launch reads its
+cache from HBM.  All inputs are resident in HBM before any timed region.
+A device error reported by any cache (tkv_get_error) aborts the run with a
+non-zero exit status and no result line.
+
+Prints ONE JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import dataclasses
 import json
 import math
@@ -41,6 +53,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode-attn KV tokens/s and achieved HBM GB/s (% of MI355X peak), 1 GPU"
 HBM_PEAK_GBS = 8000.0
 CLASS_BITS = (8, 4, 2)
+ATTN_CONFIGS = ("tiny", "llama8b", "qwen14b", "gptoss20b")
 
 
 def log(*a):
@@ -56,7 +69,7 @@ class HipEvents:
     DISABLE_SYSTEM_FENCE = 0x20000000
 
     def __init__(self, n, torch_events=False):
-        import ctypes as C
+        C = ctypes
         self.C = C
         self.torch_events = torch_events
         if torch_events:
@@ -67,6 +80,7 @@ class HipEvents:
         self.hip.hipEventCreateWithFlags.argtypes = [C.c_void_p, C.c_uint]
         self.hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
         self.hip.hipEventElapsedTime.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
         self.ev = []
         for _ in range(n):
             e = C.c_void_p()
@@ -88,56 +102,125 @@ class HipEvents:
             raise RuntimeError("hipEventElapsedTime failed")
         return ms.value
 
-
-def state_class_tokens(exported, L):
-    """Retained tokens per (sequence, class) from an exported state."""
-    out = np.zeros((L.max_seqs, 3), np.int64)
-    seq = exported["seq"].reshape(L.max_seqs, 16)
-    bt = exported["btab"].reshape(L.max_seqs, 3, L.max_blocks_per_seq)
-    blocks_used = np.zeros((L.max_seqs, 3), np.int64)
-    for c in range(3):
-        masks = exported[f"blk{c}"].reshape(-1, 4)[:, 0].astype(np.uint32)
-        pop = np.array([bin(int(m)).count("1") for m in range(1 << 16)], np.int64)
-        for s in range(L.max_seqs):
-            nb = int(seq[s, c])
-            ids = bt[s, c, :nb]
-            out[s, c] = int(pop[masks[ids]].sum())
-            blocks_used[s, c] = nb
-    return out, blocks_used
+    def close(self):
+        if not self.torch_events:
+            for e in self.ev:
+                self.hip.hipEventDestroy(e)
+        self.ev = []
 
 
-def algorithmic_bytes(tokens_c, blocks_c, L, batch, self_token=True):
-    """Bytes one attention call must move: codes + fp16 (scale, zero) of every
-    attended cached token and KV head, the block id and mask word of every
-    visited block (per KV head), the queries, outputs, statistics and the
-    staged self token."""
+# ---------------------------------------------------------------------------
+# algorithmic bytes of one attention call, from an exported state
+# ---------------------------------------------------------------------------
+_POP16 = np.array([bin(m).count("1") for m in range(1 << 16)], np.int64)
+
+
+def attn_bytes(state, L, seq_ids, q_pos, window=0, self_token=False, sinks=False):
+    """Bytes one paged_decode_attn call must move, per the byte model: codes +
+    fp16 (scale, zero) of every attended cached token and KV head; per visited
+    block its id and mask word (with a window also its largest position and
+    the 16 slot positions); the queries, outputs, statistics, sinks and the
+    staged self token.  Returns (bytes, KV-code bytes, attended cached tokens)."""
     D, g, Hkv, Hq = L.head_dim, L.group_size, L.num_kv_heads, L.num_q_heads
     NG = D // g
     per_tok = [Hkv * 2 * (D * b // 8 + NG * 4) for b in CLASS_BITS]
-    kv = sum(int(tokens_c[:, c].sum()) * per_tok[c] for c in range(3))
-    blk = int(blocks_c.sum()) * Hkv * (4 + 4)
-    io = batch * Hq * D * 2 + batch * Hq * D * 4 + batch * Hq * 12
+    seq = state["seq"].reshape(L.max_seqs, 16)
+    bt = state["btab"].reshape(L.max_seqs, 3, L.max_blocks_per_seq)
+    kv = 0
+    meta = 0
+    tokens = 0
+    for c in range(3):
+        blk = state[f"blk{c}"].reshape(-1, 4)
+        pos = state[f"slot{c}"].reshape(-1, 16, 2)[:, :, 0]
+        for i, s in enumerate(seq_ids):
+            nb = int(seq[s, c])
+            ids = bt[s, c, :nb]
+            masks = blk[ids, 0].astype(np.int64) & 0xFFFF
+            if window > 0:
+                lo = int(q_pos[i]) - window + 1
+                live = (masks != 0) & (blk[ids, 1] >= lo)
+                bits = (masks[:, None] >> np.arange(16)[None, :]) & 1
+                inw = bits.astype(bool) & (pos[ids] >= lo)
+                n = int(inw[live].sum())
+                meta += int(live.sum()) * (4 + 2 + 4 + 16 * 4)
+            else:
+                n = int(_POP16[masks].sum())
+                meta += int((masks != 0).sum()) * (4 + 2)
+            tokens += n
+            kv += n * per_tok[c]
+    B = len(seq_ids)
+    io = B * Hq * D * 2 + B * Hq * D * 4 + B * Hq * 12 + (Hq * 4 if sinks else 0)
     if self_token:
-        io += batch * Hkv * D * 4 * 2
-    return kv + blk + io, kv
+        io += B * Hkv * D * 4 * 2
+    return kv + meta + io, kv, tokens
 
 
-def measured_traffic():
-    """HBM bytes per attention launch from the committed counter summary
-    (profiles/), if the kernel's source files are still the ones the counters
-    were taken with; otherwise None."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", "k_attn_llama8b_B32_hbm_traffic.json")
+# ---------------------------------------------------------------------------
+# building and replicating states
+# ---------------------------------------------------------------------------
+def replicate(w, L=None, min_total=1 << 30, copies=0):
+    """Build the workload's state through the C-ABI, then import it into
+    enough further caches that all copies together exceed min_total bytes."""
+    import torch
+    from thought_adaptive_mixed_amd import binding, drive
+    L = L or w.layout
+    sizes = binding.buffer_sizes(drive.gpu_layout(L))
+    R = copies or max(2, math.ceil(min_total / sum(sizes[:-1])))
+    c0 = binding.Cache(drive.gpu_layout(L), w.block_order)
+    drive.build_gpu(w, c0)
+    torch.cuda.synchronize()
+    check_errors([c0], f"build of {w.name}")
+    state = c0.export()
+    caches = [c0] + [binding.Cache(drive.gpu_layout(L), w.block_order) for _ in range(R - 1)]
+    for c in caches[1:]:
+        c.import_(state)
+    return caches, state
+
+
+def check_errors(caches, what):
+    errs = [c.get_error() for c in caches]
+    bad = [(i, e) for i, e in enumerate(errs) if e[0] or e[2]]
+    if bad:
+        log(f"[bench] device errors after {what}: (copy, (kinds, lowest seq, count)) {bad[:8]}")
+        log("[bench] a result measured with skipped work is not reported")
+        sys.exit(3)
+
+
+# ---------------------------------------------------------------------------
+# the oracle as it stands (CPU baseline)
+# ---------------------------------------------------------------------------
+def _oracle_cache(w, state):
+    import oracle
+    Lw = w.layout
+    ol = oracle.OracleLayout(Lw.num_kv_heads, Lw.num_q_heads, Lw.head_dim, Lw.group_size, Lw.pool_blocks,
+                             Lw.max_seqs, Lw.max_blocks_per_seq, Lw.max_segments_per_seq, Lw.bits, Lw.num_layers,
+                             Lw.code_format)
+    oc = oracle.OracleCache(ol, w.block_order)
+    oc.import_(state)
+    return oc
+
+
+def _omp_threads(n):
     try:
-        with open(path) as f:
-            j = json.load(f)
-        h = hashlib.sha256()
-        for name in j["source_files"]:
-            with open(os.path.join(ROOT, name), "rb") as f:
-                h.update(f.read())
-    except (OSError, KeyError, ValueError):
-        return None
-    return float(j["traffic_bytes_per_launch"]) if h.hexdigest() == j["source_sha256"] else None
+        ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+    except OSError:
+        pass
+
+
+def oracle_attention_rate(w, state, window, n_seq, threads, budget_s=3.0):
+    """Attended cached KV tokens per second of the oracle's attention on the
+    first n_seq sequences of a static state (repeated up to budget_s)."""
+    oc = _oracle_cache(w, state)
+    _omp_threads(threads)
+    sel = w.seq_ids[:n_seq]
+    tokens, reps, t0 = 0, 0, time.perf_counter()
+    while True:
+        _, _, na = oc.attention(sel, w.q_pos[:n_seq], w.q_bf16[:n_seq], window=window, sinks=w.sinks)
+        tokens += int(na.sum()); reps += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return tokens / dt, reps, dt
 
 
 def cpu_baseline(w, state, ch, n_seq, budget_s=12.0, max_reps=1000, policy="ladder", r0=64, compact=False):
@@ -146,13 +229,10 @@ def cpu_baseline(w, state, ch, n_seq, budget_s=12.0, max_reps=1000, policy="ladd
     ladder or annealing plan, evict) per repetition, on all host cores the
     process may use."""
     import oracle
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    import helpers
     cores = len(os.sched_getaffinity(0))
-    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
-    oc = oracle.OracleCache(helpers.oracle_layout(w.layout), w.block_order)
-    oc.import_(state)
-    sel = np.arange(n_seq, dtype=np.int32)
+    _omp_threads(cores)
+    oc = _oracle_cache(w, state)
+    sel = w.seq_ids[:n_seq]
     q, k, v, pos = ch.step_inputs(0)
     tokens = 0
     t0 = time.perf_counter()
@@ -170,94 +250,161 @@ def cpu_baseline(w, state, ch, n_seq, budget_s=12.0, max_reps=1000, policy="ladd
             oc.evict(*ops)
             if compact:
                 oc.compact(ops[0])
-        tokens += int(na.sum())
+        tokens += int(na.sum()) - sel.size            # cached tokens (the self token excluded)
         reps += 1
         if time.perf_counter() - t0 > budget_s or reps >= max_reps:
             break
     dt = time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
-    return {"value": tokens / dt, "unit": "KV tokens/s", "cores": min(threads, cores), "kind": "oracle",
+    return {"value": tokens / dt, "unit": "KV tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{reps} full steps (attention+classify+append+{policy}+evict"
-                      f"{'+compact' if compact else ''}) on {n_seq} of "
+                      f"{'+compact' if compact else ''}) on {sel.size} of "
                       f"{w.seq_ids.size} sequences of the same cache, fp64 attention, {dt:.1f} s"}
 
 
-def workload_name(args):
-    return (workload_name_1(args)
-            + (f"; {args.layers} layers per step sharing the block tables (each layer holds the "
-               f"one-layer state's records)" if args.layers > 1 else "")
-            + ("; page code formats (R FP8 E4M3, E FP4 E2M1, T ternary)" if args.formats == "page" else ""))
-
-
-def workload_name_1(args):
-    if args.workload == "llama8b":
-        head = "llama8b-like reasoning decode, one layer: B32, Hq32/Hkv8, D128, g64, "
-        if args.policy == "ladder":
-            body = ("16k generated tokens/seq, 10% budget (1638 retained), R/E/T 8/4/2-bit, "
-                    "planted-temperature queries; step = attention+classify+append+ladder+evict")
-        else:
-            body = (f"16k generated tokens/seq, R/E/T 8/4/2-bit, TBE annealing schedule (r0 {args.r0}) applied "
-                    f"to the built state, planted-temperature queries; step = attention+classify+append+anneal+evict")
-    else:
-        head = "B256 reasoning decode loop, one layer: Hq32/Hkv8, D128, g64, "
-        body = ("lengths U{4k..32k}, 5% budget, R/E/T 8/4/2-bit, planted-temperature queries; step = "
-                "attention+classify+append+" + ("ladder" if args.policy == "ladder" else f"anneal (r0 {args.r0})")
-                + "+evict")
-    return head + body + ("+compact (gather-compaction baseline, dense start)" if args.compact else "")
-
-
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=60)
-    ap.add_argument("--warmup", type=int, default=6)
-    ap.add_argument("--copies", type=int, default=0, help="state copies (0 = enough for > 1 GiB)")
-    ap.add_argument("--cpu-seqs", type=int, default=32)
-    ap.add_argument("--policy", choices=("ladder", "anneal"), default="ladder",
-                    help="eviction planner of the step: the token-budget ladder, or the TBE annealing schedule")
-    ap.add_argument("--r0", type=int, default=64, help="first retention of the annealing schedule")
-    ap.add_argument("--compact", action="store_true",
-                    help="compact the sequences each step evicted from (gather-compaction baseline)")
-    ap.add_argument("--layers", type=int, default=1,
-                    help="layers per decode step sharing the block tables (the one-layer state replicated)")
-    ap.add_argument("--workload", choices=("llama8b", "churn256"), default="llama8b",
-                    help="the llama8b-like layer (B32, 16k, 10%% budget) or the B256 decode loop (4k..32k, 5%% budget)")
-    ap.add_argument("--formats", choices=("int", "page"), default="int",
-                    help="code formats of the 8/4/2-bit classes: asymmetric integer, or FP8 E4M3 / FP4 E2M1 / ternary")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--attn-only", action="store_true", help="time only the attention call (diagnostic)")
-    ap.add_argument("--torch-events", action="store_true", help="time with torch's default events (diagnostic)")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="before the timed region, copy MIB MiB device-to-device 3 times (a plain copy kernel of "
-                         "known size, to scale hardware byte counters by)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path shards by "
-              f"sequence with no exchange, so N GPUs would run N independent copies of this step.",
-              file=sys.stderr)
-        sys.exit(2)
-
+# ---------------------------------------------------------------------------
+# the streaming-read ceiling
+# ---------------------------------------------------------------------------
+def stream_ceiling(nbytes=2 << 30, reps=5, passes=4):
     import torch
-    from thought_adaptive_mixed_amd import binding, synth
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    import helpers
-    dv0 = lambda a: helpers.dev(a, np.int32)
+    from thought_adaptive_mixed_amd import binding
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    sh = torch.cuda.current_stream().cuda_stream
+    f = binding.stream_read(buf, sink, stream=sh, prepare=True)
+    f()
+    torch.cuda.synchronize()
+    ev = HipEvents(2 * reps)
+    for r in range(reps):
+        ev.record(2 * r, sh)
+        for _ in range(passes):
+            f()
+        ev.record(2 * r + 1, sh)
+    torch.cuda.synchronize()
+    t = sorted(ev.elapsed_ms(2 * r, 2 * r + 1) / passes for r in range(reps))
+    ev.close()
+    del buf
+    ms = t[len(t) // 2]
+    return {"GB/s": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes, "ms_median": ms,
+            "kernel": "k_stream_read (128-bit loads, grid stride, 2048 work-groups of 256 lanes)",
+            "timing": f"median of {reps} repetitions of {passes} back-to-back reads"}
 
-    total_steps = args.warmup + args.steps
-    log("[bench] building workload")
+
+# ---------------------------------------------------------------------------
+# the attention call alone on a static workload
+# ---------------------------------------------------------------------------
+def attention_config(name, reps=5, launches=50, oracle_s=3.0):
+    """Median over `reps` repetitions of `launches` back-to-back attention
+    launches rotating over state copies, per window of the workload."""
+    import torch
+    from thought_adaptive_mixed_amd import drive, synth
     t0 = time.time()
-    ch = synth.bench_cycle(steps=total_steps) if args.workload == "llama8b" else synth.churn(steps=total_steps)
+    w = synth.WORKLOADS[name]()
+    caches, state = replicate(w)
+    L = w.layout
+    B, Hq, D = w.seq_ids.size, L.num_q_heads, L.head_dim
+    dv = drive.dev
+    seq_d, pos_d, q_d = dv(w.seq_ids, np.int32), dv(w.q_pos, np.int32), dv(w.q_bf16, np.uint16)
+    sinks_d = dv(w.sinks, np.float32) if w.sinks is not None else None
+    out = torch.empty(B, Hq, D, dtype=torch.float32, device="cuda")
+    stats = torch.empty(B, Hq, 3, dtype=torch.float32, device="cuda")
+    n_att = torch.zeros(B, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(caches[0].workspace_bytes(B), 16), dtype=torch.uint8, device="cuda")
+    sh = torch.cuda.current_stream().cuda_stream
+    res = {}
+    cores = len(os.sched_getaffinity(0))
+    for window in w.windows:
+        calls = [c.attention(seq_d, pos_d, q_d, out, ws, stats=stats, n_attended=n_att, sinks=sinks_d,
+                             window=window, stream=sh, prepare=True) for c in caches]
+        for i in range(2 * len(calls)):
+            calls[i % len(calls)]()
+        torch.cuda.synchronize()
+        ev = HipEvents(2 * reps)
+        for r in range(reps):
+            ev.record(2 * r, sh)
+            for i in range(launches):
+                calls[(r * launches + i) % len(calls)]()
+            ev.record(2 * r + 1, sh)
+        torch.cuda.synchronize()
+        per = sorted(ev.elapsed_ms(2 * r, 2 * r + 1) / launches for r in range(reps))
+        ev.close()
+        check_errors(caches, f"attention on {name}")
+        ms = per[len(per) // 2]
+        nbytes, kvb, toks = attn_bytes(state, L, w.seq_ids, w.q_pos, window, sinks=w.sinks is not None)
+        got = int(n_att.sum().item())
+        assert got == toks, (name, window, got, toks)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        key = name if len(w.windows) == 1 else f"{name}_{'full' if window == 0 else f'window{window}'}"
+        ora = {}
+        n_seq = min(B, 8)
+        rate, orep, odt = oracle_attention_rate(w, state, window, n_seq, cores, oracle_s)
+        ora["oracle_kv_tokens_per_s"] = rate
+        ora["oracle_sample"] = f"{orep} calls on {n_seq} of {B} sequences, {cores} cores, {odt:.1f} s"
+        if name in ("tiny", "llama8b"):
+            rate1, orep1, odt1 = oracle_attention_rate(w, state, window, min(B, 2), 1, oracle_s)
+            ora["oracle_1thread_kv_tokens_per_s"] = rate1
+            ora["oracle_1thread_sample"] = f"{orep1} calls on {min(B, 2)} of {B} sequences, 1 thread, {odt1:.1f} s"
+        res[key] = {"batch": B, "heads": f"Hq{Hq}/Hkv{L.num_kv_heads}", "head_dim": D, "group": L.group_size,
+                    "window": window, "sinks": w.sinks is not None, "copies": len(caches),
+                    "attended_tokens": toks, "bytes_per_launch": nbytes, "kv_code_bytes": kvb,
+                    "us_per_launch": ms * 1e3, "us_per_launch_reps": [p * 1e3 for p in per],
+                    "kv_tokens_per_s": toks / (ms * 1e-3), "achieved_GBs": gbs, "frac": gbs / HBM_PEAK_GBS,
+                    **ora}
+        log(f"[bench] {key}: {ms * 1e3:.2f} us/launch, {nbytes / 1e6:.2f} MB, {gbs:.0f} GB/s "
+            f"({gbs / HBM_PEAK_GBS:.3f} of peak), {toks / (ms * 1e-3) / 1e9:.2f} G KV tokens/s")
+    del caches
+    torch.cuda.empty_cache()
+    log(f"[bench] {name} done in {time.time() - t0:.1f} s")
+    return res
+
+
+# ---------------------------------------------------------------------------
+# the decode step
+# ---------------------------------------------------------------------------
+def workload_name(args):
+    if args.workload == "llama8b":
+        head = "llama8b-like reasoning decode, one layer: B32, Hq32/Hkv8, D128, g64, 16k generated tokens/seq, "
+        body = ("10% budget (1638 retained), " if args.policy == "ladder" else "")
+    else:
+        head = "B256 eviction-churn reasoning decode loop, one layer: Hq32/Hkv8, D128, g64, "
+        body = ("starting lengths U{4k..32k}, " + ("5% budget, " if args.policy == "ladder" else ""))
+    pol = "ladder" if args.policy == "ladder" else f"anneal (TBE annealing schedule, r0 {args.r0})"
+    s = (head + body + "R/E/T 8/4/2-bit, planted-temperature queries; step = attention+classify+append+"
+         + pol + "+evict" + ("+compact (gather-compaction baseline, dense start)" if args.compact else ""))
+    if args.layers > 1:
+        s += f"; {args.layers} layers per step sharing the block tables (each layer holds the one-layer state's records)"
+    if args.formats == "page":
+        s += "; page code formats (R FP8 E4M3, E FP4 E2M1, T ternary)"
+    return s
+
+
+def step_bench(args):
+    import torch
+    from thought_adaptive_mixed_amd import binding, drive, synth
+    split_steps = 0 if args.attn_only else args.split_steps
+    total = args.warmup + args.steps + split_steps
+    log(f"[bench] building the {args.workload} workload")
+    t0 = time.time()
+    ch = synth.bench_cycle(steps=total) if args.workload == "llama8b" else synth.churn(steps=total)
     if args.formats == "page":
         ch.base = synth.page_formats(ch.base)
     w = ch.base
+    if args.compact:
+        # room to compact every sequence in one call: each class's pool doubled
+        # (a compaction pops all its new blocks before it returns the old ones)
+        Lw = w.layout
+        grow = tuple(p + p + 16 for p in Lw.pool_blocks)
+        if w.block_order is not None:
+            w.block_order = [np.concatenate([o, np.arange(Lw.pool_blocks[c], grow[c], dtype=np.int32)])
+                             for c, o in enumerate(w.block_order)]
+        w.layout = dataclasses.replace(Lw, pool_blocks=grow)
     L = w.layout
     B = w.seq_ids.size
-    sizes = binding.buffer_sizes(helpers.gpu_layout(L))
-    state_bytes = sum(sizes[:-1])
-    R = args.copies or max(2, math.ceil((1 << 30) / state_bytes))
-    log(f"[bench] state {state_bytes / 1e6:.1f} MB, {R} copies")
-    c0 = helpers.build_gpu(w)
+    NL = max(1, args.layers)
+    c0 = binding.Cache(drive.gpu_layout(L), w.block_order)
+    drive.build_gpu(w, c0)
     torch.cuda.synchronize()
+    dv0 = lambda a: drive.dev(a, np.int32)
     if args.policy == "anneal":
         # the built state has never been annealed: apply the schedule until it plans nothing
         m_all = L.max_tokens_per_call
@@ -271,12 +418,10 @@ def main():
                 break
         torch.cuda.synchronize()
     if args.compact:
-        # start dense: every sequence compacted once (one per call, so each needs only its own room)
-        for s in w.seq_ids:
-            c0.compact(dv0([s]))
+        c0.compact(dv0(w.seq_ids))                 # start dense
         torch.cuda.synchronize()
+    check_errors([c0], "the build")
     state = c0.export()
-    NL = max(1, args.layers)
     if NL > 1:
         # every layer of the layered cache holds the one-layer state's records (same bytes and work per layer)
         state1 = state
@@ -286,53 +431,53 @@ def main():
             state[f"pool{cc}"] = np.repeat(state1[f"pool{cc}"].reshape(P, 1, -1), NL, axis=1).ravel()
         del c0
         L = dataclasses.replace(L, num_layers=NL)
-        sizes = binding.buffer_sizes(helpers.gpu_layout(L))
+        sizes = binding.buffer_sizes(drive.gpu_layout(L))
         R = args.copies or max(2, math.ceil((1 << 30) / sum(sizes[:-1])))
-        caches = [binding.Cache(helpers.gpu_layout(L), w.block_order) for _ in range(R)]
+        caches = [binding.Cache(drive.gpu_layout(L), w.block_order) for _ in range(R)]
         for c in caches:
             c.import_(state)
-        log(f"[bench] {NL} layers: state {sum(sizes[:-1]) / 1e6:.1f} MB, {R} copies")
         state = state1
     else:
-        caches = [c0] + [binding.Cache(helpers.gpu_layout(L), w.block_order) for _ in range(R - 1)]
+        sizes = binding.buffer_sizes(drive.gpu_layout(L))
+        R = args.copies or max(2, math.ceil((1 << 30) / sum(sizes[:-1])))
+        caches = [c0] + [binding.Cache(drive.gpu_layout(L), w.block_order) for _ in range(R - 1)]
         for c in caches[1:]:
             c.import_(state)
-    tok_c, blk_c = state_class_tokens(state, dataclasses.replace(L, num_layers=1))
-    abytes, kvbytes = algorithmic_bytes(tok_c, blk_c, L, B)
-    log(f"[bench] built in {time.time() - t0:.1f} s; algorithmic bytes per attention call {abytes / 1e6:.2f} MB")
+    L1 = dataclasses.replace(L, num_layers=1)
+    q0, _, _, pos0 = ch.step_inputs(0)
+    abytes, kvbytes, init_tokens = attn_bytes(state, L1, w.seq_ids, pos0, 0, self_token=True)
+    log(f"[bench] state {sum(sizes[:-1]) / 1e6:.1f} MB x {R} copies, built in {time.time() - t0:.1f} s; "
+        f"algorithmic bytes per attention call {abytes / 1e6:.2f} MB")
 
-    # inputs for every step, resident on the device
-    dv = helpers.dev
+    # inputs for every step, resident on the device.  Step s runs on copy
+    # s % R as that copy's (s // R)-th decode step: each copy replays the same
+    # decode sequence (positions, planted thought types, new tokens), so every
+    # copy sees the planted segment process as one cache would.
+    dv = drive.dev
     seq_d = dv(w.seq_ids, np.int32)
-    # Step s runs on copy s % R, and it is that copy's (s // R)-th decode step:
-    # each copy replays the same decode sequence (positions, planted thought
-    # types, new tokens), so every copy sees the planted segment process as
-    # one cache would, not every R-th step of it.
     per_copy = []
-    for i in range((total_steps + R - 1) // R):
+    for i in range((total + R - 1) // R):
         q, k, v, pos = ch.step_inputs(i)
-        # with layers: each layer attends with the same query and self-token rows; the append takes every layer's
         kl, vl = np.tile(k, (1, NL, 1)), np.tile(v, (1, NL, 1))
         per_copy.append((dv(q, np.uint16), dv(k, np.float32), dv(v, np.float32), dv(pos, np.int32),
                          dv(kl, np.float32) if NL > 1 else None, dv(vl, np.float32) if NL > 1 else None))
-    steps_in = [per_copy[s // R] for s in range(total_steps)]
+    steps_in = [per_copy[s // R] for s in range(total)]
     Hq, D = L.num_q_heads, L.head_dim
     out = torch.empty(B, Hq, D, dtype=torch.float32, device="cuda")
     stats = torch.empty(B, NL, Hq, 3, dtype=torch.float32, device="cuda")   # every layer's rows of a step
-    n_att = torch.zeros(total_steps, B, dtype=torch.int32, device="cuda")   # one row per step
+    n_att = torch.zeros(total, B, dtype=torch.int32, device="cuda")         # one row per step
     ws = torch.empty(max(caches[0].workspace_bytes(B), 16), dtype=torch.uint8, device="cuda")
     labels = torch.empty(B, dtype=torch.uint8, device="cuda")
-    max_ops = 256
+    max_ops = 1024
     n_ops = torch.zeros(1, dtype=torch.int32, device="cuda")
     o_seq = torch.zeros(max_ops, dtype=torch.int32, device="cuda")
     o_seg, o_keep = torch.zeros_like(o_seq), torch.zeros_like(o_seq)
     o_bits = torch.zeros(max_ops, dtype=torch.uint8, device="cuda")
-    ev = HipEvents(2 * total_steps + 2, torch_events=args.torch_events)   # (before, after) each attention
 
     # every call's C arguments are converted once, before anything is timed
     sh = torch.cuda.current_stream().cuda_stream
     calls_a, calls_b = [], []
-    for s in range(total_steps):
+    for s in range(total):
         c = caches[s % R]
         q, k, v, pos, kl, vl = steps_in[s]
         calls_a.append([c.attention(seq_d, pos, q, out, ws, stats=stats[:, l], n_attended=n_att[s], k_self=k,
@@ -340,26 +485,28 @@ def main():
                         for l in range(NL)])
         calls_b.append([
             # classification of every layer's statistics rows, inside the append's allocation kernel
-            c.classify_append(seq_d, pos, stats.view(B, NL * Hq, 3), ch.tau[0], ch.tau[1], kl if NL > 1 else k,
-                              vl if NL > 1 else v, labels_out=labels, stream=sh, prepare=True),
-        ] + ([c.plan_anneal_evict(seq_d, args.r0, max_ops, n_ops, o_seq, o_seg, o_keep, o_bits, stream=sh,
-                                  prepare=True)]
+            ("classify+append", c.classify_append(seq_d, pos, stats.view(B, NL * Hq, 3), ch.tau[0], ch.tau[1],
+                                                  kl if NL > 1 else k, vl if NL > 1 else v, labels_out=labels,
+                                                  stream=sh, prepare=True)),
+            ("plan+evict",
+             c.plan_anneal_evict(seq_d, args.r0, max_ops, n_ops, o_seq, o_seg, o_keep, o_bits, stream=sh, prepare=True)
              if args.policy == "anneal" else
-             # the planner and the eviction's planning in one kernel (kv_plan_budget_evict / kv_plan_anneal_evict)
-             [c.plan_budget_evict(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, o_seq, o_seg, o_keep, o_bits,
-                                  stream=sh, prepare=True)])
-          + ([c.compact(o_seq, n_dev=n_ops, n=max_ops, stream=sh, prepare=True)] if args.compact else []))
+             c.plan_budget_evict(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, o_seq, o_seg, o_keep, o_bits,
+                                 stream=sh, prepare=True)),
+        ] + ([("compact", c.compact(o_seq, n_dev=n_ops, n=max_ops, stream=sh, prepare=True))] if args.compact else []))
 
-    # Steps are launched eagerly on torch's current stream: on this stack a
-    # replayed HIP graph per step measured slower than direct launches.  The
-    # attention launch is bracketed by events on the same stream.
+    ev = HipEvents(2 * total + 2, torch_events=args.torch_events)   # (before, after) each attention
+
+    # Steps are launched eagerly on torch's current stream (a replayed HIP
+    # graph per step measured slower on this stack).  The attention launch is
+    # bracketed by events on the same stream.
     def step(s):
         ev.record(2 * s, sh)
         for f in calls_a[s]:
             f()
         ev.record(2 * s + 1, sh)
         if not args.attn_only:
-            for f in calls_b[s]:
+            for _, f in calls_b[s]:
                 f()
 
     if args.copy_calibration:
@@ -377,28 +524,47 @@ def main():
         step(s)
     torch.cuda.synchronize()
     log("[bench] timed")
-    T0, T1 = 2 * total_steps, 2 * total_steps + 1
-    torch.cuda.synchronize()
+    T0, T1 = 2 * total, 2 * total + 1
     h0 = time.perf_counter()
     ev.record(T0, sh)
-    for s in range(args.warmup, total_steps):
+    for s in range(args.warmup, args.warmup + args.steps):
         step(s)
     ev.record(T1, sh)
     h1 = time.perf_counter()
     torch.cuda.synchronize()
     ms_total = ev.elapsed_ms(T0, T1)
     log(f"[bench] host enqueue {(h1 - h0) * 1e6 / args.steps:.1f} us/step, device {ms_total * 1e3 / args.steps:.1f} us/step")
-    attn_ms = [ev.elapsed_ms(2 * s, 2 * s + 1) for s in range(args.warmup, total_steps)]
-    errs = [c.get_error() for c in caches]
-    if any(e[0] for e in errs):
-        log(f"[bench] WARNING device errors: {errs}")
-    tokens1 = int(n_att[args.warmup:].sum().item())        # one layer's attended tokens
-    tokens = tokens1 * NL                                   # KV tokens attended over all layers
+    attn_ms = [ev.elapsed_ms(2 * s, 2 * s + 1) for s in range(args.warmup, args.warmup + args.steps)]
+    check_errors(caches, "the timed steps")
+
+    # per-call split: further steps with an event between every call
+    split = {}
+    if split_steps:
+        names = ["attention"] + [n for n, _ in calls_b[0]]
+        es = HipEvents((len(names) + 1) * split_steps)
+        k = len(names) + 1
+        for j, s in enumerate(range(args.warmup + args.steps, total)):
+            es.record(k * j, sh)
+            for f in calls_a[s]:
+                f()
+            es.record(k * j + 1, sh)
+            for i, (_, f) in enumerate(calls_b[s]):
+                f()
+                es.record(k * j + 2 + i, sh)
+        torch.cuda.synchronize()
+        for i, n in enumerate(names):
+            t = sorted(es.elapsed_ms(k * j + i, k * j + i + 1) * 1e3 for j in range(split_steps))
+            split[n] = t[len(t) // 2]
+        es.close()
+        check_errors(caches, "the split steps")
+
+    cached = n_att[args.warmup:args.warmup + args.steps].sum().item() - args.steps * B   # self token excluded
+    tokens1 = int(cached)                                  # one layer's attended cached tokens
+    tokens = tokens1 * NL
     ms_step = ms_total / args.steps
-    attn_avg = float(np.mean(attn_ms))                      # every layer's attention of a step
+    attn_avg = float(np.mean(attn_ms))                     # every layer's attention of a step
     # the cache changes a little from step to step (appends, evictions): scale
     # the KV part of the byte count by the attended tokens actually seen
-    init_tokens = int(tok_c[:B].sum())
     abytes_step = abytes - kvbytes + kvbytes * (tokens1 / args.steps) / max(init_tokens, 1)
     achieved = abytes_step / (attn_avg / NL * 1e-3) / 1e9
     result = {
@@ -416,23 +582,74 @@ def main():
                   "f16 MFMA (FP8 E4M3 / FP4 E2M1 codes converted exactly to fp16, ternary codes as fp16 "
                   "subnormals), f32 accumulate"),
         "data": "synthetic",
-        "config": {"workload": workload_name(args),
-                   "batch": B, "copies": R, "attended_per_step": tokens / args.steps,
-                   "launch": "eager, one stream", **({"layers": NL} if NL > 1 else {})},
+        "config": {"workload": workload_name(args), "batch": B, "copies": R,
+                   "attended_cached_per_step": tokens / args.steps, "launch": "eager, one stream",
+                   **({"layers": NL} if NL > 1 else {})},
         "attn_ms": attn_avg,
         "attn_kv_tokens_per_s": (tokens / args.steps) / (attn_avg * 1e-3),
+        "step_split_us": split,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic() if (args.workload == "llama8b" and args.policy == "ladder"
-                                                       and not args.compact and NL == 1
-                                                       and args.formats == "int") else None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "kernel": "k_attn (paged_decode_attn; one launch per layer and step)",
                      "bytes_per_launch": abytes_step},
     }
+    return result, (w, state, ch)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=6)
+    ap.add_argument("--split-steps", type=int, default=16, help="extra steps timed call by call")
+    ap.add_argument("--copies", type=int, default=0, help="state copies (0 = enough for > 1 GiB)")
+    ap.add_argument("--cpu-seqs", type=int, default=16)
+    ap.add_argument("--workload", choices=("churn256", "llama8b"), default="churn256",
+                    help="the B256 churn decode loop (4k..32k, 5%% budget) or the llama8b-like layer (B32, 16k, 10%%)")
+    ap.add_argument("--policy", choices=("ladder", "anneal"), default="ladder",
+                    help="eviction planner of the step: the token-budget ladder, or the TBE annealing schedule")
+    ap.add_argument("--r0", type=int, default=64, help="first retention of the annealing schedule")
+    ap.add_argument("--compact", action="store_true",
+                    help="compact the sequences each step evicted from (gather-compaction baseline)")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="layers per decode step sharing the block tables (the one-layer state replicated)")
+    ap.add_argument("--formats", choices=("int", "page"), default="int",
+                    help="code formats of the 8/4/2-bit classes: asymmetric integer, or FP8 E4M3 / FP4 E2M1 / ternary")
+    ap.add_argument("--configs", default=",".join(ATTN_CONFIGS),
+                    help="static workloads whose attention call is timed alone (comma list; 'none' for none)")
+    ap.add_argument("--no-stream", action="store_true", help="skip the streaming-read ceiling")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attn-only", action="store_true", help="time only the attention calls of the steps (diagnostic)")
+    ap.add_argument("--torch-events", action="store_true", help="time with torch's default events (diagnostic)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before the timed region, copy MIB MiB device-to-device 3 times (a plain copy kernel of "
+                         "known size, to scale hardware byte counters by)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path shards by "
+              f"sequence with no exchange, so N GPUs would run N independent copies of this step.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    result, (w, state, ch) = step_bench(args)
+    if not args.no_stream:
+        log("[bench] streaming-read ceiling")
+        sc = stream_ceiling()
+        result["stream_read"] = sc
+        result["roofline"]["frac_of_stream_read"] = result["roofline"]["achieved"] / sc["GB/s"]
+        log(f"[bench] stream read {sc['GB/s']:.0f} GB/s")
+    names = [] if args.configs == "none" else [n for n in args.configs.split(",") if n]
+    if names:
+        result["configs"] = {}
+        for n in names:
+            log(f"[bench] attention alone: {n}")
+            result["configs"].update(attention_config(n))
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(w, state, ch, args.cpu_seqs, policy=args.policy, r0=args.r0,
-                                              compact=args.compact)
+        result["cpu_baseline"] = cpu_baseline(w, state, ch, min(args.cpu_seqs, w.seq_ids.size), policy=args.policy,
+                                              r0=args.r0, compact=args.compact)
     print(json.dumps(result), flush=True)
 
 

@@ -29,9 +29,8 @@
  *     later items of that sequence in the same call are skipped, other
  *     sequences proceed, and a sticky error word records the kinds seen, the
  *     lowest sequence id involved and a count (tkv_get_error).
- *   - Inputs must be finite: K/V rows with magnitude below 2^8 (the
- *     attention feeds probability-weighted V scales of up to 2^8 times a
- *     group's scale as fp16 operands), queries below 2^15.
+ *   - Inputs must be finite with magnitude below 2^15 (K/V rows, queries,
+ *     sinks); outside that range results are undefined.
  *
  * State format (the buffers, all little-endian):
  *   Three precision classes c = 0, 1, 2 hold 8-, 4- and 2-bit codes.  Each
@@ -339,6 +338,14 @@ int tkv_export_state(tkv_cache* c, void* const host_bufs_h[TKV_NUM_BUFFERS]);
 int tkv_import_state(tkv_cache* c, void* const host_bufs_h[TKV_NUM_BUFFERS]);
 
 const char* tkv_strerror(int status);
+
+/* tkv_stream_read -- measurement aid, not part of the method: read `bytes`
+ * (a multiple of 16) of the device buffer `src` with 128-bit loads at a grid
+ * stride and fold them into a value that is stored to the device word `sink`
+ * only in a case that does not arise in practice.  Timing it on a buffer
+ * larger than the 256 MB Infinity Cache gives the streaming-read ceiling of
+ * HBM on this machine.  EINVAL: src or sink NULL, or bytes % 16 != 0. */
+int tkv_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

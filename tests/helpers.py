@@ -29,31 +29,21 @@ def build_oracle(w: synth.Workload):
 
 
 # ---------------------------------------------------------------------------
-# HIP path (GPU tests only)
+# HIP path (GPU tests only): the package's own drivers of the C-ABI
 # ---------------------------------------------------------------------------
 def gpu_layout(L: synth.Layout):
-    from thought_adaptive_mixed_amd import binding
-    return binding.make_layout(L.num_kv_heads, L.num_q_heads, L.head_dim, L.group_size, L.pool_blocks,
-                               L.max_seqs, L.max_blocks_per_seq, L.max_segments_per_seq, L.max_tokens_per_call,
-                               L.bits, L.num_layers, L.code_format)
+    from thought_adaptive_mixed_amd import drive
+    return drive.gpu_layout(L)
 
 
 def dev(a, dtype=None):
-    import torch
-    a = np.ascontiguousarray(a if dtype is None else np.asarray(a, dtype))
-    return torch.from_numpy(a).cuda()
+    from thought_adaptive_mixed_amd import drive
+    return drive.dev(a, dtype)
 
 
 def build_gpu(w: synth.Workload, cache=None):
-    from thought_adaptive_mixed_amd import binding
-    gc = cache or binding.Cache(gpu_layout(w.layout), w.block_order)
-    for call in w.calls:
-        if isinstance(call, synth.AppendCall):
-            k, v = w.kv(call)
-            gc.append(dev(call.seq_ids), dev(call.positions), dev(call.thought), dev(k), dev(v))
-        else:
-            gc.evict(dev(call.seq_ids), dev(call.seg_ids), dev(call.keep_n), dev(call.new_bits))
-    return gc
+    from thought_adaptive_mixed_amd import drive
+    return drive.build_gpu(w, cache)
 
 
 _TEMPLATES = {}

@@ -22,8 +22,11 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("formats", [False, True])
 def test_classify_append_lockstep(formats):
     """Decode loop on three caches: fused classify + append, the two-call path,
-    and the oracle; ladder and evictions on all three; labels every step,
-    states every 8 steps."""
+    and the oracle; ladder and evictions on all three.  Both GPU paths
+    classify the oracle's fp32 statistics, so their labels must equal the
+    oracle's bit for bit at every step and the oracle stays in the loop
+    throughout; the GPU's own statistics give the oracle's labels outside the
+    threshold ambiguity band.  States every 8 steps."""
     import torch
     import oracle
     from thought_adaptive_mixed_amd import binding
@@ -47,43 +50,121 @@ def test_classify_append_lockstep(formats):
                     [torch.zeros(max_ops, dtype=torch.uint8, device="cuda")]
     lab_a = torch.zeros(B, dtype=torch.uint8, device="cuda")
     lab_b = torch.zeros(B, dtype=torch.uint8, device="cuda")
+    lab_g = torch.zeros(B, dtype=torch.uint8, device="cuda")
     tT, tE = ch.tau
-    in_sync = True
+    amb = 0
     for s in range(ch.steps):
         q, k, v, pos = ch.step_inputs(s)
         oa, sa, na = gpu_attention(ga, w.seq_ids, pos, q, k_self=k, v_self=v)
         ob, sb, nb = gpu_attention(gb, w.seq_ids, pos, q, k_self=k, v_self=v)
         assert np.array_equal(sa, sb) and np.array_equal(oa, ob), f"step {s}: the two caches diverged"
-        pos_d, k_d, v_d = dv(pos, np.int32), dv(k, np.float32), dv(v, np.float32)
-        ga.classify_append(seq_d, pos_d, dv(sa, np.float32), tT, tE, k_d, v_d, labels_out=lab_a)
-        binding.classify(dv(sb, np.float32), tT, tE, lab_b)
+        ro, rs, rn = oc.attention(w.seq_ids, pos, q, k_self=k, v_self=v)
+        mabs, rl2 = helpers.attn_metrics(oa, ro)
+        assert mabs <= TOL_ABS and rl2 <= TOL_L2, s
+        rs32 = rs.astype(np.float32)
+        lab_o = oracle.classify(rs32, tT, tE)
+        binding.classify(dv(sa, np.float32), tT, tE, lab_g)
+        amb += _check_labels(lab_g.cpu().numpy(), lab_o, rs, tT, tE, s)
+        pos_d, k_d, v_d, st_d = dv(pos, np.int32), dv(k, np.float32), dv(v, np.float32), dv(rs32)
+        ga.classify_append(seq_d, pos_d, st_d, tT, tE, k_d, v_d, labels_out=lab_a)
+        binding.classify(st_d, tT, tE, lab_b)
         gb.append(seq_d, pos_d, lab_b, k_d, v_d)
-        la = lab_a.cpu().numpy()
-        assert np.array_equal(la, lab_b.cpu().numpy()), f"labels step {s}"
-        if in_sync:
-            ro, rs, rn = oc.attention(w.seq_ids, pos, q, k_self=k, v_self=v)
-            mabs, rl2 = helpers.attn_metrics(oa, ro)
-            assert mabs <= TOL_ABS and rl2 <= TOL_L2, s
-            lab_o = oracle.classify(rs.astype(np.float32), tT, tE)
-            if _check_labels(la, lab_o, rs, tT, tE, s):
-                in_sync = False            # a label inside the ambiguity band: the oracle stops here
-                say(f"[fused] oracle comparison stops at step {s} (label in the ambiguity band)")
-            else:
-                oc.append(w.seq_ids, pos, lab_o, k, v)
+        oc.append(w.seq_ids, pos, lab_o, k, v)
+        assert np.array_equal(lab_a.cpu().numpy(), lab_o), f"fused labels step {s}"
+        assert np.array_equal(lab_b.cpu().numpy(), lab_o), f"thought_classify labels step {s}"
         for tag, g in (("a", ga), ("b", gb)):
             n_ops, o_seq, o_seg, o_keep, o_bits = bufs[tag]
             g.plan_budget(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, o_seq, o_seg, o_keep, o_bits)
             g.evict(o_seq, o_seg, o_keep, o_bits, n_ops_dev=n_ops, n_ops=max_ops)
-        if in_sync:
-            ops = oc.plan_budget(w.seq_ids, ch.budget[0], ch.budget[1], max_ops)
-            if ops[0].size:
-                oc.evict(*ops)
+        ops = oc.plan_budget(w.seq_ids, ch.budget[0], ch.budget[1], max_ops)
+        if ops[0].size:
+            oc.evict(*ops)
         if s % 8 == 7 or s == ch.steps - 1:
             ea = ga.export()
             helpers.compare_states(L, ea, gb.export(), f"fused vs two calls, step {s}")
-            if in_sync:
-                helpers.compare_states(L, ea, oc.export(), f"fused vs oracle, step {s}")
-    assert ga.get_error() == gb.get_error()
+            helpers.compare_states(L, ea, oc.export(), f"fused vs oracle, step {s}")
+    say(f"[fused] formats={formats}: {ch.steps} steps in lockstep with the oracle, {amb} GPU-statistics labels "
+        f"in the ambiguity band")
+    assert ga.get_error() == gb.get_error() == oc.error()
+
+
+def _exact_score(row, kind):
+    """The oracle's fp32 score of one statistics row [Hq][3]: the smallest
+    fp32 threshold tau with label T (score <= tau), by bisection over the
+    ordered bit patterns of non-negative floats."""
+    import oracle
+    lo, hi = 0, 0x3F800000 + 0x100000          # [0, a little above 1]
+    r = np.ascontiguousarray(row[None], np.float32)
+    while lo < hi:
+        mid = (lo + hi) // 2
+        t = float(np.array([mid], np.uint32).view(np.float32)[0])
+        if oracle.classify(r, t, 4.0, kind)[0] == 2:
+            hi = mid
+        else:
+            lo = mid + 1
+    return np.array([lo], np.uint32).view(np.float32)[0]
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_classify_kinds_vs_oracle(kind):
+    """thought_classify and kv_classify_append against oracle.classify on the
+    same fp32 statistics (the oracle's own attention statistics of a small
+    cache, and rows with every head equal): labels bit for bit at the default
+    thresholds, and with thresholds placed exactly at a row's score and one
+    ulp either side of it, for both tau_T and tau_E."""
+    import torch
+    import oracle
+    from thought_adaptive_mixed_amd import binding
+    w = synth.small_static(seed=131, B=6, Hq=8, Hkv=2, D=64, g=32)
+    L = w.layout
+    B, Hq = w.seq_ids.size, L.num_q_heads
+    oc = helpers.build_oracle(w)
+    rng = np.random.default_rng(131)
+    _, rs, _ = oc.attention(w.seq_ids, w.q_pos, w.q_bf16)
+    st = rs.astype(np.float32)
+    # rows whose heads are all equal, at and around the default thresholds
+    flat = np.empty((4, Hq, 3), np.float32)
+    for i, base in enumerate((0.38, 0.85, 1 - 0.38, 1 - 0.85)):
+        flat[i] = rng.uniform(0, 1, 3).astype(np.float32)
+        flat[i, :, 1] = np.float32(base)
+        flat[i, :, 2] = np.float32(base)
+    st = np.concatenate([st, flat])
+    n = st.shape[0]
+    dv = helpers.dev
+    st_d = dv(st)
+    lab = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    # the fused call needs a cache and tokens to append: one fresh cache per call
+    k = rng.standard_normal((n, L.num_kv_heads, L.head_dim)).astype(np.float32)
+    v = rng.standard_normal((n, L.num_kv_heads, L.head_dim)).astype(np.float32)
+
+    def fused_labels(tT, tE):
+        from thought_adaptive_mixed_amd import drive
+        Lf = synth.Layout(L.num_kv_heads, Hq, L.head_dim, L.group_size, (16, 16, 16), n, 4, 8, 64)
+        gc = binding.Cache(drive.gpu_layout(Lf))
+        out = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        gc.classify_append(dv(np.arange(n, dtype=np.int32)), dv(np.zeros(n, np.int32)), st_d, tT, tE, dv(k), dv(v),
+                           labels_out=out, score_kind=kind)
+        torch.cuda.synchronize()
+        assert gc.get_error()[0] == 0
+        return out.cpu().numpy()
+
+    cases = [(0.38, 0.85)] if kind == 0 else [(0.38, 0.85), (0.05, 0.2)]
+    for i in range(n):
+        sc = _exact_score(st[i], kind)
+        for t in (sc, np.nextafter(sc, np.float32(-1)), np.nextafter(sc, np.float32(2))):
+            cases.append((float(t), 4.0))          # tau_T at the score
+            cases.append((-1.0, float(t)))         # tau_E at the score
+    checked = 0
+    for tT, tE in cases:
+        ref = oracle.classify(st, tT, tE, kind)
+        binding.classify(st_d, tT, tE, lab, score_kind=kind)
+        torch.cuda.synchronize()
+        assert np.array_equal(lab.cpu().numpy(), ref), (kind, tT, tE)
+        checked += 1
+    # the fused call on the default thresholds and on a few exact edges
+    for tT, tE in cases[:1] + cases[len(cases) - 6:]:
+        assert np.array_equal(fused_labels(tT, tE), oracle.classify(st, tT, tE, kind)), (kind, tT, tE)
+    say(f"[classify] kind {kind}: {checked} threshold settings x {n} rows equal to the oracle")
 
 
 def test_classify_append_layers_and_kind():

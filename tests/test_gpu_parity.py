@@ -53,7 +53,7 @@ def _check_labels(lab_g, lab_o, rs, tT, tE, step):
     return int(band.sum())
 
 
-def check_attention(tag, got, ref):
+def check_attention(tag, got, ref, tol_stat=TOL_STAT):
     (go, gs, gn), (ro, rs, rn) = got, ref
     mabs, rl2 = helpers.attn_metrics(go, ro)
     dh = float(np.abs(gs[..., 1] - rs[..., 1]).max()) if gs.size else 0.0
@@ -62,7 +62,7 @@ def check_attention(tag, got, ref):
     assert np.array_equal(gn, rn), f"{tag}: n_attended {gn} vs {rn}"
     assert np.isfinite(go).all()
     assert mabs <= TOL_ABS and rl2 <= TOL_L2, tag
-    assert dh <= TOL_STAT and dm <= TOL_STAT, tag
+    assert dh <= tol_stat and dm <= tol_stat, tag
     np.testing.assert_allclose(gs[..., 0], rs[..., 0], rtol=1e-3, atol=2e-4)
 
 

@@ -26,7 +26,8 @@ BUFFER_DTYPES = {n: (np.uint8 if n.startswith("pool") else np.int32) for n in BU
 # Entry points declared in include/tkv.h
 SYMBOLS = ["tkv_buffer_sizes", "tkv_create", "tkv_destroy", "tkv_seq_reset", "kv_append_quant", "kv_classify_append",
            "kv_evict_segment", "kv_plan_budget", "kv_plan_budget_evict", "kv_plan_anneal", "kv_plan_anneal_evict", "tkv_compact", "tkv_attn_workspace", "paged_decode_attn",
-           "thought_classify", "tkv_get_error", "tkv_export_state", "tkv_import_state", "tkv_strerror"]
+           "thought_classify", "tkv_get_error", "tkv_export_state", "tkv_import_state", "tkv_strerror",
+           "tkv_stream_read"]
 
 
 class Layout(C.Structure):
@@ -62,6 +63,9 @@ def load(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise FileNotFoundError(f"{path} is missing: build it with `python -m thought_adaptive_mixed_amd.build`")
+    # torch first: the library then binds to the HIP runtime torch has loaded
+    # (the same soname), so one runtime serves both in the process
+    import torch  # noqa: F401
     L = C.CDLL(path)
     P, I, U = C.c_void_p, C.c_int32, C.c_uint8
     L.tkv_buffer_sizes.argtypes = [P, P]
@@ -83,6 +87,7 @@ def load(path: str = LIB_PATH):
     L.tkv_export_state.argtypes = [P, P]
     L.tkv_import_state.argtypes = [P, P]
     L.tkv_strerror.argtypes = [C.c_int]; L.tkv_strerror.restype = C.c_char_p
+    L.tkv_stream_read.argtypes = [P, C.c_size_t, P, P]
     _lib = L
     return L
 
@@ -293,3 +298,10 @@ def classify(stats, tau_T, tau_E, labels_out, score_kind=0, *, stream=None, prep
     args = (B, Hq, _ptr(stats), C.c_float(tau_T), C.c_float(tau_E), int(score_kind), _ptr(labels_out),
             _stream(stream))
     return _issue(load().thought_classify, args, "thought_classify", prepare)
+
+
+def stream_read(buf, sink, *, stream=None, prepare=False):
+    """Streaming 128-bit read of a whole device tensor (the HBM read ceiling)."""
+    nbytes = int(buf.numel() * buf.element_size())
+    args = (_ptr(buf), C.c_size_t(nbytes), _ptr(sink), _stream(stream))
+    return _issue(load().tkv_stream_read, args, "tkv_stream_read", prepare)

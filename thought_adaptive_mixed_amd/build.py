@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libthinkv.so")
-SOURCES = ["tkv_api.hip", "tkv_state.hip", "tkv_attn.hip"]
+SOURCES = ["tkv_api.hip", "tkv_state.hip", "tkv_attn.hip", "tkv_probe.hip"]
 # attention: no NaN can arise (masked logits are -inf, never NaN), so fmax/fmin
 # need no operand canonicalization; MFMA accumulators stay in VGPRs so the
 # rare rescale does not copy them out of AGPRs on every block

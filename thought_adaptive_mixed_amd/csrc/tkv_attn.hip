@@ -37,8 +37,9 @@
 // and the softmax epilogue runs once for all of them on fully used lanes, then
 // P' is unpacked block by block for the P.V products.
 // Softmax runs online in the log2 domain; the running max is shared by the
-// lanes holding a head's tokens and is raised only when a step exceeds it by
-// more than 2^8 (lazy rescale).  Each lane keeps partial Z, S' = sum p (s - m)
+// lanes holding a head's tokens and is raised whenever a step exceeds it, so
+// every weight is at most 1 and p sV at most sV (below 2^15 for inputs below
+// 2^15 in magnitude: an fp16 operand).  Each lane keeps partial Z, S' = sum p (s - m)
 // and a sorted top-8 of its logits, filtered by the head-wide 8th-best bound.
 // The waves of a work-group merge their records through LDS; with one split
 // the work-group then adds the staged self token and the sink and writes the
@@ -54,7 +55,6 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 
 #define PART_X 16          // extra floats per partial record: m2, Z, S2, n, top8[8], pad
 #define TOPK 8
-#define SLACK 8.0f         // lazy-rescale slack, log2 units
 #define LOG2E 1.4426950408889634f
 #define LN2 0.6931471805599453f
 
@@ -263,20 +263,35 @@ __device__ inline void first_lanes_topk(float (&L)[TOPK], int n) {
   if (n > 32) pair_topk<32>(L);
 }
 
-// One step's data in registers: the K and V code chunks of the PK blocks
-// (lane l: chunk l of each), the metadata of this lane's own block (quad lg)
-// and, with a window, the positions of its four tokens.  Sized for the 8-bit
-// class; a class with fewer bits uses the first D*bits/128 words of a chunk.
+// Blocks per step of class C when the layout packs PK blocks side by side:
+// the 8-bit class at D = 128 takes at most two (four blocks of its codes
+// would not fit the registers of two steps); its steps leave the columns of
+// the missing block positions empty.  32-bit words of a lane's chunk: D*bits/128.
+template <int D, int PK, int C>
+constexpr int pk_class() { return (C == 0 && D == 128 && PK > 2) ? 2 : PK; }
+template <int D, int C>
+constexpr int chunk_words() { return D * (C == 0 ? 8 : (C == 1 ? 4 : 2)) / 128; }
+template <int D, int PK>
+constexpr int step_words() {
+  constexpr int a = pk_class<D, PK, 0>() * chunk_words<D, 0>(), b = pk_class<D, PK, 1>() * chunk_words<D, 1>(),
+                c = pk_class<D, PK, 2>() * chunk_words<D, 2>();
+  return a > b ? (a > c ? a : c) : (b > c ? b : c);
+}
+
+// One step's data in registers: the K and V code chunks of the step's blocks
+// (lane l: chunk l of each; block j's words at j * chunk_words), the metadata
+// of this lane's own block (quad lg) and, with a window, the positions of its
+// four tokens.  Sized for the class whose step holds the most words.
 template <int D, int GS, bool WINDOW, int PK>
 struct Buf {
   static constexpr int NG = D / GS;
-  static constexpr int CWM = D * 8 / 128;       // 32-bit words per lane chunk at 8 bits
-  uint32_t kw[PK][CWM], vw[PK][CWM];
+  static constexpr int KW = step_words<D, PK>();
+  uint32_t kw[KW], vw[KW];
   uint32_t mk[4 * NG], mv[4 * NG];
   int pos[WINDOW ? 4 : 1];
 };
 
-template <int D, int GS, int BITS, int FMT, bool WINDOW, int PK>
+template <int D, int GS, int BITS, int FMT, bool WINDOW, int PK, int PKC>
 __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj, int lo_pos,
                                     int lane, bool head_ok, const half4_t (&qB)[D / 16],
                                     const half8_t* qk_lds, const float (&sumq)[D / GS],
@@ -285,6 +300,7 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
   constexpr int KM = GS / 16;
   constexpr int NT = D / 16;
   constexpr int GP = 16 / PK;
+  constexpr int CW = D * BITS / 128;
   const int lg = lane >> 4, jl = (lane & 15) / GP;
   // integer codes of this class are in units of 2^-kUnitExp; the zero-point
   // term's sum of q (in units of 2^-24) is brought to the same unit
@@ -307,21 +323,25 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
       spk[gi] = (float4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mm = 0; mm < KM; mm += 2)
-        spk[gi] = mfma32(cat8(operand4<BITS, FMT>(b.kw[0], gi * (GS / 4) + 4 * mm),
-                              operand4<BITS, FMT>(b.kw[0], gi * (GS / 4) + 4 * mm + 4)),
+        spk[gi] = mfma32(cat8(operand4<BITS, FMT>(b.kw, gi * (GS / 4) + 4 * mm),
+                              operand4<BITS, FMT>(b.kw, gi * (GS / 4) + 4 * mm + 4)),
                          *(const half8_t*)(qrow + ((gi * KM + mm) / 2) * 1024), spk[gi]);
     }
   } else {
 #pragma unroll
-    for (int gi = 0; gi < NG; gi++) {
-      spk[gi] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    for (int gi = 0; gi < NG; gi++) spk[gi] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    // pair by pair (the scheduling barrier keeps a pair's query operands from
+    // being read ahead of the previous pair's products: 4 VGPRs each)
 #pragma unroll
-      for (int p = 0; p < PK / 2; p++)
+    for (int p = 0; p < PKC / 2; p++) {
+#pragma unroll
+      for (int gi = 0; gi < NG; gi++)
 #pragma unroll
         for (int mm = 0; mm < KM; mm++)
-          spk[gi] = mfma32(cat8(operand4<BITS, FMT>(b.kw[2 * p], gi * (GS / 4) + 4 * mm),
-                                operand4<BITS, FMT>(b.kw[2 * p + 1], gi * (GS / 4) + 4 * mm)),
+          spk[gi] = mfma32(cat8(operand4<BITS, FMT>(b.kw + 2 * p * CW, gi * (GS / 4) + 4 * mm),
+                                operand4<BITS, FMT>(b.kw + (2 * p + 1) * CW, gi * (GS / 4) + 4 * mm)),
                            *(const half8_t*)(qrow + (p * (D / 16) + gi * KM + mm) * 1024), spk[gi]);
+      if (p + 1 < PKC / 2) __builtin_amdgcn_sched_barrier(0);
     }
   }
   // this lane's block (mask mj) and token quad (lg)
@@ -355,12 +375,13 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
     s2[r] = ((vb >> r) & 1u) ? x * alpha : -INFINITY;
     lmax = fmaxf(lmax, s2[r]);
   }
-  // lazy rescale: raise the running max only when a step exceeds it by
-  // SLACK.  A head's running max is held by all its lanes, so a lane's own
-  // values decide whether any head grows; the head-wide max is only formed then.
-  if (__builtin_amdgcn_ballot_w64(lmax > st.m2 + SLACK)) {
+  // the running max is exact (every weight p <= 1, so P' = p sV stays within
+  // the fp16 range for every scale the input range allows).  A head's running
+  // max is held by all its lanes, so a lane's own values decide whether any
+  // head grows; the head-wide max is only formed then.
+  if (__builtin_amdgcn_ballot_w64(lmax > st.m2)) {
     const float bm = head_max<GP>(lmax);
-    if (bm > st.m2 + SLACK) {
+    if (bm > st.m2) {
       if (st.m2 == -INFINITY) {
         st.Z = 0.f; st.S2 = 0.f;
       } else {
@@ -394,38 +415,33 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
   // P' = p sV per group as fp16 hi + lo (packed layout), and the zero-point
   // term.  A masked token has p = 0 and finite metadata: pools are cleared
   // when the cache is created, so a slot never written (the tail of an open
-  // block, the block repeated to pad a last step) holds zeros.  p sV is an fma
-  // with a +0 addend (one mixed-precision op; a zero's sign cannot matter in
-  // sums into the accumulator).
+  // block, the block repeated to pad a last step) holds zeros.  hi = f16(p sV)
+  // and lo = f16(p sV - hi) are each one mixed-precision fma rounded to
+  // nearest into a half of the operand word (the product p sV is exact inside
+  // the fma, so hi + lo carries ~22 significant bits); rounding toward zero
+  // made every term's error one-signed, and with sharp attention the many
+  // small P' terms (whose lo part sits in the fp16 subnormal range) then added
+  // up to ~2e-3 on large-valued channels.
   half4_t pbh[NG], pbl[NG];
 #pragma unroll
   for (int gi = 0; gi < NG; gi++) {
-    float pv[4];
     float z = st.zacc[gi];
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const uint32_t m = b.mv[r * NG + gi];
-      pv[r] = fmaf(p[r], h_lo(m), 0.f);
+      const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(m & 0xFFFF));
+      const _Float16 hi = (_Float16)fmaf(p[r], (float)sv, 0.f);
+      pbh[gi][r] = hi;
+      pbl[gi][r] = (_Float16)fmaf(p[r], (float)sv, -(float)hi);
       z = fmaf(p[r], h_hi(m), z);
     }
     st.zacc[gi] = z;
-    // round to nearest (v_cvt_pk_f16_f32): the residual of the hi part is
-    // exact in fp32, and the lo part's rounding error is unbiased.  Rounding
-    // toward zero made every term's error one-signed: with sharp attention the
-    // many small P' terms (whose lo part sits in the fp16 subnormal range,
-    // step 2^-24) then added up to ~2e-3 on large-valued channels.
-    const half2_t h01 = __builtin_convertvector((float2_t){pv[0], pv[1]}, half2_t);
-    const half2_t h23 = __builtin_convertvector((float2_t){pv[2], pv[3]}, half2_t);
-    const half2_t l01 = __builtin_convertvector((float2_t){pv[0] - (float)h01[0], pv[1] - (float)h01[1]}, half2_t);
-    const half2_t l23 = __builtin_convertvector((float2_t){pv[2] - (float)h23[0], pv[3] - (float)h23[1]}, half2_t);
-    pbh[gi] = (half4_t){h01[0], h01[1], h23[0], h23[1]};
-    pbl[gi] = (half4_t){l01[0], l01[1], l23[0], l23[1]};
   }
   // O^T += V^T P', P' unpacked to each block's own columns
   if constexpr (PK == 1) {
 #pragma unroll
     for (int n = 0; n < NT; n++) {
-      const half4_t a = operand4<BITS, FMT>(b.vw[0], 4 * n);
+      const half4_t a = operand4<BITS, FMT>(b.vw, 4 * n);
       st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pbh[(16 * n) / GS], st.acc[n], 0, 0, 0);
       st.acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pbl[(16 * n) / GS], st.acc[n], 0, 0, 0);
     }
@@ -436,7 +452,7 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
     // accumulator column h collects head h % GP over the blocks at position
     // h / GP of every step; the positions are summed once at the end.
 #pragma unroll
-    for (int jp = 0; jp < PK; jp += 2) {
+    for (int jp = 0; jp < PKC; jp += 2) {
       const bool k0 = jl == jp, k1 = jl == jp + 1;
       half8_t bh[NG], bl[NG];
 #pragma unroll
@@ -446,10 +462,12 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
       }
 #pragma unroll
       for (int n = 0; n < NT; n++) {
-        const half8_t a = cat8(operand4<BITS, FMT>(b.vw[jp], 4 * n), operand4<BITS, FMT>(b.vw[jp + 1], 4 * n));
+        const half8_t a = cat8(operand4<BITS, FMT>(b.vw + jp * CW, 4 * n),
+                               operand4<BITS, FMT>(b.vw + (jp + 1) * CW, 4 * n));
         st.acc[n] = mfma32(a, bh[(16 * n) / GS], st.acc[n]);
         st.acc[n] = mfma32(a, bl[(16 * n) / GS], st.acc[n]);
       }
+      if (jp + 2 < PKC) __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -472,15 +490,16 @@ __device__ inline void load_step(Buf<D, GS, WINDOW, PK>& b, const uint8_t* pool_
                                  const int32_t* slot_c, const int2* lv, int n, int sigma, int lane, bool pad) {
   constexpr int BITS = C == 0 ? 8 : (C == 1 ? 4 : 2);
   constexpr int NG = D / GS, CB = D * BITS / 32, CW = CB / 4, R = 128 * CB + 128 * NG, GP = 16 / PK;
+  constexpr int PKC = pk_class<D, PK, C>();
   const int lg = lane >> 4, jl = (lane & 15) / GP;
-  int ids[PK];
+  int ids[PKC];
 #pragma unroll
-  for (int j = 0; j < PK; j++) {
-    const int e = sigma * PK + j;
+  for (int j = 0; j < PKC; j++) {
+    const int e = sigma * PKC + j;
     ids[j] = __builtin_amdgcn_readfirstlane(lv[e < n ? e : n - 1].x);
   }
 #pragma unroll
-  for (int j = 0; j < PK; j++) {
+  for (int j = 0; j < PKC; j++) {
     const uint8_t* rec = pool_kvh + (int64_t)ids[j] * stride;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, pad ? 0 : R, kRawBufferWord3);
     if constexpr (CW % 4 == 0) {
@@ -490,20 +509,20 @@ __device__ inline void load_step(Buf<D, GS, WINDOW, PK>& b, const uint8_t* pool_
         const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + 1024 * i, 0, 0);
         const u32x4_t y = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + 1024 * i + 64 * CB, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; e++) { b.kw[j][4 * i + e] = x[e]; b.vw[j][4 * i + e] = y[e]; }
+        for (int e = 0; e < 4; e++) { b.kw[j * CW + 4 * i + e] = x[e]; b.vw[j * CW + 4 * i + e] = y[e]; }
       }
     } else if constexpr (CW == 2) {
       const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * 8, 0, 0);
       const u32x2_t y = __builtin_amdgcn_raw_buffer_load_b64(rs, lane * 8 + 64 * CB, 0, 0);
-      b.kw[j][0] = x[0]; b.kw[j][1] = x[1]; b.vw[j][0] = y[0]; b.vw[j][1] = y[1];
+      b.kw[j * CW] = x[0]; b.kw[j * CW + 1] = x[1]; b.vw[j * CW] = y[0]; b.vw[j * CW + 1] = y[1];
     } else {
-      b.kw[j][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, 0);
-      b.vw[j][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4 + 64 * CB, 0, 0);
+      b.kw[j * CW] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, 0);
+      b.vw[j * CW] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4 + 64 * CB, 0, 0);
     }
   }
-  int idj = ids[0];                                 // this lane's block
+  int idj = ids[0];                                 // this lane's block (block 0's when it has none)
 #pragma unroll
-  for (int j = 1; j < PK; j++) idj = (jl == j && !pad) ? ids[j] : idj;
+  for (int j = 1; j < PKC; j++) idj = (jl == j && !pad) ? ids[j] : idj;
   const int lq = pad ? 0 : lg;
   const uint8_t* rj = pool_kvh + (int64_t)idj * stride + 128 * CB;
   const uint4* mkp = (const uint4*)(rj + lq * 16 * NG);
@@ -540,7 +559,8 @@ __device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax
   // index, the class branches and the block addresses stay scalar
   const int n0 = __builtin_amdgcn_readfirstlane(nl[0]), n1 = __builtin_amdgcn_readfirstlane(nl[1]),
             n2 = __builtin_amdgcn_readfirstlane(nl[2]);
-  const int c1 = (n0 + PK - 1) / PK, c2 = c1 + (n1 + PK - 1) / PK, T = c2 + (n2 + PK - 1) / PK;
+  constexpr int P0 = pk_class<D, PK, 0>(), P1 = pk_class<D, PK, 1>(), P2 = pk_class<D, PK, 2>();
+  const int c1 = (n0 + P0 - 1) / P0, c2 = c1 + (n1 + P1 - 1) / P1, T = c2 + (n2 + P2 - 1) / P2;
   const int2* l0 = live;
   const int2* l1 = live + lmax;
   const int2* l2 = live + 2 * lmax;
@@ -566,9 +586,9 @@ __device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax
     else if (g < c2) load_step<D, GS, WINDOW, PK, 1>(b, pk1, Hst * R1, slt1, l1, n1, g - c1, lane, pad);
     else load_step<D, GS, WINDOW, PK, 2>(b, pk2, Hst * R2, slt2, l2, n2, g - c2, lane, pad);
   };
-  auto mask_of = [&](const int2* lv, int n, int sigma) -> uint32_t {
-    const int e = sigma * PK + jl;                  // this lane's block
-    return e < n ? (uint32_t)lv[e].y : 0u;
+  auto mask_of = [&](const int2* lv, int n, int sigma, int pkc) -> uint32_t {
+    const int e = sigma * pkc + jl;                 // this lane's block
+    return (jl < pkc && e < n) ? (uint32_t)lv[e].y : 0u;
   };
   // alpha is the logit factor for plain values.  The operands of a class are
   // its codes in units of 2^-kUnitExp (integer codes) or the values themselves
@@ -590,15 +610,15 @@ __device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax
   };
   auto comp = [&](const B& b, int g) {
     if (g < c1) {
-      compute_step<D, GS, 8, FMT, WINDOW, PK>(b, mask_of(l0, n0, g), lo_pos, lane, head_ok, qB, qk_lds, sumq,
+      compute_step<D, GS, 8, FMT, WINDOW, PK, P0>(b, mask_of(l0, n0, g, P0), lo_pos, lane, head_ok, qB, qk_lds, sumq,
                                                alpha * u0, st);
     } else if (g < c2) {
       to_unit(u1);
-      compute_step<D, GS, 4, FMT, WINDOW, PK>(b, mask_of(l1, n1, g - c1), lo_pos, lane, head_ok, qB, qk_lds, sumq,
+      compute_step<D, GS, 4, FMT, WINDOW, PK, P1>(b, mask_of(l1, n1, g - c1, P1), lo_pos, lane, head_ok, qB, qk_lds, sumq,
                                                alpha * u1, st);
     } else {
       to_unit(u2);
-      compute_step<D, GS, 2, 0, WINDOW, PK>(b, mask_of(l2, n2, g - c2), lo_pos, lane, head_ok, qB, qk_lds, sumq,
+      compute_step<D, GS, 2, 0, WINDOW, PK, P2>(b, mask_of(l2, n2, g - c2, P2), lo_pos, lane, head_ok, qB, qk_lds, sumq,
                                              alpha * u2, st);
     }
   };
@@ -713,8 +733,11 @@ __device__ inline SelfTok load_self(const AttnParams& P, int b, int hq, int lane
 }
 
 // Add the staged self token and the sink; write the output and statistics.
+// sink: the head's sink logit (read by the caller ahead of time; unused
+// without sinks).
 template <int D>
-__device__ inline void finalize_head(const AttnParams& P, int b, int hq, int lane, Merged M, const SelfTok& self) {
+__device__ inline void finalize_head(const AttnParams& P, int b, int hq, int lane, Merged M, const SelfTok& self,
+                                     float sink) {
   const DevState& S = P.S;
   int n = M.n;
   if (P.k_self) {
@@ -738,7 +761,7 @@ __device__ inline void finalize_head(const AttnParams& P, int b, int hq, int lan
     if (st && lane == 0) { st[0] = 0.f; st[1] = 0.f; st[2] = 0.f; }
   } else {
     float den = M.Z;
-    if (P.sinks) den += exp2f(P.sinks[hq] * LOG2E - M.m);
+    if (P.sinks) den += exp2f(sink * LOG2E - M.m);
     const float inv = 1.0f / den;
     out[lane] = M.a0 * inv;
     if (D > 64) out[lane + 64] = M.a1 * inv;
@@ -764,9 +787,9 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   constexpr int GP = 16 / PK;
   constexpr int RS = D + PART_X;                 // record stride (floats)
   // Dynamic LDS: the waves' records; the live block lists are a static array.
+  // Dynamic LDS: the waves' records [nw][G][RS] floats, then the split's live
+  // block lists [3][max_blocks] (id, mask) and their counts.
   extern __shared__ __align__(16) float lds[];
-  __shared__ int2 s_live[3 * TKV_MAX_BLOCKS];
-  __shared__ int s_nlive[3];
   const DevState& S = P.S;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   // the wave index is uniform across its lanes: say so to the compiler
@@ -789,6 +812,26 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
 #pragma unroll
       for (int i = 0; i < GS / 32; i++) qraw[gi][i] = ((const uint4*)(qr + gi * GS + lg * (GS / 4)))[i];
   }
+  // What the finalize needs besides the records is read now by wave 0 and
+  // kept in LDS through the loop (s_fin): the sink logits of the group's
+  // heads and, when the self token is finalized here (one split), its V row
+  // (shared by the group's heads) and its logit for each head, computed from
+  // its K row over this lane's query dims with the query conversion below.
+  __shared__ float s_fin[2 * 64 + 2 * 16];          // V row [128], self logits [16], sinks [16]
+  const bool self_here = P.splits == 1 && P.k_self != nullptr && w == 0;
+  const float sinks_g = (w == 0 && P.sinks && lane < G) ? P.sinks[kvh * G + lane] : 0.f;
+  float4 kself[NG][GS / 16];
+  float selfv0 = 0.f, selfv1 = 0.f;
+  if (self_here) {
+    const float* kr = P.k_self + ((int64_t)b * S.Hkv + kvh) * D;
+    const float* vr = P.v_self + ((int64_t)b * S.Hkv + kvh) * D;
+#pragma unroll
+    for (int gi = 0; gi < NG; gi++)
+#pragma unroll
+      for (int i = 0; i < GS / 16; i++) kself[gi][i] = ((const float4*)(kr + gi * GS + lg * (GS / 4)))[i];
+    selfv0 = vr[lane];
+    selfv1 = D > 64 ? vr[lane + 64] : 0.f;
+  }
   const float alpha = LOG2E / sqrtf((float)D);
   AttnState<D, GS> st;
 #pragma unroll
@@ -800,41 +843,74 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   for (int i = 0; i < TOPK; i++) st.top[i] = -INFINITY;
   st.thr = -INFINITY;
   st.vunit = FMT ? 1.0f : kCodeScale;        // the unit of the first class (8-bit codes)
-  // The split's live blocks of each class, into LDS, in list order: wave c
-  // (the waves in turn when there are fewer than three) takes class c's
-  // block-table entries 64 at a time, reads their block records and keeps,
-  // by ballot, those with a valid token (and, with a window, a position
-  // inside it).  A wave's first 64 entries of its own class are read
-  // together with the sequence record, before the split's range is known.
+  // The split's live blocks of each class, into LDS, in list order: wave w
+  // takes the classes c = w, w + nw, ... (all three with one wave), reads
+  // their block-table entries 64 at a time and their block records, and
+  // keeps, by ballot, the blocks with a valid token (and, with a window, a
+  // position inside it).  The first 64 entries of each of a wave's classes
+  // are read together with the sequence record, before the split's range is
+  // known, and the block records of those first entries are read together
+  // for all of the wave's classes, so the chain of dependent reads before
+  // the first codes is three deep (sequence id; sequence record and table;
+  // block records) whatever the number of waves.
   const int lo_pos = WINDOW ? P.q_pos[b] - P.window + 1 : 0;
   const int lmax = S.max_blocks;
-  int2* live = s_live;                                    // [3][lmax]
-  int* nlive = s_nlive;
+  int2* live = (int2*)(lds + (int64_t)nw * G * RS);       // [3][lmax]
+  int* nlive = (int*)(live + 3 * lmax);
   if (seq_ok) {
     const int32_t* q = S.seq + (int64_t)s * TKV_SEQ_W;
     const int32_t* bt = S.btab + (int64_t)s * 3 * lmax;
-    const int spec = w < 3 && lane < lmax ? bt[w * lmax + lane] : 0;
+    int spec[3];
+#pragma unroll
+    for (int k = 0; k < 3; k++) {
+      const int c = w + k * nw;
+      spec[k] = c < 3 && lane < lmax ? bt[c * lmax + lane] : 0;
+    }
     const int nb0 = q[Q_NBLK + 0], nb1 = q[Q_NBLK + 1], nb2 = q[Q_NBLK + 2];
     // byte-balanced split of [8-bit | 4-bit | 2-bit] block lists (< 2^31 bytes per sequence)
     const int w0 = (int)S.bh_bytes[0], w1 = (int)S.bh_bytes[1], w2 = (int)S.bh_bytes[2];
     const int P1 = nb0 * w0, P2 = P1 + nb1 * w1, W = P2 + nb2 * w2;
     const int lo = (int)((int64_t)W * split / P.splits), hi = (int)((int64_t)W * (split + 1) / P.splits);
     const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
-    for (int c = w; c < 3; c += nw) {
-      const int off = c == 0 ? 0 : (c == 1 ? P1 : P2);
-      const int wb = c == 0 ? w0 : (c == 1 ? w1 : w2);
-      const int nbc = c == 0 ? nb0 : (c == 1 ? nb1 : nb2);
-      const int a = lo - off, z = hi - off;
-      const int j0 = a <= 0 ? 0 : min(nbc, (a + wb - 1) / wb);
-      const int j1 = z <= 0 ? 0 : min(nbc, (z + wb - 1) / wb);
+    int j0s[3], j1s[3], ids[3], ms[3];
+#pragma unroll
+    for (int k = 0; k < 3; k++) {
+      const int c = w + k * nw;
+      j0s[k] = j1s[k] = 0;
+      if (c < 3) {
+        const int off = c == 0 ? 0 : (c == 1 ? P1 : P2);
+        const int wb = c == 0 ? w0 : (c == 1 ? w1 : w2);
+        const int nbc = c == 0 ? nb0 : (c == 1 ? nb1 : nb2);
+        const int a = lo - off, z = hi - off;
+        j0s[k] = a <= 0 ? 0 : min(nbc, (a + wb - 1) / wb);
+        j1s[k] = z <= 0 ? 0 : min(nbc, (z + wb - 1) / wb);
+      }
+      const int jj = j0s[k] + lane;
+      ids[k] = jj < j1s[k] ? (j0s[k] == 0 ? spec[k] : bt[c * lmax + jj]) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < 3; k++) {
+      const int c = w + k * nw;
+      ms[k] = 0;
+      if (c < 3 && j0s[k] + lane < j1s[k]) {
+        const int2 rec = *(const int2*)(pick3(S.blk, c) + (int64_t)ids[k] * TKV_BLK_W);
+        ms[k] = rec.x;
+        if (WINDOW && rec.y < lo_pos) ms[k] = 0;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 3; k++) {
+      const int c = w + k * nw;
+      if (c >= 3) break;
       const int32_t* blk = pick3(S.blk, c);
-      int cnt = 0;
-      for (int j = j0; j < j1; j += 64) {
+      const uint64_t bal0 = __builtin_amdgcn_ballot_w64(ms[k] != 0);
+      if (ms[k] != 0) live[c * lmax + __popcll(bal0 & lt)] = make_int2(ids[k], ms[k]);
+      int cnt = __popcll(bal0);
+      for (int j = j0s[k] + 64; j < j1s[k]; j += 64) {
         const int jj = j + lane;
-        const bool in = jj < j1;
         int id = 0, m = 0;
-        if (in) {
-          id = (j == 0 && c == w) ? spec : bt[c * lmax + jj];
+        if (jj < j1s[k]) {
+          id = bt[c * lmax + jj];
           const int2 rec = *(const int2*)(blk + (int64_t)id * TKV_BLK_W);
           m = rec.x;
           if (WINDOW && rec.y < lo_pos) m = 0;
@@ -854,6 +930,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   // the four lane groups of the column), in code units
   half4_t qB[NG * KM];
   float sumq[NG];
+  float selfdot = 0.f;                                   // q . k_self over this lane's dims
 #pragma unroll
   for (int gi = 0; gi < NG; gi++) {
     uint32_t wq[GS / 8];
@@ -872,10 +949,21 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
         const float x = head_ok ? __builtin_bit_cast(float, bits) : 0.f;
         v[e] = (_Float16)x;
         sq += (float)v[e];
+        if (self_here) {
+          const float4 k4 = kself[gi][j >> 2];
+          selfdot = fmaf(x, (j & 3) == 0 ? k4.x : (j & 3) == 1 ? k4.y : (j & 3) == 2 ? k4.z : k4.w, selfdot);
+        }
       }
       qB[gi * KM + mm] = v;
     }
     sumq[gi] = pair_sum<32>(pair_sum<16>(sq)) * kCodeUnit;
+  }
+  // lane (h, lg) now holds the self logit (log2 units) of its column's head
+  if (w == 0) {
+    const float self2 = pair_sum<32>(pair_sum<16>(selfdot)) * alpha;
+    s_fin[lane] = selfv0;
+    s_fin[64 + lane] = selfv1;
+    if (lane < 16) { s_fin[128 + lane] = self2; s_fin[144 + lane] = sinks_g; }
   }
   // K-side query operands in LDS, identical in every wave (wave 0 stores
   // them), [k slice][lane].  One block per step: 16 dims per k slice.  Packed
@@ -898,22 +986,6 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   __syncthreads();
   run_steps<D, GS, WINDOW, PK, FMT>(P, live, lmax, nlive, kvh, lo_pos, lane, w, nw, head_ok, qB, s_qk, sumq,
                                     alpha, st);
-  // The self token of this wave's first head (finalized here with one split):
-  // its reads are issued now, so that their latency overlaps the reductions
-  // and the record merge (the barriers below order LDS only).
-  const bool early_self = P.splits == 1 && P.k_self != nullptr && w < G;
-  float selfq[D / 64], selfk[D / 64], selfv[D / 64];
-  if (early_self) {
-    const uint16_t* qr = P.q + ((int64_t)b * S.Hq + kvh * G + w) * D;
-    const float* kr = P.k_self + ((int64_t)b * S.Hkv + kvh) * D;
-    const float* vr = P.v_self + ((int64_t)b * S.Hkv + kvh) * D;
-#pragma unroll
-    for (int i = 0; i < D / 64; i++) {
-      selfq[i] = __builtin_bit_cast(float, (uint32_t)qr[lane + 64 * i] << 16);
-      selfk[i] = kr[lane + 64 * i];
-      selfv[i] = vr[lane + 64 * i];
-    }
-  }
   // accumulator columns h and h + GP*i hold one head (block positions): sum
   // them into every column of the row (rotations inside the 16-lane row)
   if constexpr (PK > 1) {
@@ -959,17 +1031,12 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
     const int hq = kvh * G + hh;
     if (P.splits == 1) {
       SelfTok self = {0.f, 0.f, 0.f};
-      if (hh == w && early_self) {
-        float d = 0.f;
-#pragma unroll
-        for (int i = 0; i < D / 64; i++) d = fmaf(selfq[i], selfk[i], d);
-        self.s2 = pair_sum<32>(pair_sum<16>(pair_sum<8>(pair_sum<4>(pair_sum<2>(pair_sum<1>(d)))))) * alpha;
-        self.v0 = selfv[0];
-        self.v1 = D > 64 ? selfv[D / 64 - 1] : 0.f;
-      } else if (P.k_self) {
-        self = load_self<D>(P, b, hq, lane);
+      if (P.k_self) {
+        self.s2 = s_fin[128 + hh];                       // column hh's head is head hh
+        self.v0 = s_fin[lane];
+        self.v1 = s_fin[64 + lane];
       }
-      finalize_head<D>(P, b, hq, lane, M, self);
+      finalize_head<D>(P, b, hq, lane, M, self, s_fin[144 + hh]);
     } else {
       float* rec = P.part + (((int64_t)b * S.Hq + hq) * P.splits + split) * RS;
       rec[lane] = M.a0;
@@ -995,9 +1062,10 @@ __global__ __launch_bounds__(256) void k_combine(AttnParams P) {
   if (hq >= S.Hq) return;
   const float* recs = P.part + ((int64_t)b * S.Hq + hq) * P.splits * (D + PART_X);
   const SelfTok self = P.k_self ? load_self<D>(P, b, hq, lane) : SelfTok{0.f, 0.f, 0.f};
+  const float sink = P.sinks ? P.sinks[hq] : 0.f;
   Merged M;
   merge_records<D>(recs, D + PART_X, P.splits, lane, M);
-  finalize_head<D>(P, b, hq, lane, M, self);
+  finalize_head<D>(P, b, hq, lane, M, self, sink);
 }
 
 // ---------------------------------------------------------------------------
@@ -1009,20 +1077,25 @@ __global__ __launch_bounds__(256) void k_combine(AttnParams P) {
 static const int kTargetWaves = 2048;
 static const int kMaxLds = 160 * 1024;
 
-// blocks packed per step: 16 / roundup(G, 4), and at most 2 at D = 128 so
-// that two steps of codes (the one computed and the one loading) stay within
-// the registers of two waves per SIMD
+// blocks packed side by side per step: 16 / roundup(G, 4), at most two at
+// D = 128 and none with more than two groups per head: the registers of two
+// steps (the one computed and the one loading) at two waves per SIMD allow
+// no more.  (Four 4- or 2-bit blocks per step at D = 128 fit those registers
+// too, but the compute of such a step needs more than the rest: the
+// compiler spills, and a spill reload in the loop waits for every load in
+// flight, the next step's included.)
 static int pack_of(const tkv_cache* c, int G) {
+  if (c->S.D / c->S.g > 2) return 1;
   if (G <= 4 && c->S.D == 64) return 4;
-  return G <= 8 && (c->S.D == 64 || c->S.D / c->S.g <= 2) ? 2 : 1;
+  return G <= 8 ? 2 : 1;
 }
 
-// dynamic LDS: the waves' records (the live block lists are static)
+// dynamic LDS: the waves' records, the live block lists and their counts
 static int lds_bytes(const tkv_cache* c, int nw) {
   const int D = c->S.D, G = c->S.Hq / c->S.Hkv;
-  return nw * G * (D + PART_X) * (int)sizeof(float);
+  return nw * G * (D + PART_X) * (int)sizeof(float) + 3 * c->S.max_blocks * 8 + 16;
 }
-static const int kStaticLds = 3 * TKV_MAX_BLOCKS * 8 + 16 + 8192;   // live lists and counts, query operands
+static const int kStaticLds = 8192 + 640 + 384;                     // query operands, finalize inputs (and slack)
 
 void attn_plan(const tkv_cache* c, int batch, int num_splits, int* nw_out, int* splits_out) {
   const int units = batch * c->S.Hkv > 0 ? batch * c->S.Hkv : 1;
@@ -1049,32 +1122,37 @@ size_t attn_workspace_bytes(const tkv_cache* c, int batch, int splits) {
 }
 
 template <int D, int GS, bool W, int PK, int FMT>
-static void launch_one(const AttnParams& P, dim3 grid, int nw, int lds, hipStream_t st) {
-  static bool attr_set = false;            // dynamic LDS above 64 KiB must be allowed once per kernel
+static bool launch_one(const AttnParams& P, dim3 grid, int nw, int lds, hipStream_t st) {
+  // dynamic LDS above 64 KiB must be allowed once per kernel
+  static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)k_attn<D, GS, W, PK, FMT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              kMaxLds - kStaticLds);
+    if (hipFuncSetAttribute((const void*)k_attn<D, GS, W, PK, FMT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kMaxLds - kStaticLds) != hipSuccess)
+      return false;
     attr_set = true;
   }
   k_attn<D, GS, W, PK, FMT><<<grid, 64 * nw, lds, st>>>(P);
+  return true;
 }
 
 template <int D, int GS, int FMT>
-static void launch_attn_t(const AttnParams& P, int batch, int Hkv, int Hq, int nw, int lds, bool window, int pk,
+static bool launch_attn_t(const AttnParams& P, int batch, int Hkv, int Hq, int nw, int lds, bool window, int pk,
                           hipStream_t st) {
   dim3 grid(P.splits, Hkv, batch);
-  constexpr int PK2 = D == 64 || D / GS <= 2 ? 2 : 1;   // (pack_of returns 2 only with at most two groups at D = 128)
-  constexpr int PK4 = D == 64 ? 4 : PK2;                // (and 4 only for D = 64)
+  constexpr int PK2 = D / GS <= 2 ? 2 : 1;              // (pack_of packs blocks only with at most two groups)
+  constexpr int PK4 = D / GS <= 2 ? 4 : 1;
+  bool ok;
   if (window) {
-    if (pk == 4) launch_one<D, GS, true, PK4, FMT>(P, grid, nw, lds, st);
-    else if (pk == 2) launch_one<D, GS, true, PK2, FMT>(P, grid, nw, lds, st);
-    else launch_one<D, GS, true, 1, FMT>(P, grid, nw, lds, st);
+    if (pk == 4) ok = launch_one<D, GS, true, PK4, FMT>(P, grid, nw, lds, st);
+    else if (pk == 2) ok = launch_one<D, GS, true, PK2, FMT>(P, grid, nw, lds, st);
+    else ok = launch_one<D, GS, true, 1, FMT>(P, grid, nw, lds, st);
   } else {
-    if (pk == 4) launch_one<D, GS, false, PK4, FMT>(P, grid, nw, lds, st);
-    else if (pk == 2) launch_one<D, GS, false, PK2, FMT>(P, grid, nw, lds, st);
-    else launch_one<D, GS, false, 1, FMT>(P, grid, nw, lds, st);
+    if (pk == 4) ok = launch_one<D, GS, false, PK4, FMT>(P, grid, nw, lds, st);
+    else if (pk == 2) ok = launch_one<D, GS, false, PK2, FMT>(P, grid, nw, lds, st);
+    else ok = launch_one<D, GS, false, 1, FMT>(P, grid, nw, lds, st);
   }
-  if (P.splits > 1) k_combine<D><<<dim3((Hq + 3) / 4, batch), 256, 0, st>>>(P);
+  if (ok && P.splits > 1) k_combine<D><<<dim3((Hq + 3) / 4, batch), 256, 0, st>>>(P);
+  return ok;
 }
 
 int launch_attention(tkv_cache* c, const tkv_attn_args* a, int nw, int splits, hipStream_t st) {
@@ -1089,16 +1167,18 @@ int launch_attention(tkv_cache* c, const tkv_attn_args* a, int nw, int splits, h
   const bool win = a->window > 0;
   const int pk = pack_of(c, c->S.Hq / c->S.Hkv);
   const int B = a->batch, Hkv = c->S.Hkv, Hq = c->S.Hq;
+  bool ok;
   if (c->S.fmt == 0) {
-    if (D == 128 && g == 64) launch_attn_t<128, 64, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
-    else if (D == 128 && g == 32) launch_attn_t<128, 32, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
-    else if (D == 64 && g == 64) launch_attn_t<64, 64, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
-    else launch_attn_t<64, 32, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+    if (D == 128 && g == 64) ok = launch_attn_t<128, 64, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+    else if (D == 128 && g == 32) ok = launch_attn_t<128, 32, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+    else if (D == 64 && g == 64) ok = launch_attn_t<64, 64, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+    else ok = launch_attn_t<64, 32, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
   } else {
-    if (D == 128 && g == 64) launch_attn_t<128, 64, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
-    else if (D == 128 && g == 32) launch_attn_t<128, 32, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
-    else if (D == 64 && g == 64) launch_attn_t<64, 64, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
-    else launch_attn_t<64, 32, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+    if (D == 128 && g == 64) ok = launch_attn_t<128, 64, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+    else if (D == 128 && g == 32) ok = launch_attn_t<128, 32, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+    else if (D == 64 && g == 64) ok = launch_attn_t<64, 64, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+    else ok = launch_attn_t<64, 32, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
   }
+  if (!ok) return TKV_EHIP;
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
