@@ -101,7 +101,8 @@ enum {
   TKV_EINVAL = -1,      /* bad argument                                      */
   TKV_ENOMEM = -2,      /* pool exhausted, block list or segment table full  */
   TKV_ENOSEG = -3,      /* unknown or fully evicted segment                  */
-  TKV_EHIP = -4         /* a HIP runtime call failed                         */
+  TKV_EHIP = -4,        /* a HIP runtime call failed                         */
+  TKV_ERANGE = -5       /* request larger than the static workspace          */
 };
 
 enum {
@@ -318,6 +319,21 @@ typedef struct {
    num_splits (0 = the library's choice). */
 size_t tkv_attn_workspace(const tkv_cache* c, int32_t batch, int32_t num_splits);
 int paged_decode_attn(tkv_cache* c, const tkv_attn_args* a_h, hipStream_t stream);
+
+/* paged_decode_attn_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same result as paged_decode_attn(c, a_h, stream), with
+ * a_h->workspace and a_h->workspace_bytes ignored.  The split-K partial
+ * records go to a device array of TKV_STATIC_WORKSPACE_BYTES inside the
+ * library (one per device, held until the process ends, its address looked up
+ * by tkv_create); no memory is allocated or freed by the call.  Every call on
+ * one device shares that array: calls that overlap on one device (different
+ * streams, threads or handles) race and must be serialized by the caller.
+ *   ERANGE: tkv_attn_workspace(c, batch, num_splits) exceeds
+ *   TKV_STATIC_WORKSPACE_BYTES (nothing is enqueued; pass fewer splits or a
+ *   smaller batch).  Other errors as paged_decode_attn's. */
+#define TKV_STATIC_WORKSPACE_BYTES (32u << 20)
+int paged_decode_attn_noalloc(tkv_cache* c, const tkv_attn_args* a_h, hipStream_t stream);
 
 /* thought_classify -- thought decomposition bullets: T shows the most
  * concentrated (sparse) attention, R less, E the least.  score_b = fp32 mean

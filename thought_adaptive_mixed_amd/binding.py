@@ -17,7 +17,8 @@ import numpy as np
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libthinkv.so")
 
-TKV_OK, TKV_EINVAL, TKV_ENOMEM, TKV_ENOSEG, TKV_EHIP = 0, -1, -2, -3, -4
+TKV_OK, TKV_EINVAL, TKV_ENOMEM, TKV_ENOSEG, TKV_EHIP, TKV_ERANGE = 0, -1, -2, -3, -4, -5
+STATIC_WORKSPACE_BYTES = 32 << 20
 BUFFER_NAMES = ["pool0", "pool1", "pool2", "blk0", "blk1", "blk2", "slot0", "slot1", "slot2",
                 "free0", "free1", "free2", "hdr", "seq", "btab", "sstk", "segt", "scratch"]
 NUM_BUFFERS = len(BUFFER_NAMES)
@@ -26,6 +27,7 @@ BUFFER_DTYPES = {n: (np.uint8 if n.startswith("pool") else np.int32) for n in BU
 # Entry points declared in include/tkv.h
 SYMBOLS = ["tkv_buffer_sizes", "tkv_create", "tkv_destroy", "tkv_seq_reset", "kv_append_quant", "kv_classify_append",
            "kv_evict_segment", "kv_plan_budget", "kv_plan_budget_evict", "kv_plan_anneal", "kv_plan_anneal_evict", "tkv_compact", "tkv_attn_workspace", "paged_decode_attn",
+           "paged_decode_attn_noalloc",
            "thought_classify", "tkv_get_error", "tkv_export_state", "tkv_import_state", "tkv_strerror",
            "tkv_stream_read"]
 
@@ -82,6 +84,7 @@ def load(path: str = LIB_PATH):
     L.tkv_compact.argtypes = [P, I, P, P, P]
     L.tkv_attn_workspace.argtypes = [P, I, I]; L.tkv_attn_workspace.restype = C.c_size_t
     L.paged_decode_attn.argtypes = [P, P, P]
+    L.paged_decode_attn_noalloc.argtypes = [P, P, P]
     L.thought_classify.argtypes = [I, I, P, C.c_float, C.c_float, I, P, P]
     L.tkv_get_error.argtypes = [P, P, P, P]
     L.tkv_export_state.argtypes = [P, P]
@@ -270,6 +273,17 @@ class Cache:
                      int(stats_stride))
         args = (self.h, C.byref(a), _stream(stream))
         return _issue(self.L.paged_decode_attn, args, "paged_decode_attn", prepare, keep=a)
+
+    def attention_noalloc(self, seq_ids, q_pos, q, out, stats=None, n_attended=None, k_self=None, v_self=None,
+                          sinks=None, window=0, topk=8, num_splits=0, layer=0, stats_stride=0, *, stream=None,
+                          prepare=False):
+        """paged_decode_attn_noalloc: the split-K partials in the library's static
+        device array instead of a caller workspace."""
+        a = AttnArgs(int(seq_ids.numel()), _ptr(seq_ids), _ptr(q_pos), _ptr(q), _ptr(k_self), _ptr(v_self),
+                     _ptr(sinks), int(window), int(topk), int(num_splits), _ptr(out), _ptr(stats), _ptr(n_attended),
+                     None, 0, int(layer), int(stats_stride))
+        args = (self.h, C.byref(a), _stream(stream))
+        return _issue(self.L.paged_decode_attn_noalloc, args, "paged_decode_attn_noalloc", prepare, keep=a)
 
     def get_error(self):
         k, m, n = C.c_int32(), C.c_int32(), C.c_int32()

@@ -105,7 +105,8 @@ extern "C" int tkv_create(const tkv_layout* L, void* const bufs[TKV_NUM_BUFFERS]
   S.max_seqs = L->max_seqs; S.max_blocks = L->max_blocks_per_seq; S.max_segs = L->max_segments_per_seq;
   S.max_tokens = L->max_tokens_per_call;
   c->last_stream = stream;
-  int r = launch_init(c, stream);
+  int r = hipGetDevice(&c->device) == hipSuccess ? static_workspace_setup(c->device) : TKV_EHIP;
+  if (r == TKV_OK) r = launch_init(c, stream);
   for (int k = 0; r == TKV_OK && k < 3; k++)
     if (hipMemcpyAsync(S.freestk[k], stacks[k].data(), sizes[TKV_BUF_FREE0 + k], hipMemcpyHostToDevice, stream) !=
         hipSuccess)
@@ -213,6 +214,28 @@ extern "C" size_t tkv_attn_workspace(const tkv_cache* c, int32_t batch, int32_t 
   return attn_workspace_bytes(c, batch, s);
 }
 
+static int attn_args_ok(const tkv_cache* c, const tkv_attn_args* a) {
+  if (!c || !a) return 0;
+  if (a->batch < 0 || a->batch > c->S.max_seqs) return 0;
+  if (a->topk < 1 || a->topk > 8 || a->window < 0 || a->num_splits < 0 || a->num_splits > 64) return 0;
+  if (a->layer < 0 || a->layer >= c->S.NL) return 0;
+  if (a->stats_stride != 0 && a->stats_stride < c->S.Hq * 3) return 0;
+  if (a->batch > 0 && (!a->seq_ids || !a->q_pos || !a->q || !a->out)) return 0;
+  if ((a->k_self == nullptr) != (a->v_self == nullptr)) return 0;
+  return 1;
+}
+
+extern "C" int paged_decode_attn_noalloc(tkv_cache* c, const tkv_attn_args* a, hipStream_t stream) {
+  if (!attn_args_ok(c, a)) return TKV_EINVAL;
+  int nw, s;
+  attn_plan(c, a->batch, a->num_splits, &nw, &s);
+  if (attn_workspace_bytes(c, a->batch, s) > (size_t)TKV_STATIC_WORKSPACE_BYTES) return TKV_ERANGE;
+  void* ws = static_workspace(c->device);
+  if (!ws) return TKV_EHIP;
+  c->last_stream = stream;
+  return launch_attention(c, a, nw, s, stream, ws);
+}
+
 extern "C" int paged_decode_attn(tkv_cache* c, const tkv_attn_args* a, hipStream_t stream) {
   if (!c || !a) return TKV_EINVAL;
   if (a->batch < 0 || a->batch > c->S.max_seqs) return TKV_EINVAL;
@@ -274,6 +297,7 @@ extern "C" const char* tkv_strerror(int status) {
     case TKV_ENOMEM: return "out of cache memory (pool, block list or segment table)";
     case TKV_ENOSEG: return "unknown or evicted segment";
     case TKV_EHIP: return "HIP runtime error";
+    case TKV_ERANGE: return "request exceeds the library's static workspace";
     default: return "unknown status";
   }
 }

@@ -46,6 +46,7 @@
 // outputs and statistics, otherwise it writes a partial record that a small
 // combine kernel merges across splits.
 #include "tkv_internal.h"
+#include <mutex>
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -1155,14 +1156,14 @@ static bool launch_attn_t(const AttnParams& P, int batch, int Hkv, int Hq, int n
   return ok;
 }
 
-int launch_attention(tkv_cache* c, const tkv_attn_args* a, int nw, int splits, hipStream_t st) {
+int launch_attention(tkv_cache* c, const tkv_attn_args* a, int nw, int splits, hipStream_t st, void* workspace) {
   if (a->batch == 0) return TKV_OK;
   AttnParams P;
   P.S = c->S; P.seq_ids = a->seq_ids; P.q_pos = a->q_pos; P.q = a->q;
   P.k_self = a->k_self; P.v_self = a->v_self; P.sinks = a->sinks;
   P.window = a->window; P.splits = splits; P.topk = a->topk;
   P.layer = a->layer; P.stats_stride = a->stats_stride ? a->stats_stride : c->S.Hq * 3;
-  P.part = (float*)a->workspace; P.out = a->out; P.stats = a->stats; P.n_attended = a->n_attended;
+  P.part = (float*)(workspace ? workspace : a->workspace); P.out = a->out; P.stats = a->stats; P.n_attended = a->n_attended;
   const int D = c->S.D, g = c->S.g, lds = lds_bytes(c, nw);
   const bool win = a->window > 0;
   const int pk = pack_of(c, c->S.Hq / c->S.Hkv);
@@ -1181,4 +1182,35 @@ int launch_attention(tkv_cache* c, const tkv_attn_args* a, int nw, int splits, h
   }
   if (!ok) return TKV_EHIP;
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant of the attention call: the split-K partial records
+// live in a file-scope device array instead of the caller's workspace.  Each
+// device holds its own copy of the array at its own address, which is looked
+// up once per device (with that device current) when a cache is created; the
+// host uses that address, never the array's name.  Every call on a device
+// shares the array, so calls that overlap on one device race; nothing in it
+// needs to start at zero (each call writes every partial record it reads).
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[TKV_STATIC_WORKSPACE_BYTES];
+
+#define TKV_MAX_DEVICES 64
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[TKV_MAX_DEVICES];
+
+int static_workspace_setup(int device) {
+  if (device < 0 || device >= TKV_MAX_DEVICES) return TKV_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device]) return TKV_OK;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TKV_EHIP;
+  g_scratch_ptr[device] = p;
+  return TKV_OK;
+}
+
+void* static_workspace(int device) {
+  if (device < 0 || device >= TKV_MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[device];
 }

@@ -51,6 +51,7 @@ struct tkv_cache {
   size_t size[TKV_NUM_BUFFERS];
   DevState S;
   hipStream_t last_stream;
+  int device;                     // the device current when the cache was created
 };
 
 // Per-class fields of DevState indexed by a run-time class: select among the
@@ -340,4 +341,9 @@ int launch_classify(int batch, int Hq, const float* stats, float tau_T, float ta
 // Attention
 void attn_plan(const tkv_cache* c, int batch, int num_splits, int* nw, int* splits);
 size_t attn_workspace_bytes(const tkv_cache* c, int batch, int splits);
-int launch_attention(tkv_cache* c, const tkv_attn_args* a, int nw, int splits, hipStream_t st);
+int launch_attention(tkv_cache* c, const tkv_attn_args* a, int nw, int splits, hipStream_t st,
+                     void* workspace = nullptr);
+// the allocation-free attention call's device array: address lookup (once per
+// device, with that device current) and the address found
+int static_workspace_setup(int device);
+void* static_workspace(int device);
