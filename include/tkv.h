@@ -294,7 +294,7 @@ int tkv_compact(tkv_cache* c, int32_t n, const int32_t* n_dev, const int32_t* se
  * step fill one [batch][L][Hq][3] array that thought_classify can average
  * over all layers (num_q_heads = L*Hq).
  *   EINVAL (besides the shapes): layer outside [0, L), stats_stride neither 0
- *   nor >= Hq*3. */
+ *   nor >= Hq*3, q, k_self, v_self, out or workspace not 16-byte aligned. */
 typedef struct {
   int32_t batch;              /* entries, <= max_seqs                              */
   const int32_t* seq_ids;     /* i32[batch]                                        */

@@ -222,6 +222,9 @@ static int attn_args_ok(const tkv_cache* c, const tkv_attn_args* a) {
   if (a->stats_stride != 0 && a->stats_stride < c->S.Hq * 3) return 0;
   if (a->batch > 0 && (!a->seq_ids || !a->q_pos || !a->q || !a->out)) return 0;
   if ((a->k_self == nullptr) != (a->v_self == nullptr)) return 0;
+  // the kernels move q, the self token, the outputs and the partial records in 16-byte units
+  const auto al16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  if (!al16(a->q) || !al16(a->out) || !al16(a->k_self) || !al16(a->v_self) || !al16(a->workspace)) return 0;
   return 1;
 }
 
@@ -237,13 +240,7 @@ extern "C" int paged_decode_attn_noalloc(tkv_cache* c, const tkv_attn_args* a, h
 }
 
 extern "C" int paged_decode_attn(tkv_cache* c, const tkv_attn_args* a, hipStream_t stream) {
-  if (!c || !a) return TKV_EINVAL;
-  if (a->batch < 0 || a->batch > c->S.max_seqs) return TKV_EINVAL;
-  if (a->topk < 1 || a->topk > 8 || a->window < 0 || a->num_splits < 0 || a->num_splits > 64) return TKV_EINVAL;
-  if (a->layer < 0 || a->layer >= c->S.NL) return TKV_EINVAL;
-  if (a->stats_stride != 0 && a->stats_stride < c->S.Hq * 3) return TKV_EINVAL;
-  if (a->batch > 0 && (!a->seq_ids || !a->q_pos || !a->q || !a->out)) return TKV_EINVAL;
-  if ((a->k_self == nullptr) != (a->v_self == nullptr)) return TKV_EINVAL;
+  if (!attn_args_ok(c, a)) return TKV_EINVAL;
   int nw, s;
   attn_plan(c, a->batch, a->num_splits, &nw, &s);
   const size_t need = attn_workspace_bytes(c, a->batch, s);

@@ -656,7 +656,8 @@ __device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax
 // Records: [D accumulator][m2, Z, S2, n][top8] with the zero-point term folded
 // into the accumulator, all relative to the record's own max m2 (log2 units).
 // merge_records folds nrec records (stride floats apart) into registers of
-// one wave: acc for dims lane and lane + 64, and the merged scalars.
+// one wave (the split combine): acc for dims lane and lane + 64, and the
+// merged scalars.
 // ---------------------------------------------------------------------------
 struct Merged {
   float a0, a1, m, Z, S2;
@@ -664,9 +665,7 @@ struct Merged {
   float top[TOPK];
 };
 
-// NMAX > 0: nrec <= NMAX, the accumulator reads of all records are issued
-// together and records without tokens are dropped by selects.
-template <int D, int NMAX = 0>
+template <int D>
 __device__ inline void merge_records(const float* recs, int stride, int nrec, int lane, Merged& M) {
   float mr = -INFINITY, zr = 0.f, sr = 0.f, nr = 0.f;
   if (lane < nrec) {
@@ -683,29 +682,12 @@ __device__ inline void merge_records(const float* recs, int stride, int nrec, in
   for (int i = 0; i < TOPK; i++) M.top[i] = (lane < nrec && nr > 0.f) ? recs[(int64_t)lane * stride + D + 4 + i] : -INFINITY;
   first_lanes_topk(M.top, nrec);
   float a0 = 0.f, a1 = 0.f;
-  if constexpr (NMAX > 0) {
-    float f[NMAX], x0[NMAX], x1[NMAX];
-#pragma unroll
-    for (int r = 0; r < NMAX; r++) {
-      const int rr = r < nrec ? r : 0;
-      const float fr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), rr));
-      f[r] = r < nrec ? fr : 0.f;
-      x0[r] = recs[(int64_t)rr * stride + lane];
-      x1[r] = D > 64 ? recs[(int64_t)rr * stride + lane + 64] : 0.f;
-    }
-#pragma unroll
-    for (int r = 0; r < NMAX; r++) {
-      a0 = f[r] != 0.f ? fmaf(f[r], x0[r], a0) : a0;
-      if (D > 64) a1 = f[r] != 0.f ? fmaf(f[r], x1[r], a1) : a1;
-    }
-  } else {
-    for (int r = 0; r < nrec; r++) {
-      const float f = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), r));
-      if (f == 0.f) continue;
-      const float* rec = recs + (int64_t)r * stride;
-      a0 = fmaf(f, rec[lane], a0);
-      if (D > 64) a1 = fmaf(f, rec[lane + 64], a1);
-    }
+  for (int r = 0; r < nrec; r++) {
+    const float f = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), r));
+    if (f == 0.f) continue;
+    const float* rec = recs + (int64_t)r * stride;
+    a0 = fmaf(f, rec[lane], a0);
+    if (D > 64) a1 = fmaf(f, rec[lane + 64], a1);
   }
   M.a0 = a0; M.a1 = a1; M.m = m; M.Z = Z; M.S2 = S2; M.n = (int)nn;
 }
@@ -818,7 +800,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   // heads and, when the self token is finalized here (one split), its V row
   // (shared by the group's heads) and its logit for each head, computed from
   // its K row over this lane's query dims with the query conversion below.
-  __shared__ float s_fin[2 * 64 + 2 * 16];          // V row [128], self logits [16], sinks [16]
+  __shared__ __align__(16) float s_fin[2 * 64 + 2 * 16];   // V row [128], self logits [16], sinks [16]
   const bool self_here = P.splits == 1 && P.k_self != nullptr && w == 0;
   const float sinks_g = (w == 0 && P.sinks && lane < G) ? P.sinks[kvh * G + lane] : 0.f;
   float4 kself[NG][GS / 16];
@@ -1000,55 +982,143 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
         st.acc[n][r] = v;
       }
   }
-  // this wave's record per head: sums over the lanes holding the head
+  // this wave's state per head: sums over the lanes holding the head.  From
+  // here on lane 16 lg + h (h < G) holds head h: dims 16 n + 4 lg .. + 3 of
+  // every 16-dim slice n and the head's scalars, and the epilogue runs for all
+  // heads at once on those lanes.
   st.Z = head_sum<GP>(st.Z);
   st.S2 = head_sum<GP>(st.S2);
 #pragma unroll
   for (int gi = 0; gi < NG; gi++) st.zacc[gi] = head_sum<GP>(st.zacc[gi]);
   st.natt = (int)head_sum<GP>((float)st.natt);
   head_topk<GP>(st.top);
-  // lanes 16 lg + h (h < G) hold head h both in the accumulator's columns and,
-  // after the sums above, in the packed layout (block 0)
-  if (col_ok) {
-    float* rec = lds + ((int64_t)w * G + h) * RS;
+  const int he = col_ok ? h : 0;                  // the head these lanes finish (lanes h >= G repeat head 0)
+  float4_t a[NT];
+#pragma unroll
+  for (int n = 0; n < NT; n++) a[n] = st.acc[n] * st.vunit + st.zacc[(16 * n) / GS];
+  float m = st.m2, Z = st.Z, S2 = st.S2, natt = (float)st.natt;
+  if (nw > 1) {
+    // Merge the waves' records (through LDS): every wave forms the merged
+    // scalars of its lanes' heads, finishes the slices n = w, w + nw, ... and
+    // wave 0 also the top-8 list.
+    if (col_ok) {
+      float* rec = lds + ((int64_t)w * G + h) * RS;
+#pragma unroll
+      for (int n = 0; n < NT; n++) *(float4_t*)(rec + 16 * n + 4 * lg) = a[n];
+      if (lg == 0) {
+        *(float4*)(rec + D) = make_float4(m, Z, S2, natt);
+#pragma unroll
+        for (int i = 0; i < TOPK; i += 4) *(float4*)(rec + D + 4 + i) = make_float4(st.top[i], st.top[i + 1], st.top[i + 2], st.top[i + 3]);
+      }
+    }
+    lds_barrier();
+    const float* base = lds + (int64_t)he * RS;
+    const int rstride = G * RS;
+    float mr[8], zr[8], sr[8], nr[8];
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+      float4 x = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+      if (r < nw) x = *(const float4*)(base + r * rstride + D);
+      mr[r] = x.x; zr[r] = x.y; sr[r] = x.z; nr[r] = x.w;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 8; r++) mx = nr[r] > 0.f ? fmaxf(mx, mr[r]) : mx;
+    float sc[8];
+    Z = 0.f; S2 = 0.f; natt = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+      sc[r] = nr[r] > 0.f ? exp2f(mr[r] - mx) : 0.f;
+      Z = fmaf(sc[r], zr[r], Z);
+      S2 = nr[r] > 0.f ? fmaf(sc[r], sr[r] + (mr[r] - mx) * zr[r], S2) : S2;
+      natt += nr[r];
+    }
+    m = mx;
 #pragma unroll
     for (int n = 0; n < NT; n++) {
-      const float z = st.zacc[(16 * n) / GS];
-      const float u = st.vunit;
-      *(float4*)(rec + 16 * n + 4 * lg) = make_float4(st.acc[n][0] * u + z, st.acc[n][1] * u + z,
-                                                      st.acc[n][2] * u + z, st.acc[n][3] * u + z);
-    }
-    if (lg == 0) {
-      rec[D] = st.m2; rec[D + 1] = st.Z; rec[D + 2] = st.S2; rec[D + 3] = (float)st.natt;
+      if (n % nw != w) continue;
+      float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < TOPK; i++) rec[D + 4 + i] = st.top[i];
+      for (int r = 0; r < 8; r++)
+        if (sc[r] != 0.f) s += sc[r] * *(const float4_t*)(base + r * rstride + 16 * n + 4 * lg);
+      a[n] = s;
+    }
+    if (w == 0) {
+      // lane group lg merges the lists of records lg, lg + 4; then across groups
+#pragma unroll
+      for (int i = 0; i < TOPK; i++) st.top[i] = lg < nw ? base[lg * rstride + D + 4 + i] : -INFINITY;
+      if (lg + 4 < nw) {
+        float O[TOPK];
+#pragma unroll
+        for (int i = 0; i < TOPK; i++) O[i] = base[(lg + 4) * rstride + D + 4 + i];
+        topk_merge(st.top, O);
+      }
+      pair_topk<16>(st.top);
+      pair_topk<32>(st.top);
     }
   }
-  lds_barrier();
-  // merge the waves' records; finalize here when the sequence is one split
-  for (int hh = w; hh < G; hh += nw) {
-    Merged M;
-    merge_records<D, 8>(lds + (int64_t)hh * RS, G * RS, nw, lane, M);
-    const int hq = kvh * G + hh;
-    if (P.splits == 1) {
-      SelfTok self = {0.f, 0.f, 0.f};
-      if (P.k_self) {
-        self.s2 = s_fin[128 + hh];                       // column hh's head is head hh
-        self.v0 = s_fin[lane];
-        self.v1 = s_fin[64 + lane];
-      }
-      finalize_head<D>(P, b, hq, lane, M, self, s_fin[144 + hh]);
-    } else {
-      float* rec = P.part + (((int64_t)b * S.Hq + hq) * P.splits + split) * RS;
-      rec[lane] = M.a0;
-      if (D > 64) rec[lane + 64] = M.a1;
-      if (lane < 4) rec[D + lane] = lane == 0 ? M.m : lane == 1 ? M.Z : lane == 2 ? M.S2 : (float)M.n;
-      if (lane < TOPK) {
-        float v = M.top[0];
+  // slices of this wave: n = w, w + nw, ... (every slice with one wave)
+  auto mine = [&](int n) { return nw == 1 || n % nw == w; };
+  const int hq = kvh * G + he;
+  if (P.splits == 1) {
+    // add the staged self token and the sink; write the outputs and statistics
+    if (P.k_self) {
+      const float self2 = s_fin[128 + he];
+      const float mm = fmaxf(m, self2);
+      const float sc = natt > 0.f ? exp2f(m - mm) : 0.f;
+      const float ps = exp2f(self2 - mm);
+      S2 = sc * (S2 + (natt > 0.f ? (m - mm) * Z : 0.f)) + ps * (self2 - mm);
+      Z = fmaf(sc, Z, ps);
 #pragma unroll
-        for (int i = 1; i < TOPK; i++) v = lane == i ? M.top[i] : v;
-        rec[D + 4 + lane] = v;
+      for (int n = 0; n < NT; n++)
+        if (mine(n)) {
+          const float4 v = *(const float4*)(s_fin + 16 * n + 4 * lg);
+          a[n] = (float4_t){fmaf(ps, v.x, sc * a[n][0]), fmaf(ps, v.y, sc * a[n][1]), fmaf(ps, v.z, sc * a[n][2]),
+                            fmaf(ps, v.w, sc * a[n][3])};
+        }
+      m = mm;
+      if (w == 0) topk_insert(st.top, self2);
+      natt += 1.f;
+    }
+    const int nn = (int)natt;
+    float inv = 0.f;
+    if (nn > 0) {
+      float den = Z;
+      if (P.sinks) den += exp2f(s_fin[144 + he] * LOG2E - m);
+      inv = 1.0f / den;
+    }
+    if (col_ok) {
+      float* out = P.out + ((int64_t)b * S.Hq + hq) * D;
+#pragma unroll
+      for (int n = 0; n < NT; n++)
+        if (mine(n)) *(float4_t*)(out + 16 * n + 4 * lg) = a[n] * inv;
+      if (w == 0 && lg == 0 && P.stats) {
+        float* sp = P.stats + (int64_t)b * P.stats_stride + hq * 3;
+        if (nn == 0) {
+          sp[0] = 0.f; sp[1] = 0.f; sp[2] = 0.f;
+        } else {
+          const float H = logf(Z) - LN2 * S2 / Z;
+          float mk = 0.f;
+          const int kk = P.topk < nn ? P.topk : nn;
+#pragma unroll
+          for (int i = 0; i < TOPK; i++) mk += i < kk ? exp2f(st.top[i] - m) : 0.f;
+          sp[0] = H;
+          sp[1] = nn >= 2 ? H / logf((float)nn) : 0.f;
+          sp[2] = mk / Z;
+        }
       }
+      if (w == 0 && lane == 0 && kvh == 0 && P.n_attended) P.n_attended[b] = nn;
+    }
+  } else if (col_ok) {
+    // this split's partial record; the combine kernel merges the splits
+    float* rec = P.part + (((int64_t)b * S.Hq + hq) * P.splits + split) * RS;
+#pragma unroll
+    for (int n = 0; n < NT; n++)
+      if (mine(n)) *(float4_t*)(rec + 16 * n + 4 * lg) = a[n];
+    if (w == 0 && lg == 0) {
+      *(float4*)(rec + D) = make_float4(m, Z, S2, natt);
+#pragma unroll
+      for (int i = 0; i < TOPK; i += 4) *(float4*)(rec + D + 4 + i) = make_float4(st.top[i], st.top[i + 1], st.top[i + 2], st.top[i + 3]);
     }
   }
   if (split == 0 && kvh == 0 && threadIdx.x == 0 && !seq_ok) record_error(S.hdr, TKV_EINVAL, s < 0 ? TKV_INF : s);
@@ -1141,7 +1211,7 @@ static bool launch_attn_t(const AttnParams& P, int batch, int Hkv, int Hq, int n
                           hipStream_t st) {
   dim3 grid(P.splits, Hkv, batch);
   constexpr int PK2 = D / GS <= 2 ? 2 : 1;              // (pack_of packs blocks only with at most two groups)
-  constexpr int PK4 = D / GS <= 2 ? 4 : 1;
+  constexpr int PK4 = (D == 64 && D / GS <= 2) ? 4 : PK2;   // (four only at D = 64)
   bool ok;
   if (window) {
     if (pk == 4) ok = launch_one<D, GS, true, PK4, FMT>(P, grid, nw, lds, st);
