@@ -333,15 +333,24 @@ __device__ inline void compute_step(const Buf<D, GS, WINDOW, PK>& b, uint32_t mj
     for (int gi = 0; gi < NG; gi++) spk[gi] = (float4_t){0.f, 0.f, 0.f, 0.f};
     // pair by pair (the scheduling barrier keeps a pair's query operands from
     // being read ahead of the previous pair's products: 4 VGPRs each)
+    // The operands of pair 1 (blocks 2 and 3, PK = 4) are those of pair 0
+    // moved by 8 lanes (two block positions of 4 columns): lane l reads lane
+    // l ^ 8's entry of the one table.
 #pragma unroll
     for (int p = 0; p < PKC / 2; p++) {
+      const char* qp = qrow;
+      if (p == 1) {
+        int qoff1 = (lane ^ 8) * 16;
+        asm volatile("" : "+v"(qoff1));
+        qp = (const char*)qk_lds + qoff1;
+      }
 #pragma unroll
       for (int gi = 0; gi < NG; gi++)
 #pragma unroll
         for (int mm = 0; mm < KM; mm++)
           spk[gi] = mfma32(cat8(operand4<BITS, FMT>(b.kw + 2 * p * CW, gi * (GS / 4) + 4 * mm),
                                 operand4<BITS, FMT>(b.kw + (2 * p + 1) * CW, gi * (GS / 4) + 4 * mm)),
-                           *(const half8_t*)(qrow + (p * (D / 16) + gi * KM + mm) * 1024), spk[gi]);
+                           *(const half8_t*)(qp + (gi * KM + mm) * 1024), spk[gi]);
       if (p + 1 < PKC / 2) __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -950,9 +959,9 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   }
   // K-side query operands in LDS, identical in every wave (wave 0 stores
   // them), [k slice][lane].  One block per step: 16 dims per k slice.  Packed
-  // blocks: pair p keeps the lane's query in the half of the k slice that
-  // holds its own block (2p or 2p+1), [pair][16 dims][lane].
-  __shared__ half8_t s_qk[(PK > 1 ? PK / 2 : 1) * NT * 64];
+  // blocks: the lane's query in the half of the k slice that holds its own
+  // block (position 0 or 1; zeros at positions 2 and 3), [16 dims][lane].
+  __shared__ half8_t s_qk[NT * 64];
   if (w == 0) {
     if constexpr (PK == 1) {
 #pragma unroll
@@ -960,10 +969,7 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
     } else {
       const int jq = (lane & 15) / GP;
 #pragma unroll
-      for (int p2 = 0; p2 < PK / 2; p2++)
-#pragma unroll
-        for (int i = 0; i < NT; i++)
-          s_qk[(p2 * NT + i) * 64 + lane] = cat8(keep4(qB[i], jq == 2 * p2), keep4(qB[i], jq == 2 * p2 + 1));
+      for (int i = 0; i < NT; i++) s_qk[i * 64 + lane] = cat8(keep4(qB[i], jq == 0), keep4(qB[i], jq == 1));
     }
   }
   __syncthreads();
@@ -1148,16 +1154,15 @@ __global__ __launch_bounds__(256) void k_combine(AttnParams P) {
 static const int kTargetWaves = 2048;
 static const int kMaxLds = 160 * 1024;
 
-// blocks packed side by side per step: 16 / roundup(G, 4), at most two at
-// D = 128 and none with more than two groups per head: the registers of two
-// steps (the one computed and the one loading) at two waves per SIMD allow
-// no more.  (Four 4- or 2-bit blocks per step at D = 128 fit those registers
-// too, but the compute of such a step needs more than the rest: the
-// compiler spills, and a spill reload in the loop waits for every load in
-// flight, the next step's included.)
-static int pack_of(const tkv_cache* c, int G) {
+// blocks packed side by side per step: 16 / roundup(G, 4), and none with
+// more than two groups per head.  At D = 128 the 8-bit class takes two blocks
+// per step whatever the packing (pk_class); with a window, where each lane
+// also holds its tokens' positions, the packing stays at two there: four
+// spill.  (A spill reload in the loop waits for every load in flight, the
+// next step's included.)
+static int pack_of(const tkv_cache* c, int G, bool window) {
   if (c->S.D / c->S.g > 2) return 1;
-  if (G <= 4 && c->S.D == 64) return 4;
+  if (G <= 4 && (c->S.D == 64 || !window)) return 4;
   return G <= 8 ? 2 : 1;
 }
 
@@ -1177,7 +1182,7 @@ void attn_plan(const tkv_cache* c, int batch, int num_splits, int* nw_out, int* 
     splits = (kTargetWaves + units * nw - 1) / (units * nw);
     // at most as many splits as give each wave about four steps when the
     // block lists are full (more would leave waves idle and add a combine)
-    const int pk = pack_of(c, c->S.Hq / c->S.Hkv);
+    const int pk = pack_of(c, c->S.Hq / c->S.Hkv, false);
     const int cap = (3 * c->S.max_blocks) / (4 * nw * pk) > 1 ? (3 * c->S.max_blocks) / (4 * nw * pk) : 1;
     if (splits > cap) splits = cap;
     if (splits > 64) splits = 64;
@@ -1211,10 +1216,11 @@ static bool launch_attn_t(const AttnParams& P, int batch, int Hkv, int Hq, int n
                           hipStream_t st) {
   dim3 grid(P.splits, Hkv, batch);
   constexpr int PK2 = D / GS <= 2 ? 2 : 1;              // (pack_of packs blocks only with at most two groups)
-  constexpr int PK4 = (D == 64 && D / GS <= 2) ? 4 : PK2;   // (four only at D = 64)
+  constexpr int PK4 = D / GS <= 2 ? 4 : 1;
+  constexpr int PK4W = (D == 64 && D / GS <= 2) ? 4 : PK2;  // (with a window, four only at D = 64)
   bool ok;
   if (window) {
-    if (pk == 4) ok = launch_one<D, GS, true, PK4, FMT>(P, grid, nw, lds, st);
+    if (pk == 4) ok = launch_one<D, GS, true, PK4W, FMT>(P, grid, nw, lds, st);
     else if (pk == 2) ok = launch_one<D, GS, true, PK2, FMT>(P, grid, nw, lds, st);
     else ok = launch_one<D, GS, true, 1, FMT>(P, grid, nw, lds, st);
   } else {
@@ -1236,7 +1242,7 @@ int launch_attention(tkv_cache* c, const tkv_attn_args* a, int nw, int splits, h
   P.part = (float*)(workspace ? workspace : a->workspace); P.out = a->out; P.stats = a->stats; P.n_attended = a->n_attended;
   const int D = c->S.D, g = c->S.g, lds = lds_bytes(c, nw);
   const bool win = a->window > 0;
-  const int pk = pack_of(c, c->S.Hq / c->S.Hkv);
+  const int pk = pack_of(c, c->S.Hq / c->S.Hkv, win);
   const int B = a->batch, Hkv = c->S.Hkv, Hq = c->S.Hq;
   bool ok;
   if (c->S.fmt == 0) {
