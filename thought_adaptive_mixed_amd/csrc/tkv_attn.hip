@@ -646,15 +646,15 @@ __device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax
     else if (lv == 1) __builtin_amdgcn_s_setprio(1);
     else __builtin_amdgcn_s_setprio(0);
   };
-  B A, Bn;
-  load(A, g);
+  B nxt;
+  load(nxt, g);
+  __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
+#pragma nounroll
   while (true) {
-    load(Bn, g + nw);
-    set_priority(); comp(A, g); k++;
-    g += nw;
-    if (g >= T) break;
-    load(A, g + nw);
-    set_priority(); comp(Bn, g); k++;
+    const B cur = nxt;
+    load(nxt, g + nw);
+    __builtin_amdgcn_sched_barrier(0);
+    set_priority(); comp(cur, g); k++;
     g += nw;
     if (g >= T) break;
   }
