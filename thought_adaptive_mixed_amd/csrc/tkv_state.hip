@@ -812,8 +812,12 @@ __device__ void requant_row(const DevState& S, int src, int dst, int h, int kv, 
 }
 
 // Deferred downgrade moves of all sequences, one wave per row: a flat grid
-// strides over sum(moves) * Hkv * 2 rows.
+// strides over sum(moves) * Hkv * 2 rows.  A row is a short chain of
+// dependent global reads (codes and scale of its old slot), a wave reduction
+// and stores: the grid fills the machine at the kernel's occupancy (six waves
+// per SIMD on 256 compute units) so that the chains overlap.
 #define RQ_THREADS 256
+#define RQ_GRID 1536
 __global__ __launch_bounds__(RQ_THREADS) void k_requant(DevState S) {
   __shared__ int s_off[TKV_MAX_SEQS + 1];
   __shared__ int s_tmp[48];
@@ -1164,7 +1168,7 @@ int launch_evict(tkv_cache* c, int n_ops, const int32_t* n_ops_dev, const int32_
   if (n_ops == 0) return TKV_OK;
   k_evict_plan<<<1, walker_threads(c->S.max_seqs), 0, st>>>(c->S, n_ops, n_ops_dev, seq_ids, seg_ids, keep_n, new_bits);
   k_evict_apply<<<c->S.max_seqs, EV_THREADS, 0, st>>>(c->S);
-  k_requant<<<512, RQ_THREADS, 0, st>>>(c->S);
+  k_requant<<<RQ_GRID, RQ_THREADS, 0, st>>>(c->S);
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
 
@@ -1346,7 +1350,7 @@ int launch_plan_evict(tkv_cache* c, int n, const int32_t* seq_ids, int num, int 
   if (max_ops == 0) return launch_plan(c, n, seq_ids, num, den, 0, n_ops_dev, op_seq, op_seg, op_keep, op_bits, st);
   k_plan_evict<<<1, WG, 0, st>>>(c->S, n, seq_ids, num, den, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits);
   k_evict_apply<<<c->S.max_seqs, EV_THREADS, 0, st>>>(c->S);
-  k_requant<<<512, RQ_THREADS, 0, st>>>(c->S);
+  k_requant<<<RQ_GRID, RQ_THREADS, 0, st>>>(c->S);
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
 
@@ -1454,7 +1458,7 @@ int launch_anneal_evict(tkv_cache* c, int n, const int32_t* seq_ids, int r0, int
   if (max_ops == 0) return launch_anneal(c, n, seq_ids, r0, 0, n_ops_dev, op_seq, op_seg, op_keep, op_bits, st);
   k_anneal_evict<<<1, WG, 0, st>>>(c->S, n, seq_ids, r0, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits);
   k_evict_apply<<<c->S.max_seqs, EV_THREADS, 0, st>>>(c->S);
-  k_requant<<<512, RQ_THREADS, 0, st>>>(c->S);
+  k_requant<<<RQ_GRID, RQ_THREADS, 0, st>>>(c->S);
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
 
