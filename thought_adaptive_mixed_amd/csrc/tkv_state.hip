@@ -412,11 +412,13 @@ __device__ inline void minmax_level(float& mn, float& mx) {
   }
 }
 
+// The body takes the geometry (D, g, bits) as arguments: called with
+// constants, the index arithmetic of the code layout folds to shifts and masks.
 template <int E>
-__device__ void quant_row_wave(const DevState& S, int c, int blk, int t, int h, int kv, int lane, const float (&x)[E],
-                               uint8_t* codes /* per-wave LDS, D bytes */) {
+__device__ __forceinline__ void quant_row_body(const DevState& S, const int D, const int g, const int bits, int c, int blk,
+                                               int t, int h, int kv, int lane, const float (&x)[E],
+                                               uint8_t* codes /* per-wave LDS, D bytes */) {
 #pragma clang fp contract(off)
-  const int D = S.D, g = S.g, bits = class_bits(c);
   const int lpg = g / E;                       // lanes per group
   const int gi = (lane * E) / g;
   float mn = x[0], mx = x[0];
@@ -532,7 +534,22 @@ __device__ void quant_row_wave(const DevState& S, int c, int blk, int t, int h, 
   wave_lds_sync();     // the LDS row may be reused by this wave's next row
 }
 
+// geometry read from the state
 template <int E>
+__device__ __forceinline__ void quant_row_wave(const DevState& S, int c, int blk, int t, int h, int kv, int lane,
+                                               const float (&x)[E], uint8_t* codes) {
+  quant_row_body<E>(S, S.D, S.g, class_bits(c), c, blk, t, h, kv, lane, x, codes);
+}
+// geometry fixed at compile time (D = 64 E, group G), class c chosen at run time
+template <int E, int G>
+__device__ __forceinline__ void quant_row_fixed(const DevState& S, int c, int blk, int t, int h, int kv, int lane,
+                                                const float (&x)[E], uint8_t* codes) {
+  if (c == 0) quant_row_body<E>(S, 64 * E, G, 8, c, blk, t, h, kv, lane, x, codes);
+  else if (c == 1) quant_row_body<E>(S, 64 * E, G, 4, c, blk, t, h, kv, lane, x, codes);
+  else quant_row_body<E>(S, 64 * E, G, 2, c, blk, t, h, kv, lane, x, codes);
+}
+
+template <int E, int G>
 __global__ __launch_bounds__(256) void k_append_store(DevState S, int n, const float* k, const float* v) {
   __shared__ uint8_t s_codes[4][128];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -549,7 +566,7 @@ __global__ __launch_bounds__(256) void k_append_store(DevState S, int n, const f
   const int info = scr_info(S.scratch)[i];
   if (info < 0) return;
   const int c = info >> 28, slot = info & 0x0FFFFFFF;
-  quant_row_wave<E>(S, c, slot / TKV_BS, slot % TKV_BS, h, kv, lane, x, s_codes[wv]);
+  quant_row_fixed<E, G>(S, c, slot / TKV_BS, slot % TKV_BS, h, kv, lane, x, s_codes[wv]);
 }
 
 int launch_append(tkv_cache* c, int n, const int32_t* seq_ids, const int32_t* pos, const uint8_t* thought,
@@ -560,8 +577,13 @@ int launch_append(tkv_cache* c, int n, const int32_t* seq_ids, const int32_t* po
                                                               cl ? *cl : none);
   const int64_t rows = (int64_t)n * c->S.Hst * 2;
   const int blocks = (int)((rows + 3) / 4);
-  if (c->S.D == 128) k_append_store<2><<<blocks, 256, 0, st>>>(c->S, n, k, v);
-  else k_append_store<1><<<blocks, 256, 0, st>>>(c->S, n, k, v);
+  if (c->S.D == 128) {
+    if (c->S.g == 64) k_append_store<2, 64><<<blocks, 256, 0, st>>>(c->S, n, k, v);
+    else k_append_store<2, 32><<<blocks, 256, 0, st>>>(c->S, n, k, v);
+  } else {
+    if (c->S.g == 64) k_append_store<1, 64><<<blocks, 256, 0, st>>>(c->S, n, k, v);
+    else k_append_store<1, 32><<<blocks, 256, 0, st>>>(c->S, n, k, v);
+  }
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
 
@@ -756,18 +778,22 @@ __global__ __launch_bounds__(WG) void k_evict_plan(DevState S, int n_cap, const 
 #define EV_MAXSLOT (TKV_MAX_BLOCKS * TKV_BS)   // every slot of one class of one sequence
 #define EV_BMW 1024                            // position bitmap words: segments spanning <= 32768 positions
 
-__device__ float deq_code(const DevState& S, int c, int blk, int t, int h, int kv, int d) {
+__device__ __forceinline__ float deq_code_body(const DevState& S, const int D, const int g, const int bits, int c, int blk,
+                                              int t, int h, int kv, int d) {
 #pragma clang fp contract(off)
-  const int bits = class_bits(c);
   const uint8_t* base = pick3(S.pool, c) + ((int64_t)blk * S.Hst + h) * pick3(S.bh_bytes, c);
   const int nat = natural_order(S.fmt, c);
-  int bit = kv ? v_code_bit(S.D, bits, nat, t, d) : k_code_bit(S.D, S.g, bits, nat, t, d);
+  int bit = kv ? v_code_bit(D, bits, nat, t, d) : k_code_bit(D, g, bits, nat, t, d);
   uint32_t word = *(const uint32_t*)(base + ((bit >> 5) << 2));
   unsigned code = (word >> (bit & 31)) & ((1u << bits) - 1u);
-  uint32_t m = *(const uint32_t*)(base + meta_byte(S.D, S.g, bits, kv, t, d / S.g));
+  uint32_t m = *(const uint32_t*)(base + meta_byte(D, g, bits, kv, t, d / g));
   float sf = f16_bits_to_f32((uint16_t)(m & 0xFFFF)), zf = f16_bits_to_f32((uint16_t)(m >> 16));
   float prod = sf * (nat ? fmt_value(c, code) : (float)code);     // exact product
   return prod + zf;
+}
+
+__device__ __forceinline__ float deq_code(const DevState& S, int c, int blk, int t, int h, int kv, int d) {
+  return deq_code_body(S, S.D, S.g, class_bits(c), c, blk, t, h, kv, d);
 }
 
 // Sort m (position, slot) pairs by position (unique) in LDS: bitonic network
@@ -810,14 +836,31 @@ __device__ void requant_row(const DevState& S, int src, int dst, int h, int kv, 
     quant_row_wave<1>(S, c2, ns / TKV_BS, ns % TKV_BS, h, kv, lane, x, codes);
   }
 }
+// the same with the geometry fixed at compile time (D = 64 E, group G)
+template <int E, int G>
+__device__ __forceinline__ void requant_row_fixed(const DevState& S, int src, int dst, int h, int kv, int lane,
+                                                  uint8_t* codes) {
+  const int c = src >> 28, old = src & 0x0FFFFFFF, c2 = dst >> 28, ns = dst & 0x0FFFFFFF;
+  const int ob = old / TKV_BS, ot = old % TKV_BS;
+  const int bits = c == 0 ? 8 : (c == 1 ? 4 : 2);
+  float x[E];
+#pragma unroll
+  for (int e = 0; e < E; e++) {
+    const int d = lane * E + e;
+    x[e] = bits == 8 ? deq_code_body(S, 64 * E, G, 8, c, ob, ot, h, kv, d)
+         : (bits == 4 ? deq_code_body(S, 64 * E, G, 4, c, ob, ot, h, kv, d) : deq_code_body(S, 64 * E, G, 2, c, ob, ot, h, kv, d));
+  }
+  quant_row_fixed<E, G>(S, c2, ns / TKV_BS, ns % TKV_BS, h, kv, lane, x, codes);
+}
 
 // Deferred downgrade moves of all sequences, one wave per row: a flat grid
 // strides over sum(moves) * Hkv * 2 rows.  A row is a short chain of
 // dependent global reads (codes and scale of its old slot), a wave reduction
-// and stores: the grid fills the machine at the kernel's occupancy (six waves
-// per SIMD on 256 compute units) so that the chains overlap.
+// and stores: the grid fills the machine at the kernel's occupancy (seven
+// waves per SIMD on 256 compute units at D = 128) so that the chains overlap.
 #define RQ_THREADS 256
-#define RQ_GRID 1536
+#define RQ_GRID 1792
+template <int E, int G>
 __global__ __launch_bounds__(RQ_THREADS) void k_requant(DevState S) {
   __shared__ int s_off[TKV_MAX_SEQS + 1];
   __shared__ int s_tmp[48];
@@ -846,7 +889,16 @@ __global__ __launch_bounds__(RQ_THREADS) void k_requant(DevState S) {
     while (b - a > 1) { const int mid = (a + b) >> 1; if (s_off[mid] <= mv) a = mid; else b = mid; }
     const int j = mv - s_off[a];
     const int32_t* m2 = moves + (int64_t)a * per_seq + 2 * j;
-    requant_row(S, m2[0], m2[1], h, kv, lane, s_codes[wv]);
+    requant_row_fixed<E, G>(S, m2[0], m2[1], h, kv, lane, s_codes[wv]);
+  }
+}
+static void launch_requant(const tkv_cache* c, hipStream_t st) {
+  if (c->S.D == 128) {
+    if (c->S.g == 64) k_requant<2, 64><<<RQ_GRID, RQ_THREADS, 0, st>>>(c->S);
+    else k_requant<2, 32><<<RQ_GRID, RQ_THREADS, 0, st>>>(c->S);
+  } else {
+    if (c->S.g == 64) k_requant<1, 64><<<RQ_GRID, RQ_THREADS, 0, st>>>(c->S);
+    else k_requant<1, 32><<<RQ_GRID, RQ_THREADS, 0, st>>>(c->S);
   }
 }
 
@@ -1168,7 +1220,7 @@ int launch_evict(tkv_cache* c, int n_ops, const int32_t* n_ops_dev, const int32_
   if (n_ops == 0) return TKV_OK;
   k_evict_plan<<<1, walker_threads(c->S.max_seqs), 0, st>>>(c->S, n_ops, n_ops_dev, seq_ids, seg_ids, keep_n, new_bits);
   k_evict_apply<<<c->S.max_seqs, EV_THREADS, 0, st>>>(c->S);
-  k_requant<<<RQ_GRID, RQ_THREADS, 0, st>>>(c->S);
+  launch_requant(c, st);
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
 
@@ -1350,7 +1402,7 @@ int launch_plan_evict(tkv_cache* c, int n, const int32_t* seq_ids, int num, int 
   if (max_ops == 0) return launch_plan(c, n, seq_ids, num, den, 0, n_ops_dev, op_seq, op_seg, op_keep, op_bits, st);
   k_plan_evict<<<1, WG, 0, st>>>(c->S, n, seq_ids, num, den, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits);
   k_evict_apply<<<c->S.max_seqs, EV_THREADS, 0, st>>>(c->S);
-  k_requant<<<RQ_GRID, RQ_THREADS, 0, st>>>(c->S);
+  launch_requant(c, st);
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
 
@@ -1458,7 +1510,7 @@ int launch_anneal_evict(tkv_cache* c, int n, const int32_t* seq_ids, int r0, int
   if (max_ops == 0) return launch_anneal(c, n, seq_ids, r0, 0, n_ops_dev, op_seq, op_seg, op_keep, op_bits, st);
   k_anneal_evict<<<1, WG, 0, st>>>(c->S, n, seq_ids, r0, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits);
   k_evict_apply<<<c->S.max_seqs, EV_THREADS, 0, st>>>(c->S);
-  k_requant<<<RQ_GRID, RQ_THREADS, 0, st>>>(c->S);
+  launch_requant(c, st);
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
 
