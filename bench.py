@@ -313,7 +313,7 @@ def attention_config(name, reps=5, launches=50, oracle_s=3.0):
     sh = torch.cuda.current_stream().cuda_stream
     res = {}
     cores = len(os.sched_getaffinity(0))
-    for window in w.windows:
+    def timed(window):
         calls = [c.attention(seq_d, pos_d, q_d, out, ws, stats=stats, n_attended=n_att, sinks=sinks_d,
                              window=window, stream=sh, prepare=True) for c in caches]
         for i in range(2 * len(calls)):
@@ -329,10 +329,21 @@ def attention_config(name, reps=5, launches=50, oracle_s=3.0):
         per = sorted(ev.elapsed_ms(2 * r, 2 * r + 1) / launches for r in range(reps))
         ev.close()
         check_errors(caches, f"attention on {name}")
-        ms = per[len(per) // 2]
-        nbytes, kvb, toks = attn_bytes(state, L, w.seq_ids, w.q_pos, window, sinks=w.sinks is not None)
+        _, _, toks = attn_bytes(state, L, w.seq_ids, w.q_pos, window, sinks=w.sinks is not None)
         got = int(n_att.sum().item())
         assert got == toks, (name, window, got, toks)
+        return per
+    for window in w.windows:
+        per = timed(window)
+        ms = per[len(per) // 2]
+        nbytes, kvb, toks = attn_bytes(state, L, w.seq_ids, w.q_pos, window, sinks=w.sinks is not None)
+        floor = {}
+        if window > 0:
+            # the latency floor of the windowed call: a window of one block's
+            # positions (one step per work-group, the same launch shape)
+            pf = timed(16)
+            floor = {"floor_us_window16": pf[len(pf) // 2] * 1e3,
+                     "floor_note": "same call with a 16-position window: launch, prologue, one step, epilogue"}
         gbs = nbytes / (ms * 1e-3) / 1e9
         key = name if len(w.windows) == 1 else f"{name}_{'full' if window == 0 else f'window{window}'}"
         ora = {}
@@ -349,7 +360,7 @@ def attention_config(name, reps=5, launches=50, oracle_s=3.0):
                     "attended_tokens": toks, "bytes_per_launch": nbytes, "kv_code_bytes": kvb,
                     "us_per_launch": ms * 1e3, "us_per_launch_reps": [p * 1e3 for p in per],
                     "kv_tokens_per_s": toks / (ms * 1e-3), "achieved_GBs": gbs, "frac": gbs / HBM_PEAK_GBS,
-                    **ora}
+                    **floor, **ora}
         log(f"[bench] {key}: {ms * 1e3:.2f} us/launch, {nbytes / 1e6:.2f} MB, {gbs:.0f} GB/s "
             f"({gbs / HBM_PEAK_GBS:.3f} of peak), {toks / (ms * 1e-3) / 1e9:.2f} G KV tokens/s")
     del caches
@@ -604,8 +615,9 @@ def main():
     ap.add_argument("--split-steps", type=int, default=16, help="extra steps timed call by call")
     ap.add_argument("--copies", type=int, default=0, help="state copies (0 = enough for > 1 GiB)")
     ap.add_argument("--cpu-seqs", type=int, default=16)
-    ap.add_argument("--workload", choices=("churn256", "llama8b"), default="churn256",
-                    help="the B256 churn decode loop (4k..32k, 5%% budget) or the llama8b-like layer (B32, 16k, 10%%)")
+    ap.add_argument("--workload", choices=("churn256", "llama8b", "none"), default="churn256",
+                    help="the B256 churn decode loop (4k..32k, 5%% budget) or the llama8b-like layer (B32, 16k, 10%%); "
+                         "'none' times only the --configs attention calls (diagnostic: no result line)")
     ap.add_argument("--policy", choices=("ladder", "anneal"), default="ladder",
                     help="eviction planner of the step: the token-budget ladder, or the TBE annealing schedule")
     ap.add_argument("--r0", type=int, default=64, help="first retention of the annealing schedule")
@@ -633,6 +645,14 @@ def main():
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload == "none":
+        names = [] if args.configs == "none" else [n for n in args.configs.split(",") if n]
+        out = {}
+        for n in names:
+            log(f"[bench] attention alone: {n}")
+            out.update(attention_config(n))
+        print(json.dumps({"configs": out}), flush=True)
+        return
     result, (w, state, ch) = step_bench(args)
     if not args.no_stream:
         log("[bench] streaming-read ceiling")
