@@ -175,7 +175,11 @@ int kv_append_quant(tkv_cache* c, int32_t n, const int32_t* seq_ids, const int32
  * same result as thought_classify(n, num_q_heads, stats, tau_T, tau_E,
  * score_kind, labels) followed by kv_append_quant(c, n, seq_ids, positions,
  * labels, k, v, slot_out), with the classification done inside the append's
- * allocation kernel (one launch fewer).  Token i takes the label of row i of
+ * allocation kernel (one launch fewer) when num_q_heads <= 128; longer rows
+ * (several layers' statistics) are classified by the thought_classify kernel,
+ * a wave per row reading the row in parallel, whose labels the allocation then
+ * takes (labels_out, or a region of the cache's scratch memory when it is
+ * NULL: two calls on one cache must not overlap).  Token i takes the label of row i of
  * stats fp32 [n][num_q_heads][3] (the attention batch in token order; with
  * several layers num_q_heads = L*Hq).  labels_out (nullable) u8[n] receives
  * the labels taken.

@@ -179,7 +179,9 @@ def test_classify_append_layers_and_kind():
     ga = helpers.build_gpu(w)
     gb = helpers.build_gpu(w)
     dv = helpers.dev
-    for kind, NL in ((0, 3), (1, 1), (1, 4)):
+    # up to 128 heads per row the classification runs inside the allocation
+    # kernel; longer rows (20 and 40 layers here) take thought_classify's kernel
+    for kind, NL in ((0, 3), (1, 1), (1, 4), (0, 20), (1, 40)):
         st = rng.uniform(0, 1, (B, NL * L.num_q_heads, 3)).astype(np.float32)
         pos = w.q_pos.astype(np.int32) + kind * 10 + NL
         k = rng.standard_normal((B, L.num_kv_heads, L.head_dim)).astype(np.float32)
@@ -194,6 +196,57 @@ def test_classify_append_layers_and_kind():
         assert np.array_equal(la.cpu().numpy(), lb.cpu().numpy()), (kind, NL)
         assert len(set(la.cpu().numpy().tolist())) > 1
     helpers.compare_states(L, ga.export(), gb.export(), "fused vs two calls")
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_classify_long_rows_vs_oracle(kind):
+    """Rows of 200, 1024 and 1100 heads (several layers' statistics: partial
+    64-head chunks, and more than one read batch of 16 chunks): thought_classify
+    and kv_classify_append (which hands rows this long to thought_classify's
+    kernel) against oracle.classify, at the default thresholds and with tau_T and
+    tau_E at a row's exact score and one ulp either side; the fused call without
+    labels_out leaves the state an append of the oracle's labels leaves."""
+    import torch
+    import oracle
+    from thought_adaptive_mixed_amd import binding, drive
+    rng = np.random.default_rng(733 + kind)
+    dv = helpers.dev
+    for H in (200, 1024, 1100):
+        n = 5
+        st = rng.uniform(0, 1, (n, H, 3)).astype(np.float32)
+        st[3, :, 1:] = np.float32(0.38)            # every head equal
+        st[4, :, 1:] = np.float32(1 - 0.85)
+        st_d = dv(st)
+        lab = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        cases = [(0.38, 0.85), (0.45, 0.55)]
+        for i in (0, 3, 4):
+            sc = _exact_score(st[i], kind)
+            for t in (sc, np.nextafter(sc, np.float32(-1)), np.nextafter(sc, np.float32(2))):
+                cases += [(float(t), 4.0), (-1.0, float(t))]
+        Lf = synth.Layout(2, 8, 64, 32, (16, 16, 16), n, 4, 8, 64)
+        k = rng.standard_normal((n, 2, 64)).astype(np.float32)
+        v = rng.standard_normal((n, 2, 64)).astype(np.float32)
+        for tT, tE in cases:
+            ref = oracle.classify(st, tT, tE, kind)
+            binding.classify(st_d, tT, tE, lab, score_kind=kind)
+            gc = binding.Cache(drive.gpu_layout(Lf))
+            out = torch.zeros(n, dtype=torch.uint8, device="cuda")
+            gc.classify_append(dv(np.arange(n, dtype=np.int32)), dv(np.zeros(n, np.int32)), st_d, tT, tE, dv(k),
+                               dv(v), labels_out=out, score_kind=kind)
+            torch.cuda.synchronize()
+            assert gc.get_error()[0] == 0
+            assert np.array_equal(lab.cpu().numpy(), ref), (H, kind, tT, tE)
+            assert np.array_equal(out.cpu().numpy(), ref), (H, kind, tT, tE)
+        # no labels_out: the state equals an append of the oracle's labels
+        tT, tE = cases[1]
+        ga, gb = binding.Cache(drive.gpu_layout(Lf)), binding.Cache(drive.gpu_layout(Lf))
+        ga.classify_append(dv(np.arange(n, dtype=np.int32)), dv(np.zeros(n, np.int32)), st_d, tT, tE, dv(k), dv(v),
+                           score_kind=kind)
+        gb.append(dv(np.arange(n, dtype=np.int32)), dv(np.zeros(n, np.int32)),
+                  dv(oracle.classify(st, tT, tE, kind).astype(np.uint8)), dv(k), dv(v))
+        torch.cuda.synchronize()
+        helpers.compare_states(Lf, ga.export(), gb.export(), f"classify_append without labels_out, {H} heads")
+        say(f"[classify] kind {kind}: {H}-head rows, {len(cases)} threshold settings equal to the oracle")
 
 
 @pytest.mark.parametrize("max_ops", [64, 1])

@@ -138,6 +138,9 @@ extern "C" int kv_append_quant(tkv_cache* c, int32_t n, const int32_t* seq_ids, 
   return launch_append(c, n, seq_ids, positions, thought, k, v, slot_out, stream);
 }
 
+// rows of at most this many heads are classified inside the allocation kernel
+static const int kFusedClassifyHeads = 128;
+
 extern "C" int kv_classify_append(tkv_cache* c, int32_t n, const int32_t* seq_ids, const int32_t* positions,
                                   const float* stats, int32_t num_q_heads, float tau_T, float tau_E,
                                   int32_t score_kind, uint8_t* labels_out, const float* k, const float* v,
@@ -146,6 +149,15 @@ extern "C" int kv_classify_append(tkv_cache* c, int32_t n, const int32_t* seq_id
   if (num_q_heads < 1 || (score_kind != 0 && score_kind != 1)) return TKV_EINVAL;
   if (n > 0 && (!seq_ids || !positions || !stats || !k || !v)) return TKV_EINVAL;
   c->last_stream = stream;
+  if (num_q_heads > kFusedClassifyHeads && n > 0) {
+    // many heads per row (several layers' statistics): a wave per row reads
+    // the row in parallel, then the allocation takes the labels; the labels go
+    // to an unused scratch region when the caller wants none
+    uint8_t* lab = labels_out ? labels_out : (uint8_t*)scr_status(c->S.scratch);
+    const int r = launch_classify(n, num_q_heads, stats, tau_T, tau_E, score_kind, lab, stream);
+    if (r != TKV_OK) return r;
+    return launch_append(c, n, seq_ids, positions, lab, k, v, slot_out, stream);
+  }
   const ClassifyIn cl = {stats, num_q_heads, score_kind, tau_T, tau_E, labels_out};
   return launch_append(c, n, seq_ids, positions, nullptr, k, v, slot_out, stream, &cl);
 }

@@ -71,7 +71,7 @@ __host__ __device__ inline int class_of_bits(int b) { return b == 8 ? 0 : (b == 
 #define TKV_SCR_FIXED (14 * TKV_MAX_TOK + 64)
 __host__ __device__ inline int32_t* scr_idx(int32_t* s) { return s; }                       // [MAX_TOK]
 __host__ __device__ inline int32_t* scr_info(int32_t* s) { return s + TKV_MAX_TOK; }        // [MAX_TOK]
-__host__ __device__ inline int32_t* scr_status(int32_t* s) { return s + 2 * TKV_MAX_TOK; }  // [MAX_TOK]
+__host__ __device__ inline int32_t* scr_status(int32_t* s) { return s + 2 * TKV_MAX_TOK; }  // [MAX_TOK] (u8 labels of kv_classify_append)
 __host__ __device__ inline int32_t* scr_need(int32_t* s) { return s + 3 * TKV_MAX_TOK; }    // [MAX_TOK]
 __host__ __device__ inline int32_t* scr_list(int32_t* s) { return s + 4 * TKV_MAX_TOK; }    // [MAX_TOK] ops by sequence
 __host__ __device__ inline int32_t* scr_grp(int32_t* s) { return s + 5 * TKV_MAX_TOK; }     // [3][max_seqs] off, count, downgrades
@@ -299,27 +299,6 @@ struct ClassifyIn {
 __device__ inline uint32_t thought_label(float score, float tT, float tE) {
   return score <= tT ? (uint32_t)TKV_T : (score >= tE ? (uint32_t)TKV_E : (uint32_t)TKV_R);
 }
-__device__ inline uint32_t classify_row(const float* row, const ClassifyIn& cl) {
-#pragma clang fp contract(off)
-  // 16 heads' values are read together (independent loads in flight), then
-  // added in head order
-  const int off = cl.kind == 0 ? 1 : 2;
-  float sum = 0.0f;
-  int h = 0;
-  for (; h + 16 <= cl.heads; h += 16) {
-    float v[16];
-#pragma unroll
-    for (int j = 0; j < 16; j++) v[j] = row[3 * (h + j) + off];
-#pragma unroll
-    for (int j = 0; j < 16; j++) sum = sum + (cl.kind == 0 ? v[j] : 1.0f - v[j]);
-  }
-  for (; h < cl.heads; h++) {
-    const float v = row[3 * h + off];
-    sum = sum + (cl.kind == 0 ? v : 1.0f - v);
-  }
-  return thought_label(sum / (float)cl.heads, cl.tT, cl.tE);
-}
-
 // Launchers (state kernels)
 int launch_init(tkv_cache* c, hipStream_t st);
 int launch_append(tkv_cache* c, int n, const int32_t* seq_ids, const int32_t* pos, const uint8_t* thought,

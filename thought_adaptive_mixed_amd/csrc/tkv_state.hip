@@ -294,6 +294,7 @@ __device__ void append_walk(const DevState& S, int s, SeqRec w, const C3& top, i
   }
 }
 
+#define CL_STAGE 8448    // floats of statistics staged per chunk of rows (256 rows of 32 heads + padding)
 __global__ __launch_bounds__(WG) void k_append_alloc(DevState S, int n, const int32_t* seq_ids, const int32_t* pos,
                                                      const uint8_t* thought, int32_t* slot_out, ClassifyIn cl) {
   __shared__ __align__(16) uint16_t s_seq[TKV_MAX_TOK];
@@ -304,6 +305,7 @@ __global__ __launch_bounds__(WG) void k_append_alloc(DevState S, int n, const in
   __shared__ int s_cnt[TKV_MAX_SEQS], s_off[TKV_MAX_SEQS];
   __shared__ int s_tmp[48];
   __shared__ int dry_from[3], avail[3], viol[3], total[3];
+  __shared__ float s_stat[CL_STAGE];
   const int tid = threadIdx.x, NT = blockDim.x;
   int32_t* info = scr_info(S.scratch);
   const bool walker = tid < S.max_seqs;
@@ -311,16 +313,41 @@ __global__ __launch_bounds__(WG) void k_append_alloc(DevState S, int n, const in
   if (walker) rec = load_seq_rec(S, tid);
   if (walker) s_cnt[tid] = 0;
   if (tid < 3) { dry_from[tid] = TKV_INF; avail[tid] = S.hdr[H_FREE + tid]; }
+  // the tokens' thought types: given, or classified here from their entries'
+  // statistics.  The classification's column of the rows (H/ln n or M_k of
+  // every head) is staged in LDS a chunk of rows at a time, read coalesced by
+  // the whole work-group (a row's heads are adjacent in memory; one thread
+  // per row would touch a cache line per head); then thread i adds row i's
+  // values in head order.  Rows are padded by one float so the row-per-thread
+  // reads hit distinct banks.
+  if (cl.stats) {
+#pragma clang fp contract(off)
+    const int H = cl.heads, RW = H + 1, off = cl.kind == 0 ? 1 : 2;
+    const int per = CL_STAGE / RW;
+    for (int r0 = 0; r0 < n; r0 += per) {
+      const int nr = min(per, n - r0), ne = nr * H;
+      const float* base = cl.stats + (int64_t)r0 * H * 3 + off;
+#pragma unroll 8
+      for (int e = tid; e < ne; e += NT) {
+        const int r = e / H, h = e - r * H;
+        s_stat[r * RW + h] = base[(int64_t)e * 3];
+      }
+      __syncthreads();
+      for (int i = r0 + tid; i < r0 + nr; i += NT) {
+        const float* row = s_stat + (i - r0) * RW;
+        float sum = 0.0f;
+#pragma unroll 8
+        for (int h = 0; h < H; h++) sum = sum + (cl.kind == 0 ? row[h] : 1.0f - row[h]);
+        const uint32_t y = thought_label(sum / (float)H, cl.tT, cl.tE);
+        s_flags[i] = (uint8_t)y;
+        if (cl.labels) cl.labels[i] = (uint8_t)y;
+      }
+      __syncthreads();
+    }
+  }
   for (int i = tid; i < n; i += NT) {
     const int s = seq_ids[i];
-    // the token's thought type: given, or classified here from its entry's statistics
-    uint32_t y;
-    if (cl.stats) {
-      y = classify_row(cl.stats + (int64_t)i * cl.heads * 3, cl);
-      if (cl.labels) cl.labels[i] = (uint8_t)y;
-    } else {
-      y = thought[i];
-    }
+    const uint32_t y = cl.stats ? s_flags[i] : thought[i];
     const int p = pos[i];
     info[i] = -1;
     if (slot_out) slot_out[i] = -1;
@@ -572,6 +599,7 @@ __global__ __launch_bounds__(256) void k_append_store(DevState S, int n, const f
 int launch_append(tkv_cache* c, int n, const int32_t* seq_ids, const int32_t* pos, const uint8_t* thought,
                   const float* k, const float* v, int32_t* slot_out, hipStream_t st, const ClassifyIn* cl) {
   if (n == 0) return TKV_OK;
+  if (cl && cl->stats && cl->heads + 1 > CL_STAGE) return TKV_EINVAL;   // a row must fit the LDS stage
   const ClassifyIn none = {nullptr, 0, 0, 0.f, 0.f, nullptr};
   k_append_alloc<<<1, walker_threads(c->S.max_seqs), 0, st>>>(c->S, n, seq_ids, pos, thought, slot_out,
                                                               cl ? *cl : none);
@@ -1910,27 +1938,56 @@ int launch_seq_reset(tkv_cache* c, int n, const int32_t* seq_ids, hipStream_t st
 }
 
 // ---------------------------------------------------------------------------
-// thought_classify: one wave per batch entry; lane h reads head h's statistic
-// and the sum runs over the heads in head order (fp32, sequential), then the
-// thresholds.
+// thought_classify: one wave per batch entry; lane l reads the statistic of
+// heads l, l + 64, ... (up to 16 such chunks read together), and the sum runs
+// over the heads in head order (fp32, sequential), then the thresholds.
 // ---------------------------------------------------------------------------
+#define CL_NB 16
 __global__ __launch_bounds__(256) void k_classify(int batch, int Hq, const float* stats, float tT, float tE, int kind,
                                                   uint8_t* labels) {
 #pragma clang fp contract(off)
   const int b = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (b >= batch) return;
   float sum = 0.0f;
-  for (int h0 = 0; h0 < Hq; h0 += 64) {
-    const int h = h0 + lane;
-    float v = 0.0f;
-    if (h < Hq) {
-      const float* st = stats + ((int64_t)b * Hq + h) * 3;
-      v = kind == 0 ? st[1] : 1.0f - st[2];
+  for (int c0 = 0; c0 < Hq; c0 += 64 * CL_NB) {
+    // (every lane reads, a head inside the row, so that no read waits under a branch)
+    float v[CL_NB];
+#pragma unroll
+    for (int i = 0; i < CL_NB; i++) {
+      const int h = c0 + 64 * i + lane;
+      v[i] = stats[((int64_t)b * Hq + (h < Hq ? h : Hq - 1)) * 3 + (kind == 0 ? 1 : 2)];
     }
-    const int m = Hq - h0 < 64 ? Hq - h0 : 64;
-    // the terms in head order; v_readlane (no LDS round trip per term)
-    for (int j = 0; j < m; j++)
-      sum = sum + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < CL_NB; i++) v[i] = kind == 0 ? v[i] : 1.0f - v[i];
+    // the terms in head order: whole 64-head chunks by v_readlane with a
+    // constant lane (no LDS round trip, no lane index in a register), then the
+    // partial chunk, if any
+    const int nfull = (Hq - c0) / 64 < CL_NB ? (Hq - c0) / 64 : CL_NB;
+#pragma unroll
+    for (int i = 0; i < CL_NB; i++) {
+      if (i < nfull) {
+        // eight lanes read out, then their eight terms added (the reads into
+        // distinct scalar registers need no wait between read and add)
+#pragma unroll
+        for (int j0 = 0; j0 < 64; j0 += 8) {
+          int t[8];
+#pragma unroll
+          for (int e = 0; e < 8; e++) t[e] = __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[i]), j0 + e);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int e = 0; e < 8; e++) sum = sum + __builtin_bit_cast(float, t[e]);
+        }
+      }
+    }
+    const int rem = Hq - c0 - 64 * nfull;
+    if (nfull < CL_NB && rem > 0) {
+      float vp = v[0];
+#pragma unroll
+      for (int i = 1; i < CL_NB; i++) vp = i == nfull ? v[i] : vp;
+      for (int j = 0; j < rem; j++)
+        sum = sum + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vp), j));
+    }
   }
   const float score = sum / (float)Hq;
   if (lane == 0) labels[b] = (uint8_t)thought_label(score, tT, tE);
