@@ -550,10 +550,13 @@ def step_bench(args):
 
     # per-call split: further steps with an event between every call
     split = {}
+    kernels, kernels_launches = {}, {}
     if split_steps:
         names = ["attention"] + [n for n, _ in calls_b[0]]
         es = HipEvents((len(names) + 1) * split_steps)
         k = len(names) + 1
+        for c in caches:
+            c.kernel_timing(True)            # every kernel of these steps bracketed by events (tkv_kernel_timing)
         for j, s in enumerate(range(args.warmup + args.steps, total)):
             es.record(k * j, sh)
             for f in calls_a[s]:
@@ -567,6 +570,17 @@ def step_bench(args):
             t = sorted(es.elapsed_ms(k * j + i, k * j + i + 1) * 1e3 for j in range(split_steps))
             split[n] = t[len(t) // 2]
         es.close()
+        tot = {}
+        for c in caches:
+            times, dropped = c.kernel_times()
+            for name, (us, calls) in times.items():
+                a = tot.setdefault(name, [0.0, 0])
+                a[0] += us
+                a[1] += calls
+            c.kernel_timing(False)
+        # mean duration of each kernel per step (HIP events around each launch)
+        kernels = {name: round(us / split_steps, 2) for name, (us, calls) in tot.items()}
+        kernels_launches = {name: calls / split_steps for name, (us, calls) in tot.items()}
         check_errors(caches, "the split steps")
 
     cached = n_att[args.warmup:args.warmup + args.steps].sum().item() - args.steps * B   # self token excluded
@@ -599,6 +613,11 @@ def step_bench(args):
         "attn_ms": attn_avg,
         "attn_kv_tokens_per_s": (tokens / args.steps) / (attn_avg * 1e-3),
         "step_split_us": split,
+        "step_kernels_us": kernels,
+        "step_kernels_note": (f"per kernel, microseconds per step (launches per step: "
+                              f"{ {k: round(v, 2) for k, v in kernels_launches.items()} }), from HIP events around "
+                              f"every kernel launch of {split_steps} further steps (tkv_kernel_timing)")
+        if kernels else None,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "kernel": "k_attn (paged_decode_attn; one launch per layer and step)",

@@ -359,6 +359,30 @@ int tkv_import_state(tkv_cache* c, void* const host_bufs_h[TKV_NUM_BUFFERS]);
 
 const char* tkv_strerror(int status);
 
+/* tkv_kernel_timing -- measurement aid, not part of the method: with enable
+ * != 0, every kernel the library launches for cache c from then on is
+ * bracketed by two HIP events on the stream of its call (events without the
+ * system-scope fence, so the L2 is not flushed), and tkv_kernel_times adds up
+ * the durations per kernel name; enable == 0 turns it off.  Either call drops
+ * every record so far (events recorded and not yet read are destroyed: call
+ * it when the cache's streams are idle).  The events add a small gap between
+ * the kernels of a call; nothing else changes.  The library allocates the
+ * host-side records and events; they are freed by tkv_kernel_timing(c, 0)
+ * or tkv_destroy.  EINVAL: c NULL.  EHIP: out of host memory. */
+int tkv_kernel_timing(tkv_cache* c, int32_t enable);
+
+/* tkv_kernel_times -- measurement aid: waits for the events recorded since the
+ * last read, adds their durations to the per-kernel totals and writes, for the
+ * first max_kernels kernel names in first-launch order, names (char[32] each,
+ * NUL-terminated, caller-owned [max_kernels][32]), total_us (f64) and calls
+ * (i32); *dropped (nullable) receives the launches left unrecorded because
+ * more than 65536 were waiting to be read.  Returns the number of distinct
+ * kernels timed so far (may exceed max_kernels), or EINVAL (c NULL, timing
+ * off, max_kernels < 0 or a needed pointer NULL) or EHIP (an event call
+ * failed). */
+int tkv_kernel_times(tkv_cache* c, int32_t max_kernels, char* names, double* total_us, int32_t* calls,
+                     int64_t* dropped);
+
 /* tkv_stream_read -- measurement aid, not part of the method: read `bytes`
  * (a multiple of 16) of the device buffer `src` with 128-bit loads at a grid
  * stride and fold them into a value that is stored to the device word `sink`

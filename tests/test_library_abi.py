@@ -58,4 +58,6 @@ def test_null_handle_and_strerror():
     assert lib.thought_classify(1, 4, None, C.c_float(0.3), C.c_float(0.8), 2, None, None) == binding.TKV_EINVAL
     assert binding.strerror(binding.TKV_ENOSEG) == "unknown or evicted segment"
     assert lib.tkv_stream_read(None, 16, None, None) == binding.TKV_EINVAL
+    assert lib.tkv_kernel_timing(None, 1) == binding.TKV_EINVAL
+    assert lib.tkv_kernel_times(None, 0, None, None, None, None) == binding.TKV_EINVAL
     assert lib.tkv_stream_read(C.c_void_p(16), 15, C.c_void_p(16), None) == binding.TKV_EINVAL

@@ -29,7 +29,7 @@ SYMBOLS = ["tkv_buffer_sizes", "tkv_create", "tkv_destroy", "tkv_seq_reset", "kv
            "kv_evict_segment", "kv_plan_budget", "kv_plan_budget_evict", "kv_plan_anneal", "kv_plan_anneal_evict", "tkv_compact", "tkv_attn_workspace", "paged_decode_attn",
            "paged_decode_attn_noalloc",
            "thought_classify", "tkv_get_error", "tkv_export_state", "tkv_import_state", "tkv_strerror",
-           "tkv_stream_read"]
+           "tkv_stream_read", "tkv_kernel_timing", "tkv_kernel_times"]
 
 
 class Layout(C.Structure):
@@ -91,6 +91,8 @@ def load(path: str = LIB_PATH):
     L.tkv_import_state.argtypes = [P, P]
     L.tkv_strerror.argtypes = [C.c_int]; L.tkv_strerror.restype = C.c_char_p
     L.tkv_stream_read.argtypes = [P, C.c_size_t, P, P]
+    L.tkv_kernel_timing.argtypes = [P, I]
+    L.tkv_kernel_times.argtypes = [P, I, P, P, P, P]
     _lib = L
     return L
 
@@ -284,6 +286,25 @@ class Cache:
                      None, 0, int(layer), int(stats_stride))
         args = (self.h, C.byref(a), _stream(stream))
         return _issue(self.L.paged_decode_attn_noalloc, args, "paged_decode_attn_noalloc", prepare, keep=a)
+
+    def kernel_timing(self, enable: bool):
+        """tkv_kernel_timing: bracket every kernel launched for this cache with
+        events (on), or stop (off); either drops the records so far."""
+        _check(self.L.tkv_kernel_timing(self.h, 1 if enable else 0), "tkv_kernel_timing")
+
+    def kernel_times(self, max_kernels: int = 32):
+        """tkv_kernel_times: {kernel name: (total us, launches)} since timing was
+        turned on, and the launches left unrecorded."""
+        names = C.create_string_buffer(32 * max_kernels)
+        tot = (C.c_double * max_kernels)()
+        calls = (C.c_int32 * max_kernels)()
+        dropped = C.c_int64()
+        n = self.L.tkv_kernel_times(self.h, max_kernels, names, tot, calls, C.byref(dropped))
+        if n < 0:
+            _check(n, "tkv_kernel_times")
+        raw = names.raw
+        out = {raw[32 * i:32 * i + 32].split(b"\0", 1)[0].decode(): (tot[i], calls[i]) for i in range(min(n, max_kernels))}
+        return out, dropped.value
 
     def get_error(self):
         k, m, n = C.c_int32(), C.c_int32(), C.c_int32()

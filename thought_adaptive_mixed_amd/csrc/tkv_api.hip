@@ -4,8 +4,59 @@
 // only then enqueues kernels; nothing here allocates device memory.
 #include <stdlib.h>
 #include <string.h>
+#include <new>
+#include <string>
 #include <vector>
 #include "tkv_internal.h"
+
+// ---------------------------------------------------------------------------
+// Per-kernel timing (tkv_kernel_timing / tkv_kernel_times).  Events come from
+// a pool and go back to it when their durations are read; at most
+// kMaxPending launches are recorded between two reads (later ones are
+// counted as dropped).
+// ---------------------------------------------------------------------------
+struct KernelTimes {
+  struct Rec { const char* name; hipEvent_t e0, e1; };
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> pool;
+  std::vector<std::string> names;        // first-seen order
+  std::vector<double> total_us;
+  std::vector<int32_t> calls;
+  int64_t dropped = 0;
+  int failed = 0;
+  static const size_t kMaxPending = 1 << 16;
+  hipEvent_t take() {
+    hipEvent_t e = nullptr;
+    if (!pool.empty()) { e = pool.back(); pool.pop_back(); return e; }
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) { failed = 1; return nullptr; }
+    return e;
+  }
+  void give(hipEvent_t e) { if (e) pool.push_back(e); }
+  void add(const char* name, double us) {
+    size_t i = 0;
+    while (i < names.size() && names[i] != name) i++;
+    if (i == names.size()) { names.push_back(name); total_us.push_back(0.0); calls.push_back(0); }
+    total_us[i] += us;
+    calls[i] += 1;
+  }
+  ~KernelTimes() {
+    for (auto& r : pending) { if (r.e0) hipEventDestroy(r.e0); if (r.e1) hipEventDestroy(r.e1); }
+    for (auto e : pool) hipEventDestroy(e);
+  }
+};
+
+KernelScope::KernelScope(const tkv_cache* c, hipStream_t stream, const char* name)
+    : kt(c ? c->kt : nullptr), slot(-1), st(stream) {
+  if (!kt) return;
+  if (kt->pending.size() >= KernelTimes::kMaxPending) { kt->dropped++; kt = nullptr; return; }
+  hipEvent_t a = kt->take(), b = kt->take();
+  if (!a || !b || hipEventRecord(a, st) != hipSuccess) { kt->give(a); kt->give(b); kt->failed = 1; kt = nullptr; return; }
+  kt->pending.push_back({name, a, b});
+  slot = (int)kt->pending.size() - 1;
+}
+KernelScope::~KernelScope() {
+  if (kt && slot >= 0 && hipEventRecord(kt->pending[slot].e1, st) != hipSuccess) kt->failed = 1;
+}
 
 static int layout_ok(const tkv_layout* L) {
   if (!L) return 0;
@@ -119,8 +170,47 @@ extern "C" int tkv_create(const tkv_layout* L, void* const bufs[TKV_NUM_BUFFERS]
 
 extern "C" int tkv_destroy(tkv_cache* c) {
   if (!c) return TKV_EINVAL;
+  delete c->kt;
   free(c);
   return TKV_OK;
+}
+
+extern "C" int tkv_kernel_timing(tkv_cache* c, int32_t enable) {
+  if (!c) return TKV_EINVAL;
+  delete c->kt;       // (waits for nothing: recorded events are destroyed with it)
+  c->kt = nullptr;
+  if (enable) {
+    c->kt = new (std::nothrow) KernelTimes();
+    if (!c->kt) return TKV_EHIP;
+  }
+  return TKV_OK;
+}
+
+extern "C" int tkv_kernel_times(tkv_cache* c, int32_t max_kernels, char* names, double* total_us, int32_t* calls,
+                                int64_t* dropped) {
+  if (!c || max_kernels < 0 || (max_kernels > 0 && (!names || !total_us || !calls))) return TKV_EINVAL;
+  KernelTimes* kt = c->kt;
+  if (!kt) return TKV_EINVAL;
+  int r = TKV_OK;
+  for (auto& rec : kt->pending) {
+    float ms = 0.f;
+    if (r == TKV_OK && (hipEventSynchronize(rec.e1) != hipSuccess || hipEventElapsedTime(&ms, rec.e0, rec.e1) != hipSuccess))
+      r = TKV_EHIP;
+    if (r == TKV_OK) kt->add(rec.name, 1000.0 * ms);
+    kt->give(rec.e0);
+    kt->give(rec.e1);
+  }
+  kt->pending.clear();
+  if (r != TKV_OK || kt->failed) return TKV_EHIP;
+  const int n = (int)kt->names.size();
+  for (int i = 0; i < n && i < max_kernels; i++) {
+    strncpy(names + 32 * i, kt->names[i].c_str(), 31);
+    names[32 * i + 31] = 0;
+    total_us[i] = kt->total_us[i];
+    calls[i] = kt->calls[i];
+  }
+  if (dropped) *dropped = kt->dropped;
+  return n;
 }
 
 extern "C" int tkv_seq_reset(tkv_cache* c, int32_t n, const int32_t* seq_ids, hipStream_t stream) {
@@ -154,7 +244,8 @@ extern "C" int kv_classify_append(tkv_cache* c, int32_t n, const int32_t* seq_id
     // the row in parallel, then the allocation takes the labels; the labels go
     // to an unused scratch region when the caller wants none
     uint8_t* lab = labels_out ? labels_out : (uint8_t*)scr_status(c->S.scratch);
-    const int r = launch_classify(n, num_q_heads, stats, tau_T, tau_E, score_kind, lab, stream);
+    int r;
+    TKV_TIMED(c, stream, "k_classify", r = launch_classify(n, num_q_heads, stats, tau_T, tau_E, score_kind, lab, stream));
     if (r != TKV_OK) return r;
     return launch_append(c, n, seq_ids, positions, lab, k, v, slot_out, stream);
   }

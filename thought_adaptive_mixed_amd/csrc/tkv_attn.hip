@@ -1228,7 +1228,6 @@ static bool launch_attn_t(const AttnParams& P, int batch, int Hkv, int Hq, int n
     else if (pk == 2) ok = launch_one<D, GS, false, PK2, FMT>(P, grid, nw, lds, st);
     else ok = launch_one<D, GS, false, 1, FMT>(P, grid, nw, lds, st);
   }
-  if (ok && P.splits > 1) k_combine<D><<<dim3((Hq + 3) / 4, batch), 256, 0, st>>>(P);
   return ok;
 }
 
@@ -1244,18 +1243,26 @@ int launch_attention(tkv_cache* c, const tkv_attn_args* a, int nw, int splits, h
   const bool win = a->window > 0;
   const int pk = pack_of(c, c->S.Hq / c->S.Hkv, win);
   const int B = a->batch, Hkv = c->S.Hkv, Hq = c->S.Hq;
-  bool ok;
-  if (c->S.fmt == 0) {
-    if (D == 128 && g == 64) ok = launch_attn_t<128, 64, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
-    else if (D == 128 && g == 32) ok = launch_attn_t<128, 32, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
-    else if (D == 64 && g == 64) ok = launch_attn_t<64, 64, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
-    else ok = launch_attn_t<64, 32, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
-  } else {
-    if (D == 128 && g == 64) ok = launch_attn_t<128, 64, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
-    else if (D == 128 && g == 32) ok = launch_attn_t<128, 32, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
-    else if (D == 64 && g == 64) ok = launch_attn_t<64, 64, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
-    else ok = launch_attn_t<64, 32, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+  bool ok = false;
+  {
+    KernelScope ks(c, st, "k_attn");
+    if (c->S.fmt == 0) {
+      if (D == 128 && g == 64) ok = launch_attn_t<128, 64, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+      else if (D == 128 && g == 32) ok = launch_attn_t<128, 32, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+      else if (D == 64 && g == 64) ok = launch_attn_t<64, 64, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+      else ok = launch_attn_t<64, 32, 0>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+    } else {
+      if (D == 128 && g == 64) ok = launch_attn_t<128, 64, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+      else if (D == 128 && g == 32) ok = launch_attn_t<128, 32, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+      else if (D == 64 && g == 64) ok = launch_attn_t<64, 64, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+      else ok = launch_attn_t<64, 32, 1>(P, B, Hkv, Hq, nw, lds, win, pk, st);
+    }
   }
+  if (ok && P.splits > 1)
+    TKV_TIMED(c, st, "k_combine", {
+      if (D == 128) k_combine<128><<<dim3((Hq + 3) / 4, B), 256, 0, st>>>(P);
+      else k_combine<64><<<dim3((Hq + 3) / 4, B), 256, 0, st>>>(P);
+    });
   if (!ok) return TKV_EHIP;
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }

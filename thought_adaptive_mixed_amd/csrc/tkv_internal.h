@@ -45,6 +45,7 @@ struct DevState {
   int chunk_bytes[3];             // bytes per lane chunk = D*bits/32
 };
 
+struct KernelTimes;               // per-kernel timing records (tkv_kernel_timing)
 struct tkv_cache {
   tkv_layout L;
   void* buf[TKV_NUM_BUFFERS];
@@ -52,7 +53,25 @@ struct tkv_cache {
   DevState S;
   hipStream_t last_stream;
   int device;                     // the device current when the cache was created
+  KernelTimes* kt;                // null unless per-kernel timing is on
 };
+
+// Per-kernel timing (off by default): with it on, every kernel the library
+// launches for a cache is bracketed by two HIP events on its stream (created
+// without the system-scope fence), and tkv_kernel_times adds up the measured
+// durations per kernel name.  KernelScope brackets one launch.
+struct KernelScope {
+  KernelTimes* kt;
+  int slot;
+  hipStream_t st;
+  KernelScope(const tkv_cache* c, hipStream_t stream, const char* name);
+  ~KernelScope();
+};
+#define TKV_TIMED(c, st, name, ...)     \
+  do {                                   \
+    KernelScope ks_((c), (st), (name));  \
+    __VA_ARGS__;                         \
+  } while (0)
 
 // Per-class fields of DevState indexed by a run-time class: select among the
 // three kernel-argument values (held in scalar registers) instead of indexing
