@@ -194,7 +194,8 @@ extern "C" int tkv_kernel_times(tkv_cache* c, int32_t max_kernels, char* names, 
   int r = TKV_OK;
   for (auto& rec : kt->pending) {
     float ms = 0.f;
-    if (r == TKV_OK && (hipEventSynchronize(rec.e1) != hipSuccess || hipEventElapsedTime(&ms, rec.e0, rec.e1) != hipSuccess))
+    if (r == TKV_OK &&
+        (hipEventSynchronize(rec.e1) != hipSuccess || hipEventElapsedTime(&ms, rec.e0, rec.e1) != hipSuccess))
       r = TKV_EHIP;
     if (r == TKV_OK) kt->add(rec.name, 1000.0 * ms);
     kt->give(rec.e0);
@@ -245,7 +246,8 @@ extern "C" int kv_classify_append(tkv_cache* c, int32_t n, const int32_t* seq_id
     // to an unused scratch region when the caller wants none
     uint8_t* lab = labels_out ? labels_out : (uint8_t*)scr_status(c->S.scratch);
     int r;
-    TKV_TIMED(c, stream, "k_classify", r = launch_classify(n, num_q_heads, stats, tau_T, tau_E, score_kind, lab, stream));
+    TKV_TIMED(c, stream, "k_classify",
+              r = launch_classify(n, num_q_heads, stats, tau_T, tau_E, score_kind, lab, stream));
     if (r != TKV_OK) return r;
     return launch_append(c, n, seq_ids, positions, lab, k, v, slot_out, stream);
   }

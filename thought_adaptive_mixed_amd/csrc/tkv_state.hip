@@ -601,8 +601,9 @@ int launch_append(tkv_cache* c, int n, const int32_t* seq_ids, const int32_t* po
   if (n == 0) return TKV_OK;
   if (cl && cl->stats && cl->heads + 1 > CL_STAGE) return TKV_EINVAL;   // a row must fit the LDS stage
   const ClassifyIn none = {nullptr, 0, 0, 0.f, 0.f, nullptr};
-  TKV_TIMED(c, st, "k_append_alloc", k_append_alloc<<<1, walker_threads(c->S.max_seqs), 0, st>>>(c->S, n, seq_ids, pos, thought, slot_out,
-                                                              cl ? *cl : none));
+  TKV_TIMED(c, st, "k_append_alloc",
+            k_append_alloc<<<1, walker_threads(c->S.max_seqs), 0, st>>>(c->S, n, seq_ids, pos, thought, slot_out,
+                                                                        cl ? *cl : none));
   const int64_t rows = (int64_t)n * c->S.Hst * 2;
   const int blocks = (int)((rows + 3) / 4);
   TKV_TIMED(c, st, "k_append_store", {
@@ -1250,7 +1251,9 @@ __global__ __launch_bounds__(EV_THREADS) void k_evict_apply(DevState S) {
 int launch_evict(tkv_cache* c, int n_ops, const int32_t* n_ops_dev, const int32_t* seq_ids, const int32_t* seg_ids,
                  const int32_t* keep_n, const uint8_t* new_bits, hipStream_t st) {
   if (n_ops == 0) return TKV_OK;
-  TKV_TIMED(c, st, "k_evict_plan", k_evict_plan<<<1, walker_threads(c->S.max_seqs), 0, st>>>(c->S, n_ops, n_ops_dev, seq_ids, seg_ids, keep_n, new_bits));
+  TKV_TIMED(c, st, "k_evict_plan",
+            k_evict_plan<<<1, walker_threads(c->S.max_seqs), 0, st>>>(c->S, n_ops, n_ops_dev, seq_ids, seg_ids, keep_n,
+                                                                      new_bits));
   TKV_TIMED(c, st, "k_evict_apply", k_evict_apply<<<c->S.max_seqs, EV_THREADS, 0, st>>>(c->S));
   launch_requant(c, st);
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
@@ -1414,7 +1417,8 @@ int launch_plan(tkv_cache* c, int n, const int32_t* seq_ids, int num, int den, i
                 int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st) {
   // a wave per listed sequence, up to 16 waves
   const int nt = n < 1 ? 64 : (n >= WG / 64 ? WG : 64 * n);
-  TKV_TIMED(c, st, "k_plan", k_plan<<<1, nt, 0, st>>>(c->S, n, seq_ids, num, den, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits));
+  TKV_TIMED(c, st, "k_plan",
+            k_plan<<<1, nt, 0, st>>>(c->S, n, seq_ids, num, den, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits));
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
 
@@ -1432,7 +1436,9 @@ __global__ __launch_bounds__(WG) void k_plan_evict(DevState S, int n, const int3
 int launch_plan_evict(tkv_cache* c, int n, const int32_t* seq_ids, int num, int den, int max_ops, int32_t* n_ops_dev,
                       int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st) {
   if (max_ops == 0) return launch_plan(c, n, seq_ids, num, den, 0, n_ops_dev, op_seq, op_seg, op_keep, op_bits, st);
-  TKV_TIMED(c, st, "k_plan_evict", k_plan_evict<<<1, WG, 0, st>>>(c->S, n, seq_ids, num, den, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits));
+  TKV_TIMED(c, st, "k_plan_evict",
+            k_plan_evict<<<1, WG, 0, st>>>(c->S, n, seq_ids, num, den, max_ops, n_ops_dev, op_seq, op_seg, op_keep,
+                                           op_bits));
   TKV_TIMED(c, st, "k_evict_apply", k_evict_apply<<<c->S.max_seqs, EV_THREADS, 0, st>>>(c->S));
   launch_requant(c, st);
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
@@ -1534,13 +1540,16 @@ __global__ __launch_bounds__(WG) void k_anneal_evict(DevState S, int n, const in
 int launch_anneal(tkv_cache* c, int n, const int32_t* seq_ids, int r0, int max_ops, int32_t* n_ops_dev,
                   int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st) {
   const int nt = n < 1 ? 64 : (n >= WG / 64 ? WG : 64 * n);
-  TKV_TIMED(c, st, "k_anneal", k_anneal<<<1, nt, 0, st>>>(c->S, n, seq_ids, r0, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits));
+  TKV_TIMED(c, st, "k_anneal",
+            k_anneal<<<1, nt, 0, st>>>(c->S, n, seq_ids, r0, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits));
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
 int launch_anneal_evict(tkv_cache* c, int n, const int32_t* seq_ids, int r0, int max_ops, int32_t* n_ops_dev,
                         int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st) {
   if (max_ops == 0) return launch_anneal(c, n, seq_ids, r0, 0, n_ops_dev, op_seq, op_seg, op_keep, op_bits, st);
-  TKV_TIMED(c, st, "k_anneal_evict", k_anneal_evict<<<1, WG, 0, st>>>(c->S, n, seq_ids, r0, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits));
+  TKV_TIMED(c, st, "k_anneal_evict",
+            k_anneal_evict<<<1, WG, 0, st>>>(c->S, n, seq_ids, r0, max_ops, n_ops_dev, op_seq, op_seg, op_keep,
+                                             op_bits));
   TKV_TIMED(c, st, "k_evict_apply", k_evict_apply<<<c->S.max_seqs, EV_THREADS, 0, st>>>(c->S));
   launch_requant(c, st);
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
