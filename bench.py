@@ -313,9 +313,13 @@ def attention_config(name, reps=5, launches=50, oracle_s=3.0):
     sh = torch.cuda.current_stream().cuda_stream
     res = {}
     cores = len(os.sched_getaffinity(0))
+    # the dispatch order of each copy (tkv_attn_order), made once: the state does not change here
+    orders = [torch.zeros(1 + B, dtype=torch.int32, device="cuda") for _ in caches]
+    for c, o in zip(caches, orders):
+        c.attn_order(seq_d, o)
     def timed(window):
         calls = [c.attention(seq_d, pos_d, q_d, out, ws, stats=stats, n_attended=n_att, sinks=sinks_d,
-                             window=window, stream=sh, prepare=True) for c in caches]
+                             window=window, order=o, stream=sh, prepare=True) for c, o in zip(caches, orders)]
         for i in range(2 * len(calls)):
             calls[i % len(calls)]()
         torch.cuda.synchronize()
@@ -387,6 +391,9 @@ def workload_name(args):
     if args.formats == "page":
         s += "; page code formats (R FP8 E4M3, E FP4 E2M1, T ternary)"
     return s
+
+
+ORDER_EVERY = 16       # decode steps of a copy between two dispatch orders
 
 
 def step_bench(args):
@@ -490,15 +497,25 @@ def step_bench(args):
     o_seg, o_keep = torch.zeros_like(o_seq), torch.zeros_like(o_seq)
     o_bits = torch.zeros(max_ops, dtype=torch.uint8, device="cuda")
 
+    # the attention's dispatch order (tkv_attn_order: longest sequences first),
+    # one per copy, made before the first step and again every ORDER_EVERY steps
+    # of that copy inside the steps (lengths change slowly)
+    orders = [torch.zeros(1 + B, dtype=torch.int32, device="cuda") for _ in range(R)]
+    for c, o in zip(caches, orders):
+        c.attn_order(seq_d, o)
+    torch.cuda.synchronize()
+
     # every call's C arguments are converted once, before anything is timed
     sh = torch.cuda.current_stream().cuda_stream
     calls_a, calls_b = [], []
     for s in range(total):
         c = caches[s % R]
         q, k, v, pos, kl, vl = steps_in[s]
-        calls_a.append([c.attention(seq_d, pos, q, out, ws, stats=stats[:, l], n_attended=n_att[s], k_self=k,
-                                    v_self=v, layer=l, stats_stride=NL * Hq * 3, stream=sh, prepare=True)
-                        for l in range(NL)])
+        renew = [c.attn_order(seq_d, orders[s % R], stream=sh, prepare=True)] if (s // R) % ORDER_EVERY == 0 else []
+        calls_a.append(renew + [c.attention(seq_d, pos, q, out, ws, stats=stats[:, l], n_attended=n_att[s], k_self=k,
+                                            v_self=v, layer=l, stats_stride=NL * Hq * 3, order=orders[s % R],
+                                            stream=sh, prepare=True)
+                                for l in range(NL)])
         calls_b.append([
             # classification of every layer's statistics rows, inside the append's allocation kernel
             ("classify+append", c.classify_append(seq_d, pos, stats.view(B, NL * Hq, 3), ch.tau[0], ch.tau[1],

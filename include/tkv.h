@@ -317,11 +317,29 @@ typedef struct {
   size_t workspace_bytes;
   int32_t layer;              /* 0..L-1: the layer whose K/V are attended                  */
   int32_t stats_stride;       /* floats between batch entries of stats; 0 = Hq*3, else >= Hq*3 */
+  const int32_t* order;       /* nullable i32[1 + batch] from tkv_attn_order over this batch:
+                                 the dispatch order of the entries (results do not depend on it);
+                                 ignored unless order[0] == batch                             */
 } tkv_attn_args;
 
 /* Workspace bytes paged_decode_attn needs for `batch` entries and the given
    num_splits (0 = the library's choice). */
 size_t tkv_attn_workspace(const tkv_cache* c, int32_t batch, int32_t num_splits);
+
+/* tkv_attn_order -- dispatch order for paged_decode_attn (not part of the
+ * method; its results are the same in any order): writes order[0] = batch and
+ * order[1..batch] = the batch entries, longest first (by the code bytes per KV
+ * head the sequences hold now, in 256 length buckets; the order inside a bucket
+ * is not fixed).  Passed as tkv_attn_args.order, it makes the attention deal
+ * its work-groups so that every compute unit gets a similar mix of long and
+ * short sequences (random lengths otherwise leave some compute units with
+ * several long ones), and a grid of >= 2048 (entry, KV head) units then runs as
+ * two-wave work-groups.  Lengths change slowly in decode, so one order can
+ * serve many steps over the same seq_ids; an order made for another batch size
+ * is ignored.  seq_ids: i32[batch] (the attention's); order: device i32
+ * [1 + batch], caller-owned.  One small kernel on `stream`.
+ *   EINVAL: c NULL, batch < 0 or > max_seqs, or a needed pointer NULL. */
+int tkv_attn_order(tkv_cache* c, int32_t batch, const int32_t* seq_ids, int32_t* order, hipStream_t stream);
 int paged_decode_attn(tkv_cache* c, const tkv_attn_args* a_h, hipStream_t stream);
 
 /* paged_decode_attn_noalloc -- for callers that cannot allocate device memory

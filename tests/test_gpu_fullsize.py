@@ -55,7 +55,8 @@ def test_fullsize_state_and_attention(name):
 def test_fullshape_churn():
     """The churn loop at full shape (B256, Hq32/Hkv8, D128, starting lengths
     U{4k..32k}, 5% budget) for 128 decode steps in the calls the bench times:
-    attention with the self token, kv_classify_append, kv_plan_budget_evict.
+    attention with the self token (in the dispatch order of tkv_attn_order,
+    renewed every 16 steps), kv_classify_append, kv_plan_budget_evict.
     Every step: all 256 attention rows against the oracle, the GPU's own
     labels against the oracle's outside the threshold ambiguity band, the
     fused call's labels (fed the oracle's fp32 statistics) equal to the
@@ -84,9 +85,12 @@ def test_fullshape_churn():
     tT, tE = ch.tau
     amb = n_ev = n_down = 0
     worst = 0.0
+    order = torch.zeros(1 + B, dtype=torch.int32, device="cuda")
     for s in range(steps):
         q, k, v, pos = ch.step_inputs(s)
-        go, gs, gn = gpu_attention(gc, w.seq_ids, pos, q, k_self=k, v_self=v)
+        if s % 16 == 0:                       # the dispatch order, renewed as the bench does
+            gc.attn_order(seq_d, order)
+        go, gs, gn = gpu_attention(gc, w.seq_ids, pos, q, k_self=k, v_self=v, order=order)
         ro, rs, rn = oc.attention(w.seq_ids, pos, q, k_self=k, v_self=v)
         check_attention(f"step {s} all rows", (go, gs, gn), (ro, rs, rn)) if s % 16 == 0 else None
         mabs, rl2 = helpers.attn_metrics(go, ro)

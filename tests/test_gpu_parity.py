@@ -23,7 +23,8 @@ def say(*a):
     sys.stdout.flush()
 
 
-def gpu_attention(gc, seq_ids, q_pos, q, window=0, sinks=None, k_self=None, v_self=None, splits=0, topk=8):
+def gpu_attention(gc, seq_ids, q_pos, q, window=0, sinks=None, k_self=None, v_self=None, splits=0, topk=8,
+                  order=None):
     import torch
     B = len(seq_ids)
     Hq, D = gc.Hq, gc.D
@@ -36,7 +37,7 @@ def gpu_attention(gc, seq_ids, q_pos, q, window=0, sinks=None, k_self=None, v_se
                  n_attended=n_att, k_self=None if k_self is None else dv(k_self, np.float32),
                  v_self=None if v_self is None else dv(v_self, np.float32),
                  sinks=None if sinks is None else dv(sinks, np.float32), window=window, topk=topk,
-                 num_splits=splits)
+                 num_splits=splits, order=order)
     torch.cuda.synchronize()
     return out.cpu().numpy(), stats.cpu().numpy(), n_att.cpu().numpy()
 

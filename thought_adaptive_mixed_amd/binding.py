@@ -29,7 +29,7 @@ SYMBOLS = ["tkv_buffer_sizes", "tkv_create", "tkv_destroy", "tkv_seq_reset", "kv
            "kv_evict_segment", "kv_plan_budget", "kv_plan_budget_evict", "kv_plan_anneal", "kv_plan_anneal_evict", "tkv_compact", "tkv_attn_workspace", "paged_decode_attn",
            "paged_decode_attn_noalloc",
            "thought_classify", "tkv_get_error", "tkv_export_state", "tkv_import_state", "tkv_strerror",
-           "tkv_stream_read", "tkv_kernel_timing", "tkv_kernel_times"]
+           "tkv_stream_read", "tkv_kernel_timing", "tkv_kernel_times", "tkv_attn_order"]
 
 
 class Layout(C.Structure):
@@ -46,7 +46,7 @@ class AttnArgs(C.Structure):
                 ("window", C.c_int32), ("topk", C.c_int32), ("num_splits", C.c_int32),
                 ("out", C.c_void_p), ("stats", C.c_void_p), ("n_attended", C.c_void_p),
                 ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t), ("layer", C.c_int32),
-                ("stats_stride", C.c_int32)]
+                ("stats_stride", C.c_int32), ("order", C.c_void_p)]
 
 
 class TkvError(RuntimeError):
@@ -93,6 +93,7 @@ def load(path: str = LIB_PATH):
     L.tkv_stream_read.argtypes = [P, C.c_size_t, P, P]
     L.tkv_kernel_timing.argtypes = [P, I]
     L.tkv_kernel_times.argtypes = [P, I, P, P, P, P]
+    L.tkv_attn_order.argtypes = [P, I, P, P, P]
     _lib = L
     return L
 
@@ -268,24 +269,31 @@ class Cache:
         return int(self.L.tkv_attn_workspace(self.h, int(batch), int(num_splits)))
 
     def attention(self, seq_ids, q_pos, q, out, workspace, stats=None, n_attended=None, k_self=None, v_self=None,
-                  sinks=None, window=0, topk=8, num_splits=0, layer=0, stats_stride=0, *, stream=None, prepare=False):
+                  sinks=None, window=0, topk=8, num_splits=0, layer=0, stats_stride=0, order=None, *, stream=None,
+                  prepare=False):
         a = AttnArgs(int(seq_ids.numel()), _ptr(seq_ids), _ptr(q_pos), _ptr(q), _ptr(k_self), _ptr(v_self),
                      _ptr(sinks), int(window), int(topk), int(num_splits), _ptr(out), _ptr(stats), _ptr(n_attended),
                      _ptr(workspace), int(workspace.numel() * workspace.element_size()), int(layer),
-                     int(stats_stride))
+                     int(stats_stride), _ptr(order))
         args = (self.h, C.byref(a), _stream(stream))
         return _issue(self.L.paged_decode_attn, args, "paged_decode_attn", prepare, keep=a)
 
     def attention_noalloc(self, seq_ids, q_pos, q, out, stats=None, n_attended=None, k_self=None, v_self=None,
-                          sinks=None, window=0, topk=8, num_splits=0, layer=0, stats_stride=0, *, stream=None,
-                          prepare=False):
+                          sinks=None, window=0, topk=8, num_splits=0, layer=0, stats_stride=0, order=None, *,
+                          stream=None, prepare=False):
         """paged_decode_attn_noalloc: the split-K partials in the library's static
         device array instead of a caller workspace."""
         a = AttnArgs(int(seq_ids.numel()), _ptr(seq_ids), _ptr(q_pos), _ptr(q), _ptr(k_self), _ptr(v_self),
                      _ptr(sinks), int(window), int(topk), int(num_splits), _ptr(out), _ptr(stats), _ptr(n_attended),
-                     None, 0, int(layer), int(stats_stride))
+                     None, 0, int(layer), int(stats_stride), _ptr(order))
         args = (self.h, C.byref(a), _stream(stream))
         return _issue(self.L.paged_decode_attn_noalloc, args, "paged_decode_attn_noalloc", prepare, keep=a)
+
+    def attn_order(self, seq_ids, order, *, stream=None, prepare=False):
+        """tkv_attn_order: the attention's dispatch order for this batch (order:
+        device int32 [1 + batch]), to pass as attention(..., order=order)."""
+        args = (self.h, int(seq_ids.numel()), _ptr(seq_ids), _ptr(order), _stream(stream))
+        return _issue(self.L.tkv_attn_order, args, "tkv_attn_order", prepare)
 
     def kernel_timing(self, enable: bool):
         """tkv_kernel_timing: bracket every kernel launched for this cache with

@@ -315,7 +315,7 @@ extern "C" int tkv_compact(tkv_cache* c, int32_t n, const int32_t* n_dev, const 
 extern "C" size_t tkv_attn_workspace(const tkv_cache* c, int32_t batch, int32_t num_splits) {
   if (!c || batch < 0) return 0;
   int nw, s;
-  attn_plan(c, batch, num_splits, &nw, &s);
+  attn_plan(c, batch, num_splits, false, &nw, &s);
   return attn_workspace_bytes(c, batch, s);
 }
 
@@ -333,10 +333,18 @@ static int attn_args_ok(const tkv_cache* c, const tkv_attn_args* a) {
   return 1;
 }
 
+extern "C" int tkv_attn_order(tkv_cache* c, int32_t batch, const int32_t* seq_ids, int32_t* order,
+                              hipStream_t stream) {
+  if (!c || batch < 0 || batch > c->S.max_seqs || (batch > 0 && (!seq_ids || !order))) return TKV_EINVAL;
+  if (batch == 0) return TKV_OK;
+  c->last_stream = stream;
+  return launch_attn_order(c, batch, seq_ids, order, stream);
+}
+
 extern "C" int paged_decode_attn_noalloc(tkv_cache* c, const tkv_attn_args* a, hipStream_t stream) {
   if (!attn_args_ok(c, a)) return TKV_EINVAL;
   int nw, s;
-  attn_plan(c, a->batch, a->num_splits, &nw, &s);
+  attn_plan(c, a->batch, a->num_splits, a->order != nullptr, &nw, &s);
   if (attn_workspace_bytes(c, a->batch, s) > (size_t)TKV_STATIC_WORKSPACE_BYTES) return TKV_ERANGE;
   void* ws = static_workspace(c->device);
   if (!ws) return TKV_EHIP;
@@ -347,7 +355,7 @@ extern "C" int paged_decode_attn_noalloc(tkv_cache* c, const tkv_attn_args* a, h
 extern "C" int paged_decode_attn(tkv_cache* c, const tkv_attn_args* a, hipStream_t stream) {
   if (!attn_args_ok(c, a)) return TKV_EINVAL;
   int nw, s;
-  attn_plan(c, a->batch, a->num_splits, &nw, &s);
+  attn_plan(c, a->batch, a->num_splits, a->order != nullptr, &nw, &s);
   const size_t need = attn_workspace_bytes(c, a->batch, s);
   if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return TKV_EINVAL;
   c->last_stream = stream;

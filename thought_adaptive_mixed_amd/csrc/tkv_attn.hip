@@ -181,6 +181,7 @@ struct AttnParams {
   int layer;                   // the layer attended: KV heads layer*Hkv.. of each block
   int stats_stride;            // floats between batch entries of stats
   float* part;                 // [batch][Hq][splits][D + PART_X]
+  const int32_t* order;        // nullable: [1 + batch] batch size, then the entry of each grid row
   float* out;
   float* stats;
   int32_t* n_attended;
@@ -783,7 +784,12 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   // block lists [3][max_blocks] (id, mask) and their counts.
   extern __shared__ __align__(16) float lds[];
   const DevState& S = P.S;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // grid row blockIdx.z is batch entry b, or, with a dispatch order made for
+  // this batch size, the entry the order puts there (clamped into the batch)
+  const int split = blockIdx.x, kvh = blockIdx.y, batch = gridDim.z;
+  int b = blockIdx.z;
+  if (P.order && P.order[0] == batch) b = min(max(P.order[1 + blockIdx.z], 0), batch - 1);
+  const int s = P.seq_ids[b];
   // the wave index is uniform across its lanes: say so to the compiler
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nw = blockDim.x >> 6;
   const int lg = lane >> 4, h = lane & 15;
@@ -791,7 +797,6 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   const bool col_ok = h < G;                     // MFMA column h is a real head
   const int hp = h % GP;                         // head of this lane in the packed layout
   const bool head_ok = hp < G;
-  const int s = P.seq_ids[b];
   const bool seq_ok = s >= 0 && s < S.max_seqs;
   // Query rows, read now and converted after the block lists (so that their
   // latency overlaps the list reads).  Lane (h, lg) holds the query of the
@@ -1173,10 +1178,15 @@ static int lds_bytes(const tkv_cache* c, int nw) {
 }
 static const int kStaticLds = 8192 + 640 + 384;                     // query operands, finalize inputs (and slack)
 
-void attn_plan(const tkv_cache* c, int batch, int num_splits, int* nw_out, int* splits_out) {
+void attn_plan(const tkv_cache* c, int batch, int num_splits, bool ordered, int* nw_out, int* splits_out) {
   const int units = batch * c->S.Hkv > 0 ? batch * c->S.Hkv : 1;
   int nw = 1;
   while (nw < 8 && units * nw * 2 <= kTargetWaves && lds_bytes(c, nw * 2) + kStaticLds <= kMaxLds) nw *= 2;
+  // A grid dispatched longest first runs in two rounds of two-wave
+  // work-groups: the first round holds the longest sequences, each with two
+  // waves, and the short ones follow as slots free up.  (Only where the
+  // units fill the machine by themselves, so the split count is 1 either way.)
+  if (ordered && units >= kTargetWaves && lds_bytes(c, 2) + kStaticLds <= kMaxLds) nw = 2;
   int splits = num_splits;
   if (splits <= 0) {
     splits = (kTargetWaves + units * nw - 1) / (units * nw);
@@ -1190,6 +1200,64 @@ void attn_plan(const tkv_cache* c, int batch, int num_splits, int* nw_out, int* 
   }
   *nw_out = nw;
   *splits_out = splits;
+}
+
+// Dispatch order of the batch entries, longest first.  The dispatcher deals
+// consecutive work-groups round-robin over the XCDs and their compute units,
+// so a compute unit receives work-groups far apart in the grid; in batch
+// order (lengths at random) some compute units then get several long
+// sequences and finish last, while in length order every compute unit gets
+// one work-group of each length range.  Entries are counted into 256 length
+// buckets (a counting sort on the sequence's code bytes per KV head; the
+// order inside a bucket is the order of arrival).  The attention's results do
+// not depend on this order.  One work-group, one thread per batch entry.
+__global__ __launch_bounds__(1024) void k_attn_order(DevState S, const int32_t* seq_ids, int batch, int32_t* order) {
+  __shared__ int s_hist[256];
+  __shared__ unsigned s_max;
+  const int b = threadIdx.x;
+  if (b < 256) s_hist[b] = 0;
+  if (b == 0) s_max = 1;
+  int s = -1;
+  unsigned w = 0;
+  if (b < batch) {
+    s = seq_ids[b];
+    if (s >= 0 && s < S.max_seqs) {
+      const int32_t* q = S.seq + (int64_t)s * TKV_SEQ_W;
+      w = (unsigned)q[Q_NBLK + 0] * (unsigned)S.bh_bytes[0] + (unsigned)q[Q_NBLK + 1] * (unsigned)S.bh_bytes[1] +
+          (unsigned)q[Q_NBLK + 2] * (unsigned)S.bh_bytes[2];
+    }
+  }
+  __syncthreads();
+  if (b < batch) atomicMax(&s_max, w);
+  __syncthreads();
+  // bucket 0 holds the longest entries
+  const int d = 255 - (int)(((unsigned long long)w * 255u) / s_max);
+  int at = 0;
+  if (b < batch) at = atomicAdd(&s_hist[d], 1);
+  __syncthreads();
+  // exclusive prefix of the bucket counts (one wave, four buckets per lane)
+  if (b < 64) {
+    int v[4], t = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) { v[i] = s_hist[4 * b + i]; t += v[i]; }
+    int incl = t;
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const int y = __shfl_up(incl, sh, 64);
+      if (b >= sh) incl += y;
+    }
+    int run = incl - t;
+#pragma unroll
+    for (int i = 0; i < 4; i++) { const int x = v[i]; s_hist[4 * b + i] = run; run += x; }
+  }
+  __syncthreads();
+  if (b < batch) order[1 + s_hist[d] + at] = b;
+  if (b == 0) order[0] = batch;
+}
+
+int launch_attn_order(tkv_cache* c, int batch, const int32_t* seq_ids, int32_t* order, hipStream_t st) {
+  TKV_TIMED(c, st, "k_attn_order", k_attn_order<<<1, 1024, 0, st>>>(c->S, seq_ids, batch, order));
+  return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
 
 size_t attn_workspace_bytes(const tkv_cache* c, int batch, int splits) {
@@ -1239,6 +1307,7 @@ int launch_attention(tkv_cache* c, const tkv_attn_args* a, int nw, int splits, h
   P.window = a->window; P.splits = splits; P.topk = a->topk;
   P.layer = a->layer; P.stats_stride = a->stats_stride ? a->stats_stride : c->S.Hq * 3;
   P.part = (float*)(workspace ? workspace : a->workspace); P.out = a->out; P.stats = a->stats; P.n_attended = a->n_attended;
+  P.order = a->order;
   const int D = c->S.D, g = c->S.g, lds = lds_bytes(c, nw);
   const bool win = a->window > 0;
   const int pk = pack_of(c, c->S.Hq / c->S.Hkv, win);

@@ -337,7 +337,8 @@ int launch_seq_reset(tkv_cache* c, int n, const int32_t* seq_ids, hipStream_t st
 int launch_classify(int batch, int Hq, const float* stats, float tau_T, float tau_E, int kind, uint8_t* labels,
                     hipStream_t st);
 // Attention
-void attn_plan(const tkv_cache* c, int batch, int num_splits, int* nw, int* splits);
+void attn_plan(const tkv_cache* c, int batch, int num_splits, bool ordered, int* nw, int* splits);
+int launch_attn_order(tkv_cache* c, int batch, const int32_t* seq_ids, int32_t* order, hipStream_t st);
 size_t attn_workspace_bytes(const tkv_cache* c, int batch, int splits);
 int launch_attention(tkv_cache* c, const tkv_attn_args* a, int nw, int splits, hipStream_t st,
                      void* workspace = nullptr);
