@@ -81,6 +81,7 @@ class HipEvents:
         self.hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
         self.hip.hipEventElapsedTime.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p]
         self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.hip.hipStreamWaitEvent.argtypes = [C.c_void_p, C.c_void_p, C.c_uint]
         self.ev = []
         for _ in range(n):
             e = C.c_void_p()
@@ -93,6 +94,13 @@ class HipEvents:
             self.ev[i].record()
         elif self.hip.hipEventRecord(self.ev[i], self.C.c_void_p(stream)) != 0:
             raise RuntimeError("hipEventRecord failed")
+
+    def wait(self, i, stream):
+        """Make `stream` wait for event i (recorded on another stream)."""
+        if self.torch_events:
+            raise RuntimeError("cross-stream waits need the HIP events")
+        if self.hip.hipStreamWaitEvent(self.C.c_void_p(stream), self.ev[i], 0) != 0:
+            raise RuntimeError("hipStreamWaitEvent failed")
 
     def elapsed_ms(self, i, j):
         if self.torch_events:
@@ -396,6 +404,13 @@ def workload_name(args):
 ORDER_EVERY = 16       # decode steps of a copy between two dispatch orders
 
 
+def n_copies(args, sizes):
+    """State copies: enough for more than 1 GiB (beyond the Infinity Cache),
+    a multiple of the streams (copy j always runs on stream j % streams)."""
+    R = args.copies or max(2, math.ceil((1 << 30) / sum(sizes[:-1])))
+    return -(-R // args.streams) * args.streams
+
+
 def step_bench(args):
     import torch
     from thought_adaptive_mixed_amd import binding, drive, synth
@@ -455,14 +470,14 @@ def step_bench(args):
         del c0
         L = dataclasses.replace(L, num_layers=NL)
         sizes = binding.buffer_sizes(drive.gpu_layout(L))
-        R = args.copies or max(2, math.ceil((1 << 30) / sum(sizes[:-1])))
+        R = n_copies(args, sizes)
         caches = [binding.Cache(drive.gpu_layout(L), w.block_order) for _ in range(R)]
         for c in caches:
             c.import_(state)
         state = state1
     else:
         sizes = binding.buffer_sizes(drive.gpu_layout(L))
-        R = args.copies or max(2, math.ceil((1 << 30) / sum(sizes[:-1])))
+        R = n_copies(args, sizes)
         caches = [c0] + [binding.Cache(drive.gpu_layout(L), w.block_order) for _ in range(R - 1)]
         for c in caches[1:]:
             c.import_(state)
@@ -486,16 +501,29 @@ def step_bench(args):
                          dv(kl, np.float32) if NL > 1 else None, dv(vl, np.float32) if NL > 1 else None))
     steps_in = [per_copy[s // R] for s in range(total)]
     Hq, D = L.num_q_heads, L.head_dim
-    out = torch.empty(B, Hq, D, dtype=torch.float32, device="cuda")
-    stats = torch.empty(B, NL, Hq, 3, dtype=torch.float32, device="cuda")   # every layer's rows of a step
+    # Batches in flight: copy j runs on stream j % nst, each stream with its own
+    # output, statistics, label, op-list and workspace buffers.  With two
+    # streams, the state calls of one copy's step (latency-bound kernels of one
+    # or a few work-groups) run while the other copy's attention streams the
+    # cache; the attention launches themselves never overlap (each waits for
+    # the previous step's attention to end), so every attention launch is
+    # timed alone.
+    nst = args.streams
+    streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(nst - 1)]
+    sts = [x.cuda_stream for x in streams]
+    sh = sts[0]
     n_att = torch.zeros(total, B, dtype=torch.int32, device="cuda")         # one row per step
-    ws = torch.empty(max(caches[0].workspace_bytes(B), 16), dtype=torch.uint8, device="cuda")
-    labels = torch.empty(B, dtype=torch.uint8, device="cuda")
     max_ops = 1024
-    n_ops = torch.zeros(1, dtype=torch.int32, device="cuda")
-    o_seq = torch.zeros(max_ops, dtype=torch.int32, device="cuda")
-    o_seg, o_keep = torch.zeros_like(o_seq), torch.zeros_like(o_seq)
-    o_bits = torch.zeros(max_ops, dtype=torch.uint8, device="cuda")
+
+    def buffers():
+        return dict(out=torch.empty(B, Hq, D, dtype=torch.float32, device="cuda"),
+                    stats=torch.empty(B, NL, Hq, 3, dtype=torch.float32, device="cuda"),  # every layer's rows
+                    ws=torch.empty(max(caches[0].workspace_bytes(B), 16), dtype=torch.uint8, device="cuda"),
+                    labels=torch.empty(B, dtype=torch.uint8, device="cuda"),
+                    n_ops=torch.zeros(1, dtype=torch.int32, device="cuda"),
+                    ops=[torch.zeros(max_ops, dtype=torch.int32, device="cuda") for _ in range(3)],
+                    bits=torch.zeros(max_ops, dtype=torch.uint8, device="cuda"))
+    bufs = [buffers() for _ in range(nst)]
 
     # the attention's dispatch order (tkv_attn_order: longest sequences first),
     # one per copy, made before the first step and again every ORDER_EVERY steps
@@ -505,39 +533,55 @@ def step_bench(args):
         c.attn_order(seq_d, o)
     torch.cuda.synchronize()
 
-    # every call's C arguments are converted once, before anything is timed
-    sh = torch.cuda.current_stream().cuda_stream
+    # every call's C arguments are converted once, before anything is timed;
+    # the steps after the timed region (split and per-kernel timing) run on
+    # one stream
+    n_pipe = args.warmup + args.steps
+    stream_of = lambda s: sts[s % nst] if s < n_pipe else sh
     calls_a, calls_b = [], []
     for s in range(total):
         c = caches[s % R]
+        bf = bufs[s % nst]
+        st_s = stream_of(s)
         q, k, v, pos, kl, vl = steps_in[s]
-        renew = [c.attn_order(seq_d, orders[s % R], stream=sh, prepare=True)] if (s // R) % ORDER_EVERY == 0 else []
-        calls_a.append(renew + [c.attention(seq_d, pos, q, out, ws, stats=stats[:, l], n_attended=n_att[s], k_self=k,
-                                            v_self=v, layer=l, stats_stride=NL * Hq * 3, order=orders[s % R],
-                                            stream=sh, prepare=True)
+        stats = bf["stats"]
+        renew = [c.attn_order(seq_d, orders[s % R], stream=st_s, prepare=True)] if (s // R) % ORDER_EVERY == 0 else []
+        calls_a.append(renew + [c.attention(seq_d, pos, q, bf["out"], bf["ws"], stats=stats[:, l], n_attended=n_att[s],
+                                            k_self=k, v_self=v, layer=l, stats_stride=NL * Hq * 3, order=orders[s % R],
+                                            stream=st_s, prepare=True)
                                 for l in range(NL)])
+        o_seq, o_seg, o_keep = bf["ops"]
         calls_b.append([
             # classification of every layer's statistics rows, inside the append's allocation kernel
             ("classify+append", c.classify_append(seq_d, pos, stats.view(B, NL * Hq, 3), ch.tau[0], ch.tau[1],
-                                                  kl if NL > 1 else k, vl if NL > 1 else v, labels_out=labels,
-                                                  stream=sh, prepare=True)),
+                                                  kl if NL > 1 else k, vl if NL > 1 else v, labels_out=bf["labels"],
+                                                  stream=st_s, prepare=True)),
             ("plan+evict",
-             c.plan_anneal_evict(seq_d, args.r0, max_ops, n_ops, o_seq, o_seg, o_keep, o_bits, stream=sh, prepare=True)
+             c.plan_anneal_evict(seq_d, args.r0, max_ops, bf["n_ops"], o_seq, o_seg, o_keep, bf["bits"], stream=st_s,
+                                 prepare=True)
              if args.policy == "anneal" else
-             c.plan_budget_evict(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, o_seq, o_seg, o_keep, o_bits,
-                                 stream=sh, prepare=True)),
-        ] + ([("compact", c.compact(o_seq, n_dev=n_ops, n=max_ops, stream=sh, prepare=True))] if args.compact else []))
+             c.plan_budget_evict(seq_d, ch.budget[0], ch.budget[1], max_ops, bf["n_ops"], o_seq, o_seg, o_keep,
+                                 bf["bits"], stream=st_s, prepare=True)),
+        ] + ([("compact", c.compact(o_seq, n_dev=bf["n_ops"], n=max_ops, stream=st_s, prepare=True))]
+             if args.compact else []))
 
-    ev = HipEvents(2 * total + 2, torch_events=args.torch_events)   # (before, after) each attention
+    # events: (before, after) each attention, the timed region's ends, and
+    # one join event per further stream
+    T0, T1 = 2 * total, 2 * total + 1
+    ev = HipEvents(2 * total + 2 + nst, torch_events=args.torch_events)
 
-    # Steps are launched eagerly on torch's current stream (a replayed HIP
-    # graph per step measured slower on this stack).  The attention launch is
-    # bracketed by events on the same stream.
+    # Steps are launched eagerly (a replayed HIP graph per step measured slower
+    # on this stack).  The attention launch is bracketed by events on its own
+    # stream; with several streams it first waits for the previous step's
+    # attention to end.
     def step(s):
-        ev.record(2 * s, sh)
+        st_s = stream_of(s)
+        if nst > 1 and s > 0:
+            ev.wait(2 * (s - 1) + 1, st_s)
+        ev.record(2 * s, st_s)
         for f in calls_a[s]:
             f()
-        ev.record(2 * s + 1, sh)
+        ev.record(2 * s + 1, st_s)
         if not args.attn_only:
             for _, f in calls_b[s]:
                 f()
@@ -556,12 +600,16 @@ def step_bench(args):
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    log("[bench] timed")
-    T0, T1 = 2 * total, 2 * total + 1
+    log(f"[bench] timed ({nst} stream{'s' if nst > 1 else ''})")
     h0 = time.perf_counter()
     ev.record(T0, sh)
+    for j in range(1, nst):
+        ev.wait(T0, sts[j])
     for s in range(args.warmup, args.warmup + args.steps):
         step(s)
+    for j in range(1, nst):                   # the region ends when every stream is done
+        ev.record(T1 + j, sts[j])
+        ev.wait(T1 + j, sh)
     ev.record(T1, sh)
     h1 = time.perf_counter()
     torch.cuda.synchronize()
@@ -640,7 +688,11 @@ def step_bench(args):
                   "subnormals), f32 accumulate"),
         "data": "synthetic",
         "config": {"workload": workload_name(args), "batch": B, "copies": R,
-                   "attended_cached_per_step": tokens / args.steps, "launch": "eager, one stream",
+                   "attended_cached_per_step": tokens / args.steps,
+                   "launch": ("eager, one stream" if args.streams == 1 else
+                              f"eager, {args.streams} streams: copy j on stream j % {args.streams}, the state calls "
+                              f"of one copy's step beside the next copy's attention, attention launches never "
+                              f"overlapping"),
                    **({"layers": NL} if NL > 1 else {})},
         "attn_ms": attn_avg,
         "attn_kv_tokens_per_s": (tokens / args.steps) / (attn_avg * 1e-3),
@@ -664,6 +716,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=6)
     ap.add_argument("--split-steps", type=int, default=16, help="extra steps timed call by call")
+    ap.add_argument("--streams", type=int, choices=(1, 2), default=2,
+                    help="decode batches in flight (state copies stepped on their own streams)")
     ap.add_argument("--copies", type=int, default=0, help="state copies (0 = enough for > 1 GiB)")
     ap.add_argument("--cpu-seqs", type=int, default=16)
     ap.add_argument("--workload", choices=("churn256", "llama8b", "none"), default="churn256",
@@ -694,6 +748,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.torch_events and args.streams > 1:
+        print("--torch-events times one stream only: add --streams 1", file=sys.stderr)
+        sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.workload == "none":
