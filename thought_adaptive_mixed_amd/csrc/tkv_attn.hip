@@ -1267,13 +1267,16 @@ size_t attn_workspace_bytes(const tkv_cache* c, int batch, int splits) {
 
 template <int D, int GS, bool W, int PK, int FMT>
 static bool launch_one(const AttnParams& P, dim3 grid, int nw, int lds, hipStream_t st) {
-  // dynamic LDS above 64 KiB must be allowed once per kernel
-  static bool attr_set = false;
-  if (!attr_set) {
+  // dynamic LDS above 64 KiB must be allowed once per kernel and device
+  constexpr int kDevs = 64;
+  static bool attr_set[kDevs] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return false;
+  if (!attr_set[dev]) {
     if (hipFuncSetAttribute((const void*)k_attn<D, GS, W, PK, FMT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             kMaxLds - kStaticLds) != hipSuccess)
       return false;
-    attr_set = true;
+    attr_set[dev] = true;
   }
   k_attn<D, GS, W, PK, FMT><<<grid, 64 * nw, lds, st>>>(P);
   return true;
