@@ -126,3 +126,55 @@ def test_fullshape_churn():
         f"ambiguity band, {n_ev} segment evictions, {n_down} downgrades")
     assert gc.get_error() == oc.error()
     assert n_ev > 0
+
+
+@pytest.mark.timeout(900)
+def test_fullshape_churn_1024_steps():
+    """The churn loop at full shape for 1024 decode steps (B256, Hq32/Hkv8,
+    D128, starting lengths U{4k..32k}, 5% budget): every step appends each
+    sequence's new token at its planted thought type (kv_append_quant, the
+    same labels on both sides, so the oracle needs no attention between
+    checks) and runs kv_plan_budget_evict; the op lists equal the oracle's at
+    every step, the whole state is bit for bit the oracle's every 64 steps,
+    and every 128 steps all 256 attention rows are checked against the
+    oracle's.  This is the long horizon over which allocator drift (free
+    stacks, block lists, segment tables) would show."""
+    import torch
+    steps = 1024
+    ch = synth.churn(steps=steps)
+    w = ch.base
+    L = w.layout
+    say("[churn-1024] build")
+    gc = helpers.build_gpu(w)
+    oc = helpers.build_oracle(w)
+    B = w.seq_ids.size
+    dv = helpers.dev
+    seq_d = dv(w.seq_ids, np.int32)
+    max_ops = 1024
+    n_ops = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o = [torch.zeros(max_ops, dtype=torch.int32, device="cuda") for _ in range(3)]
+    o_bits = torch.zeros(max_ops, dtype=torch.uint8, device="cuda")
+    n_ev = n_down = 0
+    for s in range(steps):
+        q, k, v, pos = ch.step_inputs(s)
+        lab = ch.target_types[s].astype(np.uint8)
+        if s % 128 == 0:
+            got = gpu_attention(gc, w.seq_ids, pos, q, k_self=k, v_self=v)
+            ref = oc.attention(w.seq_ids, pos, q, k_self=k, v_self=v)
+            check_attention(f"churn-1024 step {s} all {B} rows", got, ref)
+        gc.append(seq_d, dv(pos, np.int32), dv(lab), dv(k, np.float32), dv(v, np.float32))
+        oc.append(w.seq_ids, pos, lab, k, v)
+        gc.plan_budget_evict(seq_d, ch.budget[0], ch.budget[1], max_ops, n_ops, *o, o_bits)
+        ops = oc.plan_budget(w.seq_ids, ch.budget[0], ch.budget[1], max_ops)
+        m = int(n_ops.item())
+        assert m == ops[0].size, f"op count step {s}"
+        for a, b in zip([x.cpu().numpy()[:m] for x in (*o, o_bits)], ops):
+            assert np.array_equal(a, b), f"ops step {s}"
+        if m:
+            oc.evict(*ops)
+            n_down += int((ops[3] == 2).sum()); n_ev += int((ops[3] == 0).sum())
+        if (s + 1) % 64 == 0:
+            say(f"[churn-1024] step {s + 1}: whole state ({n_ev} evictions, {n_down} downgrades so far)")
+            helpers.compare_states(L, gc.export(), oc.export(), f"churn-1024 after step {s + 1}")
+    assert gc.get_error() == oc.error()
+    assert n_ev > 0 and n_down > 0
