@@ -772,6 +772,47 @@ __device__ inline void finalize_head(const AttnParams& P, int b, int hq, int lan
   if (P.n_attended && hq == 0 && lane == 0) P.n_attended[b] = n;
 }
 
+// Merge the records of the NW waves of a work-group (LDS, [wave][head][RS]
+// floats from base, rstride floats apart): the merged scalars of this lane's
+// head, and the slices n = w, w + NW, ... of its accumulator.  Every record's
+// reads are issued before the sums, which run in wave order; a record with
+// no tokens (scale 0) adds zeros, so the sums equal those over the non-empty
+// records alone.
+template <int NW, int NT>
+__device__ inline void merge_waves(const float* base, int rstride, int w, int lg, float& m, float& Z, float& S2,
+                                   float& natt, float4_t (&a)[NT]) {
+  float mr[NW], zr[NW], sr[NW], nr[NW];
+#pragma unroll
+  for (int r = 0; r < NW; r++) {
+    const float4 x = *(const float4*)(base + r * rstride + NT * 16);
+    mr[r] = x.x; zr[r] = x.y; sr[r] = x.z; nr[r] = x.w;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < NW; r++) mx = nr[r] > 0.f ? fmaxf(mx, mr[r]) : mx;
+  float sc[NW];
+  Z = 0.f; S2 = 0.f; natt = 0.f;
+#pragma unroll
+  for (int r = 0; r < NW; r++) {
+    sc[r] = nr[r] > 0.f ? exp2f(mr[r] - mx) : 0.f;
+    Z = fmaf(sc[r], zr[r], Z);
+    S2 = nr[r] > 0.f ? fmaf(sc[r], sr[r] + (mr[r] - mx) * zr[r], S2) : S2;
+    natt += nr[r];
+  }
+  m = mx;
+#pragma unroll
+  for (int n = 0; n < NT; n++) {
+    if (n % NW != w) continue;
+    float4_t x[NW];
+#pragma unroll
+    for (int r = 0; r < NW; r++) x[r] = *(const float4_t*)(base + r * rstride + 16 * n + 4 * lg);
+    float4_t t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < NW; r++) t += sc[r] * x[r];
+    a[n] = t;
+  }
+}
+
 template <int D, int GS, bool WINDOW, int PK, int FMT>
 __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
   constexpr int NG = D / GS;
@@ -1025,35 +1066,9 @@ __global__ __launch_bounds__(512) void k_attn(AttnParams P) {
     lds_barrier();
     const float* base = lds + (int64_t)he * RS;
     const int rstride = G * RS;
-    float mr[8], zr[8], sr[8], nr[8];
-#pragma unroll
-    for (int r = 0; r < 8; r++) {
-      float4 x = make_float4(-INFINITY, 0.f, 0.f, 0.f);
-      if (r < nw) x = *(const float4*)(base + r * rstride + D);
-      mr[r] = x.x; zr[r] = x.y; sr[r] = x.z; nr[r] = x.w;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 8; r++) mx = nr[r] > 0.f ? fmaxf(mx, mr[r]) : mx;
-    float sc[8];
-    Z = 0.f; S2 = 0.f; natt = 0.f;
-#pragma unroll
-    for (int r = 0; r < 8; r++) {
-      sc[r] = nr[r] > 0.f ? exp2f(mr[r] - mx) : 0.f;
-      Z = fmaf(sc[r], zr[r], Z);
-      S2 = nr[r] > 0.f ? fmaf(sc[r], sr[r] + (mr[r] - mx) * zr[r], S2) : S2;
-      natt += nr[r];
-    }
-    m = mx;
-#pragma unroll
-    for (int n = 0; n < NT; n++) {
-      if (n % nw != w) continue;
-      float4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int r = 0; r < 8; r++)
-        if (sc[r] != 0.f) s += sc[r] * *(const float4_t*)(base + r * rstride + 16 * n + 4 * lg);
-      a[n] = s;
-    }
+    if (nw == 2) merge_waves<2, NT>(base, rstride, w, lg, m, Z, S2, natt, a);
+    else if (nw == 4) merge_waves<4, NT>(base, rstride, w, lg, m, Z, S2, natt, a);
+    else merge_waves<8, NT>(base, rstride, w, lg, m, Z, S2, natt, a);
     if (w == 0) {
       // lane group lg merges the lists of records lg, lg + 4; then across groups
 #pragma unroll
