@@ -716,7 +716,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=6)
     ap.add_argument("--split-steps", type=int, default=16, help="extra steps timed call by call")
-    ap.add_argument("--streams", type=int, choices=(1, 2), default=2,
+    ap.add_argument("--streams", type=int, choices=(1, 2, 3, 4), default=2,
                     help="decode batches in flight (state copies stepped on their own streams)")
     ap.add_argument("--copies", type=int, default=0, help="state copies (0 = enough for > 1 GiB)")
     ap.add_argument("--cpu-seqs", type=int, default=16)
