@@ -10,7 +10,11 @@ Default workload: the B256 eviction-churn decode loop (Hq32/Hkv8, D128, g64,
 starting lengths U{4k..32k}, 5% token budget, R/E/T 8/4/2-bit codes,
 planted-temperature queries), the largest configuration; --workload llama8b
 runs the same step on the Llama-8B-like layer (B32, 16k generated tokens, 10%
-budget).  Besides the step, the line carries:
+budget).  Two decode batches are in flight by default (--streams 2): copy j of
+the state is stepped on stream j with its own buffers, each attention launch
+waits for the previous step's attention, and one copy's state calls run beside
+the other copy's attention (--streams 1: every call in order on one stream).
+Besides the step, the line carries:
   - `configs`: the attention call alone on each static workload -- tiny (B1,
     G1, D64), llama8b (B32, G4, D128), qwen14b (B64, G5, ragged lengths,
     scattered block tables), gptoss20b (B128, G8, D64, sinks) with a 128-token
