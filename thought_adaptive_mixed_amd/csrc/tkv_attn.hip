@@ -619,20 +619,6 @@ __device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax
       st.vunit = u;
     }
   };
-  auto comp = [&](const B& b, int g) {
-    if (g < c1) {
-      compute_step<D, GS, 8, FMT, WINDOW, PK, P0>(b, mask_of(l0, n0, g, P0), lo_pos, lane, head_ok, qB, qk_lds, sumq,
-                                               alpha * u0, st);
-    } else if (g < c2) {
-      to_unit(u1);
-      compute_step<D, GS, 4, FMT, WINDOW, PK, P1>(b, mask_of(l1, n1, g - c1, P1), lo_pos, lane, head_ok, qB, qk_lds, sumq,
-                                               alpha * u1, st);
-    } else {
-      to_unit(u2);
-      compute_step<D, GS, 2, 0, WINDOW, PK, P2>(b, mask_of(l2, n2, g - c2, P2), lo_pos, lane, head_ok, qB, qk_lds, sumq,
-                                             alpha * u2, st);
-    }
-  };
   int g = w;
   if (g >= T) return;
   // The two waves of a SIMD compete for issue and the arbiter favours the
@@ -650,14 +636,44 @@ __device__ inline void run_steps(const AttnParams& P, const int2* live, int lmax
   B nxt;
   load(nxt, g);
   __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
+  // one loop per class (a wave's steps go through the classes in order), so
+  // that each loop body holds one compute path: the three paths in one body
+  // kept the union of their temporaries live and copied the accumulators at
+  // the back edge (253 VGPRs; one path per loop: 194)
 #pragma nounroll
-  while (true) {
+  while (g < c1) {
     const B cur = nxt;
     load(nxt, g + nw);
     __builtin_amdgcn_sched_barrier(0);
-    set_priority(); comp(cur, g); k++;
+    set_priority();
+    compute_step<D, GS, 8, FMT, WINDOW, PK, P0>(cur, mask_of(l0, n0, g, P0), lo_pos, lane, head_ok, qB, qk_lds, sumq,
+                                             alpha * u0, st);
+    k++;
     g += nw;
-    if (g >= T) break;
+  }
+  if (g < c2) to_unit(u1);
+#pragma nounroll
+  while (g < c2) {
+    const B cur = nxt;
+    load(nxt, g + nw);
+    __builtin_amdgcn_sched_barrier(0);
+    set_priority();
+    compute_step<D, GS, 4, FMT, WINDOW, PK, P1>(cur, mask_of(l1, n1, g - c1, P1), lo_pos, lane, head_ok, qB, qk_lds,
+                                             sumq, alpha * u1, st);
+    k++;
+    g += nw;
+  }
+  if (g < T) to_unit(u2);
+#pragma nounroll
+  while (g < T) {
+    const B cur = nxt;
+    load(nxt, g + nw);
+    __builtin_amdgcn_sched_barrier(0);
+    set_priority();
+    compute_step<D, GS, 2, 0, WINDOW, PK, P2>(cur, mask_of(l2, n2, g - c2, P2), lo_pos, lane, head_ok, qB, qk_lds, sumq,
+                                           alpha * u2, st);
+    k++;
+    g += nw;
   }
   __builtin_amdgcn_s_setprio(0);
 }
