@@ -5,6 +5,7 @@ positions, segments, error word) must match bit for bit; attention outputs
 within max-abs 2e-3 and relative L2 1e-3 over [B, Hq, D]; normalized entropy
 and top-k mass within 1e-4.
 """
+import os
 import sys
 
 import numpy as np
@@ -18,9 +19,23 @@ pytestmark = pytest.mark.gpu
 TOL_ABS, TOL_L2, TOL_STAT = 2e-3, 1e-3, 1e-4
 
 
+PROGRESS = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out",
+                        "gpu_test_progress.log")
+
+
 def say(*a):
-    print(*a, flush=True)
+    """A progress line of a long GPU test: to stdout (captured by pytest) and
+    appended to gpurun_out/gpu_test_progress.log, so that a run whose output
+    pytest holds back until a test ends still shows each step it finishes."""
+    line = " ".join(str(x) for x in a)
+    print(line, flush=True)
     sys.stdout.flush()
+    try:
+        os.makedirs(os.path.dirname(PROGRESS), exist_ok=True)
+        with open(PROGRESS, "a") as f:
+            f.write(line + "\n")
+    except OSError:
+        pass
 
 
 def gpu_attention(gc, seq_ids, q_pos, q, window=0, sinks=None, k_self=None, v_self=None, splits=0, topk=8,
