@@ -51,8 +51,8 @@ def test_kernel_timing_changes_nothing_and_names_every_kernel():
     helpers.compare_states(L, a.export(), b.export(), "timed vs untimed")
     times, dropped = a.kernel_times()
     assert dropped == 0
-    for name in ("k_attn", "k_combine", "k_append_alloc", "k_append_store", "k_plan_evict", "k_evict_apply",
-                 "k_requant"):
+    for name in ("k_attn", "k_combine", "k_append_alloc", "k_append_store", "k_plan", "k_evict_plan",
+                 "k_evict_apply", "k_requant"):
         assert name in times, (name, times)
         us, calls = times[name]
         assert calls == ch.steps and us > 0, (name, us, calls)

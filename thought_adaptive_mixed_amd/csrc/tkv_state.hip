@@ -1413,35 +1413,36 @@ __global__ __launch_bounds__(WG) void k_plan(DevState S, int n, const int32_t* s
   plan_body(S, n, seq_ids, num, den, max_ops, n_ops, os, og, ok, ob);
 }
 
-int launch_plan(tkv_cache* c, int n, const int32_t* seq_ids, int num, int den, int max_ops, int32_t* n_ops_dev,
-                int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st) {
-  // a wave per listed sequence, up to 16 waves
-  const int nt = n < 1 ? 64 : (n >= WG / 64 ? WG : 64 * n);
+// a wave per listed sequence, up to max_threads / 64 waves
+static int launch_plan_t(tkv_cache* c, int n, const int32_t* seq_ids, int num, int den, int max_ops,
+                         int32_t* n_ops_dev, int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits,
+                         int max_threads, hipStream_t st) {
+  const int nt = n < 1 ? 64 : (n >= max_threads / 64 ? max_threads : 64 * n);
   TKV_TIMED(c, st, "k_plan",
             k_plan<<<1, nt, 0, st>>>(c->S, n, seq_ids, num, den, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits));
   return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
 }
-
-// The ladder and the first part of the eviction in one work-group: the op
-// list the ladder writes (global memory) is read back by the same
-// work-group after a barrier.  Then the eviction's apply and re-quantization
-// kernels as in kv_evict_segment.
-__global__ __launch_bounds__(WG) void k_plan_evict(DevState S, int n, const int32_t* seq_ids, int num, int den,
-                                                   int max_ops, int32_t* n_ops, int32_t* os, int32_t* og,
-                                                   int32_t* ok, uint8_t* ob) {
-  plan_body(S, n, seq_ids, num, den, max_ops, n_ops, os, og, ok, ob);
-  __syncthreads();
-  evict_plan_body(S, max_ops, n_ops, os, og, ok, ob);
+int launch_plan(tkv_cache* c, int n, const int32_t* seq_ids, int num, int den, int max_ops, int32_t* n_ops_dev,
+                int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st) {
+  return launch_plan_t(c, n, seq_ids, num, den, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits, WG, st);
 }
+
+// The ladder, then the eviction's kernels (kv_evict_segment with the ladder's
+// device-side op count).  In a decode loop this call runs beside the next
+// batch's attention, which holds every compute unit's registers but for a
+// slot of about 112 VGPRs per SIMD lane and ~96 KB of LDS per compute unit:
+// a ladder work-group of at most 8 waves (32 VGPRs, 57 KB of LDS) and the
+// eviction's planning work-group (256 threads at B256, 47 VGPRs, 62 KB) fit
+// there and start at once, where one work-group doing both (1024 threads,
+// 120 KB of LDS; measured 5 us faster alone) waited for a compute unit the
+// attention had left entirely.
+#define PL_EVICT_THREADS 512
 int launch_plan_evict(tkv_cache* c, int n, const int32_t* seq_ids, int num, int den, int max_ops, int32_t* n_ops_dev,
                       int32_t* op_seq, int32_t* op_seg, int32_t* op_keep, uint8_t* op_bits, hipStream_t st) {
-  if (max_ops == 0) return launch_plan(c, n, seq_ids, num, den, 0, n_ops_dev, op_seq, op_seg, op_keep, op_bits, st);
-  TKV_TIMED(c, st, "k_plan_evict",
-            k_plan_evict<<<1, WG, 0, st>>>(c->S, n, seq_ids, num, den, max_ops, n_ops_dev, op_seq, op_seg, op_keep,
-                                           op_bits));
-  TKV_TIMED(c, st, "k_evict_apply", k_evict_apply<<<c->S.max_seqs, EV_THREADS, 0, st>>>(c->S));
-  launch_requant(c, st);
-  return hipGetLastError() == hipSuccess ? TKV_OK : TKV_EHIP;
+  const int r = launch_plan_t(c, n, seq_ids, num, den, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits,
+                              PL_EVICT_THREADS, st);
+  if (r != TKV_OK || max_ops == 0) return r;
+  return launch_evict(c, max_ops, n_ops_dev, op_seq, op_seg, op_keep, op_bits, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -1527,8 +1528,10 @@ __global__ __launch_bounds__(WG) void k_anneal(DevState S, int n, const int32_t*
                                                int32_t* n_ops, int32_t* os, int32_t* og, int32_t* ok, uint8_t* ob) {
   anneal_body(S, n, seq_ids, r0, max_ops, n_ops, os, og, ok, ob);
 }
-// The annealing plan and the first part of the eviction in one work-group
-// (as k_plan_evict for the budget ladder).
+// The annealing plan and the first part of the eviction in one work-group:
+// the op list the plan writes (global memory) is read back by the same
+// work-group after a barrier; then the eviction's apply and re-quantization
+// kernels as in kv_evict_segment.
 __global__ __launch_bounds__(WG) void k_anneal_evict(DevState S, int n, const int32_t* seq_ids, int r0, int max_ops,
                                                      int32_t* n_ops, int32_t* os, int32_t* og, int32_t* ok,
                                                      uint8_t* ob) {
